@@ -1,0 +1,211 @@
+/*
+ * smoe.h - C ABI of the scattered mixture-of-experts hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed.  A sparse mixture-of-experts (SMoE) layer sends every
+ * token t to k of E experts; assignment p = t*k + j is token t's j-th choice
+ * with expert e_p and gate g[t][j]; M = T*k.  The layer output is the
+ * gate-weighted sum of the chosen experts' outputs (article "This Machine
+ * Learning Research Presents ScatterMoE: An Implementation of Sparse
+ * Mixture-of-Experts (SMoE) on GPUs", body, para. 1).  ParallelLinear runs
+ * the expert linear transforms as one grouped product fused with the
+ * reordering of rows (ScatterMoE project page, "How It Works"; review page
+ * "Scattered Mixture-of-Experts Implementation", first review, Summary):
+ * its input and its output are each either GROUPED (M rows sorted by expert,
+ * ties in ascending p) or SCATTERED (token order), giving the four
+ * group/scatter-to-group/scatter combinations (same page, second review,
+ * Summary), with no padded or copied grouped input (catalogue record
+ * "Scattered Mixture-of-Experts Implementation", abstract).  The backward
+ * pass runs through the same machinery and yields per-expert weight
+ * gradients (article, para. 4).
+ *
+ * Conventions for every entry point.
+ *  - Pointers to tensors are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or synchronises; it only enqueues work
+ *    on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *  - Tensors are row-major.  Weights are [E, d_in, d_out]: y = x W[e].
+ *    Index arrays are int32; gates and gradients of gates are fp32 [T, k].
+ *  - `dtype` is SMOE_F32 or SMOE_BF16 and applies to x, weights, y, dx and
+ *    saved activations.  Weight gradients are always fp32.
+ *  - Feature sizes (d_in, d_out, d_model, d_ff) must be multiples of 8 and
+ *    rows must be 16-byte aligned; T*k must fit in int32.
+ *  - Scratch memory comes from the caller as (ws, ws_bytes); the matching
+ *    *_workspace_bytes() gives the size needed.
+ *  - Return value: SMOE_OK or an error status.  A failed host-side check
+ *    enqueues nothing.  A launch failure returns SMOE_ERR_HIP.  The text of
+ *    the last failure on the calling thread is smoe_last_error().
+ *  - Calls that share a workspace, or write the same outputs, must be
+ *    ordered on one stream by the caller.
+ */
+#ifndef SMOE_H
+#define SMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum smoe_status {
+  SMOE_OK = 0,
+  SMOE_ERR_NULL = 1,        /* a required pointer is NULL                  */
+  SMOE_ERR_SHAPE = 2,       /* sizes out of range or inconsistent          */
+  SMOE_ERR_DTYPE = 3,       /* unknown dtype or activation                 */
+  SMOE_ERR_WORKSPACE = 4,   /* ws/saved buffer smaller than required       */
+  SMOE_ERR_UNSUPPORTED = 5, /* valid request this build does not implement */
+  SMOE_ERR_HIP = 6          /* a HIP launch failed                         */
+};
+
+enum smoe_dtype { SMOE_F32 = 0, SMOE_BF16 = 1 };
+
+/* GELU: exact erf form, two matrices W1 -> act -> W2.
+ * SWIGLU: silu(x W1[e]) * (x W3[e]) -> W2. */
+enum smoe_act { SMOE_ACT_GELU = 0, SMOE_ACT_SWIGLU = 1 };
+
+/* Static description of a status code. */
+const char* smoe_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* smoe_last_error(void);
+/* ABI version of this library. */
+int smoe_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * smoe_route - routing indices from the top-k expert choices.
+ *
+ * Implements the reordering that ParallelLinear fuses with the expert
+ * transforms (project page, "How It Works").  With e_p = expert_idxs[p]:
+ *   counts[e]   = #{p : e_p = e}
+ *   offsets[e]  = sum_{e' < e} counts[e'],  offsets[E] = number of valid p
+ *   sorted_scattered_idxs[r] = the p at grouped row r, rows sorted by
+ *                  (e_p, p) ascending (a stable sort; bit-exact)
+ *   sorted_expert_idxs[r]    = e_p of that row
+ * expert_idxs: [T, k] int32.  Outputs: [T*k], [T*k], [E], [E+1] int32.
+ * 1 <= E <= 1024, 1 <= k.  Choices outside [0, E) are dropped (never
+ * written); offsets[E] < T*k then tells the caller.  Rows past offsets[E]
+ * of the sorted arrays are left untouched.
+ * ------------------------------------------------------------------------ */
+size_t smoe_route_workspace_bytes(int64_t T, int32_t k, int32_t E);
+int smoe_route(const int32_t* expert_idxs, int64_t T, int32_t k, int32_t E,
+               int32_t* sorted_expert_idxs, int32_t* sorted_scattered_idxs,
+               int32_t* counts, int32_t* offsets,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * smoe_parallel_linear_fwd - scatter2scatter forward (all four layouts).
+ *
+ * For every grouped row r (expert e, assignment p = sorted_scattered_idxs[r]):
+ *   u_r = x_grouped ? x[r] : x[p / fan]     fan = k if x_rows == T, else 1
+ *   v_r = u_r W[e]
+ * Without gates: y is [T*k, d_out]; row r if y_grouped, row p otherwise.
+ * With gates (y_grouped must be 0): y is [T, d_out] and
+ *   y[t] = sum_j gates[t][j] v_(row of t*k+j)     (fp32 combine)
+ * x: [x_rows, d_in], x_rows = T*k if x_grouped, else T or T*k.
+ * w: [E, d_in, d_out].  Routing arrays as produced by smoe_route.
+ * Review page, first and second review, Summary; article, para. 3-4.
+ * ------------------------------------------------------------------------ */
+size_t smoe_parallel_linear_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
+                                                int64_t d_in, int64_t d_out,
+                                                int32_t with_gates, int32_t dtype);
+int smoe_parallel_linear_fwd(const void* x, int64_t x_rows, int64_t d_in,
+                             const void* w, int64_t d_out, int32_t E,
+                             int64_t T, int32_t k,
+                             const int32_t* sorted_scattered_idxs,
+                             const int32_t* offsets,
+                             int32_t x_grouped, int32_t y_grouped,
+                             const float* gates, void* y, int32_t dtype,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * smoe_parallel_linear_bwd - backward of smoe_parallel_linear_fwd.
+ *
+ * dy has the forward output's shape.  Per grouped row r (expert e, p, t):
+ *   dy_r = gates ? gates[t][j] * dy[t] : dy[row of r]
+ *   dx[input row of r] += dy_r W[e]^T   (k contributions summed, fp32,
+ *                                        when a T-row x was read k times)
+ *   dw[e]   = sum_r u_r^T dy_r          (fp32; experts with no rows get 0)
+ *   dgates[t][j] = <dy[t], u_r W[e]>    (only with gates)
+ * Any of dx, dw, dgates may be NULL to skip it (dgates needs gates).
+ * In bf16 runs dy_r with gates enters the dw contraction as bf16.
+ * Same page, first review, Summary (forward and backward through
+ * ParallelLinear); article, para. 4 (per-expert gradients).
+ * ------------------------------------------------------------------------ */
+size_t smoe_parallel_linear_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
+                                                int64_t x_rows, int64_t d_in,
+                                                int64_t d_out, int32_t x_grouped,
+                                                int32_t with_gates, int32_t dtype);
+int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in,
+                             const void* w, int64_t d_out, int32_t E,
+                             int64_t T, int32_t k,
+                             const int32_t* sorted_scattered_idxs,
+                             const int32_t* offsets,
+                             int32_t x_grouped, int32_t y_grouped,
+                             const float* gates, const void* dy,
+                             void* dx, float* dw, float* dgates, int32_t dtype,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * smoe_mlp_fwd - SMoE-MLP block: route, W1 (and W3) with the activation
+ * fused, W2 with scattered output, gate-weighted combine.
+ *
+ *   out[t] = sum_j gates[t][j] * MLP_e(x[t]),
+ *   GELU:   MLP_e(x) = gelu(x W1[e]) W2[e]
+ *   SWIGLU: MLP_e(x) = (silu(x W1[e]) * (x W3[e])) W2[e]
+ * x: [T, d_model]; w1, w3: [E, d_model, d_ff]; w2: [E, d_ff, d_model];
+ * w3 must be NULL unless SWIGLU.  expert_idxs, gates: [T, k].
+ * out: [T, d_model].  `saved` (size smoe_mlp_saved_bytes) receives what the
+ * backward needs; its layout is given by smoe_mlp_saved_offsets.
+ * In bf16 runs the grouped intermediates h (h1, h3) and a are stored in
+ * bf16; a is computed from the stored h; expert outputs and the combine
+ * stay fp32 until the final rounding of out.
+ * Article, para. 1 and 5 (SMoE MLP); project page, "How It Works".
+ * ------------------------------------------------------------------------ */
+size_t smoe_mlp_saved_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model,
+                            int64_t d_ff, int32_t act, int32_t dtype);
+/* Byte offsets inside `saved`: off[0] sorted_expert_idxs, off[1]
+ * sorted_scattered_idxs, off[2] counts, off[3] offsets, off[4] h (h1),
+ * off[5] h3 (SIZE_MAX unless SWIGLU), off[6] a.  Returns SMOE_OK. */
+int smoe_mlp_saved_offsets(int64_t T, int32_t k, int32_t E, int64_t d_model,
+                           int64_t d_ff, int32_t act, int32_t dtype, size_t off[7]);
+size_t smoe_mlp_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
+                                    int64_t d_model, int64_t d_ff, int32_t act,
+                                    int32_t dtype);
+int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2,
+                 int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                 const int32_t* expert_idxs, const float* gates,
+                 int32_t act, int32_t dtype, void* out,
+                 void* saved, size_t saved_bytes,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * smoe_mlp_bwd - backward of smoe_mlp_fwd for upstream dout [T, d_model].
+ *
+ * Per assignment (token t, choice j, expert e, gate g), with a = act(h):
+ *   dgates[t][j] = <dout[t], a W2[e]>
+ *   dA = g * dout[t] W2[e]^T
+ *   GELU:   dh = dA * gelu'(h)
+ *   SWIGLU: dh1 = dA * h3 * silu'(h1);  dh3 = dA * silu(h1)
+ *   dx[t] += dh W1[e]^T (+ dh3 W3[e]^T)            (fp32 k-sum)
+ *   dw2[e] += a^T (g dout[t]);  dw1[e] += x[t]^T dh;  dw3[e] += x[t]^T dh3
+ * Weight gradients are fp32 and fully written (experts with no tokens get
+ * 0).  dw3 must be NULL unless SWIGLU.  dgates may be NULL.  `saved` is the
+ * buffer filled by smoe_mlp_fwd with the same arguments.  In bf16 runs
+ * dh (dh1, dh3) and g*dout are rounded to bf16 before they enter the
+ * weight-gradient and dx contractions.
+ * ------------------------------------------------------------------------ */
+size_t smoe_mlp_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
+                                    int64_t d_model, int64_t d_ff, int32_t act,
+                                    int32_t dtype);
+int smoe_mlp_bwd(const void* dout, const void* x, const void* w1,
+                 const void* w3, const void* w2,
+                 int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                 const int32_t* expert_idxs, const float* gates,
+                 int32_t act, int32_t dtype,
+                 const void* saved, size_t saved_bytes,
+                 void* dx, float* dw1, float* dw3, float* dw2, float* dgates,
+                 void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SMOE_H */

@@ -1,0 +1,244 @@
+"""Python binding of libsmoe.so, the C-ABI scattered mixture-of-experts
+library for MI355X (gfx950).
+
+Argument marshalling only: torch supplies device memory (outputs, workspaces)
+and the current stream; every step of the computation runs in the library's
+HIP kernels.  The function names are the C entry points' names.  Importing
+this package fails loudly when the library has not been built.
+
+Layouts follow include/smoe.h: x [rows, d], weights [E, d_in, d_out],
+expert choices and gates [T, k], assignment p = t*k + j.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, Optional
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "SmoeError", "lib", "smoe_route", "smoe_parallel_linear_fwd",
+    "smoe_parallel_linear_bwd", "smoe_mlp_fwd", "smoe_mlp_bwd", "saved_views",
+    "header_functions", "F32", "BF16", "ACT_GELU", "ACT_SWIGLU",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsmoe.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "smoe.h")
+
+F32, BF16 = 0, 1
+ACT_GELU, ACT_SWIGLU = 0, 1
+_ACTS = {"gelu": ACT_GELU, "swiglu": ACT_SWIGLU}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m sparse_mixture_experts_top_amd.build` (hipcc, gfx950)")
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_SIGS = {
+    "smoe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "smoe_last_error": (ctypes.c_char_p, []),
+    "smoe_abi_version": (ctypes.c_int, []),
+    "smoe_route_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "smoe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "smoe_parallel_linear_fwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
+    "smoe_parallel_linear_fwd": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i32, _i64, _i32, _vp, _vp,
+                                                _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "smoe_parallel_linear_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32]),
+    "smoe_parallel_linear_bwd": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i32, _i64, _i32, _vp, _vp,
+                                                _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "smoe_mlp_saved_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
+    "smoe_mlp_saved_offsets": (ctypes.c_int, [_i64, _i32, _i32, _i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
+    "smoe_mlp_fwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
+    "smoe_mlp_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32, _i32,
+                                    _vp, _vp, _sz, _vp, _sz, _vp]),
+    "smoe_mlp_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
+    "smoe_mlp_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32,
+                                    _i32, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def header_functions():
+    """Names of the functions declared in include/smoe.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(smoe_\w+)\s*\(", text, re.M)))
+
+
+class SmoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib.smoe_last_error().decode() or lib.smoe_status_string(status).decode()
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SmoeError(status, where)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# --------------------------------------------------------------------------
+def smoe_route(expert_idxs: torch.Tensor, E: int) -> Dict[str, torch.Tensor]:
+    """Routing indices of expert_idxs [T, k] (int32, on the GPU)."""
+    _contig(expert_idxs)
+    T, k = expert_idxs.shape
+    dev = expert_idxs.device
+    M = T * k
+    out = {
+        "sorted_expert_idxs": torch.empty(M, dtype=torch.int32, device=dev),
+        "sorted_scattered_idxs": torch.empty(M, dtype=torch.int32, device=dev),
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+    }
+    ws = _ws(lib.smoe_route_workspace_bytes(T, k, E), dev)
+    _check(lib.smoe_route(_p(expert_idxs), T, k, E, _p(out["sorted_expert_idxs"]),
+                          _p(out["sorted_scattered_idxs"]), _p(out["counts"]), _p(out["offsets"]),
+                          _p(ws), ws.numel(), _stream(dev)), "smoe_route")
+    return out
+
+
+def smoe_parallel_linear_fwd(x, w, T, k, sorted_scattered_idxs, offsets, x_grouped: bool,
+                             y_grouped: bool, gates=None):
+    """scatter2scatter forward; returns y ([T*k, d_out], or [T, d_out] with gates)."""
+    _contig(x, w, sorted_scattered_idxs, offsets, gates)
+    E, d_in, d_out = w.shape
+    dev = x.device
+    dt = _dtype_code(x)
+    y = torch.empty((T if gates is not None else T * k, d_out), dtype=x.dtype, device=dev)
+    ws = _ws(lib.smoe_parallel_linear_fwd_workspace_bytes(T, k, E, d_in, d_out, int(gates is not None), dt), dev)
+    _check(lib.smoe_parallel_linear_fwd(_p(x), x.shape[0], d_in, _p(w), d_out, E, T, k,
+                                        _p(sorted_scattered_idxs), _p(offsets), int(x_grouped),
+                                        int(y_grouped), _p(gates), _p(y), dt, _p(ws), ws.numel(),
+                                        _stream(dev)), "smoe_parallel_linear_fwd")
+    return y
+
+
+def smoe_parallel_linear_bwd(x, w, T, k, sorted_scattered_idxs, offsets, x_grouped: bool,
+                             y_grouped: bool, dy, gates=None, need_dx=True, need_dw=True,
+                             need_dgates=False):
+    """Backward of smoe_parallel_linear_fwd; returns (dx, dw fp32, dgates fp32)."""
+    _contig(x, w, dy, sorted_scattered_idxs, offsets, gates)
+    E, d_in, d_out = w.shape
+    dev = x.device
+    dt = _dtype_code(x)
+    dx = torch.empty_like(x) if need_dx else None
+    dw = torch.empty((E, d_in, d_out), dtype=torch.float32, device=dev) if need_dw else None
+    dg = torch.empty((T, k), dtype=torch.float32, device=dev) if need_dgates else None
+    ws = _ws(lib.smoe_parallel_linear_bwd_workspace_bytes(T, k, E, x.shape[0], d_in, d_out, int(x_grouped),
+                                                          int(gates is not None), dt), dev)
+    _check(lib.smoe_parallel_linear_bwd(_p(x), x.shape[0], d_in, _p(w), d_out, E, T, k,
+                                        _p(sorted_scattered_idxs), _p(offsets), int(x_grouped),
+                                        int(y_grouped), _p(gates), _p(dy), _p(dx), _p(dw), _p(dg), dt,
+                                        _p(ws), ws.numel(), _stream(dev)), "smoe_parallel_linear_bwd")
+    return dx, dw, dg
+
+
+def _mlp_dims(x, w1, w2, expert_idxs):
+    T, d_model = x.shape
+    E, _, d_ff = w1.shape
+    k = expert_idxs.shape[1]
+    return T, d_model, d_ff, E, k
+
+
+def smoe_mlp_fwd(x, w1, w2, expert_idxs, gates, act: str, w3=None, ws=None):
+    """SMoE-MLP forward; returns (out [T, d_model], saved buffer)."""
+    _contig(x, w1, w2, w3, expert_idxs, gates)
+    T, d_model, d_ff, E, k = _mlp_dims(x, w1, w2, expert_idxs)
+    dev = x.device
+    dt = _dtype_code(x)
+    a = _ACTS[act]
+    out = torch.empty((T, d_model), dtype=x.dtype, device=dev)
+    saved = _ws(lib.smoe_mlp_saved_bytes(T, k, E, d_model, d_ff, a, dt), dev)
+    need = lib.smoe_mlp_fwd_workspace_bytes(T, k, E, d_model, d_ff, a, dt)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(lib.smoe_mlp_fwd(_p(x), _p(w1), _p(w3), _p(w2), T, d_model, d_ff, E, k, _p(expert_idxs),
+                            _p(gates), a, dt, _p(out), _p(saved), saved.numel(), _p(ws), ws.numel(),
+                            _stream(dev)), "smoe_mlp_fwd")
+    return out, saved
+
+
+def smoe_mlp_bwd(dout, x, w1, w2, expert_idxs, gates, act: str, saved, w3=None, ws=None,
+                 need_dgates=True):
+    """SMoE-MLP backward; returns dict dx, dw1, dw2, dw3 (fp32), dgates."""
+    _contig(dout, x, w1, w2, w3, expert_idxs, gates, saved)
+    T, d_model, d_ff, E, k = _mlp_dims(x, w1, w2, expert_idxs)
+    dev = x.device
+    dt = _dtype_code(x)
+    a = _ACTS[act]
+    dx = torch.empty_like(x)
+    dw1 = torch.empty(w1.shape, dtype=torch.float32, device=dev)
+    dw2 = torch.empty(w2.shape, dtype=torch.float32, device=dev)
+    dw3 = torch.empty(w1.shape, dtype=torch.float32, device=dev) if w3 is not None else None
+    dg = torch.empty((T, k), dtype=torch.float32, device=dev) if need_dgates else None
+    need = lib.smoe_mlp_bwd_workspace_bytes(T, k, E, d_model, d_ff, a, dt)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(lib.smoe_mlp_bwd(_p(dout), _p(x), _p(w1), _p(w3), _p(w2), T, d_model, d_ff, E, k,
+                            _p(expert_idxs), _p(gates), a, dt, _p(saved), saved.numel(), _p(dx), _p(dw1),
+                            _p(dw3), _p(dw2), _p(dg), _p(ws), ws.numel(), _stream(dev)), "smoe_mlp_bwd")
+    return {"dx": dx, "dw1": dw1, "dw2": dw2, "dw3": dw3, "dgates": dg}
+
+
+def workspace_bytes(kind: str, **kw) -> int:
+    """Bytes of scratch the named entry point needs (for callers that keep
+    one workspace across calls)."""
+    f = getattr(lib, f"smoe_{kind}_workspace_bytes")
+    return int(f(*kw.values()))
+
+
+def saved_views(saved: torch.Tensor, T: int, k: int, E: int, d_model: int, d_ff: int, act: str,
+                dtype: torch.dtype) -> Dict[str, torch.Tensor]:
+    """Views into the `saved` buffer of smoe_mlp_fwd (routing arrays, h, a)."""
+    off = (ctypes.c_size_t * 7)()
+    dt = BF16 if dtype == torch.bfloat16 else F32
+    _check(lib.smoe_mlp_saved_offsets(T, k, E, d_model, d_ff, _ACTS[act], dt, off), "smoe_mlp_saved_offsets")
+    M = T * k
+    es = 2 if dt == BF16 else 4
+
+    def view(o, n, tdt, nbytes):
+        return saved[o:o + nbytes].view(tdt)[:n]
+
+    v = {
+        "sorted_expert_idxs": view(off[0], M, torch.int32, M * 4),
+        "sorted_scattered_idxs": view(off[1], M, torch.int32, M * 4),
+        "counts": view(off[2], E, torch.int32, E * 4),
+        "offsets": view(off[3], E + 1, torch.int32, (E + 1) * 4),
+        "h": view(off[4], M * d_ff, dtype, M * d_ff * es).view(M, d_ff),
+        "a": view(off[6], M * d_ff, dtype, M * d_ff * es).view(M, d_ff),
+    }
+    if act == "swiglu":
+        v["h3"] = view(off[5], M * d_ff, dtype, M * d_ff * es).view(M, d_ff)
+    return v

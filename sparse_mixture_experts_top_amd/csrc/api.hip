@@ -1,0 +1,668 @@
+// C ABI of the scattered mixture-of-experts hot path (declared in
+// include/smoe.h): host-side validation, workspace layout and the
+// launch sequence of each entry point.  Nothing here allocates,
+// synchronises or copies device memory; everything is enqueued on the
+// caller's stream.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "smoe.h"
+
+using namespace smoe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SMOE_OK;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(SMOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures, so the *_workspace_bytes functions replay the exact layout.
+struct Arena {
+  char* base;
+  size_t used = 0;
+  explicit Arena(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    used = (used + kAlign - 1) / kAlign * kAlign;
+    void* p = base ? base + used : nullptr;
+    used += std::max<size_t>(bytes, 1);
+    return p;
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t esize(int dtype) { return dtype == SMOE_BF16 ? 2 : 4; }
+
+int check_common(int64_t T, int32_t k, int32_t E, int32_t dtype) {
+  if (dtype != SMOE_F32 && dtype != SMOE_BF16) return fail(SMOE_ERR_DTYPE, "dtype %d is not SMOE_F32/SMOE_BF16", dtype);
+  if (E < 1 || E > kMaxExperts) return fail(SMOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxExperts);
+  if (k < 1) return fail(SMOE_ERR_SHAPE, "k=%d < 1", k);
+  if (T < 0) return fail(SMOE_ERR_SHAPE, "T=%lld < 0", (long long)T);
+  if (T * int64_t(k) > INT32_MAX / 2) return fail(SMOE_ERR_SHAPE, "T*k=%lld too large", (long long)(T * k));
+  return SMOE_OK;
+}
+
+int check_dim(int64_t d, const char* name) {
+  if (d < 8 || d % 8 != 0 || d > (int64_t(1) << 24))
+    return fail(SMOE_ERR_SHAPE, "%s=%lld must be a positive multiple of 8", name, (long long)d);
+  return SMOE_OK;
+}
+
+#define SMOE_TRY(x)            \
+  do {                         \
+    int _s = (x);              \
+    if (_s != SMOE_OK) return _s; \
+  } while (0)
+
+#define SMOE_HIP(x, where)                              \
+  do {                                                  \
+    hipError_t _e = (x);                                \
+    if (_e != hipSuccess) return hip_status(_e, where); \
+  } while (0)
+
+int need_ptr(const void* p, const char* name) {
+  if (!p) return fail(SMOE_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(SMOE_ERR_SHAPE, "%s is not 16-byte aligned", name);
+  return SMOE_OK;
+}
+
+GemmArgs blank_args(const int* offsets, const int* sidx, int E, int M) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.offsets = offsets;
+  a.sidx = sidx;
+  a.E = E;
+  a.M = M;
+  a.a_fan = a.b_fan = a.aux_fan = 1;
+  return a;
+}
+
+// ---- workspace layouts ------------------------------------------------------
+struct PlFwdWs {
+  float* pairs = nullptr;
+};
+void layout_pl_fwd(Arena& ar, int64_t M, int64_t d_out, bool with_gates, PlFwdWs& w) {
+  if (with_gates) w.pairs = static_cast<float*>(ar.take(size_t(M) * d_out * 4));
+}
+
+// Upper bound of split-K partial bytes for a weight-gradient product.
+size_t dw_partial_bytes(int64_t M, int E, int64_t Mo, int64_t N, int bf16) {
+  GemmArgs a = blank_args(nullptr, nullptr, E, int(M));
+  a.Mo = int(Mo);
+  a.N = int(N);
+  GemmPlan pl;
+  plan_gemm(a, pl, SEG_K, EPI_PARTIAL, 0, bf16, 1);
+  return size_t(a.mt_ub) * size_t(Mo) * size_t(N) * 4;
+}
+
+int dg_slots(int64_t M, int E, int64_t N, int bf16) {
+  GemmArgs a = blank_args(nullptr, nullptr, E, int(M));
+  a.N = int(N);
+  GemmPlan pl;
+  plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, 1);
+  return pl.slots;
+}
+
+struct PlBwdWs {
+  float* pairs = nullptr;    // dx contributions [M, d_in] when x was read k times
+  float* dgpart = nullptr;   // [slots, M]
+  float* partial = nullptr;  // dw split-K partials
+};
+void layout_pl_bwd(Arena& ar, int64_t T, int k, int E, int64_t x_rows, int64_t d_in, int64_t d_out, bool x_grouped,
+                   bool with_gates, int bf16, PlBwdWs& w) {
+  const int64_t M = T * k;
+  const bool fan_k = !x_grouped && x_rows == T && k > 1;
+  if (fan_k) w.pairs = static_cast<float*>(ar.take(size_t(M) * d_in * 4));
+  if (with_gates) w.dgpart = static_cast<float*>(ar.take(size_t(dg_slots(M, E, d_in, bf16)) * M * 4));
+  w.partial = static_cast<float*>(ar.take(dw_partial_bytes(M, E, d_in, d_out, bf16)));
+}
+
+struct SavedLayout {
+  size_t off[7];
+  size_t total;
+};
+SavedLayout saved_layout(int64_t T, int k, int E, int64_t d_ff, int act, int dtype) {
+  const int64_t M = T * k;
+  Arena ar(nullptr);
+  SavedLayout s;
+  auto at = [&](size_t bytes) {
+    ar.take(bytes);
+    return ar.used - std::max<size_t>(bytes, 1);
+  };
+  s.off[0] = at(size_t(M) * 4);
+  s.off[1] = at(size_t(M) * 4);
+  s.off[2] = at(size_t(E) * 4);
+  s.off[3] = at(size_t(E + 1) * 4);
+  s.off[4] = at(size_t(M) * d_ff * esize(dtype));
+  s.off[5] = act == SMOE_ACT_SWIGLU ? at(size_t(M) * d_ff * esize(dtype)) : SIZE_MAX;
+  s.off[6] = at(size_t(M) * d_ff * esize(dtype));
+  s.total = ar.used;
+  return s;
+}
+
+struct MlpFwdWs {
+  void* route = nullptr;
+  float* pairs = nullptr;
+};
+void layout_mlp_fwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, MlpFwdWs& w) {
+  const int64_t M = T * k;
+  w.route = ar.take(route_ws_bytes(M, E));
+  w.pairs = static_cast<float*>(ar.take(size_t(M) * d_model * 4));
+}
+
+struct MlpBwdWs {
+  float* dgpart = nullptr;
+  void* dh1 = nullptr;
+  void* dh3 = nullptr;
+  float* pairs = nullptr;
+  float* partial = nullptr;
+};
+void layout_mlp_bwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t d_ff, int act, int dtype,
+                    MlpBwdWs& w) {
+  const int64_t M = T * k;
+  const int bf16 = dtype == SMOE_BF16;
+  w.dgpart = static_cast<float*>(ar.take(size_t(dg_slots(M, E, d_ff, bf16)) * M * 4));
+  w.dh1 = ar.take(size_t(M) * d_ff * esize(dtype));
+  if (act == SMOE_ACT_SWIGLU) w.dh3 = ar.take(size_t(M) * d_ff * esize(dtype));
+  w.pairs = static_cast<float*>(ar.take(size_t(M) * d_model * 4));
+  const size_t p1 = dw_partial_bytes(M, E, d_ff, d_model, bf16);
+  const size_t p2 = dw_partial_bytes(M, E, d_model, d_ff, bf16);
+  w.partial = static_cast<float*>(ar.take(std::max(p1, p2)));
+}
+
+// Weight gradient dw[e] = sum over e's rows of A(r)^T B(r): GEMM + reduction.
+int run_dw(GemmArgs a, int bf16, float* dw, float* partial, hipStream_t st, const char* where) {
+  a.c0 = dw;
+  a.partial = partial;
+  GemmPlan pl;
+  plan_gemm(a, pl, SEG_K, EPI_PARTIAL, 0, bf16, 1);
+  SMOE_HIP(launch_gemm(a, pl, st), where);
+  SMOE_HIP(launch_reduce_dw(partial, a.offsets, a.E, a.KS, int64_t(a.Mo) * a.N, dw, st), where);
+  return SMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* smoe_status_string(int status) {
+  switch (status) {
+    case SMOE_OK: return "ok";
+    case SMOE_ERR_NULL: return "a required pointer is NULL";
+    case SMOE_ERR_SHAPE: return "sizes out of range, inconsistent or misaligned";
+    case SMOE_ERR_DTYPE: return "unknown dtype or activation";
+    case SMOE_ERR_WORKSPACE: return "workspace or saved buffer too small";
+    case SMOE_ERR_UNSUPPORTED: return "request not supported by this build";
+    case SMOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* smoe_last_error(void) { return g_last_error.c_str(); }
+
+int smoe_abi_version(void) { return 1; }
+
+// ---------------------------------------------------------------- route --
+size_t smoe_route_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return route_ws_bytes(T * k, E);
+}
+
+int smoe_route(const int32_t* expert_idxs, int64_t T, int32_t k, int32_t E, int32_t* sorted_expert_idxs,
+               int32_t* sorted_scattered_idxs, int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes,
+               void* stream) {
+  SMOE_TRY(check_common(T, k, E, SMOE_F32));
+  const int64_t M = T * k;
+  if (M > 0 && (!expert_idxs || !sorted_expert_idxs || !sorted_scattered_idxs))
+    return fail(SMOE_ERR_NULL, "routing arrays must not be NULL");
+  if (!counts || !offsets || !ws) return fail(SMOE_ERR_NULL, "counts/offsets/ws must not be NULL");
+  if (ws_bytes < route_ws_bytes(M, E))
+    return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, route_ws_bytes(M, E));
+  SMOE_HIP(launch_route(expert_idxs, int(M), E, sorted_expert_idxs, sorted_scattered_idxs, counts, offsets, ws,
+                        static_cast<hipStream_t>(stream)),
+           "smoe_route");
+  return ok();
+}
+
+// ------------------------------------------------------ parallel linear --
+size_t smoe_parallel_linear_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_in, int64_t d_out,
+                                                int32_t with_gates, int32_t dtype) {
+  (void)E; (void)d_in; (void)dtype;
+  Arena ar(nullptr);
+  PlFwdWs w;
+  layout_pl_fwd(ar, T * k, d_out, with_gates != 0, w);
+  return ar.used;
+}
+
+int smoe_parallel_linear_fwd(const void* x, int64_t x_rows, int64_t d_in, const void* w, int64_t d_out, int32_t E,
+                             int64_t T, int32_t k, const int32_t* sorted_scattered_idxs, const int32_t* offsets,
+                             int32_t x_grouped, int32_t y_grouped, const float* gates, void* y, int32_t dtype,
+                             void* ws, size_t ws_bytes, void* stream) {
+  SMOE_TRY(check_common(T, k, E, dtype));
+  SMOE_TRY(check_dim(d_in, "d_in"));
+  SMOE_TRY(check_dim(d_out, "d_out"));
+  const int64_t M = T * k;
+  if (x_grouped ? x_rows != M : (x_rows != T && x_rows != M))
+    return fail(SMOE_ERR_SHAPE, "x_rows=%lld does not fit the layout (T=%lld, T*k=%lld)", (long long)x_rows,
+                (long long)T, (long long)M);
+  if (gates && y_grouped) return fail(SMOE_ERR_SHAPE, "the gate-weighted combine needs a scattered output");
+  SMOE_TRY(need_ptr(w, "w"));
+  SMOE_TRY(need_ptr(offsets, "offsets"));
+  if (M > 0) {
+    SMOE_TRY(need_ptr(x, "x"));
+    SMOE_TRY(need_ptr(y, "y"));
+    SMOE_TRY(need_ptr(sorted_scattered_idxs, "sorted_scattered_idxs"));
+  }
+  Arena ar(ws);
+  PlFwdWs wl;
+  layout_pl_fwd(ar, M, d_out, gates != nullptr, wl);
+  if (gates && (!ws || ws_bytes < ar.used))
+    return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, ar.used);
+  if (M == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int bf16 = dtype == SMOE_BF16;
+  GemmArgs a = blank_args(offsets, sorted_scattered_idxs, E, int(M));
+  a.N = int(d_out);
+  a.K = a.K0 = int(d_in);
+  a.a0 = a.a1 = x;
+  a.lda = d_in;
+  a.a_scat = !x_grouped;
+  a.a_fan = (!x_grouped && x_rows == T) ? k : 1;
+  a.b0 = a.b1 = w;
+  a.b_nk = 0;
+  a.ldb = d_out;
+  a.b_es = d_in * d_out;
+  a.ldc = d_out;
+  GemmPlan pl;
+  if (gates) {
+    a.c0 = wl.pairs;
+    a.c_scat = 1;
+    plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, 1);
+    SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_fwd gemm");
+    SMOE_HIP(launch_combine(wl.pairs, gates, T, k, d_out, y, bf16, st), "parallel_linear_fwd combine");
+  } else {
+    a.c0 = y;
+    a.c_scat = !y_grouped;
+    plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, !bf16);
+    SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_fwd gemm");
+  }
+  return ok();
+}
+
+size_t smoe_parallel_linear_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t x_rows, int64_t d_in,
+                                                int64_t d_out, int32_t x_grouped, int32_t with_gates,
+                                                int32_t dtype) {
+  Arena ar(nullptr);
+  PlBwdWs w;
+  layout_pl_bwd(ar, T, k, E, x_rows, d_in, d_out, x_grouped != 0, with_gates != 0, dtype == SMOE_BF16, w);
+  return ar.used;
+}
+
+int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in, const void* w, int64_t d_out, int32_t E,
+                             int64_t T, int32_t k, const int32_t* sorted_scattered_idxs, const int32_t* offsets,
+                             int32_t x_grouped, int32_t y_grouped, const float* gates, const void* dy, void* dx,
+                             float* dw, float* dgates, int32_t dtype, void* ws, size_t ws_bytes, void* stream) {
+  SMOE_TRY(check_common(T, k, E, dtype));
+  SMOE_TRY(check_dim(d_in, "d_in"));
+  SMOE_TRY(check_dim(d_out, "d_out"));
+  const int64_t M = T * k;
+  if (x_grouped ? x_rows != M : (x_rows != T && x_rows != M))
+    return fail(SMOE_ERR_SHAPE, "x_rows=%lld does not fit the layout", (long long)x_rows);
+  if (gates && y_grouped) return fail(SMOE_ERR_SHAPE, "the gate-weighted combine needs a scattered output");
+  if (dgates && !gates) return fail(SMOE_ERR_NULL, "dgates needs gates");
+  SMOE_TRY(need_ptr(w, "w"));
+  SMOE_TRY(need_ptr(offsets, "offsets"));
+  if (dx) SMOE_TRY(need_ptr(dx, "dx"));
+  if (dw) SMOE_TRY(need_ptr(dw, "dw"));
+  if (M > 0) {
+    SMOE_TRY(need_ptr(x, "x"));
+    SMOE_TRY(need_ptr(dy, "dy"));
+    SMOE_TRY(need_ptr(sorted_scattered_idxs, "sorted_scattered_idxs"));
+  }
+  Arena ar(ws);
+  PlBwdWs wl;
+  const int bf16 = dtype == SMOE_BF16;
+  layout_pl_bwd(ar, T, k, E, x_rows, d_in, d_out, x_grouped != 0, gates != nullptr, bf16, wl);
+  if (!ws || ws_bytes < ar.used) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, ar.used);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int fan = (!x_grouped && x_rows == T) ? k : 1;
+  const bool fan_k = fan > 1;
+
+  if (M == 0) {
+    if (dw) SMOE_HIP(launch_zero(dw, size_t(E) * d_in * d_out * 4, st), "parallel_linear_bwd");
+    return ok();
+  }
+  // dx (and the gate gradient): dy rows against W^T
+  if (dx || dgates) {
+    GemmArgs a = blank_args(offsets, sorted_scattered_idxs, E, int(M));
+    a.N = int(d_in);
+    a.K = a.K0 = int(d_out);
+    a.a0 = a.a1 = dy;
+    a.lda = d_out;
+    a.a_scat = gates ? 1 : !y_grouped;
+    a.a_fan = gates ? k : 1;
+    a.b0 = a.b1 = w;
+    a.b_nk = 1;
+    a.ldb = d_out;
+    a.b_es = d_in * d_out;
+    a.gate = gates;
+    a.ldc = d_in;
+    if (dgates) {
+      a.dgpart = wl.dgpart;
+      a.aux0 = x;
+      a.ldaux = d_in;
+      a.aux_scat = !x_grouped;
+      a.aux_fan = fan;
+    }
+    GemmPlan pl;
+    if (fan_k) {
+      a.c0 = dx ? wl.pairs : nullptr;
+      a.c_scat = 1;
+      plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, 1);
+    } else {
+      a.c0 = dx;
+      a.c_scat = !x_grouped;
+      plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, !bf16);
+    }
+    SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_bwd dx gemm");
+    if (fan_k && dx) SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_in, dx, bf16, st), "parallel_linear_bwd ksum");
+    if (dgates)
+      SMOE_HIP(launch_reduce_dg(wl.dgpart, pl.slots, int(M), offsets, E, sorted_scattered_idxs, dgates, st),
+               "parallel_linear_bwd dgates");
+  }
+  if (dw) {
+    GemmArgs a = blank_args(offsets, sorted_scattered_idxs, E, int(M));
+    a.Mo = int(d_in);
+    a.N = int(d_out);
+    a.a0 = x;
+    a.lda = d_in;
+    a.a_scat = !x_grouped;
+    a.a_fan = fan;
+    a.b0 = dy;
+    a.ldb = d_out;
+    a.b_scat = gates ? 1 : !y_grouped;
+    a.b_fan = gates ? k : 1;
+    a.b_gate = gates;
+    SMOE_TRY(run_dw(a, bf16, dw, wl.partial, st, "parallel_linear_bwd dw"));
+  }
+  return ok();
+}
+
+// -------------------------------------------------------------- SMoE MLP --
+static int check_mlp(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act, int32_t dtype,
+                     const void* w3) {
+  SMOE_TRY(check_common(T, k, E, dtype));
+  SMOE_TRY(check_dim(d_model, "d_model"));
+  SMOE_TRY(check_dim(d_ff, "d_ff"));
+  if (act != SMOE_ACT_GELU && act != SMOE_ACT_SWIGLU) return fail(SMOE_ERR_DTYPE, "unknown activation %d", act);
+  if ((act == SMOE_ACT_SWIGLU) != (w3 != nullptr)) return fail(SMOE_ERR_NULL, "w3 must be given exactly for SWIGLU");
+  return SMOE_OK;
+}
+
+size_t smoe_mlp_saved_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act,
+                            int32_t dtype) {
+  (void)d_model;
+  return saved_layout(T, k, E, d_ff, act, dtype).total;
+}
+
+int smoe_mlp_saved_offsets(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act,
+                           int32_t dtype, size_t off[7]) {
+  (void)d_model;
+  if (!off) return fail(SMOE_ERR_NULL, "off is NULL");
+  SavedLayout s = saved_layout(T, k, E, d_ff, act, dtype);
+  for (int i = 0; i < 7; ++i) off[i] = s.off[i];
+  return ok();
+}
+
+size_t smoe_mlp_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act,
+                                    int32_t dtype) {
+  (void)d_ff; (void)act; (void)dtype;
+  Arena ar(nullptr);
+  MlpFwdWs w;
+  layout_mlp_fwd(ar, T, k, E, d_model, w);
+  return ar.used;
+}
+
+int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, int64_t T, int64_t d_model,
+                 int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs, const float* gates, int32_t act,
+                 int32_t dtype, void* out, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                 void* stream) {
+  SMOE_TRY(check_mlp(T, k, E, d_model, d_ff, act, dtype, w3));
+  SMOE_TRY(need_ptr(w1, "w1"));
+  SMOE_TRY(need_ptr(w2, "w2"));
+  if (w3) SMOE_TRY(need_ptr(w3, "w3"));
+  SMOE_TRY(need_ptr(saved, "saved"));
+  SMOE_TRY(need_ptr(ws, "ws"));
+  const int64_t M = T * k;
+  if (M > 0) {
+    SMOE_TRY(need_ptr(x, "x"));
+    SMOE_TRY(need_ptr(out, "out"));
+    SMOE_TRY(need_ptr(expert_idxs, "expert_idxs"));
+    SMOE_TRY(need_ptr(gates, "gates"));
+  }
+  const SavedLayout sl = saved_layout(T, k, E, d_ff, act, dtype);
+  if (saved_bytes < sl.total) return fail(SMOE_ERR_WORKSPACE, "saved_bytes=%zu < %zu", saved_bytes, sl.total);
+  Arena ar(ws);
+  MlpFwdWs wl;
+  layout_mlp_fwd(ar, T, k, E, d_model, wl);
+  if (ws_bytes < ar.used) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, ar.used);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* sv = static_cast<char*>(saved);
+  int* s_exp = reinterpret_cast<int*>(sv + sl.off[0]);
+  int* s_sct = reinterpret_cast<int*>(sv + sl.off[1]);
+  int* counts = reinterpret_cast<int*>(sv + sl.off[2]);
+  int* offsets = reinterpret_cast<int*>(sv + sl.off[3]);
+  void* h1 = sv + sl.off[4];
+  void* h3 = act == SMOE_ACT_SWIGLU ? sv + sl.off[5] : nullptr;
+  void* av = sv + sl.off[6];
+  const int bf16 = dtype == SMOE_BF16;
+
+  SMOE_HIP(launch_route(expert_idxs, int(M), E, s_exp, s_sct, counts, offsets, wl.route, st), "mlp_fwd route");
+  if (M == 0) return ok();
+
+  // layer 1: scattered x rows (fan-out k) -> grouped h (h1, h3) and a
+  GemmArgs a = blank_args(offsets, s_sct, E, int(M));
+  a.N = int(d_ff);
+  a.K = a.K0 = int(d_model);
+  a.a0 = a.a1 = x;
+  a.lda = d_model;
+  a.a_scat = 1;
+  a.a_fan = k;
+  a.b0 = w1;
+  a.b1 = act == SMOE_ACT_SWIGLU ? w3 : w1;
+  a.b_nk = 0;
+  a.ldb = d_ff;
+  a.b_es = d_model * d_ff;
+  a.c0 = h1;
+  a.c1 = act == SMOE_ACT_SWIGLU ? h3 : av;
+  a.c2 = av;
+  a.ldc = d_ff;
+  GemmPlan pl;
+  if (act == SMOE_ACT_SWIGLU)
+    plan_gemm(a, pl, SEG_M, EPI_SWIGLU_FWD, 1, bf16, 0);
+  else
+    plan_gemm(a, pl, SEG_M, EPI_GELU_FWD, 0, bf16, 0);
+  SMOE_HIP(launch_gemm(a, pl, st), "mlp_fwd layer 1");
+
+  // layer 2: grouped a -> scattered fp32 expert outputs
+  GemmArgs b = blank_args(offsets, s_sct, E, int(M));
+  b.N = int(d_model);
+  b.K = b.K0 = int(d_ff);
+  b.a0 = b.a1 = av;
+  b.lda = d_ff;
+  b.b0 = b.b1 = w2;
+  b.ldb = d_model;
+  b.b_es = d_ff * d_model;
+  b.c0 = wl.pairs;
+  b.c_scat = 1;
+  b.ldc = d_model;
+  plan_gemm(b, pl, SEG_M, EPI_STORE, 0, bf16, 1);
+  SMOE_HIP(launch_gemm(b, pl, st), "mlp_fwd layer 2");
+  SMOE_HIP(launch_combine(wl.pairs, gates, T, k, d_model, out, bf16, st), "mlp_fwd combine");
+  return ok();
+}
+
+size_t smoe_mlp_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act,
+                                    int32_t dtype) {
+  Arena ar(nullptr);
+  MlpBwdWs w;
+  layout_mlp_bwd(ar, T, k, E, d_model, d_ff, act, dtype, w);
+  return ar.used;
+}
+
+int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3, const void* w2, int64_t T,
+                 int64_t d_model, int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs, const float* gates,
+                 int32_t act, int32_t dtype, const void* saved, size_t saved_bytes, void* dx, float* dw1, float* dw3,
+                 float* dw2, float* dgates, void* ws, size_t ws_bytes, void* stream) {
+  SMOE_TRY(check_mlp(T, k, E, d_model, d_ff, act, dtype, w3));
+  if ((act == SMOE_ACT_SWIGLU) != (dw3 != nullptr)) return fail(SMOE_ERR_NULL, "dw3 must be given exactly for SWIGLU");
+  SMOE_TRY(need_ptr(w1, "w1"));
+  SMOE_TRY(need_ptr(w2, "w2"));
+  if (w3) SMOE_TRY(need_ptr(w3, "w3"));
+  SMOE_TRY(need_ptr(saved, "saved"));
+  SMOE_TRY(need_ptr(ws, "ws"));
+  SMOE_TRY(need_ptr(dw1, "dw1"));
+  SMOE_TRY(need_ptr(dw2, "dw2"));
+  if (dw3) SMOE_TRY(need_ptr(dw3, "dw3"));
+  const int64_t M = T * k;
+  if (M > 0) {
+    SMOE_TRY(need_ptr(dout, "dout"));
+    SMOE_TRY(need_ptr(x, "x"));
+    SMOE_TRY(need_ptr(dx, "dx"));
+    SMOE_TRY(need_ptr(gates, "gates"));
+  }
+  (void)expert_idxs;  // the routing of the forward pass is read from `saved`
+  const SavedLayout sl = saved_layout(T, k, E, d_ff, act, dtype);
+  if (saved_bytes < sl.total) return fail(SMOE_ERR_WORKSPACE, "saved_bytes=%zu < %zu", saved_bytes, sl.total);
+  Arena ar(ws);
+  MlpBwdWs wl;
+  layout_mlp_bwd(ar, T, k, E, d_model, d_ff, act, dtype, wl);
+  if (ws_bytes < ar.used) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, ar.used);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* sv = static_cast<const char*>(saved);
+  const int* s_sct = reinterpret_cast<const int*>(sv + sl.off[1]);
+  const int* offsets = reinterpret_cast<const int*>(sv + sl.off[3]);
+  const void* h1 = sv + sl.off[4];
+  const void* h3 = act == SMOE_ACT_SWIGLU ? sv + sl.off[5] : nullptr;
+  const void* av = sv + sl.off[6];
+  const int bf16 = dtype == SMOE_BF16;
+  const bool swiglu = act == SMOE_ACT_SWIGLU;
+
+  if (M == 0) {
+    SMOE_HIP(launch_zero(dw1, size_t(E) * d_model * d_ff * 4, st), "mlp_bwd");
+    SMOE_HIP(launch_zero(dw2, size_t(E) * d_model * d_ff * 4, st), "mlp_bwd");
+    if (dw3) SMOE_HIP(launch_zero(dw3, size_t(E) * d_model * d_ff * 4, st), "mlp_bwd");
+    return ok();
+  }
+
+  // 1. dA = dout W2^T per grouped row, activation backward fused: dh (dh1, dh3)
+  //    and the gate-gradient partials <a, dout W2^T>
+  GemmArgs a = blank_args(offsets, s_sct, E, int(M));
+  a.N = int(d_ff);
+  a.K = a.K0 = int(d_model);
+  a.a0 = a.a1 = dout;
+  a.lda = d_model;
+  a.a_scat = 1;
+  a.a_fan = k;
+  a.b0 = a.b1 = w2;
+  a.b_nk = 1;
+  a.ldb = d_model;
+  a.b_es = d_ff * d_model;
+  a.gate = gates;
+  a.aux0 = h1;
+  a.aux1 = h3;
+  a.ldaux = d_ff;
+  a.dgpart = wl.dgpart;
+  a.c0 = wl.dh1;
+  a.c1 = wl.dh3;
+  a.ldc = d_ff;
+  GemmPlan pl;
+  plan_gemm(a, pl, SEG_M, swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, 0, bf16, 0);
+  SMOE_HIP(launch_gemm(a, pl, st), "mlp_bwd dA");
+  if (dgates)
+    SMOE_HIP(launch_reduce_dg(wl.dgpart, pl.slots, int(M), offsets, E, s_sct, dgates, st), "mlp_bwd dgates");
+
+  // 2. dW2[e] = sum a^T (g dout)
+  {
+    GemmArgs d = blank_args(offsets, s_sct, E, int(M));
+    d.Mo = int(d_ff);
+    d.N = int(d_model);
+    d.a0 = av;
+    d.lda = d_ff;
+    d.b0 = dout;
+    d.ldb = d_model;
+    d.b_scat = 1;
+    d.b_fan = k;
+    d.b_gate = gates;
+    SMOE_TRY(run_dw(d, bf16, dw2, wl.partial, st, "mlp_bwd dW2"));
+  }
+  // 3. dx contributions = dh W1^T (+ dh3 W3^T), then the k-sum
+  {
+    GemmArgs d = blank_args(offsets, s_sct, E, int(M));
+    d.N = int(d_model);
+    d.K0 = int(d_ff);
+    d.K = swiglu ? int(2 * d_ff) : int(d_ff);
+    d.a0 = wl.dh1;
+    d.a1 = swiglu ? wl.dh3 : wl.dh1;
+    d.lda = d_ff;
+    d.b0 = w1;
+    d.b1 = swiglu ? w3 : w1;
+    d.b_nk = 1;
+    d.ldb = d_ff;
+    d.b_es = d_model * d_ff;
+    d.c0 = wl.pairs;
+    d.c_scat = 1;
+    d.ldc = d_model;
+    GemmPlan pd;
+    plan_gemm(d, pd, SEG_M, EPI_STORE, 0, bf16, 1);
+    SMOE_HIP(launch_gemm(d, pd, st), "mlp_bwd dx");
+    SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_model, dx, bf16, st), "mlp_bwd ksum");
+  }
+  // 4. dW1[e] = sum x^T dh1 ; dW3[e] = sum x^T dh3
+  {
+    GemmArgs d = blank_args(offsets, s_sct, E, int(M));
+    d.Mo = int(d_model);
+    d.N = int(d_ff);
+    d.a0 = x;
+    d.lda = d_model;
+    d.a_scat = 1;
+    d.a_fan = k;
+    d.b0 = wl.dh1;
+    d.ldb = d_ff;
+    SMOE_TRY(run_dw(d, bf16, dw1, wl.partial, st, "mlp_bwd dW1"));
+    if (swiglu) {
+      d.b0 = wl.dh3;
+      SMOE_TRY(run_dw(d, bf16, dw3, wl.partial, st, "mlp_bwd dW3"));
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// Device helpers shared by the gfx950 kernels: bf16 bit conversions, wave64
+// scans and the data-dependent tile maps that turn per-expert row counts
+// into grouped-GEMM tiles without a device-to-host copy.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SMOE_DEV __device__ __forceinline__
+
+namespace smoe {
+
+constexpr int kWave = 64;
+
+// ---- bf16 <-> fp32 (bit level, round to nearest even) ---------------------
+SMOE_DEV float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+SMOE_DEV uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+// round to bf16 and back (the value a bf16 store would hold)
+SMOE_DEV float bfround(float f) { return bf2f(f2bf(f)); }
+
+// element load/store of the two storage types
+template <class T> SMOE_DEV float ld(const T* p);
+template <> SMOE_DEV float ld<float>(const float* p) { return *p; }
+template <> SMOE_DEV float ld<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+template <class T> SMOE_DEV void st(T* p, float v);
+template <> SMOE_DEV void st<float>(float* p, float v) { *p = v; }
+template <> SMOE_DEV void st<uint16_t>(uint16_t* p, float v) { *p = f2bf(v); }
+// value as stored by type T (rounding for bf16, identity for fp32)
+template <class T> SMOE_DEV float stored(float v);
+template <> SMOE_DEV float stored<float>(float v) { return v; }
+template <> SMOE_DEV float stored<uint16_t>(float v) { return bfround(v); }
+
+// four consecutive elements
+template <class T> SMOE_DEV void st4(T* p, const float v[4]);
+template <> SMOE_DEV void st4<float>(float* p, const float v[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> SMOE_DEV void st4<uint16_t>(uint16_t* p, const float v[4]) {
+  uint2 w;
+  w.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+  w.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+template <class T> SMOE_DEV void ld4(const T* p, float v[4]);
+template <> SMOE_DEV void ld4<float>(const float* p, float v[4]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+template <> SMOE_DEV void ld4<uint16_t>(const uint16_t* p, float v[4]) {
+  uint2 w = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+  v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
+// ---- activations (fp32) ---------------------------------------------------
+SMOE_DEV float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+SMOE_DEV float gelu_grad_f(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+         z * 0.39894228040143268f * __expf(-0.5f * z * z);
+}
+SMOE_DEV float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+SMOE_DEV float silu_f(float z) { return z * sigmoid_f(z); }
+SMOE_DEV float silu_grad_f(float z) {
+  float s = sigmoid_f(z);
+  return s * (1.0f + z * (1.0f - s));
+}
+
+// ---- wave64 helpers ------------------------------------------------------
+SMOE_DEV int lane_id() { return __lane_id(); }
+SMOE_DEV int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// ---- tile maps ------------------------------------------------------------
+// Rows of expert e are [offsets[e], offsets[e+1]).  Expert e owns
+// ceil(count_e / unit) consecutive work items (m-tiles, or row chunks for
+// the weight gradient).  find_item() maps a global item index to its expert
+// and row range; every lane of the calling wave gets the same answer.
+// Returns false if `item` is past the last item.
+struct Item {
+  int e;
+  int row0;    // first grouped row of the item
+  int row1;    // one past the last row of the item
+  int first;   // 1 if this is the expert's first item
+  int nitems;  // items of this expert
+};
+
+SMOE_DEV bool find_item(const int* __restrict__ offsets, int E, int unit, int item, Item& it) {
+  const int l = lane_id();
+  int base = 0;
+  for (int c = 0; c < E; c += kWave) {
+    const int e = c + l;
+    int lo = 0, hi = 0;
+    if (e < E) { lo = offsets[e]; hi = offsets[e + 1]; }
+    const int cnt = hi > lo ? hi - lo : 0;
+    const int n = (cnt + unit - 1) / unit;
+    const int incl = wave_incl_scan(n);
+    const int excl = incl - n;
+    const bool hit = (e < E) && item >= base + excl && item < base + incl;
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int src = __ffsll((long long)m) - 1;
+      const int ex = __shfl(excl, src, kWave);
+      const int lo_s = __shfl(lo, src, kWave);
+      const int hi_s = __shfl(hi, src, kWave);
+      const int n_s = __shfl(n, src, kWave);
+      const int local = item - base - ex;
+      it.e = c + src;
+      it.row0 = lo_s + local * unit;
+      it.row1 = min(hi_s, it.row0 + unit);
+      it.first = local == 0;
+      it.nitems = n_s;
+      return true;
+    }
+    base += __shfl(incl, kWave - 1, kWave);
+  }
+  return false;
+}
+
+// Number of items of expert e and the index of its first item (one lane).
+SMOE_DEV void expert_items(const int* __restrict__ offsets, int e, int unit, int& first_item, int& n) {
+  int base = 0;
+  for (int i = 0; i < e; ++i) {
+    const int c = offsets[i + 1] - offsets[i];
+    base += (c + unit - 1) / unit;
+  }
+  const int c = offsets[e + 1] - offsets[e];
+  first_item = base;
+  n = (c + unit - 1) / unit;
+}
+
+}  // namespace smoe

@@ -1,0 +1,115 @@
+// Internal interface between the host orchestration (api.hip) and the
+// gfx950 kernels.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace smoe {
+
+constexpr int kMaxExperts = 1024;
+
+// Segmented grouped GEMM over scattered rows.
+//
+// SEG_M (rows mode, the scatter2scatter product and its dX):
+//   for every grouped row r of expert e (offsets[e] <= r < offsets[e+1]):
+//     C[r][n] = sum_{k<K} A(r,k) * B_e(k,n),   n < N
+//   A(r,k) = (k < K0 ? a0 : a1)[arow(r) * lda + k (- K0)]
+//            arow(r) = a_scat ? sidx[r] / a_fan : r
+//   B_e(k,n): b_nk == 0: W[k][n] layout, (dual ? b0 for W1 / b1 for W3)
+//                        b0 + e*b_es + k*ldb + n
+//             b_nk == 1: W[n][k] layout (W^T product), concat along K:
+//                        (k < K0 ? b0 : b1) + e*b_es + n*ldb + k (- K0)
+// SEG_K (weights mode, groupXtY):
+//   for every expert e, row chunk [r0, r1) of its grouped rows (chunks of
+//   KS rows):  C_e[i][j] += sum_{r in chunk} A(r,i) * B(r,j),  i < Mo, j < N
+//   A(r,i) = a0[arow(r) * lda + i],  B(r,j) = g(r) * b0[brow(r) * ldb + j]
+//   brow(r) = b_scat ? sidx[r] / b_fan : r, g(r) = b_gate ? b_gate[sidx[r]] : 1
+//   An expert with one chunk writes c0 + e*Mo*N directly; otherwise each
+//   chunk writes partial + chunk*Mo*N and reduce_dw() sums them.
+enum Mode { SEG_M = 0, SEG_K = 1 };
+
+// Epilogues (SEG_M).  v is the fp32 product; "stored" means rounded to the
+// storage type of the outputs (bf16 or fp32).
+enum Epi {
+  EPI_STORE = 0,   // c0[crow(r)][n] = (gate ? g*v : v); dg partial <aux row, v>
+  EPI_GELU_FWD,    // h = stored(v) -> c0; a = stored(gelu(h)) -> c1
+  EPI_SWIGLU_FWD,  // h1 = stored(v1) -> c0; h3 = stored(v3) -> c1; a = stored(silu(h1) h3) -> c2
+  EPI_GELU_BWD,    // v = dA/g; h = aux0; dg += <stored(gelu(h)), v>; c0 = stored(g v gelu'(h))
+  EPI_SWIGLU_BWD,  // v = dA/g; h1,h3 = aux0,aux1; dg += <a, v>;
+                   // c0 = stored(g v h3 silu'(h1)); c1 = stored(g v silu(h1))
+  EPI_PARTIAL      // SEG_K fp32 tile store
+};
+
+struct GemmArgs {
+  const int* offsets;  // [E+1]
+  const int* sidx;     // sorted_scattered_idxs [M]
+  int E;
+  int M;    // T*k: grouped-row count upper bound, stride of dg partials
+  int N;    // output columns
+  int K;    // SEG_M reduction length (with concat)
+  int K0;   // SEG_M concat split (== K when single)
+  int Mo;   // SEG_K output rows
+  int KS;   // SEG_K rows per chunk
+  int mt_ub;   // SEG_M: upper bound on m-tiles; SEG_K: upper bound on chunks
+  int b_nk;
+  const void* a0;
+  const void* a1;
+  int64_t lda;
+  int a_scat, a_fan;
+  const void* b0;
+  const void* b1;
+  int64_t ldb, b_es;
+  int b_scat, b_fan;
+  const float* b_gate;
+  void* c0;
+  void* c1;
+  void* c2;
+  int64_t ldc;
+  int c_scat;
+  const float* gate;   // SEG_M epilogue gate, indexed by p = sidx[r]
+  const void* aux0;    // SEG_M epilogue loads
+  const void* aux1;
+  int64_t ldaux;
+  int aux_scat, aux_fan;
+  float* dgpart;       // [slots][M]
+  float* partial;      // SEG_K partial tiles [mt_ub][Mo*N]
+};
+
+// Launch descriptions chosen on the host.
+struct GemmPlan {
+  int mode;
+  int epi;
+  int dual;      // SwiGLU dual B (W1 and W3 share the A tile)
+  int bf16;      // 1: MFMA bf16 kernel; 0: fp32 kernel
+  int bm, bn;    // tile (bf16 kernel: 128 or 256 each)
+  int slots;     // dg partial slots written per row
+  int n_tiles;   // tiles along N (SEG_M) or tiles per chunk (SEG_K)
+  int out_f32;   // SEG_M EPI_STORE: c0 is fp32 (else the storage type)
+  int64_t grid;  // workgroups launched
+};
+
+// Chooses tiles, sizes the grid and fills plan; returns false if no kernel
+// instance exists for the request.
+bool plan_gemm(GemmArgs& a, GemmPlan& plan, int mode, int epi, int dual, int bf16, int out_f32);
+hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& plan, hipStream_t st);
+
+// routing
+size_t route_ws_bytes(int64_t M, int E);
+hipError_t launch_route(const int* eidx, int M, int E, int* s_exp, int* s_sct, int* counts, int* offsets,
+                        void* ws, hipStream_t st);
+
+// elementwise / reductions
+// out[t][c] = sum_j w(t,j) * pairs[t*k + j][c]; w = gates or 1.  pairs fp32.
+hipError_t launch_combine(const float* pairs, const float* gates, int64_t T, int k, int64_t d, void* out,
+                          int out_bf16, hipStream_t st);
+// dg[sidx[r]] = sum_s part[s*M + r] for r < offsets[E]
+hipError_t launch_reduce_dg(const float* part, int slots, int M, const int* offsets, int E, const int* sidx,
+                            float* dg, hipStream_t st);
+// expert e with 0 chunks: dw[e] = 0; with >= 2 chunks: dw[e] = sum of its partials
+hipError_t launch_reduce_dw(const float* partial, const int* offsets, int E, int KS, int64_t elems, float* dw,
+                            hipStream_t st);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace smoe

@@ -8,3 +8,16 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(scope="session")
+def smoe():
+    """The built HIP library binding; a GPU test fails (never skips) when the
+    library is missing or no GPU is visible."""
+    import torch
+    import sparse_mixture_experts_top_amd as m
+    assert torch.cuda.is_available(), "GPU test needs a visible MI355X"
+    return m

@@ -1,0 +1,47 @@
+"""Helpers for the GPU parity tests: upload seeded workloads with the exact
+bits the oracle sees, and the RMS-relative error metric."""
+import sys
+
+import numpy as np
+import torch
+
+from workloads import Workload
+
+BF16_TOL = 2e-2   # max |gpu - oracle| / RMS(oracle), bf16 path
+F32_TOL = 1e-4    # same, fp32 path
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(arr: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 bits -> bfloat16 tensor; other arrays as they are."""
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def upload(w: Workload, names=None, device="cuda"):
+    names = names or list(w.tensors)
+    return {n: dev_tensor(w.tensors[n], device) for n in names if n in w.tensors}
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "non-finite values in GPU output"
+    rms = np.sqrt(np.mean(ref ** 2))
+    if rms == 0.0:
+        return float(np.abs(got).max(initial=0.0))
+    return float(np.abs(got - ref).max(initial=0.0) / rms)
+
+
+def tol_for(w: Workload) -> float:
+    return F32_TOL if w.dtype == "f32" else BF16_TOL

@@ -1,0 +1,96 @@
+"""The C-ABI library loads on the CPU, exports every function that
+include/smoe.h declares, and rejects bad arguments on the host without
+touching a device (no compute calls here)."""
+import ctypes
+
+import pytest
+
+smoe = pytest.importorskip("sparse_mixture_experts_top_amd")
+lib = smoe.lib
+
+NULL = None
+
+
+def test_every_declared_symbol_is_exported():
+    names = smoe.header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    for n in ("smoe_route", "smoe_parallel_linear_fwd", "smoe_parallel_linear_bwd",
+              "smoe_mlp_fwd", "smoe_mlp_bwd"):
+        assert n in names
+
+
+def test_status_strings_and_version():
+    assert lib.smoe_abi_version() == 1
+    for s in range(7):
+        assert lib.smoe_status_string(s)
+    assert lib.smoe_status_string(0) == b"ok"
+
+
+def test_workspace_sizes_are_consistent():
+    assert lib.smoe_route_workspace_bytes(16384, 8, 64) >= 4 * 64 * 32
+    b_small = lib.smoe_mlp_bwd_workspace_bytes(256, 2, 8, 128, 256, smoe.ACT_GELU, smoe.F32)
+    b_big = lib.smoe_mlp_bwd_workspace_bytes(16384, 2, 8, 4096, 14336, smoe.ACT_SWIGLU, smoe.BF16)
+    assert 0 < b_small < b_big
+    s = lib.smoe_mlp_saved_bytes(16384, 2, 8, 4096, 14336, smoe.ACT_SWIGLU, smoe.BF16)
+    assert s >= 3 * 32768 * 14336 * 2
+    off = (ctypes.c_size_t * 7)()
+    assert lib.smoe_mlp_saved_offsets(100, 2, 4, 64, 96, smoe.ACT_GELU, smoe.F32, off) == 0
+    assert off[5] == ctypes.c_size_t(-1).value
+    assert all(o % 256 == 0 for i, o in enumerate(off) if i != 5)
+    assert lib.smoe_parallel_linear_fwd_workspace_bytes(8, 2, 4, 64, 64, 0, smoe.BF16) <= 256
+    assert lib.smoe_parallel_linear_fwd_workspace_bytes(8, 2, 4, 64, 64, 1, smoe.BF16) >= 16 * 64 * 4
+
+
+def _fake(addr=4096):
+    return ctypes.c_void_p(addr)
+
+
+def test_route_rejects_bad_arguments():
+    f = lib.smoe_route
+    assert f(_fake(), 4, 2, 0, _fake(), _fake(), _fake(), _fake(), _fake(), 1 << 20, NULL) == 2   # E = 0
+    assert f(_fake(), 4, 2, 2000, _fake(), _fake(), _fake(), _fake(), _fake(), 1 << 20, NULL) == 2
+    assert f(_fake(), 4, 0, 4, _fake(), _fake(), _fake(), _fake(), _fake(), 1 << 20, NULL) == 2   # k = 0
+    assert f(NULL, 4, 2, 4, _fake(), _fake(), _fake(), _fake(), _fake(), 1 << 20, NULL) == 1
+    assert f(_fake(), 4, 2, 4, _fake(), _fake(), _fake(), _fake(), _fake(), 0, NULL) == 4         # ws
+    assert b"ws_bytes" in lib.smoe_last_error()
+
+
+def test_parallel_linear_rejects_bad_arguments():
+    f = lib.smoe_parallel_linear_fwd
+    args = dict(x=_fake(), x_rows=8, d_in=64, w=_fake(), d_out=64, E=4, T=8, k=2, sidx=_fake(),
+                off=_fake(), xg=0, yg=0, gates=NULL, y=_fake(), dtype=smoe.BF16, ws=_fake(),
+                wsb=1 << 20, st=NULL)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(dtype=7) == 3
+    assert call(d_in=12) == 2                      # not a multiple of 8
+    assert call(x_rows=5) == 2                     # neither T nor T*k
+    assert call(xg=1, x_rows=8) == 2               # grouped input needs T*k rows
+    assert call(w=NULL) == 1
+    assert call(x=_fake(4098)) == 2                # misaligned
+    assert call(gates=_fake(), yg=1) == 2          # combine needs scattered output
+    assert call(gates=_fake(), wsb=16) == 4
+
+
+def test_mlp_rejects_bad_arguments():
+    f = lib.smoe_mlp_fwd
+    base = [_fake(), _fake(), NULL, _fake(), 16, 64, 128, 4, 2, _fake(), _fake(), smoe.ACT_GELU,
+            smoe.BF16, _fake(), _fake(), 1 << 30, _fake(), 1 << 30, NULL]
+    a = list(base); a[11] = 5
+    assert f(*a) == 3                              # unknown activation
+    a = list(base); a[11] = smoe.ACT_SWIGLU
+    assert f(*a) == 1                              # SwiGLU without w3
+    a = list(base); a[2] = _fake()
+    assert f(*a) == 1                              # w3 given for GELU
+    a = list(base); a[15] = 8
+    assert f(*a) == 4                              # saved too small
+    g = lib.smoe_mlp_bwd
+    assert g(_fake(), _fake(), _fake(), NULL, _fake(), 16, 64, 128, 4, 2, _fake(), _fake(),
+             smoe.ACT_GELU, smoe.BF16, _fake(), 1 << 30, _fake(), _fake(), _fake(), _fake(), NULL,
+             _fake(), 1 << 30, NULL) == 1          # dw3 given for GELU

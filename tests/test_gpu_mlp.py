@@ -1,0 +1,88 @@
+"""smoe_mlp_fwd / smoe_mlp_bwd on the GPU against the oracle: GELU and
+SwiGLU, fp32 and bf16, ragged tiles, empty experts; the tiny fp32 workload
+in full; saved routing arrays bit-exact; determinism across runs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import BF16_TOL, F32_TOL, dev_tensor, host, rel_err, say, upload
+from workloads import make_config, make_mlp
+
+pytestmark = pytest.mark.gpu
+
+
+def run_mlp(smoe, w):
+    d = upload(w)
+    out, saved = smoe.smoe_mlp_fwd(d["x"], d["w1"], d["w2"], d["expert_idxs"], d["gates"], w.act, w3=d.get("w3"))
+    g = smoe.smoe_mlp_bwd(d["dout"], d["x"], d["w1"], d["w2"], d["expert_idxs"], d["gates"], w.act, saved,
+                          w3=d.get("w3"))
+    torch.cuda.synchronize()
+    return out, saved, g
+
+
+def check_full(smoe, w):
+    tol = F32_TOL if w.dtype == "f32" else BF16_TOL
+    storage = "f64" if w.dtype == "f32" else "bf16"
+    out, saved, g = run_mlp(smoe, w)
+    f = lambda n: w.f32(n).astype(np.float64)
+    w3 = f("w3") if w.act == "swiglu" else None
+    idx, gates = w.tensors["expert_idxs"], w.tensors["gates"].astype(np.float64)
+    ref = oracle.mlp_fwd(f("x"), f("w1"), f("w2"), idx, gates, w.act, w3=w3, storage=storage)
+    e = rel_err(host(out), ref)
+    say(f"  out err {e:.2e}")
+    assert e <= tol
+    rg = oracle.mlp_bwd(f("x"), f("w1"), f("w2"), idx, gates, w.act, f("dout"), w3=w3, storage=storage)
+    names = ["dx", "dw1", "dw2", "dgates"] + (["dw3"] if w.act == "swiglu" else [])
+    for n in names:
+        e = rel_err(host(g[n]), rg[n])
+        say(f"  {n} err {e:.2e}")
+        assert e <= tol, n
+    # routing arrays saved by the forward are the oracle's, bit for bit
+    v = smoe.saved_views(saved, w.T, w.k, w.E, w.dims["d_model"], w.dims["d_ff"], w.act,
+                         torch.float32 if w.dtype == "f32" else torch.bfloat16)
+    r = oracle.route(idx, w.E)
+    for n in ("sorted_expert_idxs", "sorted_scattered_idxs", "counts", "offsets"):
+        np.testing.assert_array_equal(v[n].cpu().numpy(), r[n])
+    return out, g
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_mlp_small(smoe, dtype, act):
+    say(f"mlp small {dtype} {act}")
+    w = make_mlp(300, 136, 200, 6, 2, act, dtype, 130, routing="softmax", w_std=0.08)
+    check_full(smoe, w)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_mlp_empty_experts_and_skew(smoe, act):
+    say(f"mlp zipf empty experts bf16 {act}")
+    w = make_mlp(1200, 128, 256, 12, 3, act, "bf16", 131, routing="zipf", w_std=0.05, n_dead=3)
+    cnt = np.bincount(w.tensors["expert_idxs"].reshape(-1), minlength=12)
+    assert (cnt == 0).sum() == 3
+    out, g = check_full(smoe, w)
+    dead = np.nonzero(cnt == 0)[0]
+    assert np.all(host(g["dw1"])[dead] == 0) and np.all(host(g["dw2"])[dead] == 0)
+
+
+def test_mlp_tiny_fp32_workload(smoe):
+    """T=256, d_model=128, d_ff=256, E=8, k=2, GELU, fp32: everything in full."""
+    say("mlp tiny fp32 workload")
+    check_full(smoe, make_config(1))
+
+
+def test_mlp_single_token_and_k1(smoe):
+    say("mlp T=1 k=1 and T=3 k=4")
+    check_full(smoe, make_mlp(1, 64, 64, 4, 1, "gelu", "bf16", 132, w_std=0.1))
+    check_full(smoe, make_mlp(3, 64, 128, 4, 4, "swiglu", "f32", 133, w_std=0.1))
+
+
+def test_mlp_deterministic(smoe):
+    say("mlp determinism bf16")
+    w = make_mlp(700, 128, 192, 8, 2, "swiglu", "bf16", 134, w_std=0.05)
+    o1, _, g1 = run_mlp(smoe, w)
+    o2, _, g2 = run_mlp(smoe, w)
+    assert torch.equal(o1, o2)
+    for n in ("dx", "dw1", "dw2", "dw3", "dgates"):
+        assert torch.equal(g1[n], g2[n]), n
