@@ -126,7 +126,8 @@ int smoe_parallel_linear_fwd(const void* x, int64_t x_rows, int64_t d_in,
  *   dw[e]   = sum_r u_r^T dy_r          (fp32; experts with no rows get 0)
  *   dgates[t][j] = <dy[t], u_r W[e]>    (only with gates)
  * Any of dx, dw, dgates may be NULL to skip it (dgates needs gates).
- * In bf16 runs dy_r with gates enters the dw contraction as bf16.
+ * With gates, dw[e] = sum (g u_r)^T dy[t]; in bf16 runs g*u_r is rounded to
+ * bf16 before it enters the dw contraction.
  * Same page, first review, Summary (forward and backward through
  * ParallelLinear); article, para. 4 (per-expert gradients).
  * ------------------------------------------------------------------------ */
@@ -154,19 +155,21 @@ int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in,
  * x: [T, d_model]; w1, w3: [E, d_model, d_ff]; w2: [E, d_ff, d_model];
  * w3 must be NULL unless SWIGLU.  expert_idxs, gates: [T, k].
  * out: [T, d_model].  `saved` (size smoe_mlp_saved_bytes) receives what the
- * backward needs; its layout is given by smoe_mlp_saved_offsets.
- * In bf16 runs the grouped intermediates h (h1, h3) and a are stored in
- * bf16; a is computed from the stored h; expert outputs and the combine
- * stay fp32 until the final rounding of out.
+ * backward needs: the routing arrays and the grouped pre-activations h
+ * (h1, h3); the activation a is recomputed from them in the backward.  Its
+ * layout is given by smoe_mlp_saved_offsets.
+ * In bf16 runs h (h1, h3) and a are stored in bf16; a is computed from the
+ * stored h; expert outputs and the combine stay fp32 until the final
+ * rounding of out.
  * Article, para. 1 and 5 (SMoE MLP); project page, "How It Works".
  * ------------------------------------------------------------------------ */
 size_t smoe_mlp_saved_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model,
                             int64_t d_ff, int32_t act, int32_t dtype);
 /* Byte offsets inside `saved`: off[0] sorted_expert_idxs, off[1]
  * sorted_scattered_idxs, off[2] counts, off[3] offsets, off[4] h (h1),
- * off[5] h3 (SIZE_MAX unless SWIGLU), off[6] a.  Returns SMOE_OK. */
+ * off[5] h3 (SIZE_MAX unless SWIGLU).  Returns SMOE_OK. */
 int smoe_mlp_saved_offsets(int64_t T, int32_t k, int32_t E, int64_t d_model,
-                           int64_t d_ff, int32_t act, int32_t dtype, size_t off[7]);
+                           int64_t d_ff, int32_t act, int32_t dtype, size_t off[6]);
 size_t smoe_mlp_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
                                     int64_t d_model, int64_t d_ff, int32_t act,
                                     int32_t dtype);
@@ -186,11 +189,11 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2,
  *   GELU:   dh = dA * gelu'(h)
  *   SWIGLU: dh1 = dA * h3 * silu'(h1);  dh3 = dA * silu(h1)
  *   dx[t] += dh W1[e]^T (+ dh3 W3[e]^T)            (fp32 k-sum)
- *   dw2[e] += a^T (g dout[t]);  dw1[e] += x[t]^T dh;  dw3[e] += x[t]^T dh3
+ *   dw2[e] += (g a)^T dout[t];  dw1[e] += x[t]^T dh;  dw3[e] += x[t]^T dh3
  * Weight gradients are fp32 and fully written (experts with no tokens get
  * 0).  dw3 must be NULL unless SWIGLU.  dgates may be NULL.  `saved` is the
  * buffer filled by smoe_mlp_fwd with the same arguments.  In bf16 runs
- * dh (dh1, dh3) and g*dout are rounded to bf16 before they enter the
+ * dh (dh1, dh3) and g*a are rounded to bf16 before they enter the
  * weight-gradient and dx contractions.
  * ------------------------------------------------------------------------ */
 size_t smoe_mlp_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
@@ -204,6 +207,35 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1,
                  const void* saved, size_t saved_bytes,
                  void* dx, float* dw1, float* dw3, float* dw2, float* dgates,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement hook for benchmarks and profilers (not thread-safe).
+ *
+ * While a role has events attached, each launch of that role is bracketed
+ * on its stream by hipEventRecord(start_event) and hipEventRecord(stop_event)
+ * (hipEvent_t handles owned by the caller; a role launched several times in
+ * one call keeps the last launch).  NULL, NULL detaches.  The GEMM roles
+ * cover exactly one kernel launch each.
+ * ------------------------------------------------------------------------ */
+enum smoe_role {
+  SMOE_ROLE_ROUTE = 0,      /* the routing kernels of smoe_mlp_fwd          */
+  SMOE_ROLE_UP = 1,         /* MLP W1 (and W3) product, activation fused    */
+  SMOE_ROLE_DOWN = 2,       /* MLP W2 product, scattered fp32 output        */
+  SMOE_ROLE_COMBINE = 3,    /* gate-weighted combine                        */
+  SMOE_ROLE_DA = 4,         /* MLP dout W2^T, activation backward fused     */
+  SMOE_ROLE_DW2 = 5,        /* MLP dW2 product                              */
+  SMOE_ROLE_DX = 6,         /* MLP dh W1^T (+ dh3 W3^T) product             */
+  SMOE_ROLE_KSUM = 7,       /* k-sum of dx contributions                    */
+  SMOE_ROLE_DW1 = 8,        /* MLP dW1 product                              */
+  SMOE_ROLE_DW3 = 9,        /* MLP dW3 product                              */
+  SMOE_ROLE_DW_REDUCE = 10, /* split weight-gradient reduction              */
+  SMOE_ROLE_DG_REDUCE = 11, /* gate-gradient reduction                      */
+  SMOE_ROLE_PL_FWD = 12,    /* ParallelLinear forward product               */
+  SMOE_ROLE_PL_DX = 13,     /* ParallelLinear dx product                    */
+  SMOE_ROLE_PL_DW = 14,     /* ParallelLinear dw product                    */
+  SMOE_ROLE_COUNT = 15
+};
+int smoe_set_role_events(int32_t role, void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

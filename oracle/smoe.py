@@ -19,8 +19,10 @@ combined into T rows.
 Precision model for bf16 runs (``storage="bf16"``): every tensor that the
 method forms from fp32 values and then feeds to a bf16 contraction is stored
 in bf16 (round to nearest even): the pre-activations h (h1, h3), the
-activation a, the pre-activation gradients dh (dh1, dh3), and the
-gate-scaled gradient g*dy that enters the weight-gradient contraction.
+activation a, the pre-activation gradients dh (dh1, dh3), and, in the
+weight gradient of a gated product, the gate-scaled input row g*u (g*a for
+the second MLP matrix): dW[e] = sum (g*u)^T dy, the same exact sum as
+u^T (g*dy) with the gate applied to the operand that is stored.
 Everything else (scattered expert outputs, k-sums, final results) is kept
 exact here.  ``storage="f64"`` rounds nowhere.
 """
@@ -203,7 +205,7 @@ def parallel_linear_bwd(x, w, expert_idxs, x_grouped: bool, y_grouped: bool,
       dy_p = g[t,j] * dy[t]   (with gates)   or   dy[row of p]   (without)
       dX[input row] += dy_p @ W[e]^T         (k contributions summed when a
                                               T-row input was read k times)
-      dW[e]         += u^T (x) dy_p          (g*dy stored per ``storage``)
+      dW[e]         += u^T (x) dy_p          (with gates: (g*u stored) (x) dy[t])
       dgates[t,j]    = <dy[t], u @ W[e]>     (with gates)
     Returns (dx, dw, dgates or None).
     """
@@ -231,13 +233,12 @@ def parallel_linear_bwd(x, w, expert_idxs, x_grouped: bool, y_grouped: bool,
             u = x[in_row]
             if gates is None:
                 dyp = dy[rinv[p] if y_grouped else p]
-                dyw = dyp
+                dw[e] += np.outer(u, dyp)
             else:
                 dyp = g[t, j] * dy[t]
-                dyw = _store(dyp, storage)
                 dg[t, j] = dy[t] @ (u @ w[e])
+                dw[e] += np.outer(_store(g[t, j] * u, storage), dy[t])
             dx[in_row] += dyp @ w[e].T
-            dw[e] += np.outer(u, dyw)
     return dx, dw, dg
 
 
@@ -294,7 +295,7 @@ def mlp_bwd(x, w1, w2, expert_idxs, gates, act: str, dout, w3=None,
       GELU   : dh  = dA * gelu'(h)
       SwiGLU : dh1 = dA * h3 * silu'(h1);  dh3 = dA * silu(h1)
       dX[t] += dh W1[e]^T (+ dh3 W3[e]^T)
-      dW2[e] += a_p^T (x) dy_p;  dW1[e] += x_t^T (x) dh;  dW3[e] += x_t^T (x) dh3
+      dW2[e] += (g a_p)^T (x) dout[t];  dW1[e] += x_t^T (x) dh;  dW3[e] += x_t^T (x) dh3
     With ``tokens`` only those tokens are visited: dx and dgates rows are
     exact for them and the returned weight gradients are partial sums.
     Returns dict dx, dw1, dw2, dw3 (None without SwiGLU), dgates.
@@ -327,7 +328,7 @@ def mlp_bwd(x, w1, w2, expert_idxs, gates, act: str, dout, w3=None,
                 dh3 = _store(dA * silu(h), storage)
                 dx[t] += dh @ w1[e].T + dh3 @ w3[e].T
                 dw3[e] += np.outer(x[t], dh3)
-            dw2[e] += np.outer(a, _store(dyp, storage))
+            dw2[e] += np.outer(_store(g[t, j] * a, storage), dout[t])
             dw1[e] += np.outer(x[t], dh)
     return {"dx": dx, "dw1": dw1, "dw2": dw2, "dw3": dw3, "dgates": dg}
 
@@ -357,7 +358,8 @@ def mlp_dw_cols(x, w1, w2, expert_idxs, gates, act: str, dout, cols,
         if tt.size == 0:
             continue
         xe = x[tt]                                   # [n, d]
-        dye = g[tt, jj][:, None] * dout[tt]          # [n, d]
+        ge = g[tt, jj][:, None]                      # [n, 1]
+        dye = ge * dout[tt]                          # [n, d]
         w1c = _as64(w1[e][:, cols])
         w2c = _as64(w2[e][cols, :])
         h = _store(xe @ w1c, storage)
@@ -372,5 +374,5 @@ def mlp_dw_cols(x, w1, w2, expert_idxs, gates, act: str, dout, cols,
             dh3 = _store(dA * silu(h), storage)
             dw3[e] = xe.T @ dh3
         dw1[e] = xe.T @ dh
-        dw2[e] = a.T @ _store(dye, storage)
+        dw2[e] = _store(ge * a, storage).T @ dout[tt]
     return {"dw1": dw1, "dw2": dw2, "dw3": dw3}

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "LIB_PATH", "SmoeError", "lib", "smoe_route", "smoe_parallel_linear_fwd",
     "smoe_parallel_linear_bwd", "smoe_mlp_fwd", "smoe_mlp_bwd", "saved_views",
-    "header_functions", "F32", "BF16", "ACT_GELU", "ACT_SWIGLU",
+    "header_functions", "F32", "BF16", "ACT_GELU", "ACT_SWIGLU", "ROLES", "smoe_set_role_events",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +34,7 @@ _ACTS = {"gelu": ACT_GELU, "swiglu": ACT_SWIGLU}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m sparse_mixture_experts_top_amd.build` (hipcc, gfx950)")
+                      "`python sparse_mixture_experts_top_amd/build.py` (hipcc, gfx950)")
 lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -56,6 +56,7 @@ _SIGS = {
     "smoe_mlp_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32, _i32,
                                     _vp, _vp, _sz, _vp, _sz, _vp]),
     "smoe_mlp_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
+    "smoe_set_role_events": (ctypes.c_int, [_i32, _vp, _vp]),
     "smoe_mlp_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32,
                                     _i32, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -212,6 +213,22 @@ def smoe_mlp_bwd(dout, x, w1, w2, expert_idxs, gates, act: str, saved, w3=None, 
     return {"dx": dx, "dw1": dw1, "dw2": dw2, "dw3": dw3, "dgates": dg}
 
 
+ROLES = ["route", "up", "down", "combine", "dA", "dW2", "dX", "ksum", "dW1", "dW3", "dw_reduce",
+         "dg_reduce", "pl_fwd", "pl_dx", "pl_dw"]
+
+
+def smoe_set_role_events(role: str, start=None, stop=None):
+    """Attach torch.cuda.Event objects (enable_timing=True) to a launch role;
+    None detaches.  Events are recorded once first so that they exist."""
+    if start is not None:
+        for ev in (start, stop):
+            if not ev.cuda_event:
+                ev.record()
+    _check(lib.smoe_set_role_events(ROLES.index(role), ctypes.c_void_p(start.cuda_event) if start else None,
+                                    ctypes.c_void_p(stop.cuda_event) if stop else None),
+           "smoe_set_role_events")
+
+
 def workspace_bytes(kind: str, **kw) -> int:
     """Bytes of scratch the named entry point needs (for callers that keep
     one workspace across calls)."""
@@ -221,8 +238,8 @@ def workspace_bytes(kind: str, **kw) -> int:
 
 def saved_views(saved: torch.Tensor, T: int, k: int, E: int, d_model: int, d_ff: int, act: str,
                 dtype: torch.dtype) -> Dict[str, torch.Tensor]:
-    """Views into the `saved` buffer of smoe_mlp_fwd (routing arrays, h, a)."""
-    off = (ctypes.c_size_t * 7)()
+    """Views into the `saved` buffer of smoe_mlp_fwd (routing arrays, h)."""
+    off = (ctypes.c_size_t * 6)()
     dt = BF16 if dtype == torch.bfloat16 else F32
     _check(lib.smoe_mlp_saved_offsets(T, k, E, d_model, d_ff, _ACTS[act], dt, off), "smoe_mlp_saved_offsets")
     M = T * k
@@ -237,7 +254,6 @@ def saved_views(saved: torch.Tensor, T: int, k: int, E: int, d_model: int, d_ff:
         "counts": view(off[2], E, torch.int32, E * 4),
         "offsets": view(off[3], E + 1, torch.int32, (E + 1) * 4),
         "h": view(off[4], M * d_ff, dtype, M * d_ff * es).view(M, d_ff),
-        "a": view(off[6], M * d_ff, dtype, M * d_ff * es).view(M, d_ff),
     }
     if act == "swiglu":
         v["h3"] = view(off[5], M * d_ff, dtype, M * d_ff * es).view(M, d_ff)

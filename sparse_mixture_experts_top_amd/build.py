@@ -1,6 +1,6 @@
 """Build libsmoe.so (the C-ABI HIP library) in-tree for gfx950.
 
-    python -m sparse_mixture_experts_top_amd.build
+    python sparse_mixture_experts_top_amd/build.py
 
 Every kernel source under csrc/ is compiled with hipcc for gfx950 and linked
 into sparse_mixture_experts_top_amd/libsmoe.so.  Packed-fp32 instructions are
@@ -28,6 +28,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # interleave LDS fragment reads with MFMA issue instead of minimising
+    # register pressure (the GEMM kernels run one wave per SIMD anyway)
+    "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -43,6 +43,21 @@ int hip_status(hipError_t e, const char* where) {
 
 constexpr size_t kAlign = 256;
 
+// events attached by smoe_set_role_events
+hipEvent_t g_role_ev[SMOE_ROLE_COUNT][2] = {};
+
+// Brackets the launches issued during its lifetime with the role's events.
+struct RoleTimer {
+  int role;
+  hipStream_t st;
+  RoleTimer(int r, hipStream_t s) : role(r), st(s) {
+    if (g_role_ev[role][0]) (void)hipEventRecord(g_role_ev[role][0], st);
+  }
+  ~RoleTimer() {
+    if (g_role_ev[role][1]) (void)hipEventRecord(g_role_ev[role][1], st);
+  }
+};
+
 // Bump allocator over the caller's workspace; with base == nullptr it only
 // measures, so the *_workspace_bytes functions replay the exact layout.
 struct Arena {
@@ -133,6 +148,7 @@ int dg_slots(int64_t M, int E, int64_t N, int bf16) {
 struct PlBwdWs {
   float* pairs = nullptr;    // dx contributions [M, d_in] when x was read k times
   float* dgpart = nullptr;   // [slots, M]
+  void* xg = nullptr;        // gate-scaled input rows, grouped [M, d_in]
   float* partial = nullptr;  // dw split-K partials
 };
 void layout_pl_bwd(Arena& ar, int64_t T, int k, int E, int64_t x_rows, int64_t d_in, int64_t d_out, bool x_grouped,
@@ -140,12 +156,15 @@ void layout_pl_bwd(Arena& ar, int64_t T, int k, int E, int64_t x_rows, int64_t d
   const int64_t M = T * k;
   const bool fan_k = !x_grouped && x_rows == T && k > 1;
   if (fan_k) w.pairs = static_cast<float*>(ar.take(size_t(M) * d_in * 4));
-  if (with_gates) w.dgpart = static_cast<float*>(ar.take(size_t(dg_slots(M, E, d_in, bf16)) * M * 4));
+  if (with_gates) {
+    w.dgpart = static_cast<float*>(ar.take(size_t(dg_slots(M, E, d_in, bf16)) * M * 4));
+    w.xg = ar.take(size_t(M) * d_in * (bf16 ? 2 : 4));
+  }
   w.partial = static_cast<float*>(ar.take(dw_partial_bytes(M, E, d_in, d_out, bf16)));
 }
 
 struct SavedLayout {
-  size_t off[7];
+  size_t off[6];
   size_t total;
 };
 SavedLayout saved_layout(int64_t T, int k, int E, int64_t d_ff, int act, int dtype) {
@@ -162,18 +181,19 @@ SavedLayout saved_layout(int64_t T, int k, int E, int64_t d_ff, int act, int dty
   s.off[3] = at(size_t(E + 1) * 4);
   s.off[4] = at(size_t(M) * d_ff * esize(dtype));
   s.off[5] = act == SMOE_ACT_SWIGLU ? at(size_t(M) * d_ff * esize(dtype)) : SIZE_MAX;
-  s.off[6] = at(size_t(M) * d_ff * esize(dtype));
   s.total = ar.used;
   return s;
 }
 
 struct MlpFwdWs {
   void* route = nullptr;
-  float* pairs = nullptr;
+  void* a = nullptr;         // activation, grouped [M, d_ff]
+  float* pairs = nullptr;    // expert outputs, scattered fp32 [M, d_model]
 };
-void layout_mlp_fwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, MlpFwdWs& w) {
+void layout_mlp_fwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t d_ff, int dtype, MlpFwdWs& w) {
   const int64_t M = T * k;
   w.route = ar.take(route_ws_bytes(M, E));
+  w.a = ar.take(size_t(M) * d_ff * esize(dtype));
   w.pairs = static_cast<float*>(ar.take(size_t(M) * d_model * 4));
 }
 
@@ -181,6 +201,7 @@ struct MlpBwdWs {
   float* dgpart = nullptr;
   void* dh1 = nullptr;
   void* dh3 = nullptr;
+  void* ag = nullptr;        // gate-scaled activation g*a, grouped [M, d_ff]
   float* pairs = nullptr;
   float* partial = nullptr;
 };
@@ -191,6 +212,7 @@ void layout_mlp_bwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t
   w.dgpart = static_cast<float*>(ar.take(size_t(dg_slots(M, E, d_ff, bf16)) * M * 4));
   w.dh1 = ar.take(size_t(M) * d_ff * esize(dtype));
   if (act == SMOE_ACT_SWIGLU) w.dh3 = ar.take(size_t(M) * d_ff * esize(dtype));
+  w.ag = ar.take(size_t(M) * d_ff * esize(dtype));
   w.pairs = static_cast<float*>(ar.take(size_t(M) * d_model * 4));
   const size_t p1 = dw_partial_bytes(M, E, d_ff, d_model, bf16);
   const size_t p2 = dw_partial_bytes(M, E, d_model, d_ff, bf16);
@@ -198,12 +220,16 @@ void layout_mlp_bwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t
 }
 
 // Weight gradient dw[e] = sum over e's rows of A(r)^T B(r): GEMM + reduction.
-int run_dw(GemmArgs a, int bf16, float* dw, float* partial, hipStream_t st, const char* where) {
+int run_dw(GemmArgs a, int bf16, float* dw, float* partial, hipStream_t st, int role, const char* where) {
   a.c0 = dw;
   a.partial = partial;
   GemmPlan pl;
   plan_gemm(a, pl, SEG_K, EPI_PARTIAL, 0, bf16, 1);
-  SMOE_HIP(launch_gemm(a, pl, st), where);
+  {
+    RoleTimer t(role, st);
+    SMOE_HIP(launch_gemm(a, pl, st), where);
+  }
+  RoleTimer t(SMOE_ROLE_DW_REDUCE, st);
   SMOE_HIP(launch_reduce_dw(partial, a.offsets, a.E, a.KS, int64_t(a.Mo) * a.N, dw, st), where);
   return SMOE_OK;
 }
@@ -228,6 +254,15 @@ const char* smoe_status_string(int status) {
 const char* smoe_last_error(void) { return g_last_error.c_str(); }
 
 int smoe_abi_version(void) { return 1; }
+
+int smoe_set_role_events(int32_t role, void* start_event, void* stop_event) {
+  if (role < 0 || role >= SMOE_ROLE_COUNT) return fail(SMOE_ERR_SHAPE, "role %d outside [0, %d)", role, SMOE_ROLE_COUNT);
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(SMOE_ERR_NULL, "attach both events or neither");
+  g_role_ev[role][0] = static_cast<hipEvent_t>(start_event);
+  g_role_ev[role][1] = static_cast<hipEvent_t>(stop_event);
+  return ok();
+}
 
 // ---------------------------------------------------------------- route --
 size_t smoe_route_workspace_bytes(int64_t T, int32_t k, int32_t E) {
@@ -292,6 +327,7 @@ int smoe_parallel_linear_fwd(const void* x, int64_t x_rows, int64_t d_in, const 
   a.N = int(d_out);
   a.K = a.K0 = int(d_in);
   a.a0 = a.a1 = x;
+  a.a_rows = x_rows;
   a.lda = d_in;
   a.a_scat = !x_grouped;
   a.a_fan = (!x_grouped && x_rows == T) ? k : 1;
@@ -305,12 +341,17 @@ int smoe_parallel_linear_fwd(const void* x, int64_t x_rows, int64_t d_in, const 
     a.c0 = wl.pairs;
     a.c_scat = 1;
     plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, 1);
-    SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_fwd gemm");
+    {
+      RoleTimer t(SMOE_ROLE_PL_FWD, st);
+      SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_fwd gemm");
+    }
+    RoleTimer t(SMOE_ROLE_COMBINE, st);
     SMOE_HIP(launch_combine(wl.pairs, gates, T, k, d_out, y, bf16, st), "parallel_linear_fwd combine");
   } else {
     a.c0 = y;
     a.c_scat = !y_grouped;
     plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, !bf16);
+    RoleTimer t(SMOE_ROLE_PL_FWD, st);
     SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_fwd gemm");
   }
   return ok();
@@ -365,6 +406,7 @@ int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in, const 
     a.N = int(d_in);
     a.K = a.K0 = int(d_out);
     a.a0 = a.a1 = dy;
+    a.a_rows = gates ? T : M;
     a.lda = d_out;
     a.a_scat = gates ? 1 : !y_grouped;
     a.a_fan = gates ? k : 1;
@@ -391,26 +433,41 @@ int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in, const 
       a.c_scat = !x_grouped;
       plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, !bf16);
     }
-    SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_bwd dx gemm");
+    {
+      RoleTimer t(SMOE_ROLE_PL_DX, st);
+      SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_bwd dx gemm");
+    }
     if (fan_k && dx) SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_in, dx, bf16, st), "parallel_linear_bwd ksum");
     if (dgates)
       SMOE_HIP(launch_reduce_dg(wl.dgpart, pl.slots, int(M), offsets, E, sorted_scattered_idxs, dgates, st),
                "parallel_linear_bwd dgates");
   }
   if (dw) {
+    // with gates, dw[e] = sum (g u)^T dy[t]: the gate scales a grouped copy
+    // of the input rows, so the weight-gradient product reads plain operands
     GemmArgs a = blank_args(offsets, sorted_scattered_idxs, E, int(M));
     a.Mo = int(d_in);
     a.N = int(d_out);
-    a.a0 = x;
+    if (gates) {
+      SMOE_HIP(launch_scale_rows(x, x_grouped, fan, gates, sorted_scattered_idxs, offsets, E, int(M), d_in, wl.xg,
+                                 bf16, st),
+               "parallel_linear_bwd scale");
+      a.a0 = wl.xg;
+      a.a_rows = M;
+      a.a_scat = 0;
+    } else {
+      a.a0 = x;
+      a.a_rows = x_rows;
+      a.a_scat = !x_grouped;
+      a.a_fan = fan;
+    }
     a.lda = d_in;
-    a.a_scat = !x_grouped;
-    a.a_fan = fan;
     a.b0 = dy;
     a.ldb = d_out;
+    a.b_rows = gates ? T : M;
     a.b_scat = gates ? 1 : !y_grouped;
     a.b_fan = gates ? k : 1;
-    a.b_gate = gates;
-    SMOE_TRY(run_dw(a, bf16, dw, wl.partial, st, "parallel_linear_bwd dw"));
+    SMOE_TRY(run_dw(a, bf16, dw, wl.partial, st, SMOE_ROLE_PL_DW, "parallel_linear_bwd dw"));
   }
   return ok();
 }
@@ -433,20 +490,20 @@ size_t smoe_mlp_saved_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, in
 }
 
 int smoe_mlp_saved_offsets(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act,
-                           int32_t dtype, size_t off[7]) {
+                           int32_t dtype, size_t off[6]) {
   (void)d_model;
   if (!off) return fail(SMOE_ERR_NULL, "off is NULL");
   SavedLayout s = saved_layout(T, k, E, d_ff, act, dtype);
-  for (int i = 0; i < 7; ++i) off[i] = s.off[i];
+  for (int i = 0; i < 6; ++i) off[i] = s.off[i];
   return ok();
 }
 
 size_t smoe_mlp_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act,
                                     int32_t dtype) {
-  (void)d_ff; (void)act; (void)dtype;
+  (void)act;
   Arena ar(nullptr);
   MlpFwdWs w;
-  layout_mlp_fwd(ar, T, k, E, d_model, w);
+  layout_mlp_fwd(ar, T, k, E, d_model, d_ff, dtype, w);
   return ar.used;
 }
 
@@ -471,7 +528,7 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
   if (saved_bytes < sl.total) return fail(SMOE_ERR_WORKSPACE, "saved_bytes=%zu < %zu", saved_bytes, sl.total);
   Arena ar(ws);
   MlpFwdWs wl;
-  layout_mlp_fwd(ar, T, k, E, d_model, wl);
+  layout_mlp_fwd(ar, T, k, E, d_model, d_ff, dtype, wl);
   if (ws_bytes < ar.used) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, ar.used);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* sv = static_cast<char*>(saved);
@@ -481,10 +538,13 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
   int* offsets = reinterpret_cast<int*>(sv + sl.off[3]);
   void* h1 = sv + sl.off[4];
   void* h3 = act == SMOE_ACT_SWIGLU ? sv + sl.off[5] : nullptr;
-  void* av = sv + sl.off[6];
+  void* av = wl.a;
   const int bf16 = dtype == SMOE_BF16;
 
-  SMOE_HIP(launch_route(expert_idxs, int(M), E, s_exp, s_sct, counts, offsets, wl.route, st), "mlp_fwd route");
+  {
+    RoleTimer t(SMOE_ROLE_ROUTE, st);
+    SMOE_HIP(launch_route(expert_idxs, int(M), E, s_exp, s_sct, counts, offsets, wl.route, st), "mlp_fwd route");
+  }
   if (M == 0) return ok();
 
   // layer 1: scattered x rows (fan-out k) -> grouped h (h1, h3) and a
@@ -492,6 +552,7 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
   a.N = int(d_ff);
   a.K = a.K0 = int(d_model);
   a.a0 = a.a1 = x;
+  a.a_rows = T;
   a.lda = d_model;
   a.a_scat = 1;
   a.a_fan = k;
@@ -509,13 +570,17 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
     plan_gemm(a, pl, SEG_M, EPI_SWIGLU_FWD, 1, bf16, 0);
   else
     plan_gemm(a, pl, SEG_M, EPI_GELU_FWD, 0, bf16, 0);
-  SMOE_HIP(launch_gemm(a, pl, st), "mlp_fwd layer 1");
+  {
+    RoleTimer t(SMOE_ROLE_UP, st);
+    SMOE_HIP(launch_gemm(a, pl, st), "mlp_fwd layer 1");
+  }
 
   // layer 2: grouped a -> scattered fp32 expert outputs
   GemmArgs b = blank_args(offsets, s_sct, E, int(M));
   b.N = int(d_model);
   b.K = b.K0 = int(d_ff);
   b.a0 = b.a1 = av;
+  b.a_rows = M;
   b.lda = d_ff;
   b.b0 = b.b1 = w2;
   b.ldb = d_model;
@@ -524,7 +589,11 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
   b.c_scat = 1;
   b.ldc = d_model;
   plan_gemm(b, pl, SEG_M, EPI_STORE, 0, bf16, 1);
-  SMOE_HIP(launch_gemm(b, pl, st), "mlp_fwd layer 2");
+  {
+    RoleTimer t(SMOE_ROLE_DOWN, st);
+    SMOE_HIP(launch_gemm(b, pl, st), "mlp_fwd layer 2");
+  }
+  RoleTimer t(SMOE_ROLE_COMBINE, st);
   SMOE_HIP(launch_combine(wl.pairs, gates, T, k, d_model, out, bf16, st), "mlp_fwd combine");
   return ok();
 }
@@ -571,7 +640,6 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
   const int* offsets = reinterpret_cast<const int*>(sv + sl.off[3]);
   const void* h1 = sv + sl.off[4];
   const void* h3 = act == SMOE_ACT_SWIGLU ? sv + sl.off[5] : nullptr;
-  const void* av = sv + sl.off[6];
   const int bf16 = dtype == SMOE_BF16;
   const bool swiglu = act == SMOE_ACT_SWIGLU;
 
@@ -582,12 +650,14 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
     return ok();
   }
 
-  // 1. dA = dout W2^T per grouped row, activation backward fused: dh (dh1, dh3)
-  //    and the gate-gradient partials <a, dout W2^T>
+  // 1. dA = dout W2^T per grouped row, activation backward fused: dh (dh1,
+  //    dh3), the gate-scaled activation g*a (recomputed from the saved h) and
+  //    the gate-gradient partials <a, dout W2^T>
   GemmArgs a = blank_args(offsets, s_sct, E, int(M));
   a.N = int(d_ff);
   a.K = a.K0 = int(d_model);
   a.a0 = a.a1 = dout;
+  a.a_rows = T;
   a.lda = d_model;
   a.a_scat = 1;
   a.a_fan = k;
@@ -602,26 +672,33 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
   a.dgpart = wl.dgpart;
   a.c0 = wl.dh1;
   a.c1 = wl.dh3;
+  a.c2 = wl.ag;
   a.ldc = d_ff;
   GemmPlan pl;
   plan_gemm(a, pl, SEG_M, swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, 0, bf16, 0);
-  SMOE_HIP(launch_gemm(a, pl, st), "mlp_bwd dA");
-  if (dgates)
+  {
+    RoleTimer t(SMOE_ROLE_DA, st);
+    SMOE_HIP(launch_gemm(a, pl, st), "mlp_bwd dA");
+  }
+  if (dgates) {
+    RoleTimer t(SMOE_ROLE_DG_REDUCE, st);
     SMOE_HIP(launch_reduce_dg(wl.dgpart, pl.slots, int(M), offsets, E, s_sct, dgates, st), "mlp_bwd dgates");
+  }
 
-  // 2. dW2[e] = sum a^T (g dout)
+  // 2. dW2[e] = sum (g a)^T dout
   {
     GemmArgs d = blank_args(offsets, s_sct, E, int(M));
     d.Mo = int(d_ff);
     d.N = int(d_model);
-    d.a0 = av;
+    d.a0 = wl.ag;
+    d.a_rows = M;
     d.lda = d_ff;
     d.b0 = dout;
+    d.b_rows = T;
     d.ldb = d_model;
     d.b_scat = 1;
     d.b_fan = k;
-    d.b_gate = gates;
-    SMOE_TRY(run_dw(d, bf16, dw2, wl.partial, st, "mlp_bwd dW2"));
+    SMOE_TRY(run_dw(d, bf16, dw2, wl.partial, st, SMOE_ROLE_DW2, "mlp_bwd dW2"));
   }
   // 3. dx contributions = dh W1^T (+ dh3 W3^T), then the k-sum
   {
@@ -631,6 +708,7 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
     d.K = swiglu ? int(2 * d_ff) : int(d_ff);
     d.a0 = wl.dh1;
     d.a1 = swiglu ? wl.dh3 : wl.dh1;
+    d.a_rows = M;
     d.lda = d_ff;
     d.b0 = w1;
     d.b1 = swiglu ? w3 : w1;
@@ -642,7 +720,11 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
     d.ldc = d_model;
     GemmPlan pd;
     plan_gemm(d, pd, SEG_M, EPI_STORE, 0, bf16, 1);
-    SMOE_HIP(launch_gemm(d, pd, st), "mlp_bwd dx");
+    {
+      RoleTimer t(SMOE_ROLE_DX, st);
+      SMOE_HIP(launch_gemm(d, pd, st), "mlp_bwd dx");
+    }
+    RoleTimer t(SMOE_ROLE_KSUM, st);
     SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_model, dx, bf16, st), "mlp_bwd ksum");
   }
   // 4. dW1[e] = sum x^T dh1 ; dW3[e] = sum x^T dh3
@@ -651,15 +733,17 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
     d.Mo = int(d_model);
     d.N = int(d_ff);
     d.a0 = x;
+    d.a_rows = T;
     d.lda = d_model;
     d.a_scat = 1;
     d.a_fan = k;
     d.b0 = wl.dh1;
+    d.b_rows = M;
     d.ldb = d_ff;
-    SMOE_TRY(run_dw(d, bf16, dw1, wl.partial, st, "mlp_bwd dW1"));
+    SMOE_TRY(run_dw(d, bf16, dw1, wl.partial, st, SMOE_ROLE_DW1, "mlp_bwd dW1"));
     if (swiglu) {
       d.b0 = wl.dh3;
-      SMOE_TRY(run_dw(d, bf16, dw3, wl.partial, st, "mlp_bwd dW3"));
+      SMOE_TRY(run_dw(d, bf16, dw3, wl.partial, st, SMOE_ROLE_DW3, "mlp_bwd dW3"));
     }
   }
   return ok();

@@ -5,11 +5,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #define SMOE_DEV __device__ __forceinline__
 
 namespace smoe {
 
 constexpr int kWave = 64;
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1, so
+// register arrays indexed by i stay in registers whatever the body size.
+template <class F, int... I>
+SMOE_DEV void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+SMOE_DEV void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---- bf16 <-> fp32 (bit level, round to nearest even) ---------------------
 SMOE_DEV float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }

@@ -105,6 +105,41 @@ hipError_t launch_reduce_dw(const float* partial, const int* offsets, int E, int
   return hipGetLastError();
 }
 
+// one grouped row per block-iteration, 4 columns per thread
+template <class T>
+__global__ __launch_bounds__(kEwThreads) void scale_rows_kernel(const T* __restrict__ x, int x_grouped, int fan,
+                                                                const float* __restrict__ gates,
+                                                                const int* __restrict__ sidx,
+                                                                const int* __restrict__ offsets, int E, int64_t d,
+                                                                T* __restrict__ out) {
+  const int rows = offsets[E];
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int s = sidx[r];
+    const int64_t xr = x_grouped ? r : s / fan;
+    const float g = gates[s];
+    for (int64_t c = int64_t(threadIdx.x) * 4; c < d; c += int64_t(kEwThreads) * 4) {
+      float v[4];
+      ld4<T>(x + xr * d + c, v);
+      for (int i = 0; i < 4; ++i) v[i] *= g;
+      st4<T>(out + int64_t(r) * d + c, v);
+    }
+  }
+}
+
+hipError_t launch_scale_rows(const void* x, int x_grouped, int fan, const float* gates, const int* sidx,
+                             const int* offsets, int E, int M, int64_t d, void* out, int bf16, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const unsigned g = unsigned(std::min(M, 1 << 16));
+  if (bf16)
+    hipLaunchKernelGGL(scale_rows_kernel<uint16_t>, dim3(g), dim3(kEwThreads), 0, st,
+                       static_cast<const uint16_t*>(x), x_grouped, fan, gates, sidx, offsets, E, d,
+                       static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL(scale_rows_kernel<float>, dim3(g), dim3(kEwThreads), 0, st, static_cast<const float*>(x),
+                       x_grouped, fan, gates, sidx, offsets, E, d, static_cast<float*>(out));
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(kEwThreads) void zero_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * int64_t(kEwThreads) + threadIdx.x; i < n; i += int64_t(gridDim.x) * kEwThreads)
     p[i] = 0u;

@@ -10,25 +10,30 @@
 // Summary: grouped GEMM fused with scattered reads and writes).
 //
 // bf16 kernel (MFMA):
-//  - 256 threads = 4 waves in a 2x2 grid; block tile BM x BN (128 or 256),
-//    K step 64; each wave owns (BM/2) x (BN/2) as 32x32 fragments of
-//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
-//  - LDS holds both operands as [row][64 k] bf16 (128-byte rows), 16-byte
-//    chunk c of row j stored at chunk c ^ (j & 7): MFMA fragment reads,
-//    direct row loads and the 8x8 transposing stores are all free of bank
-//    conflicts.  Two stages; one barrier per K step.
-//  - Operands whose K axis is contiguous in memory (gathered token rows,
-//    W[e] read as W^T) are copied 16 bytes per lane.  Operands whose K axis
-//    is strided (W[e] in the forward, both operands of the weight gradient)
-//    are read as 8 K-rows x 16 bytes per lane and transposed 8x8 in
-//    registers on the way into LDS.
+//  - 512 threads = 8 waves, two per SIMD, in a 2 (M) x 4 (N) grid over a
+//    BM x BN tile (128 or 256 each), K step 64.  Each wave owns
+//    (BM/2) x (BN/4) as 32x32 fragments of v_mfma_f32_32x32x16_bf16 with
+//    fp32 accumulators; the second wave on a SIMD keeps the matrix core busy
+//    while the first waits on LDS, copies or the barrier.
+//  - Every operand moves global -> LDS with buffer loads that write LDS
+//    directly (no register staging); out-of-range offsets read as zero,
+//    which pads ragged rows, columns and K without branches.  Two LDS stages.
+//  - An operand whose K axis is contiguous in memory (gathered token rows,
+//    W[e] read as W^T) is stored [row][64 k] (128-byte rows) and fragments
+//    are 128-bit LDS reads.  An operand whose K axis is strided (W[e] in the
+//    forward, both operands of the weight gradient) is stored [64 k][mn] as
+//    it sits in memory and fragments come from gfx950's transposing LDS read
+//    (ds_read_b64_tr_b16), which hands each lane four consecutive k of one
+//    mn: no transpose is ever done in registers.
+//  - Both layouts XOR-swizzle 16-byte chunks per row so that the 16 lanes
+//    served together by the 64-bank LDS hit distinct banks.
 //  - The MFMA is issued with the B fragment first, so each lane ends up
 //    holding one output row and runs of 4 consecutive columns: epilogue
 //    stores are 8 bytes (bf16) or 16 bytes (fp32) wide.
 //  - Workgroups are renumbered so that each XCD (blockIdx % 8 on MI355X)
-//    receives a contiguous range of tiles, and tiles are ordered in groups
-//    of 8 m-tiles sweeping n, so the tiles resident on one XCD share their
-//    A rows and weight panels in that XCD's L2.
+//    receives a contiguous range of tiles, ordered in groups of 8 m-tiles
+//    sweeping n, so concurrent tiles on one XCD share A rows and weight
+//    panels in that XCD's L2.
 //
 // fp32 kernel: the same contract with plain FMA on 64x64 tiles, used for
 // fp32 runs (a small, launch-bound regime).
@@ -38,53 +43,45 @@
 namespace smoe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;   // bf16 kernel
 constexpr int kBK = 64;
-constexpr int kRowBytes = kBK * 2;
+constexpr int kKRowBytes = kBK * 2;     // K-layout row: 64 bf16
+constexpr uint32_t kOOB = 0xFFFFFFF0u;  // byte offset past every buffer: reads as 0
+
+enum Lay { LAY_K = 0, LAY_MN = 1 };
 
 SMOE_DEV int xcd_remap(int b, int nblk) {
   const int per = nblk >> 3;  // the host pads the grid to a multiple of 8
   return (b & 7) * per + (b >> 3);
 }
 
-SMOE_DEV uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+SMOE_DEV int fdiv(int x, uint32_t m, int s) { return int((uint64_t(uint32_t(x)) * m) >> s); }
 
-// 8x8 transpose of bf16 held as 8 rows of 8 (two per dword).
-SMOE_DEV void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
-  uint32_t s[32], o[32];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    s[i * 4 + 0] = in[i].x; s[i * 4 + 1] = in[i].y; s[i * 4 + 2] = in[i].z; s[i * 4 + 3] = in[i].w;
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t a = s[(2 * d) * 4 + j / 2], b = s[(2 * d + 1) * 4 + j / 2];
-      o[j * 4 + d] = (j & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u) : __builtin_amdgcn_perm(b, a, 0x05040100u);
-    }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) out[j] = make_uint4(o[j * 4 + 0], o[j * 4 + 1], o[j * 4 + 2], o[j * 4 + 3]);
+// K-layout: chunk c (8 k) of row j is stored at chunk c ^ swz_k(j).  The 16
+// rows read by one 16-lane group span two rows per 256-byte bank window
+// (split by j & 1); (j >> 1) & 7 separates the eight rows of each parity.
+SMOE_DEV int swz_k(int row) { return (row >> 1) & 7; }
+// MN-layout: chunk c (8 mn) of k-row r is stored at chunk c ^ swz_mn(r).  A
+// transposing read takes 32 bytes from each of four consecutive k-rows; the
+// masks 0, 2, 4, 6 put those eight chunks on distinct banks.
+SMOE_DEV int swz_mn(int krow) { return (krow & 3) << 1; }
+
+SMOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < int64_t(kOOB) ? bytes : int64_t(kOOB);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(uint32_t(n)), 0x00020000);
 }
-
-// multiply the 8 bf16 values of a row by g and round back to bf16
-SMOE_DEV uint4 scale8(uint4 v, float g) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const float lo = __uint_as_float(w[d] << 16) * g, hi = __uint_as_float(w[d] & 0xffff0000u) * g;
-    w[d] = uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+// the 64 lanes of the wave each copy 16 bytes (at byte offset voff of the
+// buffer) to wave_lds + 16 * lane
+SMOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, char* wave_lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)wave_lds, 16, voff, 0, 0, 0);
 }
-
-template <int BM, int BN, int MODE, int EPI, int BNK, bool DUAL>
-struct TileShape {
-  static constexpr int FM = BM / 64, FN = BN / 64;
-  static constexpr int NCOLS = DUAL ? BN / 2 : BN;  // real output columns per tile
-};
+SMOE_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Which tile this workgroup computes.  Returns false if none.
 struct TileInfo {
@@ -124,195 +121,298 @@ SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
   }
 }
 
-template <int BM, int BN, int MODE, int EPI, int BNK, bool DUAL, class OutT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-  constexpr int FM = BM / 64, FN = BN / 64;
-  constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes, STAGE = A_BYTES + B_BYTES;
-  static_assert(!DUAL || (MODE == SEG_M && BNK == 0 && BN >= 128), "dual B layout");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+// ---------------------------------------------------------------------------
+// Operand tiles in LDS.
+//
+// K-layout tile of R rows: row j at j*128 bytes.  The copy of one K step is
+// R/64 buffer loads per wave; load t of wave w fills rows (8t + w)*8 .. +8,
+// lane L taking row +(L >> 3) and storing physical chunk L & 7, i.e. the
+// logical chunk (L & 7) ^ swz_k(row) of that row.
+//
+// MN-layout tile of R mn (R = 128 or 256) by 64 k: k-row r at r*2R bytes,
+// CPR = R/8 chunks per k-row, RPI = 64/CPR k-rows per wave load; load t of
+// wave w fills k-rows (8t + w)*RPI .. +RPI, lane L taking k-row +(L / CPR)
+// and physical chunk L % CPR (logical chunk (L % CPR) ^ swz_mn(k-row)).
+// ---------------------------------------------------------------------------
+template <int R>
+struct MnGeom {
+  static constexpr int RB = 2 * R;         // bytes per k-row
+  static constexpr int CPR = R / 8;        // 16-byte chunks per k-row
+  static constexpr int RPI = 64 / CPR;     // k-rows per wave load
+  static constexpr int NI = R / 64;        // loads per wave per K step
+};
+
+// lane's k-row and logical chunk in MN-layout load t of wave `wave`
+template <int R>
+SMOE_DEV void mn_slot(int t, int wave, int lane, int& krow, int& chunk) {
+  using G = MnGeom<R>;
+  krow = (t * 8 + wave) * G::RPI + lane / G::CPR;
+  chunk = (lane % G::CPR) ^ swz_mn(krow);
+}
+
+// 32x32x16 MFMA operand (lane: row lane&31, k = 16s + 8*(lane>>5) + 0..7)
+// from a K-layout tile
+SMOE_DEV bf16x8_t frag_k(const char* tile, int row0, int s, int lane) {
+  const int row = row0 + (lane & 31);
+  const int c = (2 * s + (lane >> 5)) ^ swz_k(row);
+  return *reinterpret_cast<const bf16x8_t*>(tile + row * kKRowBytes + (c << 4));
+}
+
+// the same operand from an MN-layout tile, through two transposing reads:
+// within each 16-lane group, lane i receives element i & 3 of the 8-byte
+// pieces addressed by lanes (i >> 2) + 4j, j = 0..3; lane i therefore
+// addresses k-row kb + (i >> 2), columns mb + 4*(i & 3) .. +3, and gets
+// column mb + i at k-rows kb .. kb+3.
+template <int R>
+SMOE_DEV bf16x8_t frag_mn(const char* tile, int m0, int s, int lane) {
+  using G = MnGeom<R>;
+  const int grp = lane >> 4, i = lane & 15;
+  const int mn = m0 + 16 * (grp & 1) + 4 * (i & 3);
+  const int kr = 16 * s + 8 * (grp >> 1) + (i >> 2);
+  const int c = mn >> 3, within = (mn & 7) * 2;
+  const char* p0 = tile + kr * G::RB + ((c ^ swz_mn(kr)) << 4) + within;
+  const char* p1 = tile + (kr + 4) * G::RB + ((c ^ swz_mn(kr + 4)) << 4) + within;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const lds_void_t*)p0);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const lds_void_t*)p1);
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int BM, int BN, int MODE, int EPI, int BLAY, bool DUAL, class OutT>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
+  constexpr int ALAY = MODE == SEG_M ? LAY_K : LAY_MN;
+  constexpr int FM = BM / 64, FN = BN / 128;   // fragments per wave
+  constexpr int WM = BM / 2, WN = BN / 4;      // wave tile
+  constexpr int A_BYTES = BM * kKRowBytes, B_BYTES = BN * kKRowBytes, STAGE = A_BYTES + B_BYTES;
+  static_assert(BN >= 128 && BM >= 128, "tile");
+  static_assert(!DUAL || (MODE == SEG_M && BLAY == LAY_MN && BN == 256), "dual B layout");
+  // two LDS stages as separate objects
+  __shared__ __attribute__((aligned(16))) char smem0[STAGE];
+  __shared__ __attribute__((aligned(16))) char smem1[STAGE];
 
   TileInfo T;
   if (!tile_of_block<BM, BN, MODE, DUAL>(p, T)) return;
   const Item& it = T.it;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int kb = tid & 7;    // 16-byte chunk (8 k) this thread moves
-  const int rb = tid >> 3;   // row / 8-column block this thread moves
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // ---------------- per-thread operand addressing --------------------------
-  const uint16_t* a0 = static_cast<const uint16_t*>(p.a0);
-  const uint16_t* a1 = static_cast<const uint16_t*>(p.a1);
-  const uint16_t* b0 = static_cast<const uint16_t*>(p.b0);
-  const uint16_t* b1 = static_cast<const uint16_t*>(p.b1);
+  // ---------------- K steps ------------------------------------------------
+  // SEG_M: K is [part 0: K0 columns of a0 / b0 | part 1: K-K0 of a1 / b1];
+  // each 64-wide step lies inside one part.  SEG_K: the chunk's rows.
+  const int K0 = MODE == SEG_M ? p.K0 : it.row1 - it.row0;
+  const int K1 = MODE == SEG_M ? p.K - p.K0 : 0;
+  const int KT0 = (K0 + kBK - 1) / kBK;
+  const int KT = KT0 + (K1 + kBK - 1) / kBK;
 
-  constexpr int AR = BM / 32;                    // SEG_M: A rows per thread
-  constexpr int BR = BN / 32;                    // SEG_M, BNK: B rows per thread
-  int64_t a_off[MODE == SEG_M ? AR : 1];
-  bool a_ok[MODE == SEG_M ? AR : 1];
-  int64_t b_off[(MODE == SEG_M && BNK) ? BR : 1];
-  bool b_ok[(MODE == SEG_M && BNK) ? BR : 1];
-  const uint16_t* bt_base = nullptr;             // SEG_M, W[k][n]: column block base
-  bool bt_ok = false;
-  int Kloop;
+  // ---------------- per-lane copy addressing -------------------------------
+  constexpr int NA = BM / 64, NB = BN / 64;     // buffer loads per wave per operand
+  __amdgpu_buffer_rsrc_t rA0, rA1, rB0, rB1;
+  uint32_t a_off[NA];   // K-layout: row byte offset; MN-layout: column byte offset
+  uint32_t b_off[NB];
+  bool b_ok[NB];
 
   if constexpr (MODE == SEG_M) {
-#pragma unroll
-    for (int i = 0; i < AR; ++i) {
-      const int gr = it.row0 + rb + 32 * i;
-      a_ok[i] = gr < it.row1;
-      const int src = a_ok[i] ? (p.a_scat ? p.sidx[gr] / p.a_fan : gr) : 0;
-      a_off[i] = int64_t(src) * p.lda;
-    }
-    if constexpr (BNK) {
-#pragma unroll
-      for (int i = 0; i < BR; ++i) {
-        const int n = T.n0 + rb + 32 * i;
-        b_ok[i] = n < p.N;
-        b_off[i] = int64_t(it.e) * p.b_es + int64_t(b_ok[i] ? n : 0) * p.ldb;
-      }
+    const int64_t a_bytes = p.a_rows * p.lda * 2;
+    rA0 = make_rsrc(p.a0, a_bytes);
+    rA1 = make_rsrc(p.a1, a_bytes);
+    static_for<NA>([&](auto t) {
+      const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
+      const int gr = it.row0 + row;
+      const int src = gr < it.row1 ? (p.a_scat ? p.sidx[gr] / p.a_fan : gr) : -1;
+      a_off[t] = src >= 0 ? uint32_t(int64_t(src) * p.lda * 2) : kOOB;
+    });
+    const uint16_t* be0 = static_cast<const uint16_t*>(p.b0) + int64_t(it.e) * p.b_es;
+    const uint16_t* be1 = static_cast<const uint16_t*>(p.b1) + int64_t(it.e) * p.b_es;
+    if constexpr (BLAY == LAY_K) {
+      // W[e] viewed [n][k]: N rows of ldb
+      const int64_t b_bytes = int64_t(p.N) * p.ldb * 2;
+      rB0 = make_rsrc(be0, b_bytes);
+      rB1 = make_rsrc(be1, b_bytes);
+      static_for<NB>([&](auto t) {
+        const int n = T.n0 + (int(t) * 8 + wave) * 8 + (lane >> 3);
+        b_off[t] = n < p.N ? uint32_t(int64_t(n) * p.ldb * 2) : kOOB;
+        b_ok[t] = true;
+      });
     } else {
-      if (rb < BN / 8) {
-        const int j = rb * 8;  // tile column block
-        int col;
-        const uint16_t* base = b0;
-        if constexpr (DUAL) {
-          const int wnp = j / (BN / 2), jj = j % (BN / 2);
-          base = (jj / (BN / 4)) ? b1 : b0;
-          col = T.n0 + wnp * (BN / 4) + jj % (BN / 4);
-        } else {
-          col = T.n0 + j;
-        }
-        bt_ok = col < p.N;
-        bt_base = base + int64_t(it.e) * p.b_es + (bt_ok ? col : 0);
-      }
+      // W[e] viewed [k][n]: K rows of ldb.  Dual: the tile is two 128-column
+      // sub-tiles, W1 columns then W3 columns (loads t < NB/2 fill the first)
+      const int64_t b_bytes = int64_t(p.K0) * p.ldb * 2;
+      rB0 = make_rsrc(be0, b_bytes);
+      rB1 = make_rsrc(be1, b_bytes);
+      static_for<NB>([&](auto t) {
+        int krow, c;
+        if constexpr (DUAL) mn_slot<BN / 2>(int(t) % (NB / 2), wave, lane, krow, c);
+        else mn_slot<BN>(int(t), wave, lane, krow, c);
+        const int col = T.n0 + 8 * c;
+        b_ok[t] = col < p.N;
+        b_off[t] = uint32_t(col) * 2;
+      });
     }
-    Kloop = p.K;
   } else {
-    Kloop = it.row1 - it.row0;
+    rA0 = make_rsrc(p.a0, p.a_rows * p.lda * 2);
+    rA1 = rA0;
+    rB0 = make_rsrc(p.b0, p.b_rows * p.ldb * 2);
+    rB1 = rB0;
+    static_for<NA>([&](auto t) {
+      int krow, c;
+      mn_slot<BM>(int(t), wave, lane, krow, c);
+      const int i = T.m0 + 8 * c;
+      a_off[t] = i < p.Mo ? uint32_t(i) * 2 : kOOB;
+    });
+    static_for<NB>([&](auto t) {
+      int krow, c;
+      mn_slot<BN>(int(t), wave, lane, krow, c);
+      const int j = T.n0 + 8 * c;
+      b_ok[t] = j < p.N;
+      b_off[t] = uint32_t(j) * 2;
+    });
   }
-  const int KT = (Kloop + kBK - 1) / kBK;
 
-  // ---------------- global -> register prefetch ----------------------------
-  uint4 ra[MODE == SEG_M ? AR : 8];
-  uint4 rbv[(MODE == SEG_M && BNK) ? BR : 8];
-
-  auto load = [&](int kt) {
-    const int k0 = kt * kBK;
-    if constexpr (MODE == SEG_M) {
-      const int kk = k0 + kb * 8;
-      const bool kok = kk < p.K;
-      const uint16_t* abase = kk < p.K0 ? a0 + kk : a1 + (kk - p.K0);
-#pragma unroll
-      for (int i = 0; i < AR; ++i) ra[i] = (a_ok[i] && kok) ? ldg16(abase + a_off[i]) : make_uint4(0, 0, 0, 0);
-      if constexpr (BNK) {
-        const uint16_t* bbase = kk < p.K0 ? b0 + kk : b1 + (kk - p.K0);
-#pragma unroll
-        for (int i = 0; i < BR; ++i) rbv[i] = (b_ok[i] && kok) ? ldg16(bbase + b_off[i]) : make_uint4(0, 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int k = k0 + kb * 8 + i;
-          rbv[i] = (bt_ok && k < p.K) ? ldg16(bt_base + int64_t(k) * p.ldb) : make_uint4(0, 0, 0, 0);
-        }
-      }
-    } else {
-      // eight consecutive grouped rows of this chunk feed both operands
-      const int ia = T.m0 + rb * 8, jb = T.n0 + rb * 8;
-      const bool aok = rb < BM / 8 && ia < p.Mo;
-      const bool bok = rb < BN / 8 && jb < p.N;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = it.row0 + k0 + kb * 8 + i;
-        const bool rok = r < it.row1;
-        int s = 0;
-        if (rok && (p.a_scat || p.b_scat || p.b_gate)) s = p.sidx[r];
-        const int arow = p.a_scat ? s / p.a_fan : r;
-        const int brow = p.b_scat ? s / p.b_fan : r;
-        ra[i] = (rok && aok) ? ldg16(a0 + int64_t(arow) * p.lda + ia) : make_uint4(0, 0, 0, 0);
-        uint4 v = (rok && bok) ? ldg16(b0 + int64_t(brow) * p.ldb + jb) : make_uint4(0, 0, 0, 0);
-        if (p.b_gate) v = scale8(v, rok ? p.b_gate[s] : 0.f);
-        rbv[i] = v;
-      }
+  // SEG_K: source rows of this lane's k-rows for the next K step, fetched one
+  // step ahead so the index -> row -> data chain never stalls the loop
+  int ia_row[MODE == SEG_K ? NA : 1];
+  int ib_row[MODE == SEG_K ? NB : 1];
+  auto load_idx = [&](int kt) {
+    if constexpr (MODE == SEG_K) {
+      static_for<NA>([&](auto t) {
+        int krow, c;
+        mn_slot<BM>(int(t), wave, lane, krow, c);
+        const int r = it.row0 + kt * kBK + krow;
+        const int rc = min(r, it.row1 - 1);
+        const int src = p.a_scat ? fdiv(p.sidx[rc], p.a_fan_m, p.a_fan_s) : rc;
+        ia_row[t] = r < it.row1 ? src : -1;
+      });
+      static_for<NB>([&](auto t) {
+        int krow, c;
+        mn_slot<BN>(int(t), wave, lane, krow, c);
+        const int r = it.row0 + kt * kBK + krow;
+        const int rc = min(r, it.row1 - 1);
+        const int src = p.b_scat ? fdiv(p.sidx[rc], p.b_fan_m, p.b_fan_s) : rc;
+        ib_row[t] = r < it.row1 ? src : -1;
+      });
     }
   };
 
-  // ---------------- register -> LDS --------------------------------------
-  auto store = [&](int stage) {
-    char* As = smem + stage * STAGE;
-    char* Bs = As + A_BYTES;
+  // ---------------- copy step kt into stage `stg` -------------------------
+  auto issue = [&](int kt, char* stg) {
+    char* As = stg;
+    char* Bs = stg + A_BYTES;
     if constexpr (MODE == SEG_M) {
-#pragma unroll
-      for (int i = 0; i < AR; ++i) {
-        const int row = rb + 32 * i;
-        *reinterpret_cast<uint4*>(As + row * kRowBytes + ((kb ^ (row & 7)) << 4)) = ra[i];
-      }
-      if constexpr (BNK) {
-#pragma unroll
-        for (int i = 0; i < BR; ++i) {
-          const int row = rb + 32 * i;
-          *reinterpret_cast<uint4*>(Bs + row * kRowBytes + ((kb ^ (row & 7)) << 4)) = rbv[i];
-        }
-      } else if (rb < BN / 8) {
-        uint4 t[8];
-        transpose8(rbv, t);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint4*>(Bs + (rb * 8 + j) * kRowBytes + ((kb ^ j) << 4)) = t[j];
+      const bool part1 = kt >= KT0;
+      const int kl = (part1 ? kt - KT0 : kt) * kBK;
+      const int Kp = part1 ? K1 : K0;
+      // K-layout A: lane copies logical chunk (lane & 7) ^ swz_k(row)
+      static_for<NA>([&](auto t) {
+        const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
+        const int kb = (lane & 7) ^ swz_k(row);
+        const bool ok = a_off[t] != kOOB && kl + kb * 8 < Kp;
+        const uint32_t vo = ok ? a_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
+        dma16(part1 ? rA1 : rA0, As + (int(t) * 8 + wave) * 8 * kKRowBytes, vo);
+      });
+      if constexpr (BLAY == LAY_K) {
+        static_for<NB>([&](auto t) {
+          const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
+          const int kb = (lane & 7) ^ swz_k(row);
+          const bool ok = b_off[t] != kOOB && kl + kb * 8 < Kp;
+          const uint32_t vo = ok ? b_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
+          dma16(part1 ? rB1 : rB0, Bs + (int(t) * 8 + wave) * 8 * kKRowBytes, vo);
+        });
+      } else {
+        static_for<NB>([&](auto t) {
+          int krow, c;
+          char* dst;
+          if constexpr (DUAL) {
+            using G = MnGeom<BN / 2>;
+            constexpr int tt = int(t) % (NB / 2);
+            mn_slot<BN / 2>(tt, wave, lane, krow, c);
+            dst = Bs + (int(t) / (NB / 2)) * (BN / 2) * kKRowBytes + (tt * 8 + wave) * G::RPI * G::RB;
+          } else {
+            using G = MnGeom<BN>;
+            mn_slot<BN>(int(t), wave, lane, krow, c);
+            dst = Bs + (int(t) * 8 + wave) * G::RPI * G::RB;
+          }
+          const int k = kl + krow;
+          const bool ok = b_ok[t] && k < K0;
+          const uint32_t vo = ok ? uint32_t(int64_t(k) * p.ldb * 2) + b_off[t] : kOOB;
+          dma16((DUAL && int(t) >= NB / 2) ? rB1 : rB0, dst, vo);
+        });
       }
     } else {
-      uint4 t[8];
-      if (rb < BM / 8) {
-        transpose8(ra, t);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint4*>(As + (rb * 8 + j) * kRowBytes + ((kb ^ j) << 4)) = t[j];
-      }
-      if (rb < BN / 8) {
-        transpose8(rbv, t);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint4*>(Bs + (rb * 8 + j) * kRowBytes + ((kb ^ j) << 4)) = t[j];
-      }
+      using GA = MnGeom<BM>;
+      using GB = MnGeom<BN>;
+      static_for<NA>([&](auto t) {
+        const bool ok = ia_row[t] >= 0 && a_off[t] != kOOB;
+        const uint32_t vo = ok ? uint32_t(int64_t(ia_row[t]) * p.lda * 2) + a_off[t] : kOOB;
+        dma16(rA0, As + (int(t) * 8 + wave) * GA::RPI * GA::RB, vo);
+      });
+      static_for<NB>([&](auto t) {
+        const bool ok = ib_row[t] >= 0 && b_ok[t];
+        const uint32_t vo = ok ? uint32_t(int64_t(ib_row[t]) * p.ldb * 2) + b_off[t] : kOOB;
+        dma16(rB0, Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB, vo);
+      });
     }
   };
 
   f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  static_for<FM>([&](auto i) {
+    static_for<FN>([&](auto j) {
+      static_for<16>([&](auto v) { acc[i][j][int(v)] = 0.f; });
+    });
+  });
 
-  if (KT > 0) {
-    load(0);
-    store(0);
-  }
+  auto frags = [&](const char* As, const char* Bs, int s, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
+    static_for<FM>([&](auto fm) {
+      if constexpr (ALAY == LAY_K) af[fm] = frag_k(As, wm * WM + fm * 32, s, lane);
+      else af[fm] = frag_mn<BM>(As, wm * WM + fm * 32, s, lane);
+    });
+    static_for<FN>([&](auto fn) {
+      if constexpr (MODE == SEG_M && BLAY == LAY_K) {
+        bf[fn] = frag_k(Bs, wn * WN + fn * 32, s, lane);
+      } else if constexpr (DUAL) {
+        // fn 0: W1 sub-tile, fn 1: W3 sub-tile, same 32 columns
+        bf[fn] = frag_mn<BN / 2>(Bs + int(fn) * (BN / 2) * kKRowBytes, wn * (WN / 2), s, lane);
+      } else {
+        bf[fn] = frag_mn<BN>(Bs, wn * WN + fn * 32, s, lane);
+      }
+    });
+  };
+  auto compute = [&](const char* stg) {
+    const char* As = stg;
+    const char* Bs = stg + A_BYTES;
+    bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
+    frags(As, Bs, 0, af0, bf0);
+    // double-buffered fragments: slice s+1 is read while slice s multiplies
+    static_for<kBK / 16>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      if constexpr (S + 1 < kBK / 16) {
+        if constexpr ((S & 1) == 0) frags(As, Bs, S + 1, af1, bf1);
+        else frags(As, Bs, S + 1, af0, bf0);
+      }
+      auto& A = (S & 1) == 0 ? af0 : af1;
+      auto& B = (S & 1) == 0 ? bf0 : bf1;
+      static_for<FM>([&](auto fm) {
+        static_for<FN>([&](auto fn) {
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[fn], A[fm], acc[fm][fn], 0, 0, 0);
+        });
+      });
+    });
+  };
+
+  if constexpr (MODE == SEG_K) load_idx(0);
+  if (KT > 0) issue(0, smem0);
+  if constexpr (MODE == SEG_K) load_idx(1);
+  wait_vmem();
   __syncthreads();
-  const int rsw = lane & 7;  // fragment rows are 32-aligned, so row & 7 == lane & 7
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load(kt + 1);
-    const char* As = smem + cur * STAGE;
-    const char* Bs = As + A_BYTES;
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int coff = ((2 * s + (lane >> 5)) ^ rsw) << 4;
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[fm] = *reinterpret_cast<const bf16x8_t*>(As + (wm * (BM / 2) + fm * 32 + (lane & 31)) * kRowBytes + coff);
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        bfr[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * (BN / 2) + fn * 32 + (lane & 31)) * kRowBytes + coff);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0);
+    char* cur = (kt & 1) ? smem1 : smem0;
+    char* nxt = (kt & 1) ? smem0 : smem1;
+    if (kt + 1 < KT) issue(kt + 1, nxt);
+    if constexpr (MODE == SEG_K) {
+      if (kt + 2 < KT) load_idx(kt + 2);
     }
-    if (kt + 1 < KT) store(cur ^ 1);
+    compute(cur);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -323,22 +423,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   if constexpr (MODE == SEG_K) {
     float* dst = (it.nitems == 1) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
                                   : p.partial + int64_t(T.chunk) * p.Mo * p.N;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int i = T.m0 + wm * (BM / 2) + fm * 32 + (lane & 31);
-      if (i >= p.Mo) continue;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = T.n0 + wn * (BN / 2) + fn * 32 + 8 * q + csub;
-          if (j < p.N) {
-            const float v[4] = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
-                                acc[fm][fn][4 * q + 3]};
-            st4<float>(dst + int64_t(i) * p.N + j, v);
-          }
-        }
-    }
+    static_for<FM>([&](auto fm) {
+      const int i = T.m0 + wm * WM + fm * 32 + (lane & 31);
+      if (i < p.Mo) {
+        static_for<FN>([&](auto fn) {
+          static_for<4>([&](auto q) {
+            const int j = T.n0 + wn * WN + fn * 32 + 8 * q + csub;
+            if (j < p.N) {
+              const float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1],
+                                  acc[fm][fn][4 * int(q) + 2], acc[fm][fn][4 * int(q) + 3]};
+              st4<float>(dst + int64_t(i) * p.N + j, v);
+            }
+          });
+        });
+      }
+    });
   } else {
     OutT* c0 = static_cast<OutT*>(p.c0);
     OutT* c1 = static_cast<OutT*>(p.c1);
@@ -346,85 +445,87 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     const uint16_t* x0 = static_cast<const uint16_t*>(p.aux0);
     const uint16_t* x1 = static_cast<const uint16_t*>(p.aux1);
     constexpr int FNR = DUAL ? FN / 2 : FN;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int gr = it.row0 + wm * (BM / 2) + fm * 32 + (lane & 31);
+    static_for<FM>([&](auto fm) {
+      const int gr = it.row0 + wm * WM + fm * 32 + (lane & 31);
       const bool rok = gr < it.row1;
       const int sp = rok ? p.sidx[gr] : 0;
       const float g = (p.gate && rok) ? p.gate[sp] : 1.f;
       const int64_t crow = p.c_scat ? sp : gr;
       const int64_t xrow = p.aux_scat ? sp / p.aux_fan : gr;
       float dgacc = 0.f;
-#pragma unroll
-      for (int fn = 0; fn < FNR; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = T.n0 + (DUAL ? wn * (BN / 4) : wn * (BN / 2)) + fn * 32 + 8 * q + csub;
-          if (!rok || n >= p.N) continue;
-          float v[4] = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
-          if constexpr (EPI == EPI_STORE) {
-            if (p.dgpart) {
-              float xv[4];
-              ld4<uint16_t>(x0 + xrow * p.ldaux + n, xv);
-              dgacc += xv[0] * v[0] + xv[1] * v[1] + xv[2] * v[2] + xv[3] * v[3];
-            }
-            if (c0) {
-              if (p.gate) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] *= g;
+      static_for<FNR>([&](auto fn) {
+        static_for<4>([&](auto q) {
+          const int n = T.n0 + (DUAL ? wn * (WN / 2) : wn * WN) + fn * 32 + 8 * q + csub;
+          if (rok && n < p.N) {
+            float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1], acc[fm][fn][4 * int(q) + 2],
+                          acc[fm][fn][4 * int(q) + 3]};
+            if constexpr (EPI == EPI_STORE) {
+              if (p.dgpart) {
+                float xv[4];
+                ld4<uint16_t>(x0 + xrow * p.ldaux + n, xv);
+                dgacc += xv[0] * v[0] + xv[1] * v[1] + xv[2] * v[2] + xv[3] * v[3];
               }
-              st4<OutT>(c0 + crow * p.ldc + n, v);
+              if (c0) {
+                if (p.gate) {
+                  static_for<4>([&](auto i) { v[i] *= g; });
+                }
+                st4<OutT>(c0 + crow * p.ldc + n, v);
+              }
+            } else if constexpr (EPI == EPI_GELU_FWD) {
+              float h[4], a[4];
+              static_for<4>([&](auto i) {
+                h[i] = stored<OutT>(v[i]);
+                a[i] = gelu_f(h[i]);
+              });
+              st4<OutT>(c0 + int64_t(gr) * p.ldc + n, h);
+              st4<OutT>(c1 + int64_t(gr) * p.ldc + n, a);
+            } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+              float h1[4], h3[4], a[4];
+              static_for<4>([&](auto i) {
+                h1[i] = stored<OutT>(v[i]);
+                h3[i] = stored<OutT>(acc[fm][fn + FN / 2][4 * int(q) + int(i)]);
+                a[i] = silu_f(h1[i]) * h3[i];
+              });
+              st4<OutT>(c0 + int64_t(gr) * p.ldc + n, h1);
+              st4<OutT>(c1 + int64_t(gr) * p.ldc + n, h3);
+              st4<OutT>(c2 + int64_t(gr) * p.ldc + n, a);
+            } else if constexpr (EPI == EPI_GELU_BWD) {
+              float h[4], dh[4], ag[4];
+              ld4<uint16_t>(x0 + int64_t(gr) * p.ldaux + n, h);
+              static_for<4>([&](auto i) {
+                const float a = stored<OutT>(gelu_f(h[i]));
+                dgacc += a * v[i];
+                dh[i] = g * v[i] * gelu_grad_f(h[i]);
+                ag[i] = g * a;
+              });
+              st4<OutT>(c0 + int64_t(gr) * p.ldc + n, dh);
+              st4<OutT>(c2 + int64_t(gr) * p.ldc + n, ag);
+            } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+              float h1[4], h3[4], d1[4], d3[4], ag[4];
+              ld4<uint16_t>(x0 + int64_t(gr) * p.ldaux + n, h1);
+              ld4<uint16_t>(x1 + int64_t(gr) * p.ldaux + n, h3);
+              static_for<4>([&](auto i) {
+                const float sg = sigmoid_f(h1[i]);
+                const float si = h1[i] * sg;
+                const float a = stored<OutT>(si * h3[i]);
+                dgacc += a * v[i];
+                const float dA = g * v[i];
+                d1[i] = dA * h3[i] * (sg * (1.0f + h1[i] * (1.0f - sg)));
+                d3[i] = dA * si;
+                ag[i] = g * a;
+              });
+              st4<OutT>(c0 + int64_t(gr) * p.ldc + n, d1);
+              st4<OutT>(c1 + int64_t(gr) * p.ldc + n, d3);
+              st4<OutT>(c2 + int64_t(gr) * p.ldc + n, ag);
             }
-          } else if constexpr (EPI == EPI_GELU_FWD) {
-            float h[4], a[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              h[i] = stored<OutT>(v[i]);
-              a[i] = gelu_f(h[i]);
-            }
-            st4<OutT>(c0 + int64_t(gr) * p.ldc + n, h);
-            st4<OutT>(c1 + int64_t(gr) * p.ldc + n, a);
-          } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-            float h1[4], h3[4], a[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              h1[i] = stored<OutT>(v[i]);
-              h3[i] = stored<OutT>(acc[fm][fn + FN / 2][4 * q + i]);
-              a[i] = silu_f(h1[i]) * h3[i];
-            }
-            st4<OutT>(c0 + int64_t(gr) * p.ldc + n, h1);
-            st4<OutT>(c1 + int64_t(gr) * p.ldc + n, h3);
-            st4<OutT>(c2 + int64_t(gr) * p.ldc + n, a);
-          } else if constexpr (EPI == EPI_GELU_BWD) {
-            float h[4], dh[4];
-            ld4<uint16_t>(x0 + int64_t(gr) * p.ldaux + n, h);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              dgacc += stored<OutT>(gelu_f(h[i])) * v[i];
-              dh[i] = g * v[i] * gelu_grad_f(h[i]);
-            }
-            st4<OutT>(c0 + int64_t(gr) * p.ldc + n, dh);
-          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            float h1[4], h3[4], d1[4], d3[4];
-            ld4<uint16_t>(x0 + int64_t(gr) * p.ldaux + n, h1);
-            ld4<uint16_t>(x1 + int64_t(gr) * p.ldaux + n, h3);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float sg = silu_f(h1[i]);
-              dgacc += stored<OutT>(sg * h3[i]) * v[i];
-              const float dA = g * v[i];
-              d1[i] = dA * h3[i] * silu_grad_f(h1[i]);
-              d3[i] = dA * sg;
-            }
-            st4<OutT>(c0 + int64_t(gr) * p.ldc + n, d1);
-            st4<OutT>(c1 + int64_t(gr) * p.ldc + n, d3);
           }
-        }
+        });
+      });
       if (p.dgpart) {
         dgacc += __shfl_xor(dgacc, 32, kWave);
-        if (lane < 32 && rok) p.dgpart[int64_t(T.nt * 2 + wn) * p.M + gr] = dgacc;
+        if (lane < 32 && rok) p.dgpart[int64_t(T.nt * 4 + wn) * p.M + gr] = dgacc;
       }
-    }
+    });
   }
 }
 
@@ -433,10 +534,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 // (rows ty*4+i, columns tx*4+j).  Element-wise operand access through the
 // same contract as the bf16 kernel.
 // ============================================================================
+constexpr int kFThreads = 256;
 constexpr int kFBM = 64, kFBN = 64, kFBK = 16;
 
 template <int MODE, int EPI, int BNK, bool DUAL>
-__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kFThreads) void gemm_f32_kernel(GemmArgs p) {
   __shared__ float As[kFBK][kFBM + 4];
   __shared__ float Bs[kFBK][kFBN + 4];
   __shared__ float B3s[DUAL ? kFBK : 1][kFBN + 4];
@@ -477,20 +579,18 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
     } else {
       const int r = it.row0 + k, j = T.n0 + n;
       if (r >= it.row1 || j >= p.N) return 0.f;
-      int s = (p.b_scat || p.b_gate) ? p.sidx[r] : 0;
-      const int src = p.b_scat ? s / p.b_fan : r;
-      const float g = p.b_gate ? p.b_gate[s] : 1.f;
-      return g * b0[int64_t(src) * p.ldb + j];
+      const int src = p.b_scat ? p.sidx[r] / p.b_fan : r;
+      return b0[int64_t(src) * p.ldb + j];
     }
   };
 
   float acc[4][4] = {}, acc3[4][4] = {};
   for (int k0 = 0; k0 < Kloop; k0 += kFBK) {
-    for (int l = tid; l < kFBK * kFBM; l += kThreads) {
+    for (int l = tid; l < kFBK * kFBM; l += kFThreads) {
       const int m = l / kFBK, kk = l % kFBK;
       As[kk][m] = Aval(m, k0 + kk);
     }
-    for (int l = tid; l < kFBK * kFBN; l += kThreads) {
+    for (int l = tid; l < kFBK * kFBN; l += kFThreads) {
       const int n = l % kFBN, kk = l / kFBN;
       Bs[kk][n] = Bval(k0 + kk, n, 0);
       if constexpr (DUAL) B3s[kk][n] = Bval(k0 + kk, n, 1);
@@ -564,25 +664,31 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
           st4<float>(c1 + int64_t(gr) * p.ldc + n, acc3[i]);
           st4<float>(c2 + int64_t(gr) * p.ldc + n, a);
         } else if constexpr (EPI == EPI_GELU_BWD) {
-          float h[4], dh[4];
+          float h[4], dh[4], ag[4];
           ld4<float>(x0 + int64_t(gr) * p.ldaux + n, h);
           for (int j = 0; j < 4; ++j) {
-            dgacc += gelu_f(h[j]) * v[j];
+            const float a = gelu_f(h[j]);
+            dgacc += a * v[j];
             dh[j] = g * v[j] * gelu_grad_f(h[j]);
+            ag[j] = g * a;
           }
           st4<float>(c0 + int64_t(gr) * p.ldc + n, dh);
+          st4<float>(c2 + int64_t(gr) * p.ldc + n, ag);
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-          float h1[4], h3[4], d1[4], d3[4];
+          float h1[4], h3[4], d1[4], d3[4], ag[4];
           ld4<float>(x0 + int64_t(gr) * p.ldaux + n, h1);
           ld4<float>(x1 + int64_t(gr) * p.ldaux + n, h3);
           for (int j = 0; j < 4; ++j) {
             const float sg = silu_f(h1[j]);
-            dgacc += sg * h3[j] * v[j];
+            const float a = sg * h3[j];
+            dgacc += a * v[j];
             d1[j] = g * v[j] * h3[j] * silu_grad_f(h1[j]);
             d3[j] = g * v[j] * sg;
+            ag[j] = g * a;
           }
           st4<float>(c0 + int64_t(gr) * p.ldc + n, d1);
           st4<float>(c1 + int64_t(gr) * p.ldc + n, d3);
+          st4<float>(c2 + int64_t(gr) * p.ldc + n, ag);
         }
       }
       if (p.dgpart) {
@@ -603,10 +709,12 @@ static int64_t pad8(int64_t n) { return (n + 7) & ~int64_t(7); }
 
 bool plan_gemm(GemmArgs& a, GemmPlan& pl, int mode, int epi, int dual, int bf16, int out_f32) {
   pl.mode = mode;
-  pl.out_f32 = out_f32;
   pl.epi = epi;
   pl.dual = dual;
   pl.bf16 = bf16;
+  pl.out_f32 = out_f32;
+  fastdiv_magic(std::max(a.a_fan, 1), a.a_fan_m, a.a_fan_s);
+  fastdiv_magic(std::max(a.b_fan, 1), a.b_fan_m, a.b_fan_s);
   constexpr int kCUs = 256;
   if (!bf16) {
     pl.bm = kFBM;
@@ -622,9 +730,8 @@ bool plan_gemm(GemmArgs& a, GemmPlan& pl, int mode, int epi, int dual, int bf16,
     }
   } else {
     if (mode == SEG_M) {
-      const int ncols_needed = dual ? 2 * a.N : a.N;
       const int64_t rows_per_expert = std::max<int64_t>(1, a.M / std::max(1, a.E));
-      pl.bn = (ncols_needed >= 256) ? 256 : 128;
+      pl.bn = (dual || a.N >= 256) ? 256 : 128;
       pl.bm = (rows_per_expert >= 192) ? 256 : 128;
       // prefer smaller tiles when the big ones leave most CUs idle
       auto tiles = [&](int bm, int bn) {
@@ -632,11 +739,11 @@ bool plan_gemm(GemmArgs& a, GemmPlan& pl, int mode, int epi, int dual, int bf16,
         return (ceil_div(a.M, bm) + a.E / 2) * ceil_div(a.N, ncols);
       };
       if (tiles(pl.bm, pl.bn) < 2 * kCUs && pl.bm == 256) pl.bm = 128;
-      if (tiles(pl.bm, pl.bn) < 2 * kCUs && pl.bn == 256) pl.bn = 128;
+      if (tiles(pl.bm, pl.bn) < 2 * kCUs && pl.bn == 256 && !dual) pl.bn = 128;
       a.mt_ub = int(ceil_div(a.M, pl.bm) + a.E);
       const int ncols = dual ? pl.bn / 2 : pl.bn;
       pl.n_tiles = int(ceil_div(a.N, ncols));
-      pl.slots = 2 * pl.n_tiles;
+      pl.slots = 4 * pl.n_tiles;
       pl.grid = pad8(int64_t(a.mt_ub) * pl.n_tiles);
     } else {
       pl.bm = a.Mo >= 256 ? 256 : 128;
@@ -658,25 +765,31 @@ bool plan_gemm(GemmArgs& a, GemmPlan& pl, int mode, int epi, int dual, int bf16,
   return true;
 }
 
-template <int BM, int BN, int MODE, int EPI, int BNK, bool DUAL, class OutT>
+template <int BM, int BN, int MODE, int EPI, int BLAY, bool DUAL, class OutT>
 static void go_bf16(const GemmArgs& a, const GemmPlan& pl, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, MODE, EPI, BNK, DUAL, OutT>), dim3(unsigned(pl.grid)),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, MODE, EPI, BLAY, DUAL, OutT>), dim3(unsigned(pl.grid)),
                      dim3(kThreads), 0, st, a);
 }
 
-template <int MODE, int EPI, int BNK, bool DUAL, class OutT>
+template <int MODE, int EPI, int BLAY, bool DUAL, class OutT>
 static bool dispatch_tiles(const GemmArgs& a, const GemmPlan& pl, hipStream_t st) {
-  if (pl.bm == 256 && pl.bn == 256) go_bf16<256, 256, MODE, EPI, BNK, DUAL, OutT>(a, pl, st);
-  else if (pl.bm == 256 && pl.bn == 128) go_bf16<256, 128, MODE, EPI, BNK, DUAL, OutT>(a, pl, st);
-  else if (pl.bm == 128 && pl.bn == 256) go_bf16<128, 256, MODE, EPI, BNK, DUAL, OutT>(a, pl, st);
-  else if (pl.bm == 128 && pl.bn == 128) go_bf16<128, 128, MODE, EPI, BNK, DUAL, OutT>(a, pl, st);
-  else return false;
+  if constexpr (DUAL) {
+    if (pl.bm == 256 && pl.bn == 256) go_bf16<256, 256, MODE, EPI, BLAY, DUAL, OutT>(a, pl, st);
+    else if (pl.bm == 128 && pl.bn == 256) go_bf16<128, 256, MODE, EPI, BLAY, DUAL, OutT>(a, pl, st);
+    else return false;
+  } else {
+    if (pl.bm == 256 && pl.bn == 256) go_bf16<256, 256, MODE, EPI, BLAY, DUAL, OutT>(a, pl, st);
+    else if (pl.bm == 256 && pl.bn == 128) go_bf16<256, 128, MODE, EPI, BLAY, DUAL, OutT>(a, pl, st);
+    else if (pl.bm == 128 && pl.bn == 256) go_bf16<128, 256, MODE, EPI, BLAY, DUAL, OutT>(a, pl, st);
+    else if (pl.bm == 128 && pl.bn == 128) go_bf16<128, 128, MODE, EPI, BLAY, DUAL, OutT>(a, pl, st);
+    else return false;
+  }
   return true;
 }
 
 template <int MODE, int EPI, int BNK, bool DUAL>
 static void go_f32(const GemmArgs& a, const GemmPlan& pl, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_f32_kernel<MODE, EPI, BNK, DUAL>), dim3(unsigned(pl.grid)), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((gemm_f32_kernel<MODE, EPI, BNK, DUAL>), dim3(unsigned(pl.grid)), dim3(kFThreads), 0, st, a);
 }
 
 // out_f32: 1 when c0 is fp32 (scattered pairs, weight gradients)
@@ -695,19 +808,19 @@ static bool dispatch(const GemmArgs& a, const GemmPlan& pl, int out_f32, hipStre
     }
     return false;
   }
-  if (pl.mode == SEG_K) return dispatch_tiles<SEG_K, EPI_PARTIAL, 0, false, float>(a, pl, st);
+  if (pl.mode == SEG_K) return dispatch_tiles<SEG_K, EPI_PARTIAL, LAY_MN, false, float>(a, pl, st);
   switch (pl.epi) {
     case EPI_STORE:
       if (a.b_nk) {
-        return out_f32 ? dispatch_tiles<SEG_M, EPI_STORE, 1, false, float>(a, pl, st)
-                       : dispatch_tiles<SEG_M, EPI_STORE, 1, false, uint16_t>(a, pl, st);
+        return out_f32 ? dispatch_tiles<SEG_M, EPI_STORE, LAY_K, false, float>(a, pl, st)
+                       : dispatch_tiles<SEG_M, EPI_STORE, LAY_K, false, uint16_t>(a, pl, st);
       }
-      return out_f32 ? dispatch_tiles<SEG_M, EPI_STORE, 0, false, float>(a, pl, st)
-                     : dispatch_tiles<SEG_M, EPI_STORE, 0, false, uint16_t>(a, pl, st);
-    case EPI_GELU_FWD: return dispatch_tiles<SEG_M, EPI_GELU_FWD, 0, false, uint16_t>(a, pl, st);
-    case EPI_SWIGLU_FWD: return dispatch_tiles<SEG_M, EPI_SWIGLU_FWD, 0, true, uint16_t>(a, pl, st);
-    case EPI_GELU_BWD: return dispatch_tiles<SEG_M, EPI_GELU_BWD, 1, false, uint16_t>(a, pl, st);
-    case EPI_SWIGLU_BWD: return dispatch_tiles<SEG_M, EPI_SWIGLU_BWD, 1, false, uint16_t>(a, pl, st);
+      return out_f32 ? dispatch_tiles<SEG_M, EPI_STORE, LAY_MN, false, float>(a, pl, st)
+                     : dispatch_tiles<SEG_M, EPI_STORE, LAY_MN, false, uint16_t>(a, pl, st);
+    case EPI_GELU_FWD: return dispatch_tiles<SEG_M, EPI_GELU_FWD, LAY_MN, false, uint16_t>(a, pl, st);
+    case EPI_SWIGLU_FWD: return dispatch_tiles<SEG_M, EPI_SWIGLU_FWD, LAY_MN, true, uint16_t>(a, pl, st);
+    case EPI_GELU_BWD: return dispatch_tiles<SEG_M, EPI_GELU_BWD, LAY_K, false, uint16_t>(a, pl, st);
+    case EPI_SWIGLU_BWD: return dispatch_tiles<SEG_M, EPI_SWIGLU_BWD, LAY_K, false, uint16_t>(a, pl, st);
   }
   return false;
 }

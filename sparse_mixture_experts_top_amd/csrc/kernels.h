@@ -24,8 +24,8 @@ constexpr int kMaxExperts = 1024;
 // SEG_K (weights mode, groupXtY):
 //   for every expert e, row chunk [r0, r1) of its grouped rows (chunks of
 //   KS rows):  C_e[i][j] += sum_{r in chunk} A(r,i) * B(r,j),  i < Mo, j < N
-//   A(r,i) = a0[arow(r) * lda + i],  B(r,j) = g(r) * b0[brow(r) * ldb + j]
-//   brow(r) = b_scat ? sidx[r] / b_fan : r, g(r) = b_gate ? b_gate[sidx[r]] : 1
+//   A(r,i) = a0[arow(r) * lda + i],  B(r,j) = b0[brow(r) * ldb + j]
+//   brow(r) = b_scat ? sidx[r] / b_fan : r
 //   An expert with one chunk writes c0 + e*Mo*N directly; otherwise each
 //   chunk writes partial + chunk*Mo*N and reduce_dw() sums them.
 enum Mode { SEG_M = 0, SEG_K = 1 };
@@ -36,9 +36,10 @@ enum Epi {
   EPI_STORE = 0,   // c0[crow(r)][n] = (gate ? g*v : v); dg partial <aux row, v>
   EPI_GELU_FWD,    // h = stored(v) -> c0; a = stored(gelu(h)) -> c1
   EPI_SWIGLU_FWD,  // h1 = stored(v1) -> c0; h3 = stored(v3) -> c1; a = stored(silu(h1) h3) -> c2
-  EPI_GELU_BWD,    // v = dA/g; h = aux0; dg += <stored(gelu(h)), v>; c0 = stored(g v gelu'(h))
-  EPI_SWIGLU_BWD,  // v = dA/g; h1,h3 = aux0,aux1; dg += <a, v>;
-                   // c0 = stored(g v h3 silu'(h1)); c1 = stored(g v silu(h1))
+  EPI_GELU_BWD,    // v = dA/g; h = aux0; a = stored(gelu(h)); dg += <a, v>;
+                   // c0 = stored(g v gelu'(h)); c2 = stored(g a)
+  EPI_SWIGLU_BWD,  // v = dA/g; h1,h3 = aux0,aux1; a = stored(silu(h1) h3); dg += <a, v>;
+                   // c0 = stored(g v h3 silu'(h1)); c1 = stored(g v silu(h1)); c2 = stored(g a)
   EPI_PARTIAL      // SEG_K fp32 tile store
 };
 
@@ -57,12 +58,13 @@ struct GemmArgs {
   const void* a0;
   const void* a1;
   int64_t lda;
+  int64_t a_rows;      // rows of the A tensor(s) (bounds of the buffer loads)
   int a_scat, a_fan;
   const void* b0;
   const void* b1;
   int64_t ldb, b_es;
+  int64_t b_rows;      // SEG_K: rows of the B tensor (bounds of the buffer loads)
   int b_scat, b_fan;
-  const float* b_gate;
   void* c0;
   void* c1;
   void* c2;
@@ -75,7 +77,20 @@ struct GemmArgs {
   int aux_scat, aux_fan;
   float* dgpart;       // [slots][M]
   float* partial;      // SEG_K partial tiles [mt_ub][Mo*N]
+  // x / fan == (x * fan_m) >> fan_s for 0 <= x < 2^31 (set by plan_gemm)
+  uint32_t a_fan_m, b_fan_m;
+  int a_fan_s, b_fan_s;
 };
+
+// Multiply-shift constants for exact division by d (1 <= d < 2^16) of
+// non-negative 31-bit integers: l = ceil(log2 d), m = ceil(2^(31+l) / d).
+inline void fastdiv_magic(int d, uint32_t& m, int& s) {
+  int l = 0;
+  while ((1 << l) < d) ++l;
+  const uint64_t num = uint64_t(1) << (31 + l);
+  m = uint32_t((num + uint64_t(d) - 1) / uint64_t(d));
+  s = 31 + l;
+}
 
 // Launch descriptions chosen on the host.
 struct GemmPlan {
@@ -111,5 +126,9 @@ hipError_t launch_reduce_dg(const float* part, int slots, int M, const int* offs
 hipError_t launch_reduce_dw(const float* partial, const int* offsets, int E, int KS, int64_t elems, float* dw,
                             hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+// out[r] = g[sidx[r]] * x[xrow(r)] for grouped rows r < offsets[E], rounded
+// to the storage type; xrow(r) = x_grouped ? r : sidx[r] / fan
+hipError_t launch_scale_rows(const void* x, int x_grouped, int fan, const float* gates, const int* sidx,
+                             const int* offsets, int E, int M, int64_t d, void* out, int bf16, hipStream_t st);
 
 }  // namespace smoe

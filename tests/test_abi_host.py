@@ -34,8 +34,8 @@ def test_workspace_sizes_are_consistent():
     b_big = lib.smoe_mlp_bwd_workspace_bytes(16384, 2, 8, 4096, 14336, smoe.ACT_SWIGLU, smoe.BF16)
     assert 0 < b_small < b_big
     s = lib.smoe_mlp_saved_bytes(16384, 2, 8, 4096, 14336, smoe.ACT_SWIGLU, smoe.BF16)
-    assert s >= 3 * 32768 * 14336 * 2
-    off = (ctypes.c_size_t * 7)()
+    assert s >= 2 * 32768 * 14336 * 2
+    off = (ctypes.c_size_t * 6)()
     assert lib.smoe_mlp_saved_offsets(100, 2, 4, 64, 96, smoe.ACT_GELU, smoe.F32, off) == 0
     assert off[5] == ctypes.c_size_t(-1).value
     assert all(o % 256 == 0 for i, o in enumerate(off) if i != 5)

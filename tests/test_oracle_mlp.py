@@ -133,7 +133,7 @@ def test_dw_cols_matches_full_backward(act, storage):
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
 def test_bf16_storage_rounds_at_the_stated_points(act):
     """With bf16 storage the oracle equals the dense evaluation that rounds
-    h (h1,h3), a, dh (dh1,dh3) and g*dout; and stays within bf16 error of
+    h (h1,h3), a, dh (dh1,dh3) and g*a; and stays within bf16 error of
     the unrounded result."""
     x, w1, w2, w3, idx, gates, dout = _case(act, seed=9)
     T, k = idx.shape
