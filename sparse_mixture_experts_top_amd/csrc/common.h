@@ -8,6 +8,9 @@
 #include <utility>
 
 #define SMOE_DEV __device__ __forceinline__
+// for lambdas in kernels: keep every helper inlined so register arrays they
+// index stay in registers
+#define SMOE_INL __attribute__((always_inline))
 
 namespace smoe {
 
@@ -128,11 +131,14 @@ SMOE_DEV bool find_item(const int* __restrict__ offsets, int E, int unit, int it
       const int hi_s = __shfl(hi, src, kWave);
       const int n_s = __shfl(n, src, kWave);
       const int local = item - base - ex;
-      it.e = c + src;
-      it.row0 = lo_s + local * unit;
-      it.row1 = min(hi_s, it.row0 + unit);
-      it.first = local == 0;
-      it.nitems = n_s;
+      // the same on every lane: make that visible to the compiler, so that
+      // values derived from the item (buffer descriptors, loop bounds) live
+      // in scalar registers
+      it.e = __builtin_amdgcn_readfirstlane(c + src);
+      it.row0 = __builtin_amdgcn_readfirstlane(lo_s + local * unit);
+      it.row1 = __builtin_amdgcn_readfirstlane(min(hi_s, lo_s + local * unit + unit));
+      it.first = __builtin_amdgcn_readfirstlane(local == 0);
+      it.nitems = __builtin_amdgcn_readfirstlane(n_s);
       return true;
     }
     base += __shfl(incl, kWave - 1, kWave);

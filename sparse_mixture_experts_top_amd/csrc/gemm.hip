@@ -68,13 +68,22 @@ SMOE_DEV int fdiv(int x, uint32_t m, int s) { return int((uint64_t(uint32_t(x)) 
 // (split by j & 1); (j >> 1) & 7 separates the eight rows of each parity.
 SMOE_DEV int swz_k(int row) { return (row >> 1) & 7; }
 // MN-layout: chunk c (8 mn) of k-row r is stored at chunk c ^ swz_mn(r).  A
-// transposing read takes 32 bytes from each of four consecutive k-rows; the
-// masks 0, 2, 4, 6 put those eight chunks on distinct banks.
-SMOE_DEV int swz_mn(int krow) { return (krow & 3) << 1; }
+// 64-bit LDS read is served 32 lanes at a time; for a transposing fragment
+// read those 32 lanes take four aligned chunks from each of four consecutive
+// k-rows, and the masks 0, 4, 8, 12 put the sixteen chunks on distinct banks.
+SMOE_DEV int swz_mn(int krow) { return (krow & 3) << 2; }
 
+// Buffer descriptor over [base, base + bytes).  Base and size are the same
+// on every lane; reading them through readfirstlane keeps the descriptor in
+// scalar registers, as the buffer instructions require.
 SMOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32));
   const int64_t n = bytes < int64_t(kOOB) ? bytes : int64_t(kOOB);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(uint32_t(n)), 0x00020000);
+  const uint32_t nr = __builtin_amdgcn_readfirstlane(uint32_t(n));
+  void* ub = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, int(nr), 0x00020000);
 }
 // the 64 lanes of the wave each copy 16 bytes (at byte offset voff of the
 // buffer) to wave_lds + 16 * lane
@@ -194,7 +203,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   if (!tile_of_block<BM, BN, MODE, DUAL>(p, T)) return;
   const Item& it = T.it;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index as a scalar: everything derived from it (LDS copy targets,
+  // per-wave roles) stays wave-uniform for the compiler
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
 
   // ---------------- K steps ------------------------------------------------
@@ -207,29 +218,43 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
 
   // ---------------- per-lane copy addressing -------------------------------
   constexpr int NA = BM / 64, NB = BN / 64;     // buffer loads per wave per operand
-  __amdgpu_buffer_rsrc_t rA0, rA1, rB0, rB1;
+  // buffer descriptors of the operands (part 0 / part 1 of K; dual: W1 / W3),
+  // built from kernel arguments at each use
+  auto descA = [&](auto part) SMOE_INL {
+    const void* base;
+    if constexpr (decltype(part)::value) base = p.a1;
+    else base = p.a0;
+    return make_rsrc(base, p.a_rows * p.lda * 2);
+  };
+  auto descB = [&](auto part) SMOE_INL {
+    const uint16_t* base;
+    if constexpr (decltype(part)::value) base = static_cast<const uint16_t*>(p.b1);
+    else base = static_cast<const uint16_t*>(p.b0);
+    int64_t bytes;
+    if constexpr (MODE == SEG_K) {
+      bytes = p.b_rows * p.ldb * 2;
+    } else {
+      base += int64_t(it.e) * p.b_es;
+      bytes = int64_t(BLAY == LAY_K ? p.N : p.K0) * p.ldb * 2;
+    }
+    return make_rsrc(base, bytes);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   uint32_t a_off[NA];   // K-layout: row byte offset; MN-layout: column byte offset
   uint32_t b_off[NB];
   bool b_ok[NB];
 
   if constexpr (MODE == SEG_M) {
-    const int64_t a_bytes = p.a_rows * p.lda * 2;
-    rA0 = make_rsrc(p.a0, a_bytes);
-    rA1 = make_rsrc(p.a1, a_bytes);
-    static_for<NA>([&](auto t) {
+    static_for<NA>([&](auto t) SMOE_INL {
       const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
       const int gr = it.row0 + row;
       const int src = gr < it.row1 ? (p.a_scat ? p.sidx[gr] / p.a_fan : gr) : -1;
       a_off[t] = src >= 0 ? uint32_t(int64_t(src) * p.lda * 2) : kOOB;
     });
-    const uint16_t* be0 = static_cast<const uint16_t*>(p.b0) + int64_t(it.e) * p.b_es;
-    const uint16_t* be1 = static_cast<const uint16_t*>(p.b1) + int64_t(it.e) * p.b_es;
     if constexpr (BLAY == LAY_K) {
       // W[e] viewed [n][k]: N rows of ldb
-      const int64_t b_bytes = int64_t(p.N) * p.ldb * 2;
-      rB0 = make_rsrc(be0, b_bytes);
-      rB1 = make_rsrc(be1, b_bytes);
-      static_for<NB>([&](auto t) {
+      static_for<NB>([&](auto t) SMOE_INL {
         const int n = T.n0 + (int(t) * 8 + wave) * 8 + (lane >> 3);
         b_off[t] = n < p.N ? uint32_t(int64_t(n) * p.ldb * 2) : kOOB;
         b_ok[t] = true;
@@ -237,10 +262,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     } else {
       // W[e] viewed [k][n]: K rows of ldb.  Dual: the tile is two 128-column
       // sub-tiles, W1 columns then W3 columns (loads t < NB/2 fill the first)
-      const int64_t b_bytes = int64_t(p.K0) * p.ldb * 2;
-      rB0 = make_rsrc(be0, b_bytes);
-      rB1 = make_rsrc(be1, b_bytes);
-      static_for<NB>([&](auto t) {
+
+      static_for<NB>([&](auto t) SMOE_INL {
         int krow, c;
         if constexpr (DUAL) mn_slot<BN / 2>(int(t) % (NB / 2), wave, lane, krow, c);
         else mn_slot<BN>(int(t), wave, lane, krow, c);
@@ -250,17 +273,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       });
     }
   } else {
-    rA0 = make_rsrc(p.a0, p.a_rows * p.lda * 2);
-    rA1 = rA0;
-    rB0 = make_rsrc(p.b0, p.b_rows * p.ldb * 2);
-    rB1 = rB0;
-    static_for<NA>([&](auto t) {
+
+    static_for<NA>([&](auto t) SMOE_INL {
       int krow, c;
       mn_slot<BM>(int(t), wave, lane, krow, c);
       const int i = T.m0 + 8 * c;
       a_off[t] = i < p.Mo ? uint32_t(i) * 2 : kOOB;
     });
-    static_for<NB>([&](auto t) {
+    static_for<NB>([&](auto t) SMOE_INL {
       int krow, c;
       mn_slot<BN>(int(t), wave, lane, krow, c);
       const int j = T.n0 + 8 * c;
@@ -273,9 +293,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   // step ahead so the index -> row -> data chain never stalls the loop
   int ia_row[MODE == SEG_K ? NA : 1];
   int ib_row[MODE == SEG_K ? NB : 1];
-  auto load_idx = [&](int kt) {
+  auto load_idx = [&](int kt) SMOE_INL {
     if constexpr (MODE == SEG_K) {
-      static_for<NA>([&](auto t) {
+      static_for<NA>([&](auto t) SMOE_INL {
         int krow, c;
         mn_slot<BM>(int(t), wave, lane, krow, c);
         const int r = it.row0 + kt * kBK + krow;
@@ -283,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         const int src = p.a_scat ? fdiv(p.sidx[rc], p.a_fan_m, p.a_fan_s) : rc;
         ia_row[t] = r < it.row1 ? src : -1;
       });
-      static_for<NB>([&](auto t) {
+      static_for<NB>([&](auto t) SMOE_INL {
         int krow, c;
         mn_slot<BN>(int(t), wave, lane, krow, c);
         const int r = it.row0 + kt * kBK + krow;
@@ -295,78 +315,90 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   };
 
   // ---------------- copy step kt into stage `stg` -------------------------
-  auto issue = [&](int kt, char* stg) {
+  // SEG_M: a uniform branch on the K part picks the buffer descriptors, so
+  // each copy names a fixed (scalar) descriptor
+  auto issue_part = [&](auto part, int kl, char* stg) SMOE_INL {
+    constexpr int P = decltype(part)::value;
     char* As = stg;
     char* Bs = stg + A_BYTES;
-    if constexpr (MODE == SEG_M) {
-      const bool part1 = kt >= KT0;
-      const int kl = (part1 ? kt - KT0 : kt) * kBK;
-      const int Kp = part1 ? K1 : K0;
-      // K-layout A: lane copies logical chunk (lane & 7) ^ swz_k(row)
-      static_for<NA>([&](auto t) {
+    const int Kp = P ? K1 : K0;
+    // K-layout A: lane copies logical chunk (lane & 7) ^ swz_k(row)
+    static_for<NA>([&](auto t) SMOE_INL {
+      const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
+      const int kb = (lane & 7) ^ swz_k(row);
+      const bool ok = a_off[t] != kOOB && kl + kb * 8 < Kp;
+      const uint32_t vo = ok ? a_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
+      dma16(descA(part), As + (int(t) * 8 + wave) * 8 * kKRowBytes, vo);
+    });
+    if constexpr (BLAY == LAY_K) {
+      static_for<NB>([&](auto t) SMOE_INL {
         const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
         const int kb = (lane & 7) ^ swz_k(row);
-        const bool ok = a_off[t] != kOOB && kl + kb * 8 < Kp;
-        const uint32_t vo = ok ? a_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
-        dma16(part1 ? rA1 : rA0, As + (int(t) * 8 + wave) * 8 * kKRowBytes, vo);
+        const bool ok = b_off[t] != kOOB && kl + kb * 8 < Kp;
+        const uint32_t vo = ok ? b_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
+        dma16(descB(part), Bs + (int(t) * 8 + wave) * 8 * kKRowBytes, vo);
       });
-      if constexpr (BLAY == LAY_K) {
-        static_for<NB>([&](auto t) {
-          const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
-          const int kb = (lane & 7) ^ swz_k(row);
-          const bool ok = b_off[t] != kOOB && kl + kb * 8 < Kp;
-          const uint32_t vo = ok ? b_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
-          dma16(part1 ? rB1 : rB0, Bs + (int(t) * 8 + wave) * 8 * kKRowBytes, vo);
-        });
-      } else {
-        static_for<NB>([&](auto t) {
-          int krow, c;
-          char* dst;
-          if constexpr (DUAL) {
-            using G = MnGeom<BN / 2>;
-            constexpr int tt = int(t) % (NB / 2);
-            mn_slot<BN / 2>(tt, wave, lane, krow, c);
-            dst = Bs + (int(t) / (NB / 2)) * (BN / 2) * kKRowBytes + (tt * 8 + wave) * G::RPI * G::RB;
-          } else {
-            using G = MnGeom<BN>;
-            mn_slot<BN>(int(t), wave, lane, krow, c);
-            dst = Bs + (int(t) * 8 + wave) * G::RPI * G::RB;
-          }
-          const int k = kl + krow;
-          const bool ok = b_ok[t] && k < K0;
-          const uint32_t vo = ok ? uint32_t(int64_t(k) * p.ldb * 2) + b_off[t] : kOOB;
-          dma16((DUAL && int(t) >= NB / 2) ? rB1 : rB0, dst, vo);
-        });
-      }
     } else {
+      static_for<NB>([&](auto t) SMOE_INL {
+        int krow, c;
+        char* dst;
+        if constexpr (DUAL) {
+          using G = MnGeom<BN / 2>;
+          constexpr int tt = int(t) % (NB / 2);
+          mn_slot<BN / 2>(tt, wave, lane, krow, c);
+          dst = Bs + (int(t) / (NB / 2)) * (BN / 2) * kKRowBytes + (tt * 8 + wave) * G::RPI * G::RB;
+        } else {
+          using G = MnGeom<BN>;
+          mn_slot<BN>(int(t), wave, lane, krow, c);
+          dst = Bs + (int(t) * 8 + wave) * G::RPI * G::RB;
+        }
+        const int k = kl + krow;
+        const bool ok = b_ok[t] && k < K0;
+        const uint32_t vo = ok ? uint32_t(int64_t(k) * p.ldb * 2) + b_off[t] : kOOB;
+        if constexpr (DUAL) {
+          if constexpr (int(t) >= NB / 2) dma16(descB(P1{}), dst, vo);
+          else dma16(descB(P0{}), dst, vo);
+        } else {
+          dma16(descB(P0{}), dst, vo);
+        }
+      });
+    }
+  };
+  auto issue = [&](int kt, char* stg) SMOE_INL {
+    if constexpr (MODE == SEG_M) {
+      if (kt >= KT0) issue_part(std::integral_constant<int, 1>{}, (kt - KT0) * kBK, stg);
+      else issue_part(std::integral_constant<int, 0>{}, kt * kBK, stg);
+    } else {
+      char* As = stg;
+      char* Bs = stg + A_BYTES;
       using GA = MnGeom<BM>;
       using GB = MnGeom<BN>;
-      static_for<NA>([&](auto t) {
+      static_for<NA>([&](auto t) SMOE_INL {
         const bool ok = ia_row[t] >= 0 && a_off[t] != kOOB;
         const uint32_t vo = ok ? uint32_t(int64_t(ia_row[t]) * p.lda * 2) + a_off[t] : kOOB;
-        dma16(rA0, As + (int(t) * 8 + wave) * GA::RPI * GA::RB, vo);
+        dma16(descA(P0{}), As + (int(t) * 8 + wave) * GA::RPI * GA::RB, vo);
       });
-      static_for<NB>([&](auto t) {
+      static_for<NB>([&](auto t) SMOE_INL {
         const bool ok = ib_row[t] >= 0 && b_ok[t];
         const uint32_t vo = ok ? uint32_t(int64_t(ib_row[t]) * p.ldb * 2) + b_off[t] : kOOB;
-        dma16(rB0, Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB, vo);
+        dma16(descB(P0{}), Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB, vo);
       });
     }
   };
 
   f32x16_t acc[FM][FN];
-  static_for<FM>([&](auto i) {
-    static_for<FN>([&](auto j) {
-      static_for<16>([&](auto v) { acc[i][j][int(v)] = 0.f; });
+  static_for<FM>([&](auto i) SMOE_INL {
+    static_for<FN>([&](auto j) SMOE_INL {
+      static_for<16>([&](auto v) SMOE_INL { acc[i][j][int(v)] = 0.f; });
     });
   });
 
   auto frags = [&](const char* As, const char* Bs, int s, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
-    static_for<FM>([&](auto fm) {
+    static_for<FM>([&](auto fm) SMOE_INL {
       if constexpr (ALAY == LAY_K) af[fm] = frag_k(As, wm * WM + fm * 32, s, lane);
       else af[fm] = frag_mn<BM>(As, wm * WM + fm * 32, s, lane);
     });
-    static_for<FN>([&](auto fn) {
+    static_for<FN>([&](auto fn) SMOE_INL {
       if constexpr (MODE == SEG_M && BLAY == LAY_K) {
         bf[fn] = frag_k(Bs, wn * WN + fn * 32, s, lane);
       } else if constexpr (DUAL) {
@@ -377,13 +409,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       }
     });
   };
-  auto compute = [&](const char* stg) {
+  auto compute = [&](const char* stg) SMOE_INL {
     const char* As = stg;
     const char* Bs = stg + A_BYTES;
     bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
     frags(As, Bs, 0, af0, bf0);
     // double-buffered fragments: slice s+1 is read while slice s multiplies
-    static_for<kBK / 16>([&](auto sc) {
+    static_for<kBK / 16>([&](auto sc) SMOE_INL {
       constexpr int S = decltype(sc)::value;
       if constexpr (S + 1 < kBK / 16) {
         if constexpr ((S & 1) == 0) frags(As, Bs, S + 1, af1, bf1);
@@ -391,8 +423,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       }
       auto& A = (S & 1) == 0 ? af0 : af1;
       auto& B = (S & 1) == 0 ? bf0 : bf1;
-      static_for<FM>([&](auto fm) {
-        static_for<FN>([&](auto fn) {
+      static_for<FM>([&](auto fm) SMOE_INL {
+        static_for<FN>([&](auto fn) SMOE_INL {
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[fn], A[fm], acc[fm][fn], 0, 0, 0);
         });
       });
@@ -423,11 +455,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   if constexpr (MODE == SEG_K) {
     float* dst = (it.nitems == 1) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
                                   : p.partial + int64_t(T.chunk) * p.Mo * p.N;
-    static_for<FM>([&](auto fm) {
+    static_for<FM>([&](auto fm) SMOE_INL {
       const int i = T.m0 + wm * WM + fm * 32 + (lane & 31);
       if (i < p.Mo) {
-        static_for<FN>([&](auto fn) {
-          static_for<4>([&](auto q) {
+        static_for<FN>([&](auto fn) SMOE_INL {
+          static_for<4>([&](auto q) SMOE_INL {
             const int j = T.n0 + wn * WN + fn * 32 + 8 * q + csub;
             if (j < p.N) {
               const float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1],
@@ -445,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     const uint16_t* x0 = static_cast<const uint16_t*>(p.aux0);
     const uint16_t* x1 = static_cast<const uint16_t*>(p.aux1);
     constexpr int FNR = DUAL ? FN / 2 : FN;
-    static_for<FM>([&](auto fm) {
+    static_for<FM>([&](auto fm) SMOE_INL {
       const int gr = it.row0 + wm * WM + fm * 32 + (lane & 31);
       const bool rok = gr < it.row1;
       const int sp = rok ? p.sidx[gr] : 0;
@@ -453,8 +485,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       const int64_t crow = p.c_scat ? sp : gr;
       const int64_t xrow = p.aux_scat ? sp / p.aux_fan : gr;
       float dgacc = 0.f;
-      static_for<FNR>([&](auto fn) {
-        static_for<4>([&](auto q) {
+      static_for<FNR>([&](auto fn) SMOE_INL {
+        static_for<4>([&](auto q) SMOE_INL {
           const int n = T.n0 + (DUAL ? wn * (WN / 2) : wn * WN) + fn * 32 + 8 * q + csub;
           if (rok && n < p.N) {
             float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1], acc[fm][fn][4 * int(q) + 2],
@@ -467,13 +499,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
               }
               if (c0) {
                 if (p.gate) {
-                  static_for<4>([&](auto i) { v[i] *= g; });
+                  static_for<4>([&](auto i) SMOE_INL { v[i] *= g; });
                 }
                 st4<OutT>(c0 + crow * p.ldc + n, v);
               }
             } else if constexpr (EPI == EPI_GELU_FWD) {
               float h[4], a[4];
-              static_for<4>([&](auto i) {
+              static_for<4>([&](auto i) SMOE_INL {
                 h[i] = stored<OutT>(v[i]);
                 a[i] = gelu_f(h[i]);
               });
@@ -481,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
               st4<OutT>(c1 + int64_t(gr) * p.ldc + n, a);
             } else if constexpr (EPI == EPI_SWIGLU_FWD) {
               float h1[4], h3[4], a[4];
-              static_for<4>([&](auto i) {
+              static_for<4>([&](auto i) SMOE_INL {
                 h1[i] = stored<OutT>(v[i]);
                 h3[i] = stored<OutT>(acc[fm][fn + FN / 2][4 * int(q) + int(i)]);
                 a[i] = silu_f(h1[i]) * h3[i];
@@ -492,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
             } else if constexpr (EPI == EPI_GELU_BWD) {
               float h[4], dh[4], ag[4];
               ld4<uint16_t>(x0 + int64_t(gr) * p.ldaux + n, h);
-              static_for<4>([&](auto i) {
+              static_for<4>([&](auto i) SMOE_INL {
                 const float a = stored<OutT>(gelu_f(h[i]));
                 dgacc += a * v[i];
                 dh[i] = g * v[i] * gelu_grad_f(h[i]);
@@ -504,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
               float h1[4], h3[4], d1[4], d3[4], ag[4];
               ld4<uint16_t>(x0 + int64_t(gr) * p.ldaux + n, h1);
               ld4<uint16_t>(x1 + int64_t(gr) * p.ldaux + n, h3);
-              static_for<4>([&](auto i) {
+              static_for<4>([&](auto i) SMOE_INL {
                 const float sg = sigmoid_f(h1[i]);
                 const float si = h1[i] * sg;
                 const float a = stored<OutT>(si * h3[i]);
@@ -552,7 +584,7 @@ __global__ __launch_bounds__(kFThreads) void gemm_f32_kernel(GemmArgs p) {
   const float* b1 = static_cast<const float*>(p.b1);
   const int Kloop = MODE == SEG_M ? p.K : it.row1 - it.row0;
 
-  auto Aval = [&](int m, int k) -> float {  // m tile-local, k absolute (SEG_M) / chunk-local (SEG_K)
+  auto Aval = [&](int m, int k) SMOE_INL -> float {  // m tile-local, k absolute (SEG_M) / chunk-local (SEG_K)
     if constexpr (MODE == SEG_M) {
       const int gr = it.row0 + m;
       if (gr >= it.row1 || k >= p.K) return 0.f;
@@ -565,7 +597,7 @@ __global__ __launch_bounds__(kFThreads) void gemm_f32_kernel(GemmArgs p) {
       return a0[int64_t(src) * p.lda + i];
     }
   };
-  auto Bval = [&](int k, int n, int which) -> float {  // n tile-local
+  auto Bval = [&](int k, int n, int which) SMOE_INL -> float {  // n tile-local
     if constexpr (MODE == SEG_M) {
       const int col = T.n0 + n;
       if (col >= p.N || k >= p.K) return 0.f;
@@ -734,7 +766,7 @@ bool plan_gemm(GemmArgs& a, GemmPlan& pl, int mode, int epi, int dual, int bf16,
       pl.bn = (dual || a.N >= 256) ? 256 : 128;
       pl.bm = (rows_per_expert >= 192) ? 256 : 128;
       // prefer smaller tiles when the big ones leave most CUs idle
-      auto tiles = [&](int bm, int bn) {
+      auto tiles = [&](int bm, int bn) SMOE_INL {
         const int ncols = dual ? bn / 2 : bn;
         return (ceil_div(a.M, bm) + a.E / 2) * ceil_div(a.N, ncols);
       };
