@@ -14,13 +14,30 @@ utilisation over the expert products, the roofline of the dominant kernel
 (HIP events on the library's stream), and the CPU oracle timed on a
 bounded token sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-tokens 4]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-tokens 24]
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter runs
+(FETCH_SIZE, then WRITE_SIZE) of this script with --copy-mib, which also
+times a plain elementwise copy of known size whose counter readings give the
+KiB -> byte scale:
+
+    rocprofv3 --pmc FETCH_SIZE -d DIR_F -o run --output-format csv -- \
+        python3 bench.py --steps 1 --warmup 1 --cpu-tokens 0 --copy-mib 1024
+    (the same with WRITE_SIZE into DIR_W)
+    python bench.py --pmc-summary DIR_F DIR_W > profiles/<kernel>_traffic.txt
+
+The summary records a hash of the GEMM kernel sources; the traffic figure is
+reported only while the sources still hash to it.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +47,90 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 GEMM_ROLES = ["up", "down", "dA", "dW2", "dX", "dW1", "dW3"]
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
+# template arguments that identify each role's GEMM instance on the
+# Mixtral-shaped workload (<BM, BN, MODE, EPI, BLAY, DUAL, OutT>)
+ROLE_KERNEL = {"up": "gemm_bf16_kernel<256, 256, 0, 2, 1, true, unsigned short>"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_swiglu_mixtral_traffic.txt")
+COPY_KERNEL_HINT = "neg"
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_top_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _read_counters(d):
+    """{kernel name: [per-dispatch counter values]} from a rocprofv3 csv dir."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    assert files, f"no counter_collection.csv under {d}"
+    out = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                out.setdefault(key, 0.0)
+                out[key] += float(r["Counter_Value"])
+    per = {}
+    for (name, _), v in out.items():
+        per.setdefault(name, []).append(v)
+    return per
+
+
+def pmc_summary(dir_fetch, dir_write, copy_bytes):
+    """Text summary: per-launch HBM bytes of the "up" kernel, scaled by the
+    counters' reading for the copy kernel of known size."""
+    lines = []
+    res = {}
+    for ctr, d in (("FETCH_SIZE", dir_fetch), ("WRITE_SIZE", dir_write)):
+        per = _read_counters(d)
+        copy = [v for n, vs in per.items() if COPY_KERNEL_HINT in n and "smoe" not in n for v in vs]
+        kern = [v for n, vs in per.items() if ROLE_KERNEL["up"] in n for v in vs]
+        assert copy and kern, (ctr, sorted(per)[:20])
+        copy_kib = float(np.median(copy))
+        scale = copy_bytes / (copy_kib * 1024.0)
+        kib = float(np.mean(kern))
+        res[ctr] = kib * 1024.0 * scale
+        lines.append(f"{ctr}: up kernel {kib:.0f} KiB/dispatch (mean of {len(kern)}); copy kernel "
+                     f"{copy_kib:.0f} KiB/dispatch for {copy_bytes} bytes -> scale {scale:.4f} bytes/(KiB*1024)")
+    lines.append(f"fetch_bytes_per_launch: {res['FETCH_SIZE']:.6e}")
+    lines.append(f"write_bytes_per_launch: {res['WRITE_SIZE']:.6e}")
+    lines.append(f"kernel_sources_sha256_16: {kernel_sources_hash()}")
+    return "\n".join(lines)
+
+
+def read_traffic():
+    """HBM bytes per launch of the "up" kernel from the committed counter
+    summary, or None if absent or taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"^(\w+):\s*(\S+)\s*$", line.strip())
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_sources_sha256_16") != kernel_sources_hash():
+        return None
+    return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+
+
+def copy_calibration(mib):
+    """A plain elementwise copy (y = -x, fp32) of known size, three times:
+    each launch reads and writes mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    log(f"copy calibration: 3 launches of {mib} MiB read + {mib} MiB written")
 
 
 def gemm_flops(T, k, d, f, act):
@@ -53,8 +154,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-tokens", type=int, default=4,
+    ap.add_argument("--cpu-tokens", type=int, default=24,
                     help="tokens of the oracle's CPU-baseline sample (0 skips it)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     return ap.parse_args()
 
 
@@ -80,6 +185,9 @@ def cpu_baseline(w, n_tokens):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary, copy_bytes=(args.copy_mib or 1024) << 20))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build runs the hot path "
               "on a single MI355X and has no multi-GPU path.", file=sys.stderr)
@@ -89,6 +197,8 @@ def main():
     from workloads import make_config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
     log("generating the Mixtral-shaped workload")
     w = make_config(3)
     T, k, E = w.T, w.k, w.E
@@ -163,7 +273,8 @@ def main():
         "expert_gemm_tflop_per_step": total_flops / 1e12,
         "kernels_ms": kern_ms,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": read_traffic() if dom == "up" else None,
                      "flop_per_launch": fl[dom], "avg_launch_ms": kern_ms[dom]},
     }
     del t, ws_f, ws_b
