@@ -198,7 +198,8 @@ def parallel_linear_fwd(x, w, expert_idxs, x_grouped: bool, y_grouped: bool,
 # same grouped/scattered product; [ART] para. 4: per-expert gradients)
 # --------------------------------------------------------------------------
 def parallel_linear_bwd(x, w, expert_idxs, x_grouped: bool, y_grouped: bool,
-                        dy, gates=None, storage: str = "f64"):
+                        dy, gates=None, storage: str = "f64",
+                        tokens: Optional[Sequence[int]] = None, dw_cols=None):
     """Gradients of parallel_linear_fwd.
 
     dy has the forward output's shape.  Per assignment p with input row u:
@@ -207,6 +208,10 @@ def parallel_linear_bwd(x, w, expert_idxs, x_grouped: bool, y_grouped: bool,
                                               T-row input was read k times)
       dW[e]         += u^T (x) dy_p          (with gates: (g*u stored) (x) dy[t])
       dgates[t,j]    = <dy[t], u @ W[e]>     (with gates)
+    ``tokens`` restricts dx and dgates to those tokens' assignments (other
+    rows NaN); dW still sums over every assignment.  ``dw_cols`` restricts dW
+    to those output columns (dW[e][:, c] needs column c of each dy_p alone),
+    returned as [E, d_in, len(dw_cols)].
     Returns (dx, dw, dgates or None).
     """
     idx = np.asarray(expert_idxs)
@@ -217,14 +222,19 @@ def parallel_linear_bwd(x, w, expert_idxs, x_grouped: bool, y_grouped: bool,
     dy = _as64(dy)
     fan = _fan(x.shape[0], T, k, x_grouped)
     rinv = grouped_position(route(idx, E)["sorted_scattered_idxs"])
-    dx = np.zeros_like(x)
-    dw = np.zeros((E, d_in, d_out))
+    cols = np.arange(d_out) if dw_cols is None else np.asarray(dw_cols)
+    visit = np.ones(T, dtype=bool)
+    if tokens is not None:
+        visit[:] = False
+        visit[np.asarray(tokens, dtype=np.int64)] = True
+    dx = np.zeros_like(x) if tokens is None else np.full(x.shape, np.nan)
+    dw = np.zeros((E, d_in, cols.size))
     dg = None
     if gates is not None:
         if y_grouped:
             raise ValueError("the gate-weighted combine needs scattered output")
         g = _as64(gates)
-        dg = np.zeros((T, k))
+        dg = np.zeros((T, k)) if tokens is None else np.full((T, k), np.nan)
     for t in range(T):
         for j in range(k):
             p = t * k + j
@@ -233,12 +243,16 @@ def parallel_linear_bwd(x, w, expert_idxs, x_grouped: bool, y_grouped: bool,
             u = x[in_row]
             if gates is None:
                 dyp = dy[rinv[p] if y_grouped else p]
-                dw[e] += np.outer(u, dyp)
+                dw[e] += np.outer(u, dyp[cols])
             else:
                 dyp = g[t, j] * dy[t]
-                dg[t, j] = dy[t] @ (u @ w[e])
-                dw[e] += np.outer(_store(g[t, j] * u, storage), dy[t])
-            dx[in_row] += dyp @ w[e].T
+                dw[e] += np.outer(_store(g[t, j] * u, storage), dy[t][cols])
+            if visit[t]:
+                if gates is not None:
+                    dg[t, j] = dy[t] @ (u @ w[e])
+                if np.isnan(dx[in_row, 0]):
+                    dx[in_row] = 0.0
+                dx[in_row] += dyp @ w[e].T
     return dx, dw, dg
 
 

@@ -48,10 +48,20 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+// read-only global memory read through the scalar unit (uniform addresses)
+typedef __attribute__((address_space(4))) const int cint_t;
 
 constexpr int kThreads = 512;   // bf16 kernel
-constexpr int kBK = 64;
-constexpr int kKRowBytes = kBK * 2;     // K-layout row: 64 bf16
+#ifndef SMOE_BK
+#define SMOE_BK 32
+#endif
+#ifndef SMOE_NS
+#define SMOE_NS 4
+#endif
+constexpr int kBK = SMOE_BK;    // K of one pipeline stage (32 or 64)
+constexpr int kNS = SMOE_NS;    // LDS stages in flight
+static_assert(kBK == 32 || kBK == 64, "K step");
+static_assert(kNS >= 2, "stages");
 constexpr uint32_t kOOB = 0xFFFFFFF0u;  // byte offset past every buffer: reads as 0
 
 enum Lay { LAY_K = 0, LAY_MN = 1 };
@@ -63,34 +73,63 @@ SMOE_DEV int xcd_remap(int b, int nblk) {
 
 SMOE_DEV int fdiv(int x, uint32_t m, int s) { return int((uint64_t(uint32_t(x)) * m) >> s); }
 
-// K-layout: chunk c (8 k) of row j is stored at chunk c ^ swz_k(j).  The 16
-// rows read by one 16-lane group span two rows per 256-byte bank window
-// (split by j & 1); (j >> 1) & 7 separates the eight rows of each parity.
-SMOE_DEV int swz_k(int row) { return (row >> 1) & 7; }
+// K-layout tile: row j (one gathered token row, or one column of W read as
+// W^T) holds the stage's kBK values of k, KC 16-byte chunks.  Chunk c of row
+// j sits at chunk c ^ swz_k(j).  A 128-bit LDS read serves 16 lanes at a
+// time, i.e. 16 consecutive rows at one logical chunk; the 64 banks cover
+// 256 bytes = 2 rows of 128 bytes (kBK = 64) or 4 rows of 64 bytes (kBK =
+// 32), and the swizzle gives the rows that share banks distinct chunks.
+struct KGeom {
+  static constexpr int RB = 2 * kBK;    // bytes per row
+  static constexpr int KC = kBK / 8;    // 16-byte chunks per row
+  static constexpr int RPL = 64 / KC;   // rows per wave copy
+};
+SMOE_DEV int swz_k(int row) {
+  if constexpr (kBK == 64) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
 // MN-layout: chunk c (8 mn) of k-row r is stored at chunk c ^ swz_mn(r).  A
 // 64-bit LDS read is served 32 lanes at a time; for a transposing fragment
 // read those 32 lanes take four aligned chunks from each of four consecutive
 // k-rows, and the masks 0, 4, 8, 12 put the sixteen chunks on distinct banks.
 SMOE_DEV int swz_mn(int krow) { return (krow & 3) << 2; }
 
-// Buffer descriptor over [base, base + bytes).  Base and size are the same
-// on every lane; reading them through readfirstlane keeps the descriptor in
-// scalar registers, as the buffer instructions require.
-SMOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+// Buffer descriptor over [base, base + bytes) (raw buffer, no stride,
+// out-of-range offsets read zero).  Base and size are the same on every
+// lane; reading them through readfirstlane keeps the descriptor in scalar
+// registers, as the buffer instructions require.
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+SMOE_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(b));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32));
   const int64_t n = bytes < int64_t(kOOB) ? bytes : int64_t(kOOB);
-  const uint32_t nr = __builtin_amdgcn_readfirstlane(uint32_t(n));
-  void* ub = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, int(nr), 0x00020000);
+  rsrc_t r;
+  r.x = __builtin_amdgcn_readfirstlane(uint32_t(b));
+  r.y = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32) & 0xFFFFu);
+  r.z = __builtin_amdgcn_readfirstlane(uint32_t(n));
+  r.w = 0x00020000u;
+  return r;
 }
-// the 64 lanes of the wave each copy 16 bytes (at byte offset voff of the
-// buffer) to wave_lds + 16 * lane
-SMOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, char* wave_lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)wave_lds, 16, voff, 0, 0, 0);
+// The 64 lanes of the wave each copy 16 bytes (at byte offset voff of the
+// buffer) to wave_lds + 16 * lane, straight into LDS.  Written as inline asm
+// so that the compiler does not order later LDS reads of OTHER stages behind
+// these copies (it cannot tell the stages apart); the kernel waits for the
+// copies itself (wait_vmem) before the barrier that publishes a stage.  The
+// asm has no register outputs; its inputs are read when it issues.
+SMOE_DEV void dma16(rsrc_t r, char* wave_lds, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)wave_lds)));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(m0v)
+               : "memory", "m0");
 }
-SMOE_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order): s_waitcnt vmcnt(N), other counters free
+template <int N>
+SMOE_DEV void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Which tile this workgroup computes.  Returns false if none.
 struct TileInfo {
@@ -131,14 +170,14 @@ SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
 }
 
 // ---------------------------------------------------------------------------
-// Operand tiles in LDS.
+// Operand tiles in LDS, one stage = kBK values of k.
 //
-// K-layout tile of R rows: row j at j*128 bytes.  The copy of one K step is
-// R/64 buffer loads per wave; load t of wave w fills rows (8t + w)*8 .. +8,
-// lane L taking row +(L >> 3) and storing physical chunk L & 7, i.e. the
-// logical chunk (L & 7) ^ swz_k(row) of that row.
+// K-layout tile of R rows: row j at j*RB bytes.  The copy of one stage is
+// R*kBK/4096 buffer loads per wave; load t of wave w fills rows
+// (8t + w)*RPL .. +RPL, lane L taking row +(L / KC) and storing physical
+// chunk L % KC, i.e. the logical chunk (L % KC) ^ swz_k(row) of that row.
 //
-// MN-layout tile of R mn (R = 128 or 256) by 64 k: k-row r at r*2R bytes,
+// MN-layout tile of R mn (R = 128 or 256) by kBK k: k-row r at r*2R bytes,
 // CPR = R/8 chunks per k-row, RPI = 64/CPR k-rows per wave load; load t of
 // wave w fills k-rows (8t + w)*RPI .. +RPI, lane L taking k-row +(L / CPR)
 // and physical chunk L % CPR (logical chunk (L % CPR) ^ swz_mn(k-row)).
@@ -148,7 +187,8 @@ struct MnGeom {
   static constexpr int RB = 2 * R;         // bytes per k-row
   static constexpr int CPR = R / 8;        // 16-byte chunks per k-row
   static constexpr int RPI = 64 / CPR;     // k-rows per wave load
-  static constexpr int NI = R / 64;        // loads per wave per K step
+  static constexpr int NI = R * kBK / 4096;  // loads per wave per stage
+  static_assert(NI >= 1, "tile too small for one copy per wave");
 };
 
 // lane's k-row and logical chunk in MN-layout load t of wave `wave`
@@ -164,7 +204,7 @@ SMOE_DEV void mn_slot(int t, int wave, int lane, int& krow, int& chunk) {
 SMOE_DEV bf16x8_t frag_k(const char* tile, int row0, int s, int lane) {
   const int row = row0 + (lane & 31);
   const int c = (2 * s + (lane >> 5)) ^ swz_k(row);
-  return *reinterpret_cast<const bf16x8_t*>(tile + row * kKRowBytes + (c << 4));
+  return *reinterpret_cast<const bf16x8_t*>(tile + row * KGeom::RB + (c << 4));
 }
 
 // the same operand from an MN-layout tile, through two transposing reads:
@@ -192,12 +232,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int ALAY = MODE == SEG_M ? LAY_K : LAY_MN;
   constexpr int FM = BM / 64, FN = BN / 128;   // fragments per wave
   constexpr int WM = BM / 2, WN = BN / 4;      // wave tile
-  constexpr int A_BYTES = BM * kKRowBytes, B_BYTES = BN * kKRowBytes, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2, STAGE = A_BYTES + B_BYTES;
   static_assert(BN >= 128 && BM >= 128, "tile");
   static_assert(!DUAL || (MODE == SEG_M && BLAY == LAY_MN && BN == 256), "dual B layout");
-  // two LDS stages as separate objects
+  // one LDS object per stage, always named statically (the loop below is
+  // unrolled by kNS): the compiler can then tell a stage being read from the
+  // stages whose copies are still in flight
   __shared__ __attribute__((aligned(16))) char smem0[STAGE];
   __shared__ __attribute__((aligned(16))) char smem1[STAGE];
+  __shared__ __attribute__((aligned(16))) char smem2[kNS > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char smem3[kNS > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char smem4[kNS > 4 ? STAGE : 16];
+  static_assert(kNS <= 5, "stages");
+  auto stage = [&](auto s) SMOE_INL -> char* {
+    constexpr int S = decltype(s)::value % kNS;
+    if constexpr (S == 0) return smem0;
+    else if constexpr (S == 1) return smem1;
+    else if constexpr (S == 2) return smem2;
+    else if constexpr (S == 3) return smem3;
+    else return smem4;
+  };
 
   TileInfo T;
   if (!tile_of_block<BM, BN, MODE, DUAL>(p, T)) return;
@@ -210,14 +264,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
 
   // ---------------- K steps ------------------------------------------------
   // SEG_M: K is [part 0: K0 columns of a0 / b0 | part 1: K-K0 of a1 / b1];
-  // each 64-wide step lies inside one part.  SEG_K: the chunk's rows.
+  // each kBK-wide step lies inside one part.  SEG_K: the chunk's rows.
   const int K0 = MODE == SEG_M ? p.K0 : it.row1 - it.row0;
   const int K1 = MODE == SEG_M ? p.K - p.K0 : 0;
   const int KT0 = (K0 + kBK - 1) / kBK;
   const int KT = KT0 + (K1 + kBK - 1) / kBK;
 
   // ---------------- per-lane copy addressing -------------------------------
-  constexpr int NA = BM / 64, NB = BN / 64;     // buffer loads per wave per operand
+  constexpr int NA = BM * kBK / 4096, NB = BN * kBK / 4096;   // buffer loads per wave per operand
+  constexpr int LPS = NA + NB;                                // per stage
+  static_assert(NA >= 1 && NB >= 1 && (!DUAL || NB % 2 == 0), "copy split");
+  using GA = MnGeom<BM>;
+  using GB = MnGeom<BN>;
   // buffer descriptors of the operands (part 0 / part 1 of K; dual: W1 / W3),
   // built from kernel arguments at each use
   auto descA = [&](auto part) SMOE_INL {
@@ -247,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
 
   if constexpr (MODE == SEG_M) {
     static_for<NA>([&](auto t) SMOE_INL {
-      const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
+      const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
       const int gr = it.row0 + row;
       const int src = gr < it.row1 ? (p.a_scat ? p.sidx[gr] / p.a_fan : gr) : -1;
       a_off[t] = src >= 0 ? uint32_t(int64_t(src) * p.lda * 2) : kOOB;
@@ -255,14 +313,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     if constexpr (BLAY == LAY_K) {
       // W[e] viewed [n][k]: N rows of ldb
       static_for<NB>([&](auto t) SMOE_INL {
-        const int n = T.n0 + (int(t) * 8 + wave) * 8 + (lane >> 3);
+        const int n = T.n0 + (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
         b_off[t] = n < p.N ? uint32_t(int64_t(n) * p.ldb * 2) : kOOB;
         b_ok[t] = true;
       });
     } else {
-      // W[e] viewed [k][n]: K rows of ldb.  Dual: the tile is two 128-column
+      // W[e] viewed [k][n]: K rows of ldb.  Dual: the tile is two BN/2-column
       // sub-tiles, W1 columns then W3 columns (loads t < NB/2 fill the first)
-
       static_for<NB>([&](auto t) SMOE_INL {
         int krow, c;
         if constexpr (DUAL) mn_slot<BN / 2>(int(t) % (NB / 2), wave, lane, krow, c);
@@ -273,7 +330,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       });
     }
   } else {
-
     static_for<NA>([&](auto t) SMOE_INL {
       int krow, c;
       mn_slot<BM>(int(t), wave, lane, krow, c);
@@ -289,28 +345,30 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     });
   }
 
-  // SEG_K: source rows of this lane's k-rows for the next K step, fetched one
-  // step ahead so the index -> row -> data chain never stalls the loop
-  int ia_row[MODE == SEG_K ? NA : 1];
-  int ib_row[MODE == SEG_K ? NB : 1];
-  auto load_idx = [&](int kt) SMOE_INL {
+  // SEG_K: the source rows of the gathered operand come from
+  // sorted_scattered_idxs.  Load t of wave w covers RPI consecutive grouped
+  // rows, a wave-uniform range, so their indices are read with scalar loads
+  // one stage ahead (the vector-memory counter then counts operand copies
+  // only, which the stage waits rely on).
+  constexpr int SA = MODE == SEG_K ? NA : 1, SB = MODE == SEG_K ? NB : 1;
+  int sa[SA][GA::RPI];
+  int sb[SB][GB::RPI];
+  auto sload = [&](int kt) SMOE_INL {
     if constexpr (MODE == SEG_K) {
-      static_for<NA>([&](auto t) SMOE_INL {
-        int krow, c;
-        mn_slot<BM>(int(t), wave, lane, krow, c);
-        const int r = it.row0 + kt * kBK + krow;
-        const int rc = min(r, it.row1 - 1);
-        const int src = p.a_scat ? fdiv(p.sidx[rc], p.a_fan_m, p.a_fan_s) : rc;
-        ia_row[t] = r < it.row1 ? src : -1;
-      });
-      static_for<NB>([&](auto t) SMOE_INL {
-        int krow, c;
-        mn_slot<BN>(int(t), wave, lane, krow, c);
-        const int r = it.row0 + kt * kBK + krow;
-        const int rc = min(r, it.row1 - 1);
-        const int src = p.b_scat ? fdiv(p.sidx[rc], p.b_fan_m, p.b_fan_s) : rc;
-        ib_row[t] = r < it.row1 ? src : -1;
-      });
+      const cint_t* cs = (const cint_t*)(p.sidx);
+      const int last = it.row1 - 1;
+      if (p.a_scat) {
+        static_for<NA>([&](auto t) SMOE_INL {
+          const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GA::RPI;
+          static_for<GA::RPI>([&](auto i) SMOE_INL { sa[t][i] = cs[min(r0 + int(i), last)]; });
+        });
+      }
+      if (p.b_scat) {
+        static_for<NB>([&](auto t) SMOE_INL {
+          const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GB::RPI;
+          static_for<GB::RPI>([&](auto i) SMOE_INL { sb[t][i] = cs[min(r0 + int(i), last)]; });
+        });
+      }
     }
   };
 
@@ -322,21 +380,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     char* As = stg;
     char* Bs = stg + A_BYTES;
     const int Kp = P ? K1 : K0;
-    // K-layout A: lane copies logical chunk (lane & 7) ^ swz_k(row)
+    // K-layout A: lane copies logical chunk (lane % KC) ^ swz_k(row)
     static_for<NA>([&](auto t) SMOE_INL {
-      const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
-      const int kb = (lane & 7) ^ swz_k(row);
+      const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
+      const int kb = (lane % KGeom::KC) ^ swz_k(row);
       const bool ok = a_off[t] != kOOB && kl + kb * 8 < Kp;
       const uint32_t vo = ok ? a_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
-      dma16(descA(part), As + (int(t) * 8 + wave) * 8 * kKRowBytes, vo);
+      dma16(descA(part), As + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB, vo);
     });
     if constexpr (BLAY == LAY_K) {
       static_for<NB>([&](auto t) SMOE_INL {
-        const int row = (int(t) * 8 + wave) * 8 + (lane >> 3);
-        const int kb = (lane & 7) ^ swz_k(row);
+        const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
+        const int kb = (lane % KGeom::KC) ^ swz_k(row);
         const bool ok = b_off[t] != kOOB && kl + kb * 8 < Kp;
         const uint32_t vo = ok ? b_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
-        dma16(descB(part), Bs + (int(t) * 8 + wave) * 8 * kKRowBytes, vo);
+        dma16(descB(part), Bs + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB, vo);
       });
     } else {
       static_for<NB>([&](auto t) SMOE_INL {
@@ -346,11 +404,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           using G = MnGeom<BN / 2>;
           constexpr int tt = int(t) % (NB / 2);
           mn_slot<BN / 2>(tt, wave, lane, krow, c);
-          dst = Bs + (int(t) / (NB / 2)) * (BN / 2) * kKRowBytes + (tt * 8 + wave) * G::RPI * G::RB;
+          dst = Bs + (int(t) / (NB / 2)) * (BN / 2) * kBK * 2 + (tt * 8 + wave) * G::RPI * G::RB;
         } else {
-          using G = MnGeom<BN>;
           mn_slot<BN>(int(t), wave, lane, krow, c);
-          dst = Bs + (int(t) * 8 + wave) * G::RPI * G::RB;
+          dst = Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB;
         }
         const int k = kl + krow;
         const bool ok = b_ok[t] && k < K0;
@@ -366,21 +423,38 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   };
   auto issue = [&](int kt, char* stg) SMOE_INL {
     if constexpr (MODE == SEG_M) {
-      if (kt >= KT0) issue_part(std::integral_constant<int, 1>{}, (kt - KT0) * kBK, stg);
-      else issue_part(std::integral_constant<int, 0>{}, kt * kBK, stg);
+      if (kt >= KT0) issue_part(P1{}, (kt - KT0) * kBK, stg);
+      else issue_part(P0{}, kt * kBK, stg);
     } else {
       char* As = stg;
       char* Bs = stg + A_BYTES;
-      using GA = MnGeom<BM>;
-      using GB = MnGeom<BN>;
       static_for<NA>([&](auto t) SMOE_INL {
-        const bool ok = ia_row[t] >= 0 && a_off[t] != kOOB;
-        const uint32_t vo = ok ? uint32_t(int64_t(ia_row[t]) * p.lda * 2) + a_off[t] : kOOB;
+        const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GA::RPI;
+        const int i = lane / GA::CPR;
+        int src = r0 + i;
+        if (p.a_scat) {
+          // the lane's row among the RPI wave-uniform indices
+          static_for<GA::RPI>([&](auto q) SMOE_INL {
+            const int v = fdiv(sa[t][q], p.a_fan_m, p.a_fan_s);
+            src = (int(q) == 0 || i == int(q)) ? v : src;
+          });
+        }
+        const bool ok = r0 + i < it.row1 && a_off[t] != kOOB;
+        const uint32_t vo = ok ? uint32_t(int64_t(src) * p.lda * 2) + a_off[t] : kOOB;
         dma16(descA(P0{}), As + (int(t) * 8 + wave) * GA::RPI * GA::RB, vo);
       });
       static_for<NB>([&](auto t) SMOE_INL {
-        const bool ok = ib_row[t] >= 0 && b_ok[t];
-        const uint32_t vo = ok ? uint32_t(int64_t(ib_row[t]) * p.ldb * 2) + b_off[t] : kOOB;
+        const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GB::RPI;
+        const int i = lane / GB::CPR;
+        int src = r0 + i;
+        if (p.b_scat) {
+          static_for<GB::RPI>([&](auto q) SMOE_INL {
+            const int v = fdiv(sb[t][q], p.b_fan_m, p.b_fan_s);
+            src = (int(q) == 0 || i == int(q)) ? v : src;
+          });
+        }
+        const bool ok = r0 + i < it.row1 && b_ok[t];
+        const uint32_t vo = ok ? uint32_t(int64_t(src) * p.ldb * 2) + b_off[t] : kOOB;
         dma16(descB(P0{}), Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB, vo);
       });
     }
@@ -403,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         bf[fn] = frag_k(Bs, wn * WN + fn * 32, s, lane);
       } else if constexpr (DUAL) {
         // fn 0: W1 sub-tile, fn 1: W3 sub-tile, same 32 columns
-        bf[fn] = frag_mn<BN / 2>(Bs + int(fn) * (BN / 2) * kKRowBytes, wn * (WN / 2), s, lane);
+        bf[fn] = frag_mn<BN / 2>(Bs + int(fn) * (BN / 2) * kBK * 2, wn * (WN / 2), s, lane);
       } else {
         bf[fn] = frag_mn<BN>(Bs, wn * WN + fn * 32, s, lane);
       }
@@ -431,22 +505,39 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     });
   };
 
-  if constexpr (MODE == SEG_K) load_idx(0);
-  if (KT > 0) issue(0, smem0);
-  if constexpr (MODE == SEG_K) load_idx(1);
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    char* cur = (kt & 1) ? smem1 : smem0;
-    char* nxt = (kt & 1) ? smem0 : smem1;
-    if (kt + 1 < KT) issue(kt + 1, nxt);
-    if constexpr (MODE == SEG_K) {
-      if (kt + 2 < KT) load_idx(kt + 2);
+  // ---------------- pipeline -----------------------------------------------
+  // kNS stages: while stage kt is multiplied, the copies of the next kNS-1
+  // stages are in flight.  At the top of step kt each wave waits until its
+  // own copies of stage kt have landed (the later kNS-2 stages may still be
+  // in flight), then the barrier publishes every wave's copies and frees the
+  // stage multiplied in step kt-1, which receives stage kt+kNS-1.
+  // The barrier is a bare s_barrier: every wave has consumed its fragment
+  // reads of step kt-1 (the multiplies used them) and has waited for its own
+  // copies of stage kt, which is all the ordering the stages need.
+  static_for<kNS - 1>([&](auto s) SMOE_INL {
+    if (int(s) < KT) {
+      sload(int(s));
+      issue(int(s), stage(s));
     }
-    compute(cur);
-    wait_vmem();
-    __syncthreads();
+  });
+  sload(kNS - 1);
+  for (int k0 = 0; k0 < KT; k0 += kNS) {
+    static_for<kNS>([&](auto s) SMOE_INL {
+      const int kt = k0 + int(s);
+      if (kt < KT) {
+        if (kt + kNS - 2 < KT) wait_vmem<(kNS - 2) * LPS>();
+        else wait_vmem<0>();
+        asm volatile("s_barrier" ::: "memory");
+        const int nk = kt + kNS - 1;
+        if (nk < KT) {
+          issue(nk, stage(std::integral_constant<int, int(s) + kNS - 1>{}));
+          sload(nk + 1);
+        }
+        compute(stage(s));
+      }
+    });
   }
+  // the epilogue's stores go to global memory only; no LDS is reused
 
   // ---------------- epilogue ----------------------------------------------
   // lane holds, for fragment (fm, fn): row (lane & 31) and columns

@@ -43,5 +43,28 @@ def rel_err(got, ref) -> float:
     return float(np.abs(got - ref).max(initial=0.0) / rms)
 
 
+def bf16_half_ulp(v) -> np.ndarray:
+    """Half the spacing of bf16 numbers at |v| (8 significant bits): the
+    largest error of rounding a value of that size to bf16."""
+    _, e = np.frexp(np.abs(np.asarray(v, dtype=np.float64)))
+    return np.ldexp(1.0, e - 9)
+
+
+def rel_err_stored_bf16(got, ref) -> float:
+    """rel_err for a result the path stores in bf16: each element's error
+    beyond the final rounding to bf16 (half an ulp at its magnitude), over
+    RMS(oracle).  A bf16 tensor cannot hold an element of 8*RMS or more to
+    within 2e-2*RMS, so the bound applies to the computation before that one
+    storage rounding."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "non-finite values in GPU output"
+    rms = np.sqrt(np.mean(ref ** 2))
+    excess = np.abs(got - ref) - bf16_half_ulp(np.maximum(np.abs(got), np.abs(ref)))
+    worst = float(np.maximum(excess, 0.0).max(initial=0.0))
+    return worst / rms if rms > 0.0 else worst
+
+
 def tol_for(w: Workload) -> float:
     return F32_TOL if w.dtype == "f32" else BF16_TOL

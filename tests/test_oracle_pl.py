@@ -179,3 +179,30 @@ def test_bf16_storage_only_touches_gated_weight_gradient():
     np.testing.assert_array_equal(a[2], b[2])
     assert not np.array_equal(a[1], b[1])
     np.testing.assert_allclose(a[1], b[1], rtol=0, atol=2.0 ** -7 * np.abs(a[1]).max() * 4)
+
+
+@pytest.mark.parametrize("xg,yg,use_gates", [(False, True, False), (True, False, True), (False, False, True)])
+def test_backward_token_and_column_restriction(xg, yg, use_gates):
+    """The restricted backward (sampled tokens, a column slice of dW) is the
+    full backward's rows and columns exactly."""
+    x_s, x_g, w, idx = _case(T=11, E=4, k=2, d_in=6, d_out=7, seed=9)
+    T, k = idx.shape
+    x = x_g if xg else x_s
+    gates = None
+    if use_gates:
+        _, gates = topk_softmax_routing(np.random.default_rng(90).standard_normal((T, 4)), k)
+        gates = gates.astype(np.float64)
+    dy = np.random.default_rng(91).standard_normal((T if use_gates else T * k, 7))
+    dx, dw, dg = oracle.parallel_linear_bwd(x, w, idx, xg, yg, dy, gates=gates, storage="bf16")
+    toks = [0, 4, 10]
+    cols = [0, 3, 6]
+    rdx, rdw, rdg = oracle.parallel_linear_bwd(x, w, idx, xg, yg, dy, gates=gates, storage="bf16",
+                                               tokens=toks, dw_cols=cols)
+    np.testing.assert_array_equal(rdw, dw[:, :, cols])
+    rinv = oracle.grouped_position(oracle.route(idx, 4)["sorted_scattered_idxs"])
+    rows = [rinv[t * k + j] for t in toks for j in range(k)] if xg else toks
+    np.testing.assert_allclose(rdx[rows], dx[rows], rtol=1e-13, atol=1e-13)
+    others = np.setdiff1d(np.arange(x.shape[0]), rows)
+    assert np.all(np.isnan(rdx[others]))
+    if use_gates:
+        np.testing.assert_allclose(rdg[toks], dg[toks], rtol=1e-13, atol=1e-13)

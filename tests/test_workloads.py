@@ -45,3 +45,21 @@ def test_pl_workload_shapes():
     assert w.tensors["x_grouped"].shape == (128, 32)
     assert w.tensors["w"].shape == (4, 32, 16)
     assert w.tensors["dy"].shape == (128, 16)
+
+
+def test_bf16_half_ulp_bounds_rounding():
+    """The stored-bf16 error metric removes exactly the largest rounding
+    error: half an ulp at each magnitude (checked against bf16 rounding)."""
+    import oracle
+    from tests.gpu_util import bf16_half_ulp, rel_err_stored_bf16
+    v = np.random.default_rng(5).standard_normal(20000) * np.exp(np.random.default_rng(6).uniform(-8, 8, 20000))
+    r = oracle.bf16_round(v)
+    assert np.all(np.abs(r - v) <= bf16_half_ulp(v) * (1 + 1e-12))
+    # at 10 * RMS a bf16 value can be off by more than 2e-2 * RMS ...
+    x = np.concatenate([np.ones(999) * 0.1, [10.03]])
+    assert np.abs(oracle.bf16_round(x) - x).max() / np.sqrt(np.mean(x ** 2)) > 2e-2
+    # ... which the stored metric does not count, while any further error counts
+    assert rel_err_stored_bf16(oracle.bf16_round(x), x) == 0.0
+    y = oracle.bf16_round(x).copy()
+    y[0] += 0.05
+    assert rel_err_stored_bf16(y, x) > 0.0
