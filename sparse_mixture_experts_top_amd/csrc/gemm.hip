@@ -467,7 +467,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     });
   });
 
-  auto frags = [&](const char* As, const char* Bs, int s, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
+  auto frags = [&](const char* stg, int s, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) SMOE_INL {
+    const char* As = stg;
+    const char* Bs = stg + A_BYTES;
     static_for<FM>([&](auto fm) SMOE_INL {
       if constexpr (ALAY == LAY_K) af[fm] = frag_k(As, wm * WM + fm * 32, s, lane);
       else af[fm] = frag_mn<BM>(As, wm * WM + fm * 32, s, lane);
@@ -483,37 +485,31 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       }
     });
   };
-  auto compute = [&](const char* stg) SMOE_INL {
-    const char* As = stg;
-    const char* Bs = stg + A_BYTES;
-    bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
-    frags(As, Bs, 0, af0, bf0);
-    // double-buffered fragments: slice s+1 is read while slice s multiplies
-    static_for<kBK / 16>([&](auto sc) SMOE_INL {
-      constexpr int S = decltype(sc)::value;
-      if constexpr (S + 1 < kBK / 16) {
-        if constexpr ((S & 1) == 0) frags(As, Bs, S + 1, af1, bf1);
-        else frags(As, Bs, S + 1, af0, bf0);
-      }
-      auto& A = (S & 1) == 0 ? af0 : af1;
-      auto& B = (S & 1) == 0 ? bf0 : bf1;
-      static_for<FM>([&](auto fm) SMOE_INL {
-        static_for<FN>([&](auto fn) SMOE_INL {
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[fn], A[fm], acc[fm][fn], 0, 0, 0);
-        });
+  // fragments of two 16-wide k slices: slot 0 / slot 1
+  bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto mfmas = [&](bf16x8_t (&A)[FM], bf16x8_t (&B)[FN]) SMOE_INL {
+    static_for<FM>([&](auto fm) SMOE_INL {
+      static_for<FN>([&](auto fn) SMOE_INL {
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[fn], A[fm], acc[fm][fn], 0, 0, 0);
       });
     });
   };
 
   // ---------------- pipeline -----------------------------------------------
-  // kNS stages: while stage kt is multiplied, the copies of the next kNS-1
-  // stages are in flight.  At the top of step kt each wave waits until its
-  // own copies of stage kt have landed (the later kNS-2 stages may still be
-  // in flight), then the barrier publishes every wave's copies and frees the
-  // stage multiplied in step kt-1, which receives stage kt+kNS-1.
-  // The barrier is a bare s_barrier: every wave has consumed its fragment
-  // reads of step kt-1 (the multiplies used them) and has waited for its own
-  // copies of stage kt, which is all the ordering the stages need.
+  // kNS stages.  At the top of step kt each wave waits until its own copies
+  // of stages kt and kt+1 have landed (later stages may still be in flight);
+  // the barrier then publishes every wave's copies and frees the stage
+  // multiplied in step kt-1, which receives stage kt+kNS-1.  Because stage
+  // kt+1 is published one step early, each wave reads the first fragments
+  // of step kt+1 while the last multiplies of step kt run, and arrives at
+  // the next barrier with them in registers.  The barrier is a bare
+  // s_barrier: the fragment reads of step kt-1 were consumed by its
+  // multiplies, which is all the ordering the stages need.
+  static_assert(kNS >= 3, "the next stage is published one step early");
+  constexpr int NSL = kBK / 16;   // k slices per stage (even)
+  // LDS read instructions per slice: one per K-layout fragment, two per
+  // transposed (MN-layout) fragment
+  constexpr int kFragReads = FM * (ALAY == LAY_K ? 1 : 2) + FN * ((MODE == SEG_M && BLAY == LAY_K) ? 1 : 2);
   static_for<kNS - 1>([&](auto s) SMOE_INL {
     if (int(s) < KT) {
       sload(int(s));
@@ -521,23 +517,52 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     }
   });
   sload(kNS - 1);
+  // first fragments of step 0 (read before the loop, so that every step's
+  // code sees the same outstanding LDS reads and the compiler's waits for
+  // them stay exact)
+  if (kNS - 2 < KT) wait_vmem<(kNS - 3) * LPS>();
+  else wait_vmem<0>();
+  asm volatile("s_barrier" ::: "memory");
+  frags(stage(std::integral_constant<int, 0>{}), 0, fa0, fb0);
   for (int k0 = 0; k0 < KT; k0 += kNS) {
     static_for<kNS>([&](auto s) SMOE_INL {
       const int kt = k0 + int(s);
       if (kt < KT) {
-        if (kt + kNS - 2 < KT) wait_vmem<(kNS - 2) * LPS>();
+        if (kt + kNS - 2 < KT) wait_vmem<(kNS - 3) * LPS>();
         else wait_vmem<0>();
         asm volatile("s_barrier" ::: "memory");
-        const int nk = kt + kNS - 1;
-        if (nk < KT) {
-          issue(nk, stage(std::integral_constant<int, int(s) + kNS - 1>{}));
-          sload(nk + 1);
-        }
-        compute(stage(s));
+        static_for<NSL>([&](auto j) SMOE_INL {
+          constexpr int J = decltype(j)::value;
+          auto& A = (J & 1) == 0 ? fa0 : fa1;
+          auto& B = (J & 1) == 0 ? fb0 : fb1;
+          auto& An = (J & 1) == 0 ? fa1 : fa0;
+          auto& Bn = (J & 1) == 0 ? fb1 : fb0;
+          // read the next slice (the next stage's first one after the last;
+          // unconditionally, so the outstanding LDS reads are the same on
+          // every path: after the last step the values are simply unused)
+          if constexpr (J + 1 < NSL) frags(stage(s), J + 1, An, Bn);
+          else frags(stage(std::integral_constant<int, int(s) + 1>{}), 0, An, Bn);
+          mfmas(A, B);
+          // schedule: one multiply, then a share of the fragment reads, so
+          // the reads of the next slice run under this slice's multiplies
+          static_for<FM * FN>([&](auto i) SMOE_INL {
+            constexpr int r0 = int(i) * kFragReads / (FM * FN), r1 = (int(i) + 1) * kFragReads / (FM * FN);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);
+          });
+          if constexpr (J == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int nk = kt + kNS - 1;
+            if (nk < KT) {
+              issue(nk, stage(std::integral_constant<int, int(s) + kNS - 1>{}));
+              sload(nk + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
       }
     });
   }
-  // the epilogue's stores go to global memory only; no LDS is reused
 
   // ---------------- epilogue ----------------------------------------------
   // lane holds, for fragment (fm, fn): row (lane & 31) and columns
