@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #define SMOE_DEV __device__ __forceinline__
@@ -27,14 +28,18 @@ SMOE_DEV void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// ---- bf16 <-> fp32 (bit level, round to nearest even) ---------------------
+// ---- bf16 <-> fp32 --------------------------------------------------------
+// fp32 -> bf16 is gfx950's v_cvt_pk_bf16_f32 (round to nearest even, NaN
+// quieted), two values per instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 SMOE_DEV float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-SMOE_DEV uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// {lo, hi} -> one dword holding bf16(lo) | bf16(hi) << 16
+SMOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+SMOE_DEV uint16_t f2bf(float f) { return uint16_t(pack_bf16x2(f, 0.f)); }
 // round to bf16 and back (the value a bf16 store would hold)
 SMOE_DEV float bfround(float f) { return bf2f(f2bf(f)); }
 
@@ -57,9 +62,20 @@ template <> SMOE_DEV void st4<float>(float* p, const float v[4]) {
 }
 template <> SMOE_DEV void st4<uint16_t>(uint16_t* p, const float v[4]) {
   uint2 w;
-  w.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
-  w.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<uint2*>(p) = w;
+}
+// four values <-> two dwords of bf16
+SMOE_DEV uint2 pack4_bf16(const float v[4]) {
+  uint2 w;
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  return w;
+}
+SMOE_DEV void unpack4_bf16(uint2 w, float v[4]) {
+  v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+  v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 template <class T> SMOE_DEV void ld4(const T* p, float v[4]);
 template <> SMOE_DEV void ld4<float>(const float* p, float v[4]) {
@@ -78,7 +94,9 @@ SMOE_DEV float gelu_grad_f(float z) {
   return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
          z * 0.39894228040143268f * __expf(-0.5f * z * z);
 }
-SMOE_DEV float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// 1 / (1 + e^-z) with the hardware reciprocal (about 1 ulp) instead of an
+// IEEE division; e^-z = +inf gives 0, e^-z = 0 gives 1
+SMOE_DEV float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 SMOE_DEV float silu_f(float z) { return z * sigmoid_f(z); }
 SMOE_DEV float silu_grad_f(float z) {
   float s = sigmoid_f(z);

@@ -58,6 +58,9 @@ constexpr int kThreads = 512;   // bf16 kernel
 #ifndef SMOE_NS
 #define SMOE_NS 4
 #endif
+#ifndef SMOE_SCHED
+#define SMOE_SCHED 0
+#endif
 constexpr int kBK = SMOE_BK;    // K of one pipeline stage (32 or 64)
 constexpr int kNS = SMOE_NS;    // LDS stages in flight
 static_assert(kBK == 32 || kBK == 64, "K step");
@@ -543,6 +546,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           if constexpr (J + 1 < NSL) frags(stage(s), J + 1, An, Bn);
           else frags(stage(std::integral_constant<int, int(s) + 1>{}), 0, An, Bn);
           mfmas(A, B);
+#if SMOE_SCHED == 1
           // schedule: one multiply, then a share of the fragment reads, so
           // the reads of the next slice run under this slice's multiplies
           static_for<FM * FN>([&](auto i) SMOE_INL {
@@ -550,6 +554,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);
           });
+#else
+          // schedule: every fragment read of the next slice first, then this
+          // slice's multiplies (a wave issues in order, so reads placed after
+          // a multiply would wait for the matrix unit)
+          __builtin_amdgcn_sched_group_barrier(0x100, kFragReads, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+#endif
           if constexpr (J == 0) {
             __builtin_amdgcn_sched_barrier(0);
             const int nk = kt + kNS - 1;
@@ -593,85 +604,133 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     const uint16_t* x0 = static_cast<const uint16_t*>(p.aux0);
     const uint16_t* x1 = static_cast<const uint16_t*>(p.aux1);
     constexpr int FNR = DUAL ? FN / 2 : FN;
+    // the epilogue reads bf16 operands (h / h1, h3 of the backward
+    // epilogues; the input rows of the gate gradient) for every output
+    constexpr bool AUX0 = EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD || EPI == EPI_STORE;
+    constexpr bool AUX1 = EPI == EPI_SWIGLU_BWD;
+    const bool aux0_on = EPI == EPI_STORE ? p.dgpart != nullptr : AUX0;
+
+    // row information of the lane's FM rows, read up front
+    int gr[FM], sp[FM];
+    bool rok[FM];
+    float g[FM];
     static_for<FM>([&](auto fm) SMOE_INL {
-      const int gr = it.row0 + wm * WM + fm * 32 + (lane & 31);
-      const bool rok = gr < it.row1;
-      const int sp = rok ? p.sidx[gr] : 0;
-      const float g = (p.gate && rok) ? p.gate[sp] : 1.f;
-      const int64_t crow = p.c_scat ? sp : gr;
-      const int64_t xrow = p.aux_scat ? sp / p.aux_fan : gr;
+      gr[fm] = it.row0 + wm * WM + fm * 32 + (lane & 31);
+      rok[fm] = gr[fm] < it.row1;
+      sp[fm] = rok[fm] ? p.sidx[gr[fm]] : 0;
+    });
+    static_for<FM>([&](auto fm) SMOE_INL { g[fm] = (p.gate && rok[fm]) ? p.gate[sp[fm]] : 1.f; });
+    auto col = [&](auto fn, auto q) SMOE_INL {
+      return T.n0 + (DUAL ? wn * (WN / 2) : wn * WN) + int(fn) * 32 + 8 * int(q) + csub;
+    };
+    // aux operands of one fragment row, 4 bf16 per (fn, q); double-buffered
+    // over fm so the reads of row fm+1 are in flight while row fm is
+    // computed and stored.  Masked lanes read a clamped, valid address.
+    uint2 ax0[2][FNR][4], ax1[2][AUX1 ? FNR : 1][4];
+    auto load_aux = [&](auto fm, auto buf) SMOE_INL {
+      if constexpr (AUX0) {
+        if (aux0_on) {
+          const int64_t row = EPI == EPI_STORE ? (p.aux_scat ? sp[fm] / p.aux_fan : gr[fm]) : gr[fm];
+          const int64_t rr = rok[fm] ? row : (EPI == EPI_STORE && p.aux_scat ? 0 : it.row0);
+          static_for<FNR>([&](auto fn) SMOE_INL {
+            static_for<4>([&](auto q) SMOE_INL {
+              const int n = col(fn, q);
+              const int nn = n < p.N ? n : 0;
+              ax0[buf][fn][q] = *reinterpret_cast<const uint2*>(x0 + rr * p.ldaux + nn);
+              if constexpr (AUX1) ax1[buf][fn][q] = *reinterpret_cast<const uint2*>(x1 + rr * p.ldaux + nn);
+            });
+          });
+        }
+      }
+    };
+    auto unpack = [&](uint2 w, float v[4]) SMOE_INL { unpack4_bf16(w, v); };
+    load_aux(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    static_for<FM>([&](auto fm) SMOE_INL {
+      constexpr int BUF = int(fm) & 1;
+      if constexpr (int(fm) + 1 < FM)
+        load_aux(std::integral_constant<int, int(fm) + 1>{}, std::integral_constant<int, BUF ^ 1>{});
+      const int64_t grow = gr[fm];
+      const int64_t crow = p.c_scat ? sp[fm] : grow;
       float dgacc = 0.f;
       static_for<FNR>([&](auto fn) SMOE_INL {
         static_for<4>([&](auto q) SMOE_INL {
-          const int n = T.n0 + (DUAL ? wn * (WN / 2) : wn * WN) + fn * 32 + 8 * q + csub;
-          if (rok && n < p.N) {
+          const int n = col(fn, q);
+          if (rok[fm] && n < p.N) {
             float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1], acc[fm][fn][4 * int(q) + 2],
                           acc[fm][fn][4 * int(q) + 3]};
             if constexpr (EPI == EPI_STORE) {
               if (p.dgpart) {
                 float xv[4];
-                ld4<uint16_t>(x0 + xrow * p.ldaux + n, xv);
+                unpack(ax0[BUF][fn][q], xv);
                 dgacc += xv[0] * v[0] + xv[1] * v[1] + xv[2] * v[2] + xv[3] * v[3];
               }
               if (c0) {
                 if (p.gate) {
-                  static_for<4>([&](auto i) SMOE_INL { v[i] *= g; });
+                  static_for<4>([&](auto i) SMOE_INL { v[i] *= g[fm]; });
                 }
                 st4<OutT>(c0 + crow * p.ldc + n, v);
               }
             } else if constexpr (EPI == EPI_GELU_FWD) {
+              // h stored in bf16; a computed from the stored h
+              static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
+              const uint2 wh = pack4_bf16(v);
               float h[4], a[4];
-              static_for<4>([&](auto i) SMOE_INL {
-                h[i] = stored<OutT>(v[i]);
-                a[i] = gelu_f(h[i]);
-              });
-              st4<OutT>(c0 + int64_t(gr) * p.ldc + n, h);
-              st4<OutT>(c1 + int64_t(gr) * p.ldc + n, a);
+              unpack4_bf16(wh, h);
+              static_for<4>([&](auto i) SMOE_INL { a[i] = gelu_f(h[i]); });
+              *reinterpret_cast<uint2*>(c0 + grow * p.ldc + n) = wh;
+              st4<OutT>(c1 + grow * p.ldc + n, a);
             } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-              float h1[4], h3[4], a[4];
-              static_for<4>([&](auto i) SMOE_INL {
-                h1[i] = stored<OutT>(v[i]);
-                h3[i] = stored<OutT>(acc[fm][fn + FN / 2][4 * int(q) + int(i)]);
-                a[i] = silu_f(h1[i]) * h3[i];
-              });
-              st4<OutT>(c0 + int64_t(gr) * p.ldc + n, h1);
-              st4<OutT>(c1 + int64_t(gr) * p.ldc + n, h3);
-              st4<OutT>(c2 + int64_t(gr) * p.ldc + n, a);
+              static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
+              float v3[4], h1[4], h3[4], a[4];
+              static_for<4>([&](auto i) SMOE_INL { v3[i] = acc[fm][fn + FN / 2][4 * int(q) + int(i)]; });
+              const uint2 w1 = pack4_bf16(v), w3 = pack4_bf16(v3);
+              unpack4_bf16(w1, h1);
+              unpack4_bf16(w3, h3);
+              static_for<4>([&](auto i) SMOE_INL { a[i] = silu_f(h1[i]) * h3[i]; });
+              *reinterpret_cast<uint2*>(c0 + grow * p.ldc + n) = w1;
+              *reinterpret_cast<uint2*>(c1 + grow * p.ldc + n) = w3;
+              st4<OutT>(c2 + grow * p.ldc + n, a);
             } else if constexpr (EPI == EPI_GELU_BWD) {
-              float h[4], dh[4], ag[4];
-              ld4<uint16_t>(x0 + int64_t(gr) * p.ldaux + n, h);
+              static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
+              float h[4], a[4], dh[4], ag[4];
+              unpack(ax0[BUF][fn][q], h);
+              static_for<4>([&](auto i) SMOE_INL { a[i] = gelu_f(h[i]); });
+              unpack4_bf16(pack4_bf16(a), a);   // a as stored in the forward
               static_for<4>([&](auto i) SMOE_INL {
-                const float a = stored<OutT>(gelu_f(h[i]));
-                dgacc += a * v[i];
-                dh[i] = g * v[i] * gelu_grad_f(h[i]);
-                ag[i] = g * a;
+                dgacc += a[i] * v[i];
+                dh[i] = g[fm] * v[i] * gelu_grad_f(h[i]);
+                ag[i] = g[fm] * a[i];
               });
-              st4<OutT>(c0 + int64_t(gr) * p.ldc + n, dh);
-              st4<OutT>(c2 + int64_t(gr) * p.ldc + n, ag);
+              st4<OutT>(c0 + grow * p.ldc + n, dh);
+              st4<OutT>(c2 + grow * p.ldc + n, ag);
             } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-              float h1[4], h3[4], d1[4], d3[4], ag[4];
-              ld4<uint16_t>(x0 + int64_t(gr) * p.ldaux + n, h1);
-              ld4<uint16_t>(x1 + int64_t(gr) * p.ldaux + n, h3);
+              static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
+              float h1[4], h3[4], sg[4], si[4], a[4], d1[4], d3[4], ag[4];
+              unpack(ax0[BUF][fn][q], h1);
+              unpack(ax1[BUF][fn][q], h3);
               static_for<4>([&](auto i) SMOE_INL {
-                const float sg = sigmoid_f(h1[i]);
-                const float si = h1[i] * sg;
-                const float a = stored<OutT>(si * h3[i]);
-                dgacc += a * v[i];
-                const float dA = g * v[i];
-                d1[i] = dA * h3[i] * (sg * (1.0f + h1[i] * (1.0f - sg)));
-                d3[i] = dA * si;
-                ag[i] = g * a;
+                sg[i] = sigmoid_f(h1[i]);
+                si[i] = h1[i] * sg[i];
+                a[i] = si[i] * h3[i];
               });
-              st4<OutT>(c0 + int64_t(gr) * p.ldc + n, d1);
-              st4<OutT>(c1 + int64_t(gr) * p.ldc + n, d3);
-              st4<OutT>(c2 + int64_t(gr) * p.ldc + n, ag);
+              unpack4_bf16(pack4_bf16(a), a);   // a as stored in the forward
+              static_for<4>([&](auto i) SMOE_INL {
+                dgacc += a[i] * v[i];
+                const float dA = g[fm] * v[i];
+                d1[i] = dA * h3[i] * (sg[i] * (1.0f + h1[i] * (1.0f - sg[i])));
+                d3[i] = dA * si[i];
+                ag[i] = g[fm] * a[i];
+              });
+              st4<OutT>(c0 + grow * p.ldc + n, d1);
+              st4<OutT>(c1 + grow * p.ldc + n, d3);
+              st4<OutT>(c2 + grow * p.ldc + n, ag);
             }
           }
         });
       });
       if (p.dgpart) {
         dgacc += __shfl_xor(dgacc, 32, kWave);
-        if (lane < 32 && rok) p.dgpart[int64_t(T.nt * 4 + wn) * p.M + gr] = dgacc;
+        if (lane < 32 && rok[fm]) p.dgpart[int64_t(T.nt * 4 + wn) * p.M + gr[fm]] = dgacc;
       }
     });
   }
