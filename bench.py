@@ -24,7 +24,7 @@ KiB -> byte scale:
     rocprofv3 --pmc FETCH_SIZE -d DIR_F -o run --output-format csv -- \
         python3 bench.py --steps 1 --warmup 1 --cpu-tokens 0 --copy-mib 1024
     (the same with WRITE_SIZE into DIR_W)
-    python bench.py --pmc-summary DIR_F DIR_W > profiles/<kernel>_traffic.txt
+    python bench.py --pmc-summary DIR_F DIR_W > profiles/gemm_traffic_mixtral.txt
 
 The summary records a hash of the GEMM kernel sources; the traffic figure is
 reported only while the sources still hash to it.
@@ -50,10 +50,11 @@ GEMM_ROLES = ["up", "down", "dA", "dW2", "dX", "dW1", "dW3"]
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
-# template arguments that identify each role's GEMM instance on the
-# Mixtral-shaped workload (<BM, BN, MODE, EPI, BLAY, DUAL, OutT>)
-ROLE_KERNEL = {"up": "gemm_bf16_kernel<256, 256, 0, 2, 1, true, unsigned short>"}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_swiglu_mixtral_traffic.txt")
+# one step launches the grouped-product kernel once per role, in this order
+# (route, then up, down, combine, dA, dgates, dW2, dX, k-sum, dW1, dW3)
+GEMM_ORDER = ["up", "down", "dA", "dW2", "dX", "dW1", "dW3"]
+GEMM_KERNEL_HINT = "smoe::gemm_bf16_kernel<"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_mixtral.txt")
 COPY_KERNEL_HINT = "neg"
 
 
@@ -65,47 +66,49 @@ def kernel_sources_hash():
     return h.hexdigest()[:16]
 
 
-def _read_counters(d):
-    """{kernel name: [per-dispatch counter values]} from a rocprofv3 csv dir."""
+def _read_dispatches(d):
+    """[(dispatch id, kernel name, counter value)] in dispatch order from a
+    rocprofv3 csv directory (values of one dispatch summed over instances)."""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     assert files, f"no counter_collection.csv under {d}"
     out = {}
     for fn in files:
         with open(fn) as f:
             for r in csv.DictReader(f):
-                key = (r["Kernel_Name"], r["Dispatch_Id"])
-                out.setdefault(key, 0.0)
-                out[key] += float(r["Counter_Value"])
-    per = {}
-    for (name, _), v in out.items():
-        per.setdefault(name, []).append(v)
-    return per
+                key = int(r["Dispatch_Id"])
+                name, v = out.get(key, (r["Kernel_Name"], 0.0))
+                out[key] = (name, v + float(r["Counter_Value"]))
+    return [(k, n, v) for k, (n, v) in sorted(out.items())]
 
 
 def pmc_summary(dir_fetch, dir_write, copy_bytes):
-    """Text summary: per-launch HBM bytes of the "up" kernel, scaled by the
-    counters' reading for the copy kernel of known size."""
+    """Text summary: per-launch HBM bytes of each grouped-product role, from
+    the two counter runs, scaled by the counters' reading for the copy
+    kernel of known size.  Roles are assigned by launch order within a step."""
     lines = []
     res = {}
     for ctr, d in (("FETCH_SIZE", dir_fetch), ("WRITE_SIZE", dir_write)):
-        per = _read_counters(d)
-        copy = [v for n, vs in per.items() if COPY_KERNEL_HINT in n and "smoe" not in n for v in vs]
-        kern = [v for n, vs in per.items() if ROLE_KERNEL["up"] in n for v in vs]
-        assert copy and kern, (ctr, sorted(per)[:20])
+        disp = _read_dispatches(d)
+        copy = [v for _, n, v in disp if COPY_KERNEL_HINT in n and "smoe" not in n]
+        gemm = [v for _, n, v in disp if GEMM_KERNEL_HINT in n]
+        assert copy and gemm and len(gemm) % len(GEMM_ORDER) == 0, (ctr, len(copy), len(gemm))
         copy_kib = float(np.median(copy))
         scale = copy_bytes / (copy_kib * 1024.0)
-        kib = float(np.mean(kern))
-        res[ctr] = kib * 1024.0 * scale
-        lines.append(f"{ctr}: up kernel {kib:.0f} KiB/dispatch (mean of {len(kern)}); copy kernel "
-                     f"{copy_kib:.0f} KiB/dispatch for {copy_bytes} bytes -> scale {scale:.4f} bytes/(KiB*1024)")
-    lines.append(f"fetch_bytes_per_launch: {res['FETCH_SIZE']:.6e}")
-    lines.append(f"write_bytes_per_launch: {res['WRITE_SIZE']:.6e}")
+        lines.append(f"{ctr}: copy kernel {copy_kib:.0f} KiB/dispatch for {copy_bytes} bytes -> "
+                     f"scale {scale:.4f}; {len(gemm) // len(GEMM_ORDER)} steps")
+        for i, role in enumerate(GEMM_ORDER):
+            kib = float(np.mean(gemm[i::len(GEMM_ORDER)]))
+            res.setdefault(role, {})[ctr] = kib * 1024.0 * scale
+            lines.append(f"  {role}: {kib:.0f} KiB/dispatch")
+    for role in GEMM_ORDER:
+        lines.append(f"{role}_fetch_bytes_per_launch: {res[role]['FETCH_SIZE']:.6e}")
+        lines.append(f"{role}_write_bytes_per_launch: {res[role]['WRITE_SIZE']:.6e}")
     lines.append(f"kernel_sources_sha256_16: {kernel_sources_hash()}")
     return "\n".join(lines)
 
 
-def read_traffic():
-    """HBM bytes per launch of the "up" kernel from the committed counter
+def read_traffic(role):
+    """HBM bytes per launch of a role's kernel from the committed counter
     summary, or None if absent or taken on other kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -116,7 +119,9 @@ def read_traffic():
             kv[m.group(1)] = m.group(2)
     if kv.get("kernel_sources_sha256_16") != kernel_sources_hash():
         return None
-    return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    if f"{role}_fetch_bytes_per_launch" not in kv:
+        return None
+    return float(kv[f"{role}_fetch_bytes_per_launch"]) + float(kv[f"{role}_write_bytes_per_launch"])
 
 
 def copy_calibration(mib):
@@ -274,7 +279,7 @@ def main():
         "kernels_ms": kern_ms,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": read_traffic() if dom == "up" else None,
+                     "traffic": read_traffic(dom),
                      "flop_per_launch": fl[dom], "avg_launch_ms": kern_ms[dom]},
     }
     del t, ws_f, ws_b
