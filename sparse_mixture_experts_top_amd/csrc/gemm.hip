@@ -165,8 +165,15 @@ SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
     if (g >= p.mt_ub * tpc) return false;
     t.chunk = g / tpc;
     const int rem = g - t.chunk * tpc;
-    t.m0 = (rem / tj) * BM;
-    t.n0 = (rem % tj) * BN;
+    // groups of 8 output row blocks sweeping the column blocks, as in rows
+    // mode: concurrent tiles on an XCD then share 8 A panels and a few B
+    // panels instead of one A panel and 32 distinct B panels
+    constexpr int GM = 8;
+    const int group = rem / (GM * tj);
+    const int gs = min(GM, ti - group * GM);
+    const int local = rem - group * GM * tj;
+    t.m0 = (group * GM + local % gs) * BM;
+    t.n0 = (local / gs) * BN;
     t.nt = 0;
     return find_item(p.offsets, p.E, p.KS, t.chunk, t.it);
   }
@@ -354,22 +361,23 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   // one stage ahead (the vector-memory counter then counts operand copies
   // only, which the stage waits rely on).
   constexpr int SA = MODE == SEG_K ? NA : 1, SB = MODE == SEG_K ? NB : 1;
-  int sa[SA][GA::RPI];
-  int sb[SB][GB::RPI];
-  auto sload = [&](int kt) SMOE_INL {
+  // two sets, by the parity of the step they serve
+  int sa[2][SA][GA::RPI];
+  int sb[2][SB][GB::RPI];
+  auto sload = [&](int kt, auto set) SMOE_INL {
     if constexpr (MODE == SEG_K) {
       const cint_t* cs = (const cint_t*)(p.sidx);
       const int last = it.row1 - 1;
       if (p.a_scat) {
         static_for<NA>([&](auto t) SMOE_INL {
           const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GA::RPI;
-          static_for<GA::RPI>([&](auto i) SMOE_INL { sa[t][i] = cs[min(r0 + int(i), last)]; });
+          static_for<GA::RPI>([&](auto i) SMOE_INL { sa[set][t][i] = cs[min(r0 + int(i), last)]; });
         });
       }
       if (p.b_scat) {
         static_for<NB>([&](auto t) SMOE_INL {
           const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GB::RPI;
-          static_for<GB::RPI>([&](auto i) SMOE_INL { sb[t][i] = cs[min(r0 + int(i), last)]; });
+          static_for<GB::RPI>([&](auto i) SMOE_INL { sb[set][t][i] = cs[min(r0 + int(i), last)]; });
         });
       }
     }
@@ -424,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       });
     }
   };
-  auto issue = [&](int kt, char* stg) SMOE_INL {
+  auto issue = [&](int kt, char* stg, auto set) SMOE_INL {
     if constexpr (MODE == SEG_M) {
       if (kt >= KT0) issue_part(P1{}, (kt - KT0) * kBK, stg);
       else issue_part(P0{}, kt * kBK, stg);
@@ -438,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         if (p.a_scat) {
           // the lane's row among the RPI wave-uniform indices
           static_for<GA::RPI>([&](auto q) SMOE_INL {
-            const int v = fdiv(sa[t][q], p.a_fan_m, p.a_fan_s);
+            const int v = fdiv(sa[set][t][q], p.a_fan_m, p.a_fan_s);
             src = (int(q) == 0 || i == int(q)) ? v : src;
           });
         }
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         int src = r0 + i;
         if (p.b_scat) {
           static_for<GB::RPI>([&](auto q) SMOE_INL {
-            const int v = fdiv(sb[t][q], p.b_fan_m, p.b_fan_s);
+            const int v = fdiv(sb[set][t][q], p.b_fan_m, p.b_fan_s);
             src = (int(q) == 0 || i == int(q)) ? v : src;
           });
         }
@@ -509,17 +517,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   // s_barrier: the fragment reads of step kt-1 were consumed by its
   // multiplies, which is all the ordering the stages need.
   static_assert(kNS >= 3, "the next stage is published one step early");
+  static_assert(kNS % 2 == 0, "index sets alternate with the step parity; the loop is unrolled by kNS");
   constexpr int NSL = kBK / 16;   // k slices per stage (even)
   // LDS read instructions per slice: one per K-layout fragment, two per
   // transposed (MN-layout) fragment
   constexpr int kFragReads = FM * (ALAY == LAY_K ? 1 : 2) + FN * ((MODE == SEG_M && BLAY == LAY_K) ? 1 : 2);
   static_for<kNS - 1>([&](auto s) SMOE_INL {
     if (int(s) < KT) {
-      sload(int(s));
-      issue(int(s), stage(s));
+      sload(int(s), std::integral_constant<int, int(s) & 1>{});
+      issue(int(s), stage(s), std::integral_constant<int, int(s) & 1>{});
     }
   });
-  sload(kNS - 1);
+  sload(kNS - 1, std::integral_constant<int, (kNS - 1) & 1>{});
   // first fragments of step 0 (read before the loop, so that every step's
   // code sees the same outstanding LDS reads and the compiler's waits for
   // them stay exact)
@@ -533,6 +542,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       if (kt < KT) {
         if (kt + kNS - 2 < KT) wait_vmem<(kNS - 3) * LPS>();
         else wait_vmem<0>();
+        // gather indices of the stage issued in the next step: scalar loads
+        // share the LDS counter and complete out of order, so they are
+        // issued here, where their latency overlaps the barrier, rather than
+        // between fragment reads and the multiplies that wait on them
+        if (kt + kNS < KT) sload(kt + kNS, std::integral_constant<int, (int(s) + kNS) & 1>{});
         asm volatile("s_barrier" ::: "memory");
         static_for<NSL>([&](auto j) SMOE_INL {
           constexpr int J = decltype(j)::value;
@@ -564,10 +578,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           if constexpr (J == 0) {
             __builtin_amdgcn_sched_barrier(0);
             const int nk = kt + kNS - 1;
-            if (nk < KT) {
-              issue(nk, stage(std::integral_constant<int, int(s) + kNS - 1>{}));
-              sload(nk + 1);
-            }
+            if (nk < KT)
+              issue(nk, stage(std::integral_constant<int, int(s) + kNS - 1>{}),
+                    std::integral_constant<int, (int(s) + kNS - 1) & 1>{});
             __builtin_amdgcn_sched_barrier(0);
           }
         });
