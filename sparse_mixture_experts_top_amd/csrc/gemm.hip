@@ -592,23 +592,69 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   // lane holds, for fragment (fm, fn): row (lane & 31) and columns
   // 8q + 4*(lane >> 5) + {0..3}, q = 0..3, values acc[fm][fn][4q + i].
   const int csub = 4 * (lane >> 5);
+
+  // Results leave through LDS: each wave writes the 32 rows of one fragment
+  // row (per output) into a private slot, then reads them back as whole
+  // 16-byte chunks of consecutive columns, so that every global store
+  // instruction writes complete 128-byte lines instead of 16 bytes into 32
+  // lines.  The stage buffers are free once every wave is past the loop.
+  using ST = typename std::conditional<MODE == SEG_K, float, OutT>::type;
+  constexpr int OB = sizeof(ST);                           // bytes per element
+  constexpr int WC = (MODE == SEG_M && DUAL) ? WN / 2 : WN;  // output columns per wave
+  constexpr int RBE = WC * OB;                              // bytes per staged row
+  constexpr int CH = RBE / 16;                              // 16-byte chunks per row
+  constexpr int RPR = 64 / CH;                              // rows per read-back instruction
+  constexpr int NOUT = (MODE == SEG_M && (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD)) ? 3
+                       : (MODE == SEG_M && (EPI == EPI_GELU_FWD || EPI == EPI_GELU_BWD)) ? 2 : 1;
+  static_assert((CH & (CH - 1)) == 0 && CH <= 64 && 32 % RPR == 0, "staging geometry");
+  static_assert(NOUT * 32 * RBE <= STAGE / 2, "staging slot");
+  asm volatile("s_barrier" ::: "memory");
+  char* slot;
+  {
+    const int ob = (wave >> 1) & 3;
+    char* base = ob == 0 ? smem0 : ob == 1 ? smem1 : ob == 2 ? smem2 : smem3;
+    slot = base + (wave & 1) * (STAGE / 2);
+  }
+  // lane's 4 values of fragment (fn, q) of one fragment row -> output o
+  auto put = [&](int o, auto fn, auto q, const float v[4]) SMOE_INL {
+    const int row = lane & 31;
+    char* rb = slot + o * 32 * RBE + row * RBE;
+    if constexpr (OB == 2) {
+      const int c = int(fn) * 4 + int(q);
+      *reinterpret_cast<uint2*>(rb + ((c ^ (row & (CH - 1))) << 4) + (lane >> 5) * 8) = pack4_bf16(v);
+    } else {
+      const int c = int(fn) * 8 + 2 * int(q) + (lane >> 5);
+      *reinterpret_cast<float4*>(rb + ((c ^ (row & (CH - 1))) << 4)) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  };
+  // staged output o -> global: row j of the fragment row goes to
+  // base + rowoff(j) + colbase; rowoff / ok are held by lane j
+  auto flush = [&](int o, ST* base, int64_t rowoff, bool ok, int colbase) SMOE_INL {
+    const uint32_t ro_lo = uint32_t(rowoff), ro_hi = uint32_t(uint64_t(rowoff) >> 32);
+    static_for<32 / RPR>([&](auto i) SMOE_INL {
+      const int j = int(i) * RPR + lane / CH, c = lane % CH;
+      const uint4 d = *reinterpret_cast<const uint4*>(slot + o * 32 * RBE + j * RBE + ((c ^ (j & (CH - 1))) << 4));
+      const int64_t ro = int64_t((uint64_t(uint32_t(__shfl(int(ro_hi), j, kWave))) << 32) |
+                                 uint32_t(__shfl(int(ro_lo), j, kWave)));
+      const bool rok_j = __shfl(int(ok), j, kWave) != 0;
+      const int colc = colbase + c * (16 / OB);
+      if (rok_j && colc < p.N) *reinterpret_cast<uint4*>(base + ro + colc) = d;
+    });
+  };
+
   if constexpr (MODE == SEG_K) {
     float* dst = (it.nitems == 1) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
                                   : p.partial + int64_t(T.chunk) * p.Mo * p.N;
     static_for<FM>([&](auto fm) SMOE_INL {
       const int i = T.m0 + wm * WM + fm * 32 + (lane & 31);
-      if (i < p.Mo) {
-        static_for<FN>([&](auto fn) SMOE_INL {
-          static_for<4>([&](auto q) SMOE_INL {
-            const int j = T.n0 + wn * WN + fn * 32 + 8 * q + csub;
-            if (j < p.N) {
-              const float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1],
-                                  acc[fm][fn][4 * int(q) + 2], acc[fm][fn][4 * int(q) + 3]};
-              st4<float>(dst + int64_t(i) * p.N + j, v);
-            }
-          });
+      static_for<FN>([&](auto fn) SMOE_INL {
+        static_for<4>([&](auto q) SMOE_INL {
+          const float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1],
+                              acc[fm][fn][4 * int(q) + 2], acc[fm][fn][4 * int(q) + 3]};
+          put(0, fn, q, v);
         });
-      }
+      });
+      flush(0, dst, int64_t(i) * p.N, i < p.Mo, T.n0 + wn * WN);
     });
   } else {
     OutT* c0 = static_cast<OutT*>(p.c0);
@@ -677,12 +723,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
                 unpack(ax0[BUF][fn][q], xv);
                 dgacc += xv[0] * v[0] + xv[1] * v[1] + xv[2] * v[2] + xv[3] * v[3];
               }
-              if (c0) {
-                if (p.gate) {
-                  static_for<4>([&](auto i) SMOE_INL { v[i] *= g[fm]; });
-                }
-                st4<OutT>(c0 + crow * p.ldc + n, v);
+              if (p.gate) {
+                static_for<4>([&](auto i) SMOE_INL { v[i] *= g[fm]; });
               }
+              put(0, fn, q, v);
             } else if constexpr (EPI == EPI_GELU_FWD) {
               // h stored in bf16; a computed from the stored h
               static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
@@ -690,8 +734,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
               float h[4], a[4];
               unpack4_bf16(wh, h);
               static_for<4>([&](auto i) SMOE_INL { a[i] = gelu_f(h[i]); });
-              *reinterpret_cast<uint2*>(c0 + grow * p.ldc + n) = wh;
-              st4<OutT>(c1 + grow * p.ldc + n, a);
+              float hs[4];
+              unpack4_bf16(wh, hs);
+              put(0, fn, q, hs);
+              put(1, fn, q, a);
             } else if constexpr (EPI == EPI_SWIGLU_FWD) {
               static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
               float v3[4], h1[4], h3[4], a[4];
@@ -700,9 +746,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
               unpack4_bf16(w1, h1);
               unpack4_bf16(w3, h3);
               static_for<4>([&](auto i) SMOE_INL { a[i] = silu_f(h1[i]) * h3[i]; });
-              *reinterpret_cast<uint2*>(c0 + grow * p.ldc + n) = w1;
-              *reinterpret_cast<uint2*>(c1 + grow * p.ldc + n) = w3;
-              st4<OutT>(c2 + grow * p.ldc + n, a);
+              put(0, fn, q, h1);
+              put(1, fn, q, h3);
+              put(2, fn, q, a);
             } else if constexpr (EPI == EPI_GELU_BWD) {
               static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
               float h[4], a[4], dh[4], ag[4];
@@ -714,8 +760,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
                 dh[i] = g[fm] * v[i] * gelu_grad_f(h[i]);
                 ag[i] = g[fm] * a[i];
               });
-              st4<OutT>(c0 + grow * p.ldc + n, dh);
-              st4<OutT>(c2 + grow * p.ldc + n, ag);
+              put(0, fn, q, dh);
+              put(1, fn, q, ag);
             } else if constexpr (EPI == EPI_SWIGLU_BWD) {
               static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
               float h1[4], h3[4], sg[4], si[4], a[4], d1[4], d3[4], ag[4];
@@ -734,9 +780,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
                 d3[i] = dA * si[i];
                 ag[i] = g[fm] * a[i];
               });
-              st4<OutT>(c0 + grow * p.ldc + n, d1);
-              st4<OutT>(c1 + grow * p.ldc + n, d3);
-              st4<OutT>(c2 + grow * p.ldc + n, ag);
+              put(0, fn, q, d1);
+              put(1, fn, q, d3);
+              put(2, fn, q, ag);
             }
           }
         });
@@ -744,6 +790,25 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       if (p.dgpart) {
         dgacc += __shfl_xor(dgacc, 32, kWave);
         if (lane < 32 && rok[fm]) p.dgpart[int64_t(T.nt * 4 + wn) * p.M + gr[fm]] = dgacc;
+      }
+      // staged rows -> global (grouped rows, or scattered for EPI_STORE)
+      const int cb = T.n0 + (DUAL ? wn * (WN / 2) : wn * WN);
+      if constexpr (EPI == EPI_STORE) {
+        if (c0) flush(0, c0, crow * p.ldc, rok[fm], cb);
+      } else if constexpr (EPI == EPI_GELU_FWD) {
+        flush(0, c0, grow * p.ldc, rok[fm], cb);
+        flush(1, c1, grow * p.ldc, rok[fm], cb);
+      } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+        flush(0, c0, grow * p.ldc, rok[fm], cb);
+        flush(1, c1, grow * p.ldc, rok[fm], cb);
+        flush(2, c2, grow * p.ldc, rok[fm], cb);
+      } else if constexpr (EPI == EPI_GELU_BWD) {
+        flush(0, c0, grow * p.ldc, rok[fm], cb);
+        flush(1, c2, grow * p.ldc, rok[fm], cb);
+      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        flush(0, c0, grow * p.ldc, rok[fm], cb);
+        flush(1, c1, grow * p.ldc, rok[fm], cb);
+        flush(2, c2, grow * p.ldc, rok[fm], cb);
       }
     });
   }
