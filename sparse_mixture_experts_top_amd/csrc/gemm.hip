@@ -48,8 +48,6 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-// read-only global memory read through the scalar unit (uniform addresses)
-typedef __attribute__((address_space(4))) const int cint_t;
 
 constexpr int kThreads = 512;   // bf16 kernel
 #ifndef SMOE_BK
@@ -122,6 +120,15 @@ SMOE_DEV void dma16(rsrc_t r, char* wave_lds, uint32_t voff) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(
       uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)wave_lds)));
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(m0v)
+               : "memory", "m0");
+}
+// the same with 4 bytes per lane (64 consecutive dwords)
+SMOE_DEV void dma4(rsrc_t r, char* wave_lds, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)wave_lds)));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(r), "s"(m0v)
                : "memory", "m0");
@@ -356,30 +363,33 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   }
 
   // SEG_K: the source rows of the gathered operand come from
-  // sorted_scattered_idxs.  Load t of wave w covers RPI consecutive grouped
-  // rows, a wave-uniform range, so their indices are read with scalar loads
-  // one stage ahead (the vector-memory counter then counts operand copies
-  // only, which the stage waits rely on).
-  constexpr int SA = MODE == SEG_K ? NA : 1, SB = MODE == SEG_K ? NB : 1;
-  // two sets, by the parity of the step they serve
-  int sa[2][SA][GA::RPI];
-  int sb[2][SB][GB::RPI];
-  auto sload = [&](int kt, auto set) SMOE_INL {
+  // sorted_scattered_idxs.  The indices of the 32 grouped rows of step j are
+  // copied into an LDS ring (slot j % kRing, 64 dwords: every wave copies the
+  // same 64 indices, so each wave's count of copies per step is the same) in
+  // step j-5, ahead of the copies of stage j-2; the stage waits therefore
+  // also cover them, and the barrier of step j-3 publishes them before step
+  // j-3 issues stage j.  The indices are read back with LDS reads, which keep
+  // the LDS counter in order (no scalar loads in the loop).
+  constexpr int kRing = 8, kIdxAhead = kNS + 1;
+  constexpr int IDX = MODE == SEG_K ? 1 : 0;   // index copies per step
+  __shared__ __attribute__((aligned(16))) int ring[MODE == SEG_K ? kRing * 64 : 1];
+  auto idx_copy = [&](int j) SMOE_INL {
     if constexpr (MODE == SEG_K) {
-      const cint_t* cs = (const cint_t*)(p.sidx);
-      const int last = it.row1 - 1;
-      if (p.a_scat) {
-        static_for<NA>([&](auto t) SMOE_INL {
-          const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GA::RPI;
-          static_for<GA::RPI>([&](auto i) SMOE_INL { sa[set][t][i] = cs[min(r0 + int(i), last)]; });
-        });
-      }
-      if (p.b_scat) {
-        static_for<NB>([&](auto t) SMOE_INL {
-          const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GB::RPI;
-          static_for<GB::RPI>([&](auto i) SMOE_INL { sb[set][t][i] = cs[min(r0 + int(i), last)]; });
-        });
-      }
+      const uint32_t r = uint32_t(it.row0 + j * kBK + lane);
+      dma4(make_rsrc(p.sidx, int64_t(p.M) * 4), reinterpret_cast<char*>(ring + (j % kRing) * 64), r * 4u);
+    }
+  };
+  // the lane's raw indices for the copies of step j, read into registers
+  // right after the barrier that published them, ahead of the fragment reads
+  constexpr int SA = MODE == SEG_K ? NA : 1, SB = MODE == SEG_K ? NB : 1;
+  int gia[SA], gib[SB];
+  auto idx_fetch = [&](int j) SMOE_INL {
+    if constexpr (MODE == SEG_K) {
+      const int* slot = ring + (j % kRing) * 64;
+      if (p.a_scat)
+        static_for<NA>([&](auto t) SMOE_INL { gia[t] = slot[(int(t) * 8 + wave) * GA::RPI + lane / GA::CPR]; });
+      if (p.b_scat)
+        static_for<NB>([&](auto t) SMOE_INL { gib[t] = slot[(int(t) * 8 + wave) * GB::RPI + lane / GB::CPR]; });
     }
   };
 
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       });
     }
   };
-  auto issue = [&](int kt, char* stg, auto set) SMOE_INL {
+  auto issue = [&](int kt, char* stg) SMOE_INL {
     if constexpr (MODE == SEG_M) {
       if (kt >= KT0) issue_part(P1{}, (kt - KT0) * kBK, stg);
       else issue_part(P0{}, kt * kBK, stg);
@@ -443,13 +453,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GA::RPI;
         const int i = lane / GA::CPR;
         int src = r0 + i;
-        if (p.a_scat) {
-          // the lane's row among the RPI wave-uniform indices
-          static_for<GA::RPI>([&](auto q) SMOE_INL {
-            const int v = fdiv(sa[set][t][q], p.a_fan_m, p.a_fan_s);
-            src = (int(q) == 0 || i == int(q)) ? v : src;
-          });
-        }
+        if (p.a_scat) src = fdiv(gia[t], p.a_fan_m, p.a_fan_s);
         const bool ok = r0 + i < it.row1 && a_off[t] != kOOB;
         const uint32_t vo = ok ? uint32_t(int64_t(src) * p.lda * 2) + a_off[t] : kOOB;
         dma16(descA(P0{}), As + (int(t) * 8 + wave) * GA::RPI * GA::RB, vo);
@@ -458,12 +462,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GB::RPI;
         const int i = lane / GB::CPR;
         int src = r0 + i;
-        if (p.b_scat) {
-          static_for<GB::RPI>([&](auto q) SMOE_INL {
-            const int v = fdiv(sb[set][t][q], p.b_fan_m, p.b_fan_s);
-            src = (int(q) == 0 || i == int(q)) ? v : src;
-          });
-        }
+        if (p.b_scat) src = fdiv(gib[t], p.b_fan_m, p.b_fan_s);
         const bool ok = r0 + i < it.row1 && b_ok[t];
         const uint32_t vo = ok ? uint32_t(int64_t(src) * p.ldb * 2) + b_off[t] : kOOB;
         dma16(descB(P0{}), Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB, vo);
@@ -517,22 +516,27 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   // s_barrier: the fragment reads of step kt-1 were consumed by its
   // multiplies, which is all the ordering the stages need.
   static_assert(kNS >= 3, "the next stage is published one step early");
-  static_assert(kNS % 2 == 0, "index sets alternate with the step parity; the loop is unrolled by kNS");
   constexpr int NSL = kBK / 16;   // k slices per stage (even)
   // LDS read instructions per slice: one per K-layout fragment, two per
   // transposed (MN-layout) fragment
   constexpr int kFragReads = FM * (ALAY == LAY_K ? 1 : 2) + FN * ((MODE == SEG_M && BLAY == LAY_K) ? 1 : 2);
+  if constexpr (MODE == SEG_K) {
+    // indices of the steps issued before the loop's own index copies land
+    for (int j = 0; j < kIdxAhead; ++j) idx_copy(j);
+    wait_vmem<0>();
+    asm volatile("s_barrier" ::: "memory");
+  }
   static_for<kNS - 1>([&](auto s) SMOE_INL {
     if (int(s) < KT) {
-      sload(int(s), std::integral_constant<int, int(s) & 1>{});
-      issue(int(s), stage(s), std::integral_constant<int, int(s) & 1>{});
+      if constexpr (MODE == SEG_K) idx_copy(int(s) + kIdxAhead);
+      idx_fetch(int(s));
+      issue(int(s), stage(s));
     }
   });
-  sload(kNS - 1, std::integral_constant<int, (kNS - 1) & 1>{});
   // first fragments of step 0 (read before the loop, so that every step's
   // code sees the same outstanding LDS reads and the compiler's waits for
   // them stay exact)
-  if (kNS - 2 < KT) wait_vmem<(kNS - 3) * LPS>();
+  if (kNS - 2 < KT) wait_vmem<(kNS - 3) * (LPS + IDX)>();
   else wait_vmem<0>();
   asm volatile("s_barrier" ::: "memory");
   frags(stage(std::integral_constant<int, 0>{}), 0, fa0, fb0);
@@ -540,14 +544,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     static_for<kNS>([&](auto s) SMOE_INL {
       const int kt = k0 + int(s);
       if (kt < KT) {
-        if (kt + kNS - 2 < KT) wait_vmem<(kNS - 3) * LPS>();
+        if (kt + kNS - 2 < KT) wait_vmem<(kNS - 3) * (LPS + IDX)>();
         else wait_vmem<0>();
-        // gather indices of the stage issued in the next step: scalar loads
-        // share the LDS counter and complete out of order, so they are
-        // issued here, where their latency overlaps the barrier, rather than
-        // between fragment reads and the multiplies that wait on them
-        if (kt + kNS < KT) sload(kt + kNS, std::integral_constant<int, (int(s) + kNS) & 1>{});
         asm volatile("s_barrier" ::: "memory");
+        if (kt + kNS - 1 < KT) idx_fetch(kt + kNS - 1);
         static_for<NSL>([&](auto j) SMOE_INL {
           constexpr int J = decltype(j)::value;
           auto& A = (J & 1) == 0 ? fa0 : fa1;
@@ -578,9 +578,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           if constexpr (J == 0) {
             __builtin_amdgcn_sched_barrier(0);
             const int nk = kt + kNS - 1;
-            if (nk < KT)
-              issue(nk, stage(std::integral_constant<int, int(s) + kNS - 1>{}),
-                    std::integral_constant<int, (int(s) + kNS - 1) & 1>{});
+            if (nk < KT) {
+              // the index copy precedes the stage copies, so the stage waits
+              // cover it (see the ring above)
+              if constexpr (MODE == SEG_K) idx_copy(nk + kIdxAhead - (kNS - 1));
+              issue(nk, stage(std::integral_constant<int, int(s) + kNS - 1>{}));
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
         });
