@@ -165,6 +165,10 @@ def parse():
                     help="also run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl"],
+                    help="mixtral (the measured line); the others print supplementary lines: "
+                         "granular = high-granularity Zipf SMoE-MLP, moa = Mixture-of-Attention "
+                         "projections, pl = single ParallelLinear in its four layouts")
     return ap.parse_args()
 
 
@@ -204,6 +208,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_mib:
         copy_calibration(args.copy_mib)
+    if args.workload != "mixtral":
+        print(json.dumps(supplementary(args)), flush=True)
+        return
     log("generating the Mixtral-shaped workload")
     w = make_config(3)
     T, k, E = w.T, w.k, w.E
@@ -288,6 +295,104 @@ def main():
         log(f"CPU oracle on {args.cpu_tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def _dev(a):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def _time_steps(step, steps, warmup):
+    """Mean wall time per step (ms) between device synchronisations."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def supplementary(args):
+    """One JSON line for a workload other than the measured Mixtral-shaped
+    one: step time, tokens/s, expert-product TFLOP/s and per-launch times."""
+    import torch
+    import sparse_mixture_experts_top_amd as smoe
+    from workloads import make_config
+    steps, warmup = args.steps, args.warmup
+    if args.workload == "granular":
+        w = make_config(4)
+        T, k, E = w.T, w.k, w.E
+        d, f, act = w.dims["d_model"], w.dims["d_ff"], w.act
+        t = {n: _dev(w.tensors[n]) for n in ("x", "w1", "w2", "expert_idxs", "gates", "dout")}
+
+        def step():
+            out, saved = smoe.smoe_mlp_fwd(t["x"], t["w1"], t["w2"], t["expert_idxs"], t["gates"], act)
+            smoe.smoe_mlp_bwd(t["dout"], t["x"], t["w1"], t["w2"], t["expert_idxs"], t["gates"], act, saved)
+
+        roles = [r for r in GEMM_ROLES if r != "dW3"]
+        fl = sum(gemm_flops(T, k, d, f, act).values())
+        name = ("high-granularity SMoE-MLP fwd+bwd: T=16384, d_model=1024, d_ff=512, E=64, k=8, "
+                "Zipf(1.1) routing with 8 empty experts, GELU, bf16")
+    elif args.workload == "moa":
+        w = make_config(5)
+        T, k, E = w.T, w.k, w.E
+        d, hd = w.dims["d_model"], w.dims["head_dim"]
+        t = {n: _dev(w.tensors[n]) for n in ("x", "wq", "wo", "o_in", "dq", "dout", "gates", "expert_idxs")}
+
+        def step():
+            rt = smoe.smoe_route(t["expert_idxs"], E)
+            s, off = rt["sorted_scattered_idxs"], rt["offsets"]
+            smoe.smoe_parallel_linear_fwd(t["x"], t["wq"], T, k, s, off, False, True)
+            smoe.smoe_parallel_linear_fwd(t["o_in"], t["wo"], T, k, s, off, True, False, t["gates"])
+            smoe.smoe_parallel_linear_bwd(t["x"], t["wq"], T, k, s, off, False, True, t["dq"])
+            smoe.smoe_parallel_linear_bwd(t["o_in"], t["wo"], T, k, s, off, True, False, t["dout"], t["gates"],
+                                          need_dgates=True)
+
+        roles = ["pl_fwd", "pl_dx", "pl_dw"]
+        fl = 6 * 2.0 * T * k * d * hd
+        name = ("Mixture-of-Attention projections fwd+bwd: T=8192, d_model=2048, E=16 heads of 128, k=4, "
+                "Q scattered->grouped, O grouped->scattered with the combine, bf16")
+    else:
+        w = make_config(2)
+        T, k, E = w.T, w.k, w.E
+        d_in, d_out = w.dims["d_in"], w.dims["d_out"]
+        x, xg, wt = _dev(w.tensors["x"]), _dev(w.tensors["x_grouped"]), _dev(w.tensors["w"])
+        rt = smoe.smoe_route(_dev(w.tensors["expert_idxs"]), E)
+        s, off = rt["sorted_scattered_idxs"], rt["offsets"]
+        fl = 2.0 * T * k * d_in * d_out
+        variants = {}
+        for xgrp, ygrp, label in ((False, True, "scatter->group"), (False, False, "scatter->scatter"),
+                                  (True, True, "group->group"), (True, False, "group->scatter")):
+            step = lambda: smoe.smoe_parallel_linear_fwd(xg if xgrp else x, wt, T, k, s, off, xgrp, ygrp)
+            ms = _time_steps(step, steps, warmup)
+            variants[label] = {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12}
+        best = min(v["ms"] for v in variants.values())
+        return {"metric": "ParallelLinear forward TFLOP/s per layout (supplementary), 1 MI355X",
+                "value": fl / (best * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+                "warmup": warmup, "dtype": "bf16", "data": "synthetic",
+                "config": {"workload": "single ParallelLinear forward: T=8192, 2048->2048, E=16, k=2, "
+                                       "distinct uniform expert pairs, bf16"},
+                "variants": variants, "mfma_util_pct_best": 100.0 * fl / (best * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    ms = _time_steps(step, steps, warmup)
+    evs = {r: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for r in roles}
+    for r in roles:
+        smoe.smoe_set_role_events(r, *evs[r])
+    step()
+    torch.cuda.synchronize()
+    for r in roles:
+        smoe.smoe_set_role_events(r, None, None)
+    tflops = fl / (ms * 1e-3) / 1e12
+    return {"metric": "tokens/s fwd+bwd (supplementary), 1 MI355X", "value": T / (ms * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+            "dtype": "bf16", "data": "synthetic", "config": {"workload": name},
+            "tflops": tflops, "mfma_util_pct": 100.0 * tflops / PEAK_BF16_TFLOPS,
+            "expert_gemm_tflop_per_step": fl / 1e12,
+            "kernels_ms_last_launch": {r: evs[r][0].elapsed_time(evs[r][1]) for r in roles}}
 
 
 if __name__ == "__main__":
