@@ -685,25 +685,42 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     auto col = [&](auto fn, auto q) SMOE_INL {
       return T.n0 + (DUAL ? wn * (WN / 2) : wn * WN) + int(fn) * 32 + 8 * int(q) + csub;
     };
-    // aux operands of one fragment row, 4 bf16 per (fn, q); double-buffered
-    // over fm so the reads of row fm+1 are in flight while row fm is
-    // computed and stored.  Masked lanes read a clamped, valid address.
-    uint2 ax0[2][FNR][4], ax1[2][AUX1 ? FNR : 1][4];
+    // aux operands of one fragment row.  The lane needs 4 bf16 of each of
+    // the four 8-column chunks of a fragment's 32 columns (half lane >> 5
+    // of each chunk); lane half h reads chunks 2h and 2h+1 whole (16 bytes
+    // each, half the load instructions and line accesses of 8-byte reads)
+    // and the halves it lacks are swapped with lane l ^ 32 when the row is
+    // used.  Double-buffered over fm so the reads of row fm+1 are in flight
+    // while row fm is computed and stored.  Masked lanes read a clamped,
+    // valid address.
+    const int hh = lane >> 5;
+    uint4 rx0[2][FNR][2], rx1[2][AUX1 ? FNR : 1][2];
     auto load_aux = [&](auto fm, auto buf) SMOE_INL {
       if constexpr (AUX0) {
         if (aux0_on) {
           const int64_t row = EPI == EPI_STORE ? (p.aux_scat ? sp[fm] / p.aux_fan : gr[fm]) : gr[fm];
           const int64_t rr = rok[fm] ? row : (EPI == EPI_STORE && p.aux_scat ? 0 : it.row0);
           static_for<FNR>([&](auto fn) SMOE_INL {
-            static_for<4>([&](auto q) SMOE_INL {
-              const int n = col(fn, q);
+            static_for<2>([&](auto j) SMOE_INL {
+              const int n = T.n0 + wn * WN + int(fn) * 32 + 8 * (2 * hh + int(j));
               const int nn = n < p.N ? n : 0;
-              ax0[buf][fn][q] = *reinterpret_cast<const uint2*>(x0 + rr * p.ldaux + nn);
-              if constexpr (AUX1) ax1[buf][fn][q] = *reinterpret_cast<const uint2*>(x1 + rr * p.ldaux + nn);
+              rx0[buf][fn][j] = *reinterpret_cast<const uint4*>(x0 + rr * p.ldaux + nn);
+              if constexpr (AUX1) rx1[buf][fn][j] = *reinterpret_cast<const uint4*>(x1 + rr * p.ldaux + nn);
             });
           });
         }
       }
+    };
+    // the lane's 4 values of chunk q of fragment fn from the 16-byte reads
+    auto aux_vals = [&](uint4 (&rx)[2], uint2 (&ax)[4]) SMOE_INL {
+      static_for<2>([&](auto j) SMOE_INL {
+        const uint2 lo = make_uint2(rx[j].x, rx[j].y), hi = make_uint2(rx[j].z, rx[j].w);
+        const uint2 own = hh ? hi : lo, send = hh ? lo : hi;
+        const uint2 recv = make_uint2(uint32_t(__shfl_xor(int(send.x), 32, kWave)),
+                                      uint32_t(__shfl_xor(int(send.y), 32, kWave)));
+        ax[int(j)] = hh ? recv : own;
+        ax[2 + int(j)] = hh ? own : recv;
+      });
     };
     auto unpack = [&](uint2 w, float v[4]) SMOE_INL { unpack4_bf16(w, v); };
     load_aux(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -715,6 +732,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       const int64_t crow = p.c_scat ? sp[fm] : grow;
       float dgacc = 0.f;
       static_for<FNR>([&](auto fn) SMOE_INL {
+        uint2 ax0[4], ax1[4];
+        if constexpr (AUX0) {
+          if (aux0_on) aux_vals(rx0[BUF][fn], ax0);
+        }
+        if constexpr (AUX1) aux_vals(rx1[BUF][fn], ax1);
         static_for<4>([&](auto q) SMOE_INL {
           const int n = col(fn, q);
           if (rok[fm] && n < p.N) {
@@ -723,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
             if constexpr (EPI == EPI_STORE) {
               if (p.dgpart) {
                 float xv[4];
-                unpack(ax0[BUF][fn][q], xv);
+                unpack(ax0[q], xv);
                 dgacc += xv[0] * v[0] + xv[1] * v[1] + xv[2] * v[2] + xv[3] * v[3];
               }
               if (p.gate) {
@@ -755,7 +777,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
             } else if constexpr (EPI == EPI_GELU_BWD) {
               static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
               float h[4], a[4], dh[4], ag[4];
-              unpack(ax0[BUF][fn][q], h);
+              unpack(ax0[q], h);
               static_for<4>([&](auto i) SMOE_INL { a[i] = gelu_f(h[i]); });
               unpack4_bf16(pack4_bf16(a), a);   // a as stored in the forward
               static_for<4>([&](auto i) SMOE_INL {
@@ -768,8 +790,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
             } else if constexpr (EPI == EPI_SWIGLU_BWD) {
               static_assert(std::is_same<OutT, uint16_t>::value, "bf16 epilogue");
               float h1[4], h3[4], sg[4], si[4], a[4], d1[4], d3[4], ag[4];
-              unpack(ax0[BUF][fn][q], h1);
-              unpack(ax1[BUF][fn][q], h3);
+              unpack(ax0[q], h1);
+              unpack(ax1[q], h3);
               static_for<4>([&](auto i) SMOE_INL {
                 sg[i] = sigmoid_f(h1[i]);
                 si[i] = h1[i] * sg[i];
