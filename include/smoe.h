@@ -29,6 +29,9 @@
  *    saved activations.  Weight gradients are always fp32.
  *  - Feature sizes (d_in, d_out, d_model, d_ff) must be multiples of 8 and
  *    rows must be 16-byte aligned; T*k must fit in int32.
+ *  - bf16: T*k rows of any feature size, and one expert's weights, must
+ *    each be under 4 GiB (the grouped products address their operands
+ *    with 32-bit byte offsets); larger calls fail with SMOE_ERR_SHAPE.
  *  - Scratch memory comes from the caller as (ws, ws_bytes); the matching
  *    *_workspace_bytes() gives the size needed.
  *  - Return value: SMOE_OK or an error status.  A failed host-side check

@@ -90,6 +90,17 @@ int check_dim(int64_t d, const char* name) {
   return SMOE_OK;
 }
 
+// bf16 grouped products address their operands through buffer descriptors
+// with 32-bit byte offsets: every tensor they read (a [T*k, d] activation,
+// one expert's [d_in, d_out] weights) must stay below 4 GiB
+int check_extent(int32_t dtype, int64_t rows, int64_t cols, const char* what) {
+  constexpr int64_t kMaxBytes = int64_t(0xFFFFFFF0u);
+  if (dtype == SMOE_BF16 && rows * cols * 2 > kMaxBytes)
+    return fail(SMOE_ERR_SHAPE, "%s of %lld x %lld bf16 exceeds the 4 GiB operand limit", what, (long long)rows,
+                (long long)cols);
+  return SMOE_OK;
+}
+
 #define SMOE_TRY(x)            \
   do {                         \
     int _s = (x);              \
@@ -307,6 +318,8 @@ int smoe_parallel_linear_fwd(const void* x, int64_t x_rows, int64_t d_in, const 
   if (x_grouped ? x_rows != M : (x_rows != T && x_rows != M))
     return fail(SMOE_ERR_SHAPE, "x_rows=%lld does not fit the layout (T=%lld, T*k=%lld)", (long long)x_rows,
                 (long long)T, (long long)M);
+  SMOE_TRY(check_extent(dtype, M, d_in, "x"));
+  SMOE_TRY(check_extent(dtype, d_in, d_out, "w[e]"));
   if (gates && y_grouped) return fail(SMOE_ERR_SHAPE, "the gate-weighted combine needs a scattered output");
   SMOE_TRY(need_ptr(w, "w"));
   SMOE_TRY(need_ptr(offsets, "offsets"));
@@ -376,6 +389,9 @@ int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in, const 
   const int64_t M = T * k;
   if (x_grouped ? x_rows != M : (x_rows != T && x_rows != M))
     return fail(SMOE_ERR_SHAPE, "x_rows=%lld does not fit the layout", (long long)x_rows);
+  SMOE_TRY(check_extent(dtype, M, d_in, "x"));
+  SMOE_TRY(check_extent(dtype, M, d_out, "dy"));
+  SMOE_TRY(check_extent(dtype, d_in, d_out, "w[e]"));
   if (gates && y_grouped) return fail(SMOE_ERR_SHAPE, "the gate-weighted combine needs a scattered output");
   if (dgates && !gates) return fail(SMOE_ERR_NULL, "dgates needs gates");
   SMOE_TRY(need_ptr(w, "w"));
@@ -478,6 +494,9 @@ static int check_mlp(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d
   SMOE_TRY(check_common(T, k, E, dtype));
   SMOE_TRY(check_dim(d_model, "d_model"));
   SMOE_TRY(check_dim(d_ff, "d_ff"));
+  SMOE_TRY(check_extent(dtype, T * k, d_model, "token rows"));
+  SMOE_TRY(check_extent(dtype, T * k, d_ff, "hidden rows"));
+  SMOE_TRY(check_extent(dtype, d_model, d_ff, "w[e]"));
   if (act != SMOE_ACT_GELU && act != SMOE_ACT_SWIGLU) return fail(SMOE_ERR_DTYPE, "unknown activation %d", act);
   if ((act == SMOE_ACT_SWIGLU) != (w3 != nullptr)) return fail(SMOE_ERR_NULL, "w3 must be given exactly for SWIGLU");
   return SMOE_OK;

@@ -94,3 +94,24 @@ def test_mlp_rejects_bad_arguments():
     assert g(_fake(), _fake(), _fake(), NULL, _fake(), 16, 64, 128, 4, 2, _fake(), _fake(),
              smoe.ACT_GELU, smoe.BF16, _fake(), 1 << 30, _fake(), _fake(), _fake(), _fake(), NULL,
              _fake(), 1 << 30, NULL) == 1          # dw3 given for GELU
+
+
+def test_bf16_operands_beyond_32bit_offsets_are_rejected():
+    """bf16 grouped products address operands with 32-bit byte offsets: a
+    call whose [T*k, d] rows or one expert's weights reach 4 GiB fails on
+    the host with a shape error instead of reading wrapped offsets."""
+    f = lib.smoe_parallel_linear_fwd
+    T, k = 300000, 2
+    # [T*k, 4096] bf16 = 4.9 GB
+    assert f(_fake(), T, 4096, _fake(), 64, 4, T, k, _fake(), _fake(), 0, 0, NULL, _fake(), smoe.BF16,
+             _fake(), 1 << 30, NULL) == 2
+    assert b"4 GiB" in lib.smoe_last_error()
+    # one expert's weights [65536, 40000] bf16 = 5.2 GB
+    assert f(_fake(), 8, 65536, _fake(), 40000, 4, 8, 2, _fake(), _fake(), 0, 0, NULL, _fake(), smoe.BF16,
+             _fake(), 1 << 30, NULL) == 2
+    assert b"w[e]" in lib.smoe_last_error()
+    g = lib.smoe_mlp_fwd
+    # hidden rows [2 * 160000, 14336] bf16 = 9.2 GB
+    assert g(_fake(), _fake(), NULL, _fake(), 160000, 64, 14336, 4, 2, _fake(), _fake(), smoe.ACT_GELU,
+             smoe.BF16, _fake(), _fake(), 1 << 40, _fake(), 1 << 40, NULL) == 2
+    assert b"hidden rows" in lib.smoe_last_error()
