@@ -116,9 +116,11 @@ SMOE_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // these copies (it cannot tell the stages apart); the kernel waits for the
 // copies itself (wait_vmem) before the barrier that publishes a stage.  The
 // asm has no register outputs; its inputs are read when it issues.
+// The LDS address is the low 32 bits of the flat address of wave_lds (the
+// LDS aperture starts at a multiple of 4 GiB).
+SMOE_DEV uint32_t lds_addr(const char* p) { return uint32_t(reinterpret_cast<uintptr_t>(p)); }
 SMOE_DEV void dma16(rsrc_t r, char* wave_lds, uint32_t voff) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)wave_lds)));
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(wave_lds));
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(r), "s"(m0v)
@@ -126,8 +128,7 @@ SMOE_DEV void dma16(rsrc_t r, char* wave_lds, uint32_t voff) {
 }
 // the same with 4 bytes per lane (64 consecutive dwords)
 SMOE_DEV void dma4(rsrc_t r, char* wave_lds, uint32_t voff) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)wave_lds)));
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(wave_lds));
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(r), "s"(m0v)
@@ -316,23 +317,27 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  uint32_t a_off[NA];   // K-layout: row byte offset; MN-layout: column byte offset
+  // row pitches in bytes (every operand is under 4 GiB)
+  const uint32_t lda2 = uint32_t(p.lda * 2), ldb2 = uint32_t(p.ldb * 2);
+  // K-layout: row byte offset; MN-layout: column byte offset.  Rows and
+  // columns outside the tile's valid range read other (in-range) data:
+  // their products land only in outputs that are never stored.  Only k
+  // beyond the end of the reduction must read zero, on both operands.
+  uint32_t a_off[NA];
   uint32_t b_off[NB];
-  bool b_ok[NB];
 
   if constexpr (MODE == SEG_M) {
     static_for<NA>([&](auto t) SMOE_INL {
       const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
       const int gr = it.row0 + row;
       const int src = gr < it.row1 ? (p.a_scat ? p.sidx[gr] / p.a_fan : gr) : -1;
-      a_off[t] = src >= 0 ? uint32_t(int64_t(src) * p.lda * 2) : kOOB;
+      a_off[t] = src >= 0 ? uint32_t(int64_t(src) * p.lda * 2) : 0u;
     });
     if constexpr (BLAY == LAY_K) {
       // W[e] viewed [n][k]: N rows of ldb
       static_for<NB>([&](auto t) SMOE_INL {
         const int n = T.n0 + (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
-        b_off[t] = n < p.N ? uint32_t(int64_t(n) * p.ldb * 2) : kOOB;
-        b_ok[t] = true;
+        b_off[t] = n < p.N ? uint32_t(int64_t(n) * p.ldb * 2) : 0u;
       });
     } else {
       // W[e] viewed [k][n]: K rows of ldb.  Dual: the tile is two BN/2-column
@@ -342,7 +347,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         if constexpr (DUAL) mn_slot<BN / 2>(int(t) % (NB / 2), wave, lane, krow, c);
         else mn_slot<BN>(int(t), wave, lane, krow, c);
         const int col = T.n0 + 8 * c;
-        b_ok[t] = col < p.N;
         b_off[t] = uint32_t(col) * 2;
       });
     }
@@ -351,13 +355,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       int krow, c;
       mn_slot<BM>(int(t), wave, lane, krow, c);
       const int i = T.m0 + 8 * c;
-      a_off[t] = i < p.Mo ? uint32_t(i) * 2 : kOOB;
+      a_off[t] = uint32_t(i) * 2;
     });
     static_for<NB>([&](auto t) SMOE_INL {
       int krow, c;
       mn_slot<BN>(int(t), wave, lane, krow, c);
       const int j = T.n0 + 8 * c;
-      b_ok[t] = j < p.N;
       b_off[t] = uint32_t(j) * 2;
     });
   }
@@ -385,11 +388,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   int gia[SA], gib[SB];
   auto idx_fetch = [&](int j) SMOE_INL {
     if constexpr (MODE == SEG_K) {
+      // read for both operands, gathered or not (no branch: the copies
+      // select the index or the plain row)
       const int* slot = ring + (j % kRing) * 64;
-      if (p.a_scat)
-        static_for<NA>([&](auto t) SMOE_INL { gia[t] = slot[(int(t) * 8 + wave) * GA::RPI + lane / GA::CPR]; });
-      if (p.b_scat)
-        static_for<NB>([&](auto t) SMOE_INL { gib[t] = slot[(int(t) * 8 + wave) * GB::RPI + lane / GB::CPR]; });
+      static_for<NA>([&](auto t) SMOE_INL { gia[t] = slot[(int(t) * 8 + wave) * GA::RPI + lane / GA::CPR]; });
+      static_for<NB>([&](auto t) SMOE_INL { gib[t] = slot[(int(t) * 8 + wave) * GB::RPI + lane / GB::CPR]; });
     }
   };
 
@@ -405,16 +408,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     static_for<NA>([&](auto t) SMOE_INL {
       const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
       const int kb = (lane % KGeom::KC) ^ swz_k(row);
-      const bool ok = a_off[t] != kOOB && kl + kb * 8 < Kp;
-      const uint32_t vo = ok ? a_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
+      const uint32_t vo = kl + kb * 8 < Kp ? a_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
       dma16(descA(part), As + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB, vo);
     });
     if constexpr (BLAY == LAY_K) {
       static_for<NB>([&](auto t) SMOE_INL {
         const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
         const int kb = (lane % KGeom::KC) ^ swz_k(row);
-        const bool ok = b_off[t] != kOOB && kl + kb * 8 < Kp;
-        const uint32_t vo = ok ? b_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
+        const uint32_t vo = kl + kb * 8 < Kp ? b_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
         dma16(descB(part), Bs + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB, vo);
       });
     } else {
@@ -431,8 +432,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           dst = Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB;
         }
         const int k = kl + krow;
-        const bool ok = b_ok[t] && k < K0;
-        const uint32_t vo = ok ? uint32_t(int64_t(k) * p.ldb * 2) + b_off[t] : kOOB;
+        const uint32_t vo = k < K0 ? uint32_t(k) * ldb2 + b_off[t] : kOOB;
         if constexpr (DUAL) {
           if constexpr (int(t) >= NB / 2) dma16(descB(P1{}), dst, vo);
           else dma16(descB(P0{}), dst, vo);
@@ -452,19 +452,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       static_for<NA>([&](auto t) SMOE_INL {
         const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GA::RPI;
         const int i = lane / GA::CPR;
-        int src = r0 + i;
-        if (p.a_scat) src = fdiv(gia[t], p.a_fan_m, p.a_fan_s);
-        const bool ok = r0 + i < it.row1 && a_off[t] != kOOB;
-        const uint32_t vo = ok ? uint32_t(int64_t(src) * p.lda * 2) + a_off[t] : kOOB;
+        const int src = p.a_scat ? fdiv(gia[t], p.a_fan_m, p.a_fan_s) : r0 + i;
+        const uint32_t vo = r0 + i < it.row1 ? uint32_t(src) * lda2 + a_off[t] : kOOB;
         dma16(descA(P0{}), As + (int(t) * 8 + wave) * GA::RPI * GA::RB, vo);
       });
       static_for<NB>([&](auto t) SMOE_INL {
         const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GB::RPI;
         const int i = lane / GB::CPR;
-        int src = r0 + i;
-        if (p.b_scat) src = fdiv(gib[t], p.b_fan_m, p.b_fan_s);
-        const bool ok = r0 + i < it.row1 && b_ok[t];
-        const uint32_t vo = ok ? uint32_t(int64_t(src) * p.ldb * 2) + b_off[t] : kOOB;
+        const int src = p.b_scat ? fdiv(gib[t], p.b_fan_m, p.b_fan_s) : r0 + i;
+        const uint32_t vo = r0 + i < it.row1 ? uint32_t(src) * ldb2 + b_off[t] : kOOB;
         dma16(descB(P0{}), Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB, vo);
       });
     }
