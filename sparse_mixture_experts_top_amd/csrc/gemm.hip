@@ -319,6 +319,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   using P1 = std::integral_constant<int, 1>;
   // row pitches in bytes (every operand is under 4 GiB)
   const uint32_t lda2 = uint32_t(p.lda * 2), ldb2 = uint32_t(p.ldb * 2);
+  // SEG_K: all-ones when the operand's rows are gathered (a mask rather
+  // than a condition, so that the copies carry no branch)
+  const int scat_a = -int(p.a_scat != 0), scat_b = -int(p.b_scat != 0);
   // K-layout: row byte offset; MN-layout: column byte offset.  Rows and
   // columns outside the tile's valid range read other (in-range) data:
   // their products land only in outputs that are never stored.  Only k
@@ -452,14 +455,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       static_for<NA>([&](auto t) SMOE_INL {
         const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GA::RPI;
         const int i = lane / GA::CPR;
-        const int src = p.a_scat ? fdiv(gia[t], p.a_fan_m, p.a_fan_s) : r0 + i;
+        const int src = (fdiv(gia[t], p.a_fan_m, p.a_fan_s) & scat_a) | ((r0 + i) & ~scat_a);
         const uint32_t vo = r0 + i < it.row1 ? uint32_t(src) * lda2 + a_off[t] : kOOB;
         dma16(descA(P0{}), As + (int(t) * 8 + wave) * GA::RPI * GA::RB, vo);
       });
       static_for<NB>([&](auto t) SMOE_INL {
         const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GB::RPI;
         const int i = lane / GB::CPR;
-        const int src = p.b_scat ? fdiv(gib[t], p.b_fan_m, p.b_fan_s) : r0 + i;
+        const int src = (fdiv(gib[t], p.b_fan_m, p.b_fan_s) & scat_b) | ((r0 + i) & ~scat_b);
         const uint32_t vo = r0 + i < it.row1 ? uint32_t(src) * ldb2 + b_off[t] : kOOB;
         dma16(descB(P0{}), Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB, vo);
       });
