@@ -126,6 +126,16 @@ SMOE_DEV void dma16(rsrc_t r, char* wave_lds, uint32_t voff) {
                : "v"(voff), "s"(r), "s"(m0v)
                : "memory", "m0");
 }
+// the same at byte offset voff + soff: soff is the wave-uniform part (the
+// step's advance along k), so a copy inside the buffer needs no vector
+// arithmetic per step.  Only used where voff + soff stays in range.
+SMOE_DEV void dma16s(rsrc_t r, char* wave_lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(wave_lds));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(m0v), "s"(soff)
+               : "memory", "m0");
+}
 // the same with 4 bytes per lane (64 consecutive dwords)
 SMOE_DEV void dma4(rsrc_t r, char* wave_lds, uint32_t voff) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(wave_lds));
@@ -322,25 +332,34 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   // SEG_K: all-ones when the operand's rows are gathered (a mask rather
   // than a condition, so that the copies carry no branch)
   const int scat_a = -int(p.a_scat != 0), scat_b = -int(p.b_scat != 0);
-  // K-layout: row byte offset; MN-layout: column byte offset.  Rows and
-  // columns outside the tile's valid range read other (in-range) data:
+  // Per copy and lane, the byte offset of the lane's 16 bytes at k = 0 of
+  // the part (SEG_M) or chunk (SEG_K), and the lane's k within a step (ka,
+  // kb: k offset of its chunk for K-layout, k-row for MN-layout).  A full
+  // step then advances every copy by one wave-uniform scalar offset.  Rows
+  // and columns outside the tile's valid range read other (in-range) data:
   // their products land only in outputs that are never stored.  Only k
-  // beyond the end of the reduction must read zero, on both operands.
-  uint32_t a_off[NA];
-  uint32_t b_off[NB];
+  // beyond the end of the reduction must read zero, on both operands; the
+  // step that crosses it takes a per-lane path.
+  uint32_t a_off[NA], b_off[NB];
+  int ka[NA], kb_[NB];
+  // SEG_K: column byte offset of the lane (a_col / b_col) for gathered rows
+  uint32_t a_col[MODE == SEG_K ? NA : 1], b_col[MODE == SEG_K ? NB : 1];
 
   if constexpr (MODE == SEG_M) {
     static_for<NA>([&](auto t) SMOE_INL {
       const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
       const int gr = it.row0 + row;
       const int src = gr < it.row1 ? (p.a_scat ? p.sidx[gr] / p.a_fan : gr) : -1;
-      a_off[t] = src >= 0 ? uint32_t(int64_t(src) * p.lda * 2) : 0u;
+      ka[t] = ((lane % KGeom::KC) ^ swz_k(row)) * 8;
+      a_off[t] = (src >= 0 ? uint32_t(int64_t(src) * p.lda * 2) : 0u) + uint32_t(ka[t]) * 2;
     });
     if constexpr (BLAY == LAY_K) {
       // W[e] viewed [n][k]: N rows of ldb
       static_for<NB>([&](auto t) SMOE_INL {
-        const int n = T.n0 + (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
-        b_off[t] = n < p.N ? uint32_t(int64_t(n) * p.ldb * 2) : 0u;
+        const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
+        const int n = T.n0 + row;
+        kb_[t] = ((lane % KGeom::KC) ^ swz_k(row)) * 8;
+        b_off[t] = (n < p.N ? uint32_t(int64_t(n) * p.ldb * 2) : 0u) + uint32_t(kb_[t]) * 2;
       });
     } else {
       // W[e] viewed [k][n]: K rows of ldb.  Dual: the tile is two BN/2-column
@@ -350,23 +369,31 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         if constexpr (DUAL) mn_slot<BN / 2>(int(t) % (NB / 2), wave, lane, krow, c);
         else mn_slot<BN>(int(t), wave, lane, krow, c);
         const int col = T.n0 + 8 * c;
-        b_off[t] = uint32_t(col) * 2;
+        kb_[t] = krow;
+        b_off[t] = uint32_t(krow) * ldb2 + uint32_t(col) * 2;
       });
     }
   } else {
     static_for<NA>([&](auto t) SMOE_INL {
       int krow, c;
       mn_slot<BM>(int(t), wave, lane, krow, c);
-      const int i = T.m0 + 8 * c;
-      a_off[t] = uint32_t(i) * 2;
+      a_col[t] = uint32_t(T.m0 + 8 * c) * 2;
+      ka[t] = (int(t) * 8 + wave) * GA::RPI + lane / GA::CPR;   // row within the step
+      a_off[t] = uint32_t(ka[t]) * lda2 + a_col[t];
     });
     static_for<NB>([&](auto t) SMOE_INL {
       int krow, c;
       mn_slot<BN>(int(t), wave, lane, krow, c);
-      const int j = T.n0 + 8 * c;
-      b_off[t] = uint32_t(j) * 2;
+      b_col[t] = uint32_t(T.n0 + 8 * c) * 2;
+      kb_[t] = (int(t) * 8 + wave) * GB::RPI + lane / GB::CPR;
+      b_off[t] = uint32_t(kb_[t]) * ldb2 + b_col[t];
     });
   }
+  // descriptors, built once
+  const rsrc_t rA0 = descA(std::integral_constant<int, 0>{});
+  const rsrc_t rA1 = descA(std::integral_constant<int, 1>{});
+  const rsrc_t rB0 = descB(std::integral_constant<int, 0>{});
+  const rsrc_t rB1 = descB(std::integral_constant<int, 1>{});
 
   // SEG_K: the source rows of the gathered operand come from
   // sorted_scattered_idxs.  The indices of the 32 grouped rows of step j are
@@ -400,72 +427,84 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   };
 
   // ---------------- copy step kt into stage `stg` -------------------------
-  // SEG_M: a uniform branch on the K part picks the buffer descriptors, so
-  // each copy names a fixed (scalar) descriptor
+  // SEG_M: a uniform branch on the K part picks the buffer descriptors.  A
+  // step inside the reduction advances every copy by one scalar offset; the
+  // step that crosses its end (a uniform branch, at most one per part)
+  // zero-fills the lanes past it.
   auto issue_part = [&](auto part, int kl, char* stg) SMOE_INL {
     constexpr int P = decltype(part)::value;
     char* As = stg;
     char* Bs = stg + A_BYTES;
     const int Kp = P ? K1 : K0;
-    // K-layout A: lane copies logical chunk (lane % KC) ^ swz_k(row)
-    static_for<NA>([&](auto t) SMOE_INL {
-      const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
-      const int kb = (lane % KGeom::KC) ^ swz_k(row);
-      const uint32_t vo = kl + kb * 8 < Kp ? a_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
-      dma16(descA(part), As + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB, vo);
-    });
-    if constexpr (BLAY == LAY_K) {
-      static_for<NB>([&](auto t) SMOE_INL {
-        const int row = (int(t) * 8 + wave) * KGeom::RPL + lane / KGeom::KC;
-        const int kb = (lane % KGeom::KC) ^ swz_k(row);
-        const uint32_t vo = kl + kb * 8 < Kp ? b_off[t] + uint32_t(kl + kb * 8) * 2 : kOOB;
-        dma16(descB(part), Bs + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB, vo);
+    const rsrc_t& rA = P ? rA1 : rA0;
+    const rsrc_t& rB = P ? rB1 : rB0;
+    auto copies = [&](auto full) SMOE_INL {
+      constexpr bool F = decltype(full)::value;
+      // K-layout A: lane copies logical chunk (lane % KC) ^ swz_k(row)
+      static_for<NA>([&](auto t) SMOE_INL {
+        char* dst = As + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB;
+        if constexpr (F) dma16s(rA, dst, a_off[t], uint32_t(kl) * 2);
+        else dma16(rA, dst, kl + ka[t] < Kp ? a_off[t] + uint32_t(kl) * 2 : kOOB);
       });
-    } else {
-      static_for<NB>([&](auto t) SMOE_INL {
-        int krow, c;
-        char* dst;
-        if constexpr (DUAL) {
-          using G = MnGeom<BN / 2>;
-          constexpr int tt = int(t) % (NB / 2);
-          mn_slot<BN / 2>(tt, wave, lane, krow, c);
-          dst = Bs + (int(t) / (NB / 2)) * (BN / 2) * kBK * 2 + (tt * 8 + wave) * G::RPI * G::RB;
-        } else {
-          mn_slot<BN>(int(t), wave, lane, krow, c);
-          dst = Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB;
-        }
-        const int k = kl + krow;
-        const uint32_t vo = k < K0 ? uint32_t(k) * ldb2 + b_off[t] : kOOB;
-        if constexpr (DUAL) {
-          if constexpr (int(t) >= NB / 2) dma16(descB(P1{}), dst, vo);
-          else dma16(descB(P0{}), dst, vo);
-        } else {
-          dma16(descB(P0{}), dst, vo);
-        }
-      });
-    }
+      if constexpr (BLAY == LAY_K) {
+        static_for<NB>([&](auto t) SMOE_INL {
+          char* dst = Bs + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB;
+          if constexpr (F) dma16s(rB, dst, b_off[t], uint32_t(kl) * 2);
+          else dma16(rB, dst, kl + kb_[t] < Kp ? b_off[t] + uint32_t(kl) * 2 : kOOB);
+        });
+      } else {
+        // one K part: W[e] viewed [k][n] has K0 rows
+        static_for<NB>([&](auto t) SMOE_INL {
+          char* dst;
+          if constexpr (DUAL) {
+            using G = MnGeom<BN / 2>;
+            constexpr int tt = int(t) % (NB / 2);
+            dst = Bs + (int(t) / (NB / 2)) * (BN / 2) * kBK * 2 + (tt * 8 + wave) * G::RPI * G::RB;
+          } else {
+            dst = Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB;
+          }
+          // dual: loads t >= NB/2 read W3
+          const rsrc_t& r = (DUAL && int(t) >= NB / 2) ? rB1 : rB0;
+          if constexpr (F) dma16s(r, dst, b_off[t], uint32_t(kl) * ldb2);
+          else dma16(r, dst, kl + kb_[t] < K0 ? b_off[t] + uint32_t(kl) * ldb2 : kOOB);
+        });
+      }
+    };
+    const bool full = kl + kBK <= Kp && (BLAY == LAY_K || kl + kBK <= K0);
+    if (full) copies(std::true_type{});
+    else copies(std::false_type{});
   };
   auto issue = [&](int kt, char* stg) SMOE_INL {
     if constexpr (MODE == SEG_M) {
       if (kt >= KT0) issue_part(P1{}, (kt - KT0) * kBK, stg);
       else issue_part(P0{}, kt * kBK, stg);
     } else {
+      // SEG_K: a plain operand advances by the step's first row (a scalar
+      // offset); a gathered one addresses each row from its index
       char* As = stg;
       char* Bs = stg + A_BYTES;
-      static_for<NA>([&](auto t) SMOE_INL {
-        const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GA::RPI;
-        const int i = lane / GA::CPR;
-        const int src = (fdiv(gia[t], p.a_fan_m, p.a_fan_s) & scat_a) | ((r0 + i) & ~scat_a);
-        const uint32_t vo = r0 + i < it.row1 ? uint32_t(src) * lda2 + a_off[t] : kOOB;
-        dma16(descA(P0{}), As + (int(t) * 8 + wave) * GA::RPI * GA::RB, vo);
-      });
-      static_for<NB>([&](auto t) SMOE_INL {
-        const int r0 = it.row0 + kt * kBK + (int(t) * 8 + wave) * GB::RPI;
-        const int i = lane / GB::CPR;
-        const int src = (fdiv(gib[t], p.b_fan_m, p.b_fan_s) & scat_b) | ((r0 + i) & ~scat_b);
-        const uint32_t vo = r0 + i < it.row1 ? uint32_t(src) * ldb2 + b_off[t] : kOOB;
-        dma16(descB(P0{}), Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB, vo);
-      });
+      const int r0 = it.row0 + kt * kBK;
+      const uint32_t sa = (uint32_t(r0) * lda2) & uint32_t(~scat_a);
+      const uint32_t sb = (uint32_t(r0) * ldb2) & uint32_t(~scat_b);
+      auto copies = [&](auto full) SMOE_INL {
+        constexpr bool F = decltype(full)::value;
+        static_for<NA>([&](auto t) SMOE_INL {
+          const uint32_t g = uint32_t(fdiv(gia[t], p.a_fan_m, p.a_fan_s)) * lda2 + a_col[t];
+          const uint32_t vo = (g & uint32_t(scat_a)) | (a_off[t] & uint32_t(~scat_a));
+          char* dst = As + (int(t) * 8 + wave) * GA::RPI * GA::RB;
+          if constexpr (F) dma16s(rA0, dst, vo, sa);
+          else dma16(rA0, dst, r0 + ka[t] < it.row1 ? vo + sa : kOOB);
+        });
+        static_for<NB>([&](auto t) SMOE_INL {
+          const uint32_t g = uint32_t(fdiv(gib[t], p.b_fan_m, p.b_fan_s)) * ldb2 + b_col[t];
+          const uint32_t vo = (g & uint32_t(scat_b)) | (b_off[t] & uint32_t(~scat_b));
+          char* dst = Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB;
+          if constexpr (F) dma16s(rB0, dst, vo, sb);
+          else dma16(rB0, dst, r0 + kb_[t] < it.row1 ? vo + sb : kOOB);
+        });
+      };
+      if (r0 + kBK <= it.row1) copies(std::true_type{});
+      else copies(std::false_type{});
     }
   };
 
