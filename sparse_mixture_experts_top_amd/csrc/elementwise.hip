@@ -16,37 +16,70 @@ static unsigned grid_for(int64_t n, int per_block) {
 }
 
 // out[t][c] = sum_j w(t,j) * pairs[t*k+j][c], 4 columns per thread, fp32 sum
-// in ascending j.
-template <class OutT>
+// in ascending j.  Grid: x over 4-column groups, y over tokens.  The k rows
+// of a token are loaded before any is summed (KK = k known at compile time,
+// or groups of four), so each thread keeps several loads in flight: with one
+// load per trip a thread waits a full memory latency per row.
+template <class OutT, int KK>
 __global__ __launch_bounds__(kEwThreads) void combine_kernel(const float* __restrict__ pairs,
                                                              const float* __restrict__ gates, int64_t T, int k,
                                                              int64_t d4, OutT* __restrict__ out) {
-  const int64_t n = T * d4;
-  for (int64_t i = blockIdx.x * int64_t(kEwThreads) + threadIdx.x; i < n; i += int64_t(gridDim.x) * kEwThreads) {
-    const int64_t t = i / d4, c = (i - t * d4) * 4;
+  const int64_t c4 = int64_t(blockIdx.x) * kEwThreads + threadIdx.x;
+  if (c4 >= d4) return;
+  const float4* pv = reinterpret_cast<const float4*>(pairs);
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
     float s[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int64_t p = t * k + j;
-      const float w = gates ? gates[p] : 1.f;
-      const float4 v = *reinterpret_cast<const float4*>(pairs + p * (d4 * 4) + c);
+    auto add = [&](float w, const float4& v) SMOE_INL {
       s[0] += w * v.x; s[1] += w * v.y; s[2] += w * v.z; s[3] += w * v.w;
+    };
+    if constexpr (KK > 0) {
+      float4 v[KK];
+      float w[KK];
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        v[j] = pv[(t * KK + j) * d4 + c4];
+        w[j] = gates ? gates[t * KK + j] : 1.f;
+      }
+#pragma unroll
+      for (int j = 0; j < KK; ++j) add(w[j], v[j]);
+    } else {
+      int j = 0;
+      for (; j + 4 <= k; j += 4) {
+        float4 v[4];
+        float w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = pv[(t * k + j + q) * d4 + c4];
+          w[q] = gates ? gates[t * k + j + q] : 1.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) add(w[q], v[q]);
+      }
+      for (; j < k; ++j) add(gates ? gates[t * k + j] : 1.f, pv[(t * k + j) * d4 + c4]);
     }
-    st4<OutT>(out + t * (d4 * 4) + c, s);
+    st4<OutT>(out + t * (d4 * 4) + c4 * 4, s);
+  }
+}
+
+template <class OutT>
+static void go_combine(const float* pairs, const float* gates, int64_t T, int k, int64_t d4, OutT* out,
+                       hipStream_t st) {
+  const dim3 grid(unsigned((d4 + kEwThreads - 1) / kEwThreads), unsigned(std::min<int64_t>(T, 65535)));
+  switch (k) {
+    case 1: hipLaunchKernelGGL((combine_kernel<OutT, 1>), grid, dim3(kEwThreads), 0, st, pairs, gates, T, k, d4, out); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<OutT, 2>), grid, dim3(kEwThreads), 0, st, pairs, gates, T, k, d4, out); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<OutT, 4>), grid, dim3(kEwThreads), 0, st, pairs, gates, T, k, d4, out); break;
+    case 8: hipLaunchKernelGGL((combine_kernel<OutT, 8>), grid, dim3(kEwThreads), 0, st, pairs, gates, T, k, d4, out); break;
+    default: hipLaunchKernelGGL((combine_kernel<OutT, 0>), grid, dim3(kEwThreads), 0, st, pairs, gates, T, k, d4, out);
   }
 }
 
 hipError_t launch_combine(const float* pairs, const float* gates, int64_t T, int k, int64_t d, void* out,
                           int out_bf16, hipStream_t st) {
   const int64_t d4 = d / 4;
-  const int64_t n = T * d4;
-  if (n == 0) return hipSuccess;
-  const unsigned g = grid_for(n, kEwThreads);
-  if (out_bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(g), dim3(kEwThreads), 0, st, pairs, gates, T, k, d4,
-                       static_cast<uint16_t*>(out));
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(g), dim3(kEwThreads), 0, st, pairs, gates, T, k, d4,
-                       static_cast<float*>(out));
+  if (T == 0 || d4 == 0) return hipSuccess;
+  if (out_bf16) go_combine(pairs, gates, T, k, d4, static_cast<uint16_t*>(out), st);
+  else go_combine(pairs, gates, T, k, d4, static_cast<float*>(out), st);
   return hipGetLastError();
 }
 
@@ -86,10 +119,22 @@ __global__ __launch_bounds__(kEwThreads) void reduce_dw_kernel(const float* __re
   const int first = first_s, n = n_s;
   if (n == 1) return;
   float4* out = reinterpret_cast<float4*>(dw) + int64_t(e) * elems4;
+  const float4* pv = reinterpret_cast<const float4*>(partial) + int64_t(first) * elems4;
   for (int64_t i = blockIdx.x * int64_t(kEwThreads) + threadIdx.x; i < elems4; i += int64_t(gridDim.x) * kEwThreads) {
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c = 0; c < n; ++c) {
-      const float4 v = reinterpret_cast<const float4*>(partial)[int64_t(first + c) * elems4 + i];
+    // chunks in ascending order; four loads in flight before they are summed
+    int c = 0;
+    for (; c + 4 <= n; c += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = pv[int64_t(c + q) * elems4 + i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s.x += v[q].x; s.y += v[q].y; s.z += v[q].z; s.w += v[q].w;
+      }
+    }
+    for (; c < n; ++c) {
+      const float4 v = pv[int64_t(c) * elems4 + i];
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
     out[i] = s;
