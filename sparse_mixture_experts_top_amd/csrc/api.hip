@@ -3,6 +3,7 @@
 // launch sequence of each entry point.  Nothing here allocates,
 // synchronises or copies device memory; everything is enqueued on the
 // caller's stream.
+#include <mutex>
 #include <stdint.h>
 #include <string.h>
 
@@ -47,6 +48,32 @@ constexpr size_t kAlign = 256;
 hipEvent_t g_role_ev[SMOE_ROLE_COUNT][2] = {};
 
 // Brackets the launches issued during its lifetime with the role's events.
+// A second stream per device, forked from and joined back to the caller's
+// stream with events; created on first use (default priority) and kept
+// until the process ends.
+constexpr int kMaxDevices = 64;
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+AuxStream g_aux[kMaxDevices];
+std::mutex g_aux_mu;
+hipError_t aux_stream(AuxStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_aux_mu);
+  AuxStream& a = g_aux[dev];
+  if (!a.s) {
+    if ((e = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &a;
+  return hipSuccess;
+}
+
 struct RoleTimer {
   int role;
   hipStream_t st;
@@ -215,6 +242,7 @@ struct MlpBwdWs {
   void* ag = nullptr;        // gate-scaled activation g*a, grouped [M, d_ff]
   float* pairs = nullptr;
   float* partial = nullptr;
+  float* partial2 = nullptr;
 };
 void layout_mlp_bwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t d_ff, int act, int dtype,
                     MlpBwdWs& w) {
@@ -228,6 +256,7 @@ void layout_mlp_bwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t
   const size_t p1 = dw_partial_bytes(M, E, d_ff, d_model, bf16);
   const size_t p2 = dw_partial_bytes(M, E, d_model, d_ff, bf16);
   w.partial = static_cast<float*>(ar.take(std::max(p1, p2)));
+  w.partial2 = static_cast<float*>(ar.take(p2));   // dW1 on the second stream
 }
 
 // Weight gradient dw[e] = sum over e's rows of A(r)^T B(r): GEMM + reduction.
@@ -704,67 +733,87 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
     SMOE_HIP(launch_reduce_dg(wl.dgpart, pl.slots, int(M), offsets, E, s_sct, dgates, st), "mlp_bwd dgates");
   }
 
-  // 2. dW2[e] = sum (g a)^T dout
+  // dW2[e] = sum (g a)^T dout
+  GemmArgs dw2a = blank_args(offsets, s_sct, E, int(M));
+  dw2a.Mo = int(d_ff);
+  dw2a.N = int(d_model);
+  dw2a.a0 = wl.ag;
+  dw2a.a_rows = M;
+  dw2a.lda = d_ff;
+  dw2a.b0 = dout;
+  dw2a.b_rows = T;
+  dw2a.ldb = d_model;
+  dw2a.b_scat = 1;
+  dw2a.b_fan = k;
+  // dW1[e] = sum x^T dh1 ; dW3[e] = sum x^T dh3
+  GemmArgs dw1a = blank_args(offsets, s_sct, E, int(M));
+  dw1a.Mo = int(d_model);
+  dw1a.N = int(d_ff);
+  dw1a.a0 = x;
+  dw1a.a_rows = T;
+  dw1a.lda = d_model;
+  dw1a.a_scat = 1;
+  dw1a.a_fan = k;
+  dw1a.b0 = wl.dh1;
+  dw1a.b_rows = M;
+  dw1a.ldb = d_ff;
+  GemmArgs dw3a = dw1a;
+  dw3a.b0 = wl.dh3;
+
+  // 2. dx contributions = dh W1^T (+ dh3 W3^T), then the k-sum.  The
+  //    product's tiles that fill whole rounds of the chip go first; once
+  //    they are done dW1 starts on a second stream, so that it fills the
+  //    CUs the last, partial round of dx tiles leaves idle, and the caller's
+  //    stream waits for it before dW2 (the two streams overlap only there:
+  //    products running side by side for longer contend for L2).
+  GemmArgs d = blank_args(offsets, s_sct, E, int(M));
+  d.N = int(d_model);
+  d.K0 = int(d_ff);
+  d.K = swiglu ? int(2 * d_ff) : int(d_ff);
+  d.a0 = wl.dh1;
+  d.a1 = swiglu ? wl.dh3 : wl.dh1;
+  d.a_rows = M;
+  d.lda = d_ff;
+  d.b0 = w1;
+  d.b1 = swiglu ? w3 : w1;
+  d.b_nk = 1;
+  d.ldb = d_ff;
+  d.b_es = d_model * d_ff;
+  d.c0 = wl.pairs;
+  d.c_scat = 1;
+  d.ldc = d_model;
+  GemmPlan pd;
+  plan_gemm(d, pd, SEG_M, EPI_STORE, 0, bf16, 1);
+  const int64_t head = whole_round_tiles(d, pd);
+  const bool overlap = head > 0 && head < pd.grid;
+  AuxStream* ax = nullptr;
+  if (overlap) SMOE_HIP(aux_stream(&ax), "mlp_bwd stream");
   {
-    GemmArgs d = blank_args(offsets, s_sct, E, int(M));
-    d.Mo = int(d_ff);
-    d.N = int(d_model);
-    d.a0 = wl.ag;
-    d.a_rows = M;
-    d.lda = d_ff;
-    d.b0 = dout;
-    d.b_rows = T;
-    d.ldb = d_model;
-    d.b_scat = 1;
-    d.b_fan = k;
-    SMOE_TRY(run_dw(d, bf16, dw2, wl.partial, st, SMOE_ROLE_DW2, "mlp_bwd dW2"));
-  }
-  // 3. dx contributions = dh W1^T (+ dh3 W3^T), then the k-sum
-  {
-    GemmArgs d = blank_args(offsets, s_sct, E, int(M));
-    d.N = int(d_model);
-    d.K0 = int(d_ff);
-    d.K = swiglu ? int(2 * d_ff) : int(d_ff);
-    d.a0 = wl.dh1;
-    d.a1 = swiglu ? wl.dh3 : wl.dh1;
-    d.a_rows = M;
-    d.lda = d_ff;
-    d.b0 = w1;
-    d.b1 = swiglu ? w3 : w1;
-    d.b_nk = 1;
-    d.ldb = d_ff;
-    d.b_es = d_model * d_ff;
-    d.c0 = wl.pairs;
-    d.c_scat = 1;
-    d.ldc = d_model;
-    GemmPlan pd;
-    plan_gemm(d, pd, SEG_M, EPI_STORE, 0, bf16, 1);
-    {
-      RoleTimer t(SMOE_ROLE_DX, st);
+    RoleTimer t(SMOE_ROLE_DX, st);
+    if (overlap) {
+      GemmPlan p1 = pd, p2 = pd;
+      p1.grid = head;
+      SMOE_HIP(launch_gemm(d, p1, st), "mlp_bwd dx");
+      SMOE_HIP(hipEventRecord(ax->fork, st), "mlp_bwd fork");
+      SMOE_HIP(hipStreamWaitEvent(ax->s, ax->fork, 0), "mlp_bwd fork");
+      SMOE_TRY(run_dw(dw1a, bf16, dw1, wl.partial2, ax->s, SMOE_ROLE_DW1, "mlp_bwd dW1"));
+      SMOE_HIP(hipEventRecord(ax->join, ax->s), "mlp_bwd join");
+      d.g_base = int(head);
+      p2.grid = (pd.grid - head + 7) / 8 * 8;
+      SMOE_HIP(launch_gemm(d, p2, st), "mlp_bwd dx");
+    } else {
       SMOE_HIP(launch_gemm(d, pd, st), "mlp_bwd dx");
     }
+  }
+  {
     RoleTimer t(SMOE_ROLE_KSUM, st);
     SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_model, dx, bf16, st), "mlp_bwd ksum");
   }
-  // 4. dW1[e] = sum x^T dh1 ; dW3[e] = sum x^T dh3
-  {
-    GemmArgs d = blank_args(offsets, s_sct, E, int(M));
-    d.Mo = int(d_model);
-    d.N = int(d_ff);
-    d.a0 = x;
-    d.a_rows = T;
-    d.lda = d_model;
-    d.a_scat = 1;
-    d.a_fan = k;
-    d.b0 = wl.dh1;
-    d.b_rows = M;
-    d.ldb = d_ff;
-    SMOE_TRY(run_dw(d, bf16, dw1, wl.partial, st, SMOE_ROLE_DW1, "mlp_bwd dW1"));
-    if (swiglu) {
-      d.b0 = wl.dh3;
-      SMOE_TRY(run_dw(d, bf16, dw3, wl.partial, st, SMOE_ROLE_DW3, "mlp_bwd dW3"));
-    }
-  }
+  if (overlap) SMOE_HIP(hipStreamWaitEvent(st, ax->join, 0), "mlp_bwd join");
+  // 3. the weight gradients
+  SMOE_TRY(run_dw(dw2a, bf16, dw2, wl.partial, st, SMOE_ROLE_DW2, "mlp_bwd dW2"));
+  if (!overlap) SMOE_TRY(run_dw(dw1a, bf16, dw1, wl.partial, st, SMOE_ROLE_DW1, "mlp_bwd dW1"));
+  if (swiglu) SMOE_TRY(run_dw(dw3a, bf16, dw3, wl.partial, st, SMOE_ROLE_DW3, "mlp_bwd dW3"));
   return ok();
 }
 

@@ -163,7 +163,7 @@ struct TileInfo {
 
 template <int BM, int BN, int MODE, bool DUAL>
 SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
-  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = (MODE == SEG_M ? p.g_base : 0) + xcd_remap(blockIdx.x, gridDim.x);
   if constexpr (MODE == SEG_M) {
     constexpr int NCOLS = DUAL ? BN / 2 : BN;
     const int ntn = (p.N + NCOLS - 1) / NCOLS;
@@ -1171,6 +1171,17 @@ static bool dispatch(const GemmArgs& a, const GemmPlan& pl, int out_f32, hipStre
     case EPI_SWIGLU_BWD: return dispatch_tiles<SEG_M, EPI_SWIGLU_BWD, LAY_K, false, uint16_t>(a, pl, st);
   }
   return false;
+}
+
+int64_t whole_round_tiles(const GemmArgs& a, const GemmPlan& pl) {
+  constexpr int kCUs = 256, kGM = 8;
+  if (!pl.bf16 || pl.mode != SEG_M) return 0;
+  // every expert's rows fill at least ceil(M / bm) m-tiles in all; tiles
+  // come in groups of kGM m-tiles by all n-tiles, so whole groups below that
+  // count are real
+  const int64_t mt_real = ceil_div(a.M, pl.bm);
+  const int64_t t = (mt_real / kGM) * kGM * pl.n_tiles;
+  return (t / kCUs) * kCUs;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, hipStream_t st) {

@@ -54,6 +54,7 @@ struct GemmArgs {
   int Mo;   // SEG_K output rows
   int KS;   // SEG_K rows per chunk
   int mt_ub;   // SEG_M: upper bound on m-tiles; SEG_K: upper bound on chunks
+  int g_base;  // SEG_M: index of this launch's first tile (a launch may cover a range)
   int b_nk;
   const void* a0;
   const void* a1;
@@ -108,6 +109,9 @@ struct GemmPlan {
 // Chooses tiles, sizes the grid and fills plan; returns false if no kernel
 // instance exists for the request.
 bool plan_gemm(GemmArgs& a, GemmPlan& plan, int mode, int epi, int dual, int bf16, int out_f32);
+// SEG_M, bf16: the number of leading tiles that are certainly real (whatever
+// the per-expert row counts) and fill whole rounds of the chip; 0 if none.
+int64_t whole_round_tiles(const GemmArgs& a, const GemmPlan& plan);
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& plan, hipStream_t st);
 
 // routing
