@@ -52,7 +52,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
 # one step launches the grouped-product kernel once per role, in this order
 # (route, then up, down, combine, dA, dgates, dW2, dX, k-sum, dW1, dW3)
-GEMM_ORDER = ["up", "down", "dA", "dW2", "dX", "dW1", "dW3"]
+# grouped-product launches of one step in enqueue order (the dX product is
+# two launches: its whole rounds of tiles, then the rest, with dW1 enqueued
+# on the second stream in between); a role's bytes are summed over its
+# launches
+GEMM_ORDER = ["up", "down", "dA", "dX", "dW1", "dX", "dW2", "dW3"]
 GEMM_KERNEL_HINT = "smoe::gemm_bf16_kernel<"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_mixtral.txt")
 COPY_KERNEL_HINT = "neg"
@@ -96,11 +100,13 @@ def pmc_summary(dir_fetch, dir_write, copy_bytes):
         scale = copy_bytes / (copy_kib * 1024.0)
         lines.append(f"{ctr}: copy kernel {copy_kib:.0f} KiB/dispatch for {copy_bytes} bytes -> "
                      f"scale {scale:.4f}; {len(gemm) // len(GEMM_ORDER)} steps")
+        per_role = {}
         for i, role in enumerate(GEMM_ORDER):
-            kib = float(np.mean(gemm[i::len(GEMM_ORDER)]))
+            per_role[role] = per_role.get(role, 0.0) + float(np.mean(gemm[i::len(GEMM_ORDER)]))
+        for role, kib in per_role.items():
             res.setdefault(role, {})[ctr] = kib * 1024.0 * scale
-            lines.append(f"  {role}: {kib:.0f} KiB/dispatch")
-    for role in GEMM_ORDER:
+            lines.append(f"  {role}: {kib:.0f} KiB per launch of the product")
+    for role in dict.fromkeys(GEMM_ORDER):
         lines.append(f"{role}_fetch_bytes_per_launch: {res[role]['FETCH_SIZE']:.6e}")
         lines.append(f"{role}_write_bytes_per_launch: {res[role]['WRITE_SIZE']:.6e}")
     lines.append(f"kernel_sources_sha256_16: {kernel_sources_hash()}")
