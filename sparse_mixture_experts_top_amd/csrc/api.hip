@@ -50,7 +50,10 @@ hipEvent_t g_role_ev[SMOE_ROLE_COUNT][2] = {};
 // Brackets the launches issued during its lifetime with the role's events.
 // A second stream per device, forked from and joined back to the caller's
 // stream with events; created on first use (default priority) and kept
-// until the process ends.
+// until the process ends.  The events are shared, so a call holds g_aux_mu
+// from its fork to its join: calls from several host threads then enqueue
+// their fork/join pairs one after another (their second-stream work runs in
+// that order).
 constexpr int kMaxDevices = 64;
 struct AuxStream {
   hipStream_t s = nullptr;
@@ -58,12 +61,12 @@ struct AuxStream {
 };
 AuxStream g_aux[kMaxDevices];
 std::mutex g_aux_mu;
+// caller holds g_aux_mu
 hipError_t aux_stream(AuxStream** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lk(g_aux_mu);
   AuxStream& a = g_aux[dev];
   if (!a.s) {
     if ((e = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking)) != hipSuccess) return e;
@@ -787,7 +790,11 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
   const int64_t head = whole_round_tiles(d, pd);
   const bool overlap = head > 0 && head < pd.grid;
   AuxStream* ax = nullptr;
-  if (overlap) SMOE_HIP(aux_stream(&ax), "mlp_bwd stream");
+  std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
+  if (overlap) {
+    aux_lock.lock();
+    SMOE_HIP(aux_stream(&ax), "mlp_bwd stream");
+  }
   {
     RoleTimer t(SMOE_ROLE_DX, st);
     if (overlap) {
@@ -809,7 +816,10 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
     RoleTimer t(SMOE_ROLE_KSUM, st);
     SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_model, dx, bf16, st), "mlp_bwd ksum");
   }
-  if (overlap) SMOE_HIP(hipStreamWaitEvent(st, ax->join, 0), "mlp_bwd join");
+  if (overlap) {
+    SMOE_HIP(hipStreamWaitEvent(st, ax->join, 0), "mlp_bwd join");
+    aux_lock.unlock();
+  }
   // 3. the weight gradients
   SMOE_TRY(run_dw(dw2a, bf16, dw2, wl.partial, st, SMOE_ROLE_DW2, "mlp_bwd dW2"));
   if (!overlap) SMOE_TRY(run_dw(dw1a, bf16, dw1, wl.partial, st, SMOE_ROLE_DW1, "mlp_bwd dW1"));

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import BF16_TOL, F32_TOL, dev_tensor, host, rel_err, say, upload
+from tests.gpu_util import BF16_TOL, F32_TOL, dev_tensor, host, rel_err, rel_err_stored_bf16, say, upload
 from workloads import make_config, make_mlp
 
 pytestmark = pytest.mark.gpu
@@ -86,3 +86,37 @@ def test_mlp_deterministic(smoe):
     assert torch.equal(o1, o2)
     for n in ("dx", "dw1", "dw2", "dw3", "dgates"):
         assert torch.equal(g1[n], g2[n]), n
+
+
+def test_mlp_backward_with_second_stream(smoe):
+    """A shape whose dX product has whole rounds of tiles and a partial last
+    round (T=4096, d_model=2048, d_ff=512, E=8, k=2, SwiGLU, bf16): dW1 then
+    runs on the library's second stream beside that last round.  Two calls
+    in a row give identical results (the fork/join events are reused), and
+    dx / dgates of sampled tokens and dW1 / dW3 / dW2 slices over every token
+    match the oracle."""
+    say("mlp backward with the second stream")
+    w = make_mlp(4096, 2048, 512, 8, 2, "swiglu", "bf16", 135, w_std=0.02)
+    o1, _, g1 = run_mlp(smoe, w)
+    o2, _, g2 = run_mlp(smoe, w)
+    assert torch.equal(o1, o2)
+    for n in ("dx", "dw1", "dw2", "dw3", "dgates"):
+        assert torch.equal(g1[n], g2[n]), n
+    f = lambda n: w.f32(n).astype(np.float64)
+    x, w1, w2, w3, dout = f("x"), f("w1"), f("w2"), f("w3"), f("dout")
+    idx, gates = w.tensors["expert_idxs"], w.tensors["gates"].astype(np.float64)
+    rng = np.random.default_rng(1351)
+    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 24, replace=False)]))
+    ref = oracle.mlp_bwd(x, w1, w2, idx, gates, "swiglu", dout, w3=w3, storage="bf16", tokens=toks)
+    for n in ("dx", "dgates"):
+        metric = rel_err if n == "dgates" else rel_err_stored_bf16
+        e = metric(host(g1[n])[toks], ref[n][toks])
+        say(f"  {n}[tokens] err {e:.2e}")
+        assert e <= BF16_TOL, n
+    cols = np.unique(np.concatenate([[0, 511], rng.choice(512, 10, replace=False)]))
+    rc = oracle.mlp_dw_cols(x, w1, w2, idx, gates, "swiglu", dout, cols, w3=w3, storage="bf16")
+    for n, got in (("dw1", host(g1["dw1"])[:, :, cols]), ("dw3", host(g1["dw3"])[:, :, cols]),
+                   ("dw2", host(g1["dw2"])[:, cols, :])):
+        e = rel_err(got, rc[n])
+        say(f"  {n}[cols] err {e:.2e}")
+        assert e <= BF16_TOL, n
