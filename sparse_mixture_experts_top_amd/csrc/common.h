@@ -89,10 +89,33 @@ template <> SMOE_DEV void ld4<uint16_t>(const uint16_t* p, float v[4]) {
 }
 
 // ---- activations (fp32) ---------------------------------------------------
-SMOE_DEV float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// Standard normal CDF Phi(z) = (1 + erf(z / sqrt 2)) / 2 and e = exp(-z^2/2)
+// (the density's exponential, shared with GELU's derivative).  erf comes
+// from Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
+// for x >= 0, 1 - erf(x) = (a1 t + ... + a5 t^5) exp(-x^2), t = 1/(1 + p x),
+// absolute error at most 1.5e-7.  With x = |z|/sqrt 2, exp(-x^2) is e, and
+// the lower tail Phi(-|z|) = (1 - erf(x)) / 2 is formed directly (no
+// cancellation against 1).
+SMOE_DEV void normal_cdf(float z, float& phi, float& e) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * x);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  e = __expf(-0.5f * z * z);
+  const float tail = 0.5f * poly * e;   // Phi(-|z|)
+  phi = z >= 0.0f ? 1.0f - tail : tail;
+}
+// GELU with the exact (erf) form, z Phi(z), and its derivative
+// Phi(z) + z phi(z), phi(z) = e / sqrt(2 pi)
+SMOE_DEV float gelu_f(float z) {
+  float phi, e;
+  normal_cdf(z, phi, e);
+  return z * phi;
+}
 SMOE_DEV float gelu_grad_f(float z) {
-  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
-         z * 0.39894228040143268f * __expf(-0.5f * z * z);
+  float phi, e;
+  normal_cdf(z, phi, e);
+  return phi + z * 0.39894228040143268f * e;
 }
 // 1 / (1 + e^-z) with the hardware reciprocal (about 1 ulp) instead of an
 // IEEE division; e^-z = +inf gives 0, e^-z = 0 gives 1
