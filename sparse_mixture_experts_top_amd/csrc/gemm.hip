@@ -1101,9 +1101,11 @@ bool plan_gemm(GemmArgs& a, GemmPlan& pl, int mode, int epi, int dual, int bf16,
     }
   }
   if (mode == SEG_K) {
-    // rows per chunk: enough chunks to give ~4 tiles per CU, at least one K
-    // step per chunk; experts with fewer rows form a single chunk.
-    const int64_t want_chunks = std::max<int64_t>(1, ceil_div(4 * kCUs, pl.n_tiles));
+    // rows per chunk: enough chunks to give ~2 tiles per CU (more chunks
+    // cost more in partials written and summed than they gain in balance),
+    // at least one K step per chunk; experts with fewer rows form a single
+    // chunk.
+    const int64_t want_chunks = std::max<int64_t>(1, ceil_div(2 * kCUs, pl.n_tiles));
     int64_t ks = ceil_div(std::max(a.M, 1), want_chunks);
     ks = std::max<int64_t>(256, ceil_div(ks, 64) * 64);
     a.KS = int(std::min<int64_t>(ks, int64_t(1) << 30));
