@@ -800,12 +800,14 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
     if (overlap) {
       GemmPlan p1 = pd, p2 = pd;
       p1.grid = head;
+      d.g_count = int(head);
       SMOE_HIP(launch_gemm(d, p1, st), "mlp_bwd dx");
       SMOE_HIP(hipEventRecord(ax->fork, st), "mlp_bwd fork");
       SMOE_HIP(hipStreamWaitEvent(ax->s, ax->fork, 0), "mlp_bwd fork");
       SMOE_TRY(run_dw(dw1a, bf16, dw1, wl.partial2, ax->s, SMOE_ROLE_DW1, "mlp_bwd dW1"));
       SMOE_HIP(hipEventRecord(ax->join, ax->s), "mlp_bwd join");
       d.g_base = int(head);
+      d.g_count = 0;
       p2.grid = (pd.grid - head + 7) / 8 * 8;
       SMOE_HIP(launch_gemm(d, p2, st), "mlp_bwd dx");
     } else {

@@ -187,6 +187,21 @@ SMOE_DEV bool find_item(const int* __restrict__ offsets, int E, int unit, int it
   return false;
 }
 
+// Items of all experts together: the sum over e of ceil(count_e / unit)
+// (wave-uniform).
+SMOE_DEV int total_items(const int* __restrict__ offsets, int E, int unit) {
+  const int l = lane_id();
+  int s = 0;
+  for (int c = 0; c < E; c += kWave) {
+    const int e = c + l;
+    if (e < E) {
+      const int cnt = offsets[e + 1] - offsets[e];
+      s += cnt > 0 ? (cnt + unit - 1) / unit : 0;
+    }
+  }
+  return __builtin_amdgcn_readfirstlane(__shfl(wave_incl_scan(s), kWave - 1, kWave));
+}
+
 // Number of items of expert e and the index of its first item (one lane).
 SMOE_DEV void expert_items(const int* __restrict__ offsets, int e, int unit, int& first_item, int& n) {
   int base = 0;

@@ -31,9 +31,10 @@
 //    holding one output row and runs of 4 consecutive columns: epilogue
 //    stores are 8 bytes (bf16) or 16 bytes (fp32) wide.
 //  - Workgroups are renumbered so that each XCD (blockIdx % 8 on MI355X)
-//    receives a contiguous range of tiles, ordered in groups of 8 m-tiles
+//    receives an equal, contiguous run of the tiles that exist (counted on
+//    the device from the expert row counts), ordered in groups of 8 m-tiles
 //    sweeping n, so concurrent tiles on one XCD share A rows and weight
-//    panels in that XCD's L2.
+//    panels in that XCD's L2 and no XCD idles on the grid's empty tail.
 //
 // fp32 kernel: the same contract with plain FMA on 64x64 tiles, used for
 // fp32 runs (a small, launch-bound regime).
@@ -66,11 +67,6 @@ static_assert(kNS >= 2, "stages");
 constexpr uint32_t kOOB = 0xFFFFFFF0u;  // byte offset past every buffer: reads as 0
 
 enum Lay { LAY_K = 0, LAY_MN = 1 };
-
-SMOE_DEV int xcd_remap(int b, int nblk) {
-  const int per = nblk >> 3;  // the host pads the grid to a multiple of 8
-  return (b & 7) * per + (b >> 3);
-}
 
 SMOE_DEV int fdiv(int x, uint32_t m, int s) { return int((uint64_t(uint32_t(x)) * m) >> s); }
 
@@ -163,14 +159,38 @@ struct TileInfo {
 
 template <int BM, int BN, int MODE, bool DUAL>
 SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
-  const int g = (MODE == SEG_M ? p.g_base : 0) + xcd_remap(blockIdx.x, gridDim.x);
+  // The grid is sized for an upper bound on the tiles; how many exist
+  // depends on the per-expert row counts and is counted here.  Blocks are
+  // dealt to the XCDs round-robin (block b runs on XCD b % 8): each XCD
+  // takes a contiguous run of this launch's real tiles, the runs as even as
+  // the count divides, and the blocks past a run have no tile.  (Runs over
+  // the upper-bound range would leave the last XCDs with the empty tail:
+  // with 8 experts and 2 split-K chunks' room, 2 of 10 chunks are empty.)
+  constexpr int kXcd = 8;
+  constexpr int GM = 8;
+  constexpr int NCOLS = DUAL ? BN / 2 : BN;
+  int n_real, units = 0;
+  const int ntn = (p.N + NCOLS - 1) / NCOLS;
+  const int ti = (p.Mo + BM - 1) / BM, tj = (p.N + BN - 1) / BN, tpc = ti * tj;
   if constexpr (MODE == SEG_M) {
-    constexpr int NCOLS = DUAL ? BN / 2 : BN;
-    const int ntn = (p.N + NCOLS - 1) / NCOLS;
-    if (g >= p.mt_ub * ntn) return false;
-    constexpr int GM = 8;
+    units = total_items(p.offsets, p.E, BM);   // real m-tiles
+    n_real = units * ntn;
+  } else {
+    n_real = total_items(p.offsets, p.E, p.KS) * tpc;
+  }
+  const int lo = MODE == SEG_M ? p.g_base : 0;
+  const int hi = (MODE == SEG_M && p.g_count > 0) ? min(n_real, lo + p.g_count) : n_real;
+  if (hi <= lo) return false;
+  const int per = (hi - lo + kXcd - 1) / kXcd;
+  const int j = int(blockIdx.x) / kXcd;
+  if (j >= per) return false;
+  const int g = lo + (int(blockIdx.x) % kXcd) * per + j;
+  if (g >= hi) return false;
+  if constexpr (MODE == SEG_M) {
+    // groups of GM m-tiles sweeping the n-tiles: concurrent tiles on an XCD
+    // share GM A panels and a few weight panels
     const int group = g / (GM * ntn);
-    const int gs = min(GM, p.mt_ub - group * GM);
+    const int gs = min(GM, units - group * GM);
     const int local = g - group * GM * ntn;
     const int mt = group * GM + local % gs;
     t.nt = local / gs;
@@ -179,14 +199,11 @@ SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
     t.chunk = 0;
     return find_item(p.offsets, p.E, BM, mt, t.it);
   } else {
-    const int ti = (p.Mo + BM - 1) / BM, tj = (p.N + BN - 1) / BN, tpc = ti * tj;
-    if (g >= p.mt_ub * tpc) return false;
     t.chunk = g / tpc;
     const int rem = g - t.chunk * tpc;
     // groups of 8 output row blocks sweeping the column blocks, as in rows
     // mode: concurrent tiles on an XCD then share 8 A panels and a few B
     // panels instead of one A panel and 32 distinct B panels
-    constexpr int GM = 8;
     const int group = rem / (GM * tj);
     const int gs = min(GM, ti - group * GM);
     const int local = rem - group * GM * tj;

@@ -55,6 +55,7 @@ struct GemmArgs {
   int KS;   // SEG_K rows per chunk
   int mt_ub;   // SEG_M: upper bound on m-tiles; SEG_K: upper bound on chunks
   int g_base;  // SEG_M: index of this launch's first tile (a launch may cover a range)
+  int g_count; // SEG_M: tiles in this launch (0: all from g_base on)
   int b_nk;
   const void* a0;
   const void* a1;
