@@ -23,8 +23,8 @@
  *  - Pointers to tensors are DEVICE pointers owned by the caller.  The
  *    library never allocates device memory, frees or synchronises; it only
  *    enqueues work on `stream` (a hipStream_t; NULL = the default stream)
- *    and returns (smoe_mlp_bwd also uses one library-owned stream, forked
- *    from and joined back to `stream`; see there).
+ *    and returns (smoe_mlp_fwd and smoe_mlp_bwd also use one library-owned
+ *    stream, forked from and joined back to `stream`; see smoe_mlp_bwd).
  *  - Tensors are row-major.  Weights are [E, d_in, d_out]: y = x W[e].
  *    Index arrays are int32; gates and gradients of gates are fp32 [T, k].
  *  - `dtype` is SMOE_F32 or SMOE_BF16 and applies to x, weights, y, dx and
@@ -200,12 +200,13 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2,
  * buffer filled by smoe_mlp_fwd with the same arguments.  In bf16 runs
  * dh (dh1, dh3) and g*a are rounded to bf16 before they enter the
  * weight-gradient and dx contractions.
- * In bf16 runs part of the work (dw1) runs on a second stream that the
- * library creates once per device (default priority, kept until the process
- * ends): it is forked from `stream` with an event after the dx product's
- * whole rounds of tiles and joined back to `stream` before dw2, so every
- * output is ordered on `stream` when the call returns, as for the other
- * entry points (and a capture of `stream` records both branches).
+ * In bf16 runs part of the work runs on a second stream that the library
+ * creates once per device (default priority, kept until the process ends):
+ * here dw1, forked from `stream` with an event after the dx product's whole
+ * rounds of tiles and joined back before dw2; in smoe_mlp_fwd both layers'
+ * routing-dependent m-tiles, joined back before the combine.  Every output
+ * is ordered on `stream` when the call returns, as for the other entry
+ * points (and a capture of `stream` records both branches).
  * ------------------------------------------------------------------------ */
 size_t smoe_mlp_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
                                     int64_t d_model, int64_t d_ff, int32_t act,

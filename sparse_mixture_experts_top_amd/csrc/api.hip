@@ -102,6 +102,8 @@ struct Arena {
   }
 };
 
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t esize(int dtype) { return dtype == SMOE_BF16 ? 2 : 4; }
 
@@ -621,10 +623,6 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
     plan_gemm(a, pl, SEG_M, EPI_SWIGLU_FWD, 1, bf16, 0);
   else
     plan_gemm(a, pl, SEG_M, EPI_GELU_FWD, 0, bf16, 0);
-  {
-    RoleTimer t(SMOE_ROLE_UP, st);
-    SMOE_HIP(launch_gemm(a, pl, st), "mlp_fwd layer 1");
-  }
 
   // layer 2: grouped a -> scattered fp32 expert outputs
   GemmArgs b = blank_args(offsets, s_sct, E, int(M));
@@ -639,10 +637,49 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
   b.c0 = wl.pairs;
   b.c_scat = 1;
   b.ldc = d_model;
-  plan_gemm(b, pl, SEG_M, EPI_STORE, 0, bf16, 1);
+  GemmPlan pb;
+  plan_gemm(b, pb, SEG_M, EPI_STORE, 0, bf16, 1);
+
+  // The m-tiles that exist whatever the routing (whole groups of 8 below
+  // ceil(M / BM)) run both layers on the caller's stream; the remaining,
+  // routing-dependent m-tiles run both layers on a second stream beside
+  // them, so the last, partly filled round of layer 2 overlaps layer 1's
+  // work instead of leaving most CUs idle.  Each layer-2 tile reads only
+  // the rows its own m-tile's layer-1 tiles wrote, on the same stream.
+  const int64_t mt_head = (ceil_div64(M, pl.bm) / 8) * 8;
+  const bool split = bf16 && pl.bm == pb.bm && mt_head > 0 && mt_head * pb.n_tiles < pb.grid;
+  AuxStream* ax = nullptr;
+  std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
+  if (split) {
+    aux_lock.lock();
+    SMOE_HIP(aux_stream(&ax), "mlp_fwd stream");
+    SMOE_HIP(hipEventRecord(ax->fork, st), "mlp_fwd fork");
+    SMOE_HIP(hipStreamWaitEvent(ax->s, ax->fork, 0), "mlp_fwd fork");
+    GemmArgs at = a, bt = b;
+    GemmPlan plt = pl, pbt = pb;
+    at.g_base = int(mt_head * pl.n_tiles);
+    bt.g_base = int(mt_head * pb.n_tiles);
+    plt.grid = (pl.grid - at.g_base + 7) / 8 * 8;
+    pbt.grid = (pb.grid - bt.g_base + 7) / 8 * 8;
+    SMOE_HIP(launch_gemm(at, plt, ax->s), "mlp_fwd layer 1");
+    SMOE_HIP(launch_gemm(bt, pbt, ax->s), "mlp_fwd layer 2");
+    SMOE_HIP(hipEventRecord(ax->join, ax->s), "mlp_fwd join");
+    a.g_count = int(mt_head * pl.n_tiles);
+    b.g_count = int(mt_head * pb.n_tiles);
+    pl.grid = a.g_count;
+    pb.grid = b.g_count;
+  }
+  {
+    RoleTimer t(SMOE_ROLE_UP, st);
+    SMOE_HIP(launch_gemm(a, pl, st), "mlp_fwd layer 1");
+  }
   {
     RoleTimer t(SMOE_ROLE_DOWN, st);
-    SMOE_HIP(launch_gemm(b, pl, st), "mlp_fwd layer 2");
+    SMOE_HIP(launch_gemm(b, pb, st), "mlp_fwd layer 2");
+  }
+  if (split) {
+    SMOE_HIP(hipStreamWaitEvent(st, ax->join, 0), "mlp_fwd join");
+    aux_lock.unlock();
   }
   RoleTimer t(SMOE_ROLE_COMBINE, st);
   SMOE_HIP(launch_combine(wl.pairs, gates, T, k, d_model, out, bf16, st), "mlp_fwd combine");
