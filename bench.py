@@ -295,12 +295,41 @@ def main():
                      "traffic": read_traffic(dom),
                      "flop_per_launch": fl[dom], "avg_launch_ms": kern_ms[dom]},
     }
+    # the matrix cores' reachable rate on this device (register-only MFMA
+    # loop, outside the timed region), the second reference for utilisation
+    loop = mfma_loop_peak()
+    res["mfma_loop_peak"] = {"tflops": loop, "util_pct_of_loop": 100.0 * tflops / loop,
+                             "probe": "bf16 32x32x16 MFMA loop on registers: 2048 workgroups x 4 waves x "
+                                      f"{MFMA_LOOP_ITERS} rounds of 16 multiplies, best of 3"}
     del t, ws_f, ws_b
     torch.cuda.empty_cache()
     if args.cpu_tokens > 0:
         log(f"CPU oracle on {args.cpu_tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+MFMA_LOOP_ITERS = 4000
+
+
+def mfma_loop_peak():
+    """TFLOP/s of smoe_probe_mfma_loop (best of three launches)."""
+    import torch
+    import sparse_mixture_experts_top_amd as smoe
+    blocks = 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    smoe.smoe_probe_mfma_loop(out, blocks, 100)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        smoe.smoe_probe_mfma_loop(out, blocks, MFMA_LOOP_ITERS)
+        b.record()
+        torch.cuda.synchronize()
+        fl = blocks * 4.0 * MFMA_LOOP_ITERS * 16 * 32768
+        best = max(best, fl / (a.elapsed_time(b) * 1e-3) / 1e12)
+    return best
 
 
 def _dev(a):

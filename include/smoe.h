@@ -249,6 +249,19 @@ enum smoe_role {
 };
 int smoe_set_role_events(int32_t role, void* start_event, void* stop_event);
 
+/* ------------------------------------------------------------------------
+ * smoe_probe_mfma_loop - diagnostic (for the caller's measurement of the
+ * device, not part of the method): enqueues on `stream` one kernel of
+ * `blocks` workgroups of 256 threads in which every wave issues `iters`
+ * rounds of 16 independent bf16 v_mfma_f32_32x32x16 on registers (no memory
+ * traffic in the loop) and writes one float per thread to out[blocks*256]
+ * (device, caller-owned).  FLOP = blocks * 4 * iters * 16 * 32768; timing it
+ * gives the matrix cores' reachable rate (and the clock the chip then
+ * holds), the reference for the products' utilisation.  blocks and iters
+ * must be positive; nothing is enqueued otherwise (SMOE_ERR_SHAPE).
+ * ------------------------------------------------------------------------ */
+int smoe_probe_mfma_loop(float* out, int32_t blocks, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

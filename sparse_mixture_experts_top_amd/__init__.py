@@ -22,6 +22,7 @@ __all__ = [
     "LIB_PATH", "SmoeError", "lib", "smoe_route", "smoe_parallel_linear_fwd",
     "smoe_parallel_linear_bwd", "smoe_mlp_fwd", "smoe_mlp_bwd", "saved_views",
     "header_functions", "F32", "BF16", "ACT_GELU", "ACT_SWIGLU", "ROLES", "smoe_set_role_events",
+    "smoe_probe_mfma_loop",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +58,7 @@ _SIGS = {
                                     _vp, _vp, _sz, _vp, _sz, _vp]),
     "smoe_mlp_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_set_role_events": (ctypes.c_int, [_i32, _vp, _vp]),
+    "smoe_probe_mfma_loop": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "smoe_mlp_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32,
                                     _i32, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -227,6 +229,14 @@ def smoe_set_role_events(role: str, start=None, stop=None):
     _check(lib.smoe_set_role_events(ROLES.index(role), ctypes.c_void_p(start.cuda_event) if start else None,
                                     ctypes.c_void_p(stop.cuda_event) if stop else None),
            "smoe_set_role_events")
+
+
+def smoe_probe_mfma_loop(out: torch.Tensor, blocks: int, iters: int):
+    """Enqueue the matrix-core rate probe on the current stream; out is a
+    float32 device tensor of blocks*256 elements.  FLOP = blocks * 4 * iters
+    * 16 * 32768."""
+    assert out.dtype == torch.float32 and out.is_cuda and out.numel() >= blocks * 256
+    _check(lib.smoe_probe_mfma_loop(_p(out), blocks, iters, _stream(out.device)), "smoe_probe_mfma_loop")
 
 
 def workspace_bytes(kind: str, **kw) -> int:

@@ -47,7 +47,6 @@ constexpr size_t kAlign = 256;
 // events attached by smoe_set_role_events
 hipEvent_t g_role_ev[SMOE_ROLE_COUNT][2] = {};
 
-// Brackets the launches issued during its lifetime with the role's events.
 // A second stream per device, forked from and joined back to the caller's
 // stream with events; created on first use (default priority) and kept
 // until the process ends.  The events are shared, so a call holds g_aux_mu
@@ -77,6 +76,7 @@ hipError_t aux_stream(AuxStream** out) {
   return hipSuccess;
 }
 
+// Brackets the launches issued during its lifetime with the role's events.
 struct RoleTimer {
   int role;
   hipStream_t st;
@@ -299,6 +299,13 @@ const char* smoe_status_string(int status) {
 const char* smoe_last_error(void) { return g_last_error.c_str(); }
 
 int smoe_abi_version(void) { return 1; }
+
+int smoe_probe_mfma_loop(float* out, int32_t blocks, int32_t iters, void* stream) {
+  SMOE_TRY(need_ptr(out, "out"));
+  if (blocks < 1 || iters < 1) return fail(SMOE_ERR_SHAPE, "blocks=%d and iters=%d must be positive", blocks, iters);
+  SMOE_HIP(launch_mfma_loop(out, blocks, iters, static_cast<hipStream_t>(stream)), "probe_mfma_loop");
+  return ok();
+}
 
 int smoe_set_role_events(int32_t role, void* start_event, void* stop_event) {
   if (role < 0 || role >= SMOE_ROLE_COUNT) return fail(SMOE_ERR_SHAPE, "role %d outside [0, %d)", role, SMOE_ROLE_COUNT);

@@ -113,6 +113,10 @@ bool plan_gemm(GemmArgs& a, GemmPlan& plan, int mode, int epi, int dual, int bf1
 // SEG_M, bf16: the number of leading tiles that are certainly real (whatever
 // the per-expert row counts) and fill whole rounds of the chip; 0 if none.
 int64_t whole_round_tiles(const GemmArgs& a, const GemmPlan& plan);
+
+// Matrix-core rate probe (probe.hip): blocks x 256 threads, each wave
+// iters rounds of 16 bf16 32x32x16 multiplies on registers.
+hipError_t launch_mfma_loop(float* out, int blocks, int iters, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& plan, hipStream_t st);
 
 // routing

@@ -115,3 +115,10 @@ def test_bf16_operands_beyond_32bit_offsets_are_rejected():
     assert g(_fake(), _fake(), NULL, _fake(), 160000, 64, 14336, 4, 2, _fake(), _fake(), smoe.ACT_GELU,
              smoe.BF16, _fake(), _fake(), 1 << 40, _fake(), 1 << 40, NULL) == 2
     assert b"hidden rows" in lib.smoe_last_error()
+
+
+def test_probe_rejects_bad_arguments():
+    f = lib.smoe_probe_mfma_loop
+    assert f(NULL, 8, 10, NULL) == 1
+    assert f(_fake(), 0, 10, NULL) == 2
+    assert f(_fake(), 8, 0, NULL) == 2
