@@ -52,11 +52,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
 # one step launches the grouped-product kernel once per role, in this order
 # (route, then up, down, combine, dA, dgates, dW2, dX, k-sum, dW1, dW3)
-# grouped-product launches of one step in enqueue order (the dX product is
-# two launches: its whole rounds of tiles, then the rest, with dW1 enqueued
-# on the second stream in between); a role's bytes are summed over its
-# launches
-GEMM_ORDER = ["up", "down", "dA", "dX", "dW1", "dX", "dW2", "dW3"]
+# grouped-product launches of one step in enqueue order: the forward
+# enqueues both layers' routing-dependent m-tiles on the second stream first,
+# then the rest of each layer; the dX product is two launches (its whole
+# rounds of tiles, then the rest, with dW1 enqueued on the second stream in
+# between).  A role's bytes are summed over its launches.
+GEMM_ORDER = ["up", "down", "up", "down", "dA", "dX", "dW1", "dX", "dW2", "dW3"]
 GEMM_KERNEL_HINT = "smoe::gemm_bf16_kernel<"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_mixtral.txt")
 COPY_KERNEL_HINT = "neg"
