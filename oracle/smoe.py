@@ -1,5 +1,6 @@
 """Plain fp64 CPU oracle: routing indices, ParallelLinear (four layouts),
-top-k combine, SMoE-MLP (GELU / SwiGLU) and their backward passes.
+top-k combine, SMoE-MLP (GELU / SwiGLU), the top-k softmax router and their
+backward passes.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow and obvious on
 purpose: loops over tokens t and their k choices j, one vector-matrix product
@@ -37,7 +38,7 @@ from scipy.special import erf, expit
 __all__ = [
     "bf16_round", "route", "grouped_position", "parallel_linear_fwd",
     "parallel_linear_bwd", "mlp_fwd", "mlp_bwd", "mlp_dw_cols",
-    "gelu", "gelu_grad", "silu", "silu_grad",
+    "gelu", "gelu_grad", "silu", "silu_grad", "router_fwd", "router_bwd",
 ]
 
 
@@ -390,3 +391,61 @@ def mlp_dw_cols(x, w1, w2, expert_idxs, gates, act: str, dout, cols,
         dw1[e] = xe.T @ dh
         dw2[e] = _store(ge * a, storage).T @ dout[tt]
     return {"dw1": dw1, "dw2": dw2, "dw3": dw3}
+
+
+# --------------------------------------------------------------------------
+# Router: gate product, top-k and softmax over the chosen logits, backward
+# --------------------------------------------------------------------------
+def router_fwd(x, g, k: int) -> Dict[str, np.ndarray]:
+    """SMoE router ([ART] para. 1: each token goes to k of E experts, its
+    output the gate-weighted sum of theirs).  Readings: logits = x G with
+    G [d_model, E] (the weight layout of every product here); token t's
+    choices are the k largest logits in descending order, ties going to the
+    lower expert id (choice j = rank j); the gates are the softmax over the k
+    chosen logits (max subtracted).
+
+    x [T, d], g [d, E] -> logits [T, E] (fp64), expert_idxs [T, k] int32,
+    gates [T, k] fp64."""
+    x = _as64(x)
+    g = _as64(g)
+    T, E = x.shape[0], g.shape[1]
+    logits = np.empty((T, E))
+    for t in range(T):
+        logits[t] = x[t] @ g
+    idx = np.empty((T, k), dtype=np.int32)
+    gates = np.empty((T, k))
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:k]
+        idx[t] = order
+        z = logits[t, order]
+        w = np.exp(z - z.max())
+        gates[t] = w / w.sum()
+    return {"logits": logits, "expert_idxs": idx, "gates": gates}
+
+
+def router_bwd(x, g, expert_idxs, gates, dgates) -> Dict[str, np.ndarray]:
+    """Backward of router_fwd for upstream dgates [T, k] (the choice is
+    piecewise constant, so only the softmax carries gradient):
+
+      dlogits[t, e_j] = g_j (dg_j - sum_i g_i dg_i),   0 for experts not chosen
+      dG = x^T dlogits        [d, E]
+      dx = dlogits G^T        [T, d]   (the router's part of the input gradient)
+    """
+    x = _as64(x)
+    g = _as64(g)
+    gates = _as64(gates)
+    dgates = _as64(dgates)
+    idx = np.asarray(expert_idxs)
+    T, k = idx.shape
+    E = g.shape[1]
+    dlogits = np.zeros((T, E))
+    for t in range(T):
+        s = sum(gates[t, i] * dgates[t, i] for i in range(k))
+        for j in range(k):
+            dlogits[t, idx[t, j]] = gates[t, j] * (dgates[t, j] - s)
+    dg = np.zeros_like(g)
+    dx = np.empty_like(x)
+    for t in range(T):
+        dg += np.outer(x[t], dlogits[t])
+        dx[t] = g @ dlogits[t]
+    return {"dlogits": dlogits, "dG": dg, "dx": dx}
