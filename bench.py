@@ -172,10 +172,11 @@ def parse():
                     help="also run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl"],
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl", "router"],
                     help="mixtral (the measured line); the others print supplementary lines: "
                          "granular = high-granularity Zipf SMoE-MLP, moa = Mixture-of-Attention "
-                         "projections, pl = single ParallelLinear in its four layouts")
+                         "projections, pl = single ParallelLinear in its four layouts, router = the "
+                         "top-k softmax router forward and backward at the three workloads' shapes")
     return ap.parse_args()
 
 
@@ -360,6 +361,8 @@ def supplementary(args):
     import sparse_mixture_experts_top_amd as smoe
     from workloads import make_config
     steps, warmup = args.steps, args.warmup
+    if args.workload == "router":
+        return router_lines(args)
     if args.workload == "granular":
         w = make_config(4)
         T, k, E = w.T, w.k, w.E
@@ -429,6 +432,50 @@ def supplementary(args):
             "tflops": tflops, "mfma_util_pct": 100.0 * tflops / PEAK_BF16_TFLOPS,
             "expert_gemm_tflop_per_step": fl / 1e12,
             "kernels_ms_last_launch": {r: evs[r][0].elapsed_time(evs[r][1]) for r in roles}}
+
+
+def _event_ms(fn, steps, warmup):
+    """Mean device time per call (ms), events on the stream the calls use."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def router_lines(args):
+    """Router forward (logits, top-k, softmax) and backward (dx written, dG)
+    at the token counts and widths of the three bf16 workloads: time per
+    call and GB/s of algorithmic bytes (x, G, routing arrays and outputs;
+    the backward's per-chunk partials are scratch and not counted)."""
+    import sparse_mixture_experts_top_amd as smoe
+    from workloads import make_router
+    steps, warmup = max(args.steps, 20), max(args.warmup, 3)
+    shapes = {"mixtral": (16384, 4096, 8, 2), "granular": (16384, 1024, 64, 8), "moa": (8192, 2048, 16, 4)}
+    out = {}
+    for name, (T, d, E, k) in shapes.items():
+        w = make_router(T, d, E, k, "bf16", 900 + E)
+        x, g, dgs = _dev(w.tensors["x"]), _dev(w.tensors["gate_w"]), _dev(w.tensors["dgates"])
+        r = smoe.smoe_router_fwd(x, g, k)
+        fwd_ms = _event_ms(lambda: smoe.smoe_router_fwd(x, g, k), steps, warmup)
+        bwd_ms = _event_ms(lambda: smoe.smoe_router_bwd(x, g, r["expert_idxs"], r["gates"], dgs), steps, warmup)
+        fwd_b = 2 * T * d + 2 * d * E + 8 * T * k
+        bwd_b = 4 * T * d + 2 * d * E + 12 * T * k + 4 * d * E
+        out[name] = {"T": T, "d_model": d, "E": E, "k": k, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+                     "bytes": fwd_b + bwd_b,
+                     "fwd_GBps": fwd_b / (fwd_ms * 1e-3) / 1e9, "bwd_GBps": bwd_b / (bwd_ms * 1e-3) / 1e9}
+    m = out["mixtral"]
+    return {"metric": "router fwd+bwd GB/s (supplementary), 1 MI355X",
+            "value": m["bytes"] / ((m["fwd_ms"] + m["bwd_ms"]) * 1e-3) / 1e9, "unit": "GB/s",
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "top-k softmax router, bf16: logits x G, top-k, softmax; backward dx, dG; "
+                                   "value at T=16384, d_model=4096, E=8, k=2"},
+            "peak_GBps": 8000.0, "shapes": out}
 
 
 if __name__ == "__main__":

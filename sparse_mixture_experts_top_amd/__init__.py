@@ -22,7 +22,7 @@ __all__ = [
     "LIB_PATH", "SmoeError", "lib", "smoe_route", "smoe_parallel_linear_fwd",
     "smoe_parallel_linear_bwd", "smoe_mlp_fwd", "smoe_mlp_bwd", "saved_views",
     "header_functions", "F32", "BF16", "ACT_GELU", "ACT_SWIGLU", "ROLES", "smoe_set_role_events",
-    "smoe_probe_mfma_loop",
+    "smoe_probe_mfma_loop", "smoe_router_fwd", "smoe_router_bwd",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,10 @@ _SIGS = {
     "smoe_mlp_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_set_role_events": (ctypes.c_int, [_i32, _vp, _vp]),
     "smoe_probe_mfma_loop": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
+    "smoe_router_fwd": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "smoe_router_bwd_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "smoe_router_bwd": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
+                                       _vp, _sz, _vp]),
     "smoe_mlp_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32,
                                     _i32, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -130,6 +134,40 @@ def smoe_route(expert_idxs: torch.Tensor, E: int) -> Dict[str, torch.Tensor]:
                           _p(out["sorted_scattered_idxs"]), _p(out["counts"]), _p(out["offsets"]),
                           _p(ws), ws.numel(), _stream(dev)), "smoe_route")
     return out
+
+
+def smoe_router_fwd(x: torch.Tensor, g: torch.Tensor, k: int, want_logits: bool = False) -> Dict[str, torch.Tensor]:
+    """Top-k softmax router: x [T, d], gate matrix g [d, E] -> expert_idxs
+    [T, k] int32, gates [T, k] fp32 (and logits [T, E] fp32)."""
+    _contig(x, g)
+    T, d = x.shape
+    E = g.shape[1]
+    dev = x.device
+    out = {"expert_idxs": torch.empty((T, k), dtype=torch.int32, device=dev),
+           "gates": torch.empty((T, k), dtype=torch.float32, device=dev)}
+    if want_logits:
+        out["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _check(lib.smoe_router_fwd(_p(x), _p(g), T, d, E, k, _dtype_code(x), _p(out["expert_idxs"]), _p(out["gates"]),
+                               _p(out.get("logits")), _stream(dev)), "smoe_router_fwd")
+    return out
+
+
+def smoe_router_bwd(x, g, expert_idxs, gates, dgates, dx=None, accumulate: bool = False):
+    """Backward of smoe_router_fwd: returns (dg [d, E] fp32, dx [T, d]); with
+    accumulate the router's dx is added to the given dx."""
+    _contig(x, g, expert_idxs, gates, dgates, dx)
+    T, d = x.shape
+    E = g.shape[1]
+    k = expert_idxs.shape[1]
+    dev = x.device
+    dg = torch.empty((d, E), dtype=torch.float32, device=dev)
+    if dx is None:
+        dx = torch.empty_like(x)
+        accumulate = False
+    ws = _ws(lib.smoe_router_bwd_workspace_bytes(T, d, E), dev)
+    _check(lib.smoe_router_bwd(_p(x), _p(g), T, d, E, k, _dtype_code(x), _p(expert_idxs), _p(gates), _p(dgates),
+                               _p(dg), _p(dx), int(accumulate), _p(ws), ws.numel(), _stream(dev)), "smoe_router_bwd")
+    return dg, dx
 
 
 def smoe_parallel_linear_fwd(x, w, T, k, sorted_scattered_idxs, offsets, x_grouped: bool,

@@ -300,6 +300,58 @@ const char* smoe_last_error(void) { return g_last_error.c_str(); }
 
 int smoe_abi_version(void) { return 1; }
 
+static int check_router(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype) {
+  if (dtype != SMOE_F32 && dtype != SMOE_BF16) return fail(SMOE_ERR_DTYPE, "dtype %d is not SMOE_F32/SMOE_BF16", dtype);
+  if (T < 0 || T > INT32_MAX / 2) return fail(SMOE_ERR_SHAPE, "T=%lld out of range", (long long)T);
+  SMOE_TRY(check_dim(d_model, "d_model"));
+  if (E < 1 || E > 64) return fail(SMOE_ERR_UNSUPPORTED, "router: E=%d outside [1, 64]", E);
+  if (k < 1 || k > E || k > 8) return fail(SMOE_ERR_UNSUPPORTED, "router: k=%d outside [1, min(E, 8)]", k);
+  return SMOE_OK;
+}
+
+int smoe_router_fwd(const void* x, const void* g, int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
+                    int32_t* expert_idxs, float* gates, float* logits, void* stream) {
+  SMOE_TRY(check_router(T, d_model, E, k, dtype));
+  SMOE_TRY(need_ptr(g, "g"));
+  if (T > 0) {
+    SMOE_TRY(need_ptr(x, "x"));
+    SMOE_TRY(need_ptr(expert_idxs, "expert_idxs"));
+    SMOE_TRY(need_ptr(gates, "gates"));
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SMOE_HIP(launch_gate_fwd(x, g, T, int(d_model), E, k, dtype == SMOE_BF16, expert_idxs, gates, logits, st),
+           "router_fwd");
+  return ok();
+}
+
+size_t smoe_router_bwd_workspace_bytes(int64_t T, int64_t d_model, int32_t E) {
+  if (T < 0 || d_model < 1 || d_model > INT32_MAX || E < 1) return 0;
+  return gate_bwd_ws_bytes(T, int(d_model), E);
+}
+
+int smoe_router_bwd(const void* x, const void* g, int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
+                    const int32_t* expert_idxs, const float* gates, const float* dgates, float* dg_out, void* dx,
+                    int32_t accumulate_dx, void* ws, size_t ws_bytes, void* stream) {
+  SMOE_TRY(check_router(T, d_model, E, k, dtype));
+  SMOE_TRY(need_ptr(g, "g"));
+  SMOE_TRY(need_ptr(dg_out, "dg_out"));
+  if (T > 0) {
+    SMOE_TRY(need_ptr(x, "x"));
+    SMOE_TRY(need_ptr(expert_idxs, "expert_idxs"));
+    SMOE_TRY(need_ptr(gates, "gates"));
+    SMOE_TRY(need_ptr(dgates, "dgates"));
+    SMOE_TRY(need_ptr(dx, "dx"));
+    SMOE_TRY(need_ptr(ws, "ws"));
+    const size_t need = smoe_router_bwd_workspace_bytes(T, d_model, E);
+    if (ws_bytes < need) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SMOE_HIP(launch_gate_bwd(x, g, T, int(d_model), E, k, dtype == SMOE_BF16, expert_idxs, gates, dgates, dg_out, dx,
+                           accumulate_dx, ws, st),
+           "router_bwd");
+  return ok();
+}
+
 int smoe_probe_mfma_loop(float* out, int32_t blocks, int32_t iters, void* stream) {
   SMOE_TRY(need_ptr(out, "out"));
   if (blocks < 1 || iters < 1) return fail(SMOE_ERR_SHAPE, "blocks=%d and iters=%d must be positive", blocks, iters);

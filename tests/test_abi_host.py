@@ -122,3 +122,34 @@ def test_probe_rejects_bad_arguments():
     assert f(NULL, 8, 10, NULL) == 1
     assert f(_fake(), 0, 10, NULL) == 2
     assert f(_fake(), 8, 0, NULL) == 2
+
+
+def test_router_rejects_bad_arguments():
+    fwd, bwd = lib.smoe_router_fwd, lib.smoe_router_bwd
+
+    def f(T=64, d=128, E=8, k=2, dtype=smoe.F32, x=_fake(), g=_fake()):
+        return fwd(x, g, T, d, E, k, dtype, _fake(), _fake(), NULL, NULL)
+
+    assert f(E=65) == 5                              # beyond one wave of experts
+    assert f(E=0) == 5
+    assert f(k=9, E=16) == 5                         # k beyond 8
+    assert f(k=5, E=4) == 5                          # k beyond E
+    assert f(k=0) == 5
+    assert f(d=12) == 2                              # not a multiple of 8
+    assert f(T=-1) == 2
+    assert f(dtype=7) == 3
+    assert f(g=NULL) == 1
+    assert f(x=NULL) == 1
+    assert f(x=_fake(4100)) == 2                     # misaligned
+    ws = lib.smoe_router_bwd_workspace_bytes(1000, 256, 8)
+    assert ws >= 1000 * 8 * 4 + 256 * 8 * 4
+    assert lib.smoe_router_bwd_workspace_bytes(0, 256, 8) > 0
+    assert lib.smoe_router_bwd_workspace_bytes(-1, 256, 8) == 0
+
+    def b(wsb=ws, E=8, dx=_fake()):
+        return bwd(_fake(), _fake(), 1000, 256, E, 2, smoe.F32, _fake(), _fake(), _fake(), _fake(), dx, 0,
+                   _fake(), wsb, NULL)
+
+    assert b(wsb=ws - 1) == 4
+    assert b(E=100) == 5
+    assert b(dx=NULL) == 1

@@ -1,0 +1,185 @@
+"""smoe_router_fwd / smoe_router_bwd on the GPU against the oracle.
+
+The GPU forms the logits in fp32 from the stored inputs; the oracle in fp64.
+Each logit's error is bounded by the fp32 summation bound
+(ceil(d/64) + 7) * 2^-24 * sum_i |x_i g_ie| (a 64-lane split of the d
+products, each lane summing its share in order, then a 6-level butterfly,
+plus one rounding per product).  A token's choice is unique where the gaps
+between its sorted oracle logits, down to the (k+1)-th, exceed twice that
+bound: there the expert ids must match exactly; elsewhere the GPU's choice
+must be a valid top-k (distinct ids whose oracle logits lie within the bound
+of the sorted ones).  The gates are checked against the softmax of the
+oracle's logits at the GPU's ids.  The backward takes the oracle's forward
+choice as input on both sides; dG is fp32 (tolerance 1e-4 of its RMS), dx is
+stored in the input dtype (bf16: beyond its final rounding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import F32_TOL, dev_tensor, host, rel_err, rel_err_stored_bf16, say
+from workloads import make_config, make_router
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+def logit_bound(x, g):
+    d = x.shape[1]
+    return (-(-d // 64) + 7) * U32 * (np.abs(x) @ np.abs(g))
+
+
+def check_fwd(smoe, x, g, k, xd, gd):
+    T, E = x.shape[0], g.shape[1]
+    r = smoe.smoe_router_fwd(xd, gd, k, want_logits=True)
+    torch.cuda.synchronize()
+    ref = oracle.router_fwd(x, g, k)
+    bound = logit_bound(x, g)
+    lg = host(r["logits"])
+    assert lg.shape == (T, E)
+    assert np.all(np.abs(lg - ref["logits"]) <= bound), float(np.max(np.abs(lg - ref["logits"]) - bound))
+    idx = r["expert_idxs"].cpu().numpy()
+    gates = host(r["gates"])
+    if T == 0:
+        return r, ref
+    # unique choices: every gap down to the (k+1)-th sorted logit is wide
+    zs = -np.sort(-ref["logits"], axis=1)
+    tb = bound.max(axis=1, keepdims=True)
+    nk = min(k + 1, E)
+    gaps = zs[:, :nk - 1] - zs[:, 1:nk]
+    unique = np.all(gaps > 2 * tb, axis=1) if nk > 1 else np.ones(T, bool)
+    say(f"  {unique.sum()}/{T} tokens with a unique choice")
+    np.testing.assert_array_equal(idx[unique], ref["expert_idxs"][unique])
+    # the rest: a valid top-k within the bound
+    assert np.all((idx >= 0) & (idx < E))
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1])
+    z_at = np.take_along_axis(ref["logits"], idx.astype(np.int64), axis=1)
+    assert np.all(np.abs(z_at - zs[:, :k]) <= 2 * tb)
+    # gates: softmax of the oracle logits at the GPU's choice
+    w = np.exp(z_at - z_at.max(axis=1, keepdims=True))
+    want = w / w.sum(axis=1, keepdims=True)
+    gerr = np.abs(gates - want).max()
+    say(f"  gates max abs err {gerr:.2e}")
+    assert gerr <= 4 * tb.max() + 1e-6
+    return r, ref
+
+
+def check_bwd(smoe, x, g, ref_fwd, dgates, xd, gd, dtype, dx_in=None, dx_in_d=None):
+    idx = ref_fwd["expert_idxs"]
+    gates32 = ref_fwd["gates"].astype(np.float32)
+    dev = xd.device
+    dg, dx = smoe.smoe_router_bwd(xd, gd, torch.from_numpy(idx).to(dev), torch.from_numpy(gates32).to(dev),
+                                  torch.from_numpy(dgates).to(dev),
+                                  dx=dx_in_d, accumulate=dx_in_d is not None)
+    torch.cuda.synchronize()
+    rb = oracle.router_bwd(x, g, idx, gates32.astype(np.float64), dgates.astype(np.float64))
+    e = rel_err(host(dg), rb["dG"])
+    say(f"  dG err {e:.2e}")
+    assert e <= F32_TOL
+    want_dx = rb["dx"] + (dx_in if dx_in is not None else 0.0)
+    got_dx = host(dx)
+    e = rel_err(got_dx, want_dx) if dtype == "f32" else rel_err_stored_bf16(got_dx, want_dx)
+    say(f"  dx err {e:.2e}")
+    assert e <= F32_TOL
+    return dg, dx
+
+
+def run_case(smoe, T, d, E, k, dtype, cid, accumulate=False):
+    say(f"router T={T} d={d} E={E} k={k} {dtype} acc={accumulate}")
+    w = make_router(T, d, E, k, dtype, cid)
+    x = w.f32("x").astype(np.float64)
+    g = w.f32("gate_w").astype(np.float64)
+    xd, gd = dev_tensor(w.tensors["x"]), dev_tensor(w.tensors["gate_w"])
+    _, ref = check_fwd(smoe, x, g, k, xd, gd)
+    dx_in = w.f32("dx_in").astype(np.float64) if accumulate else None
+    dx_in_d = dev_tensor(w.tensors["dx_in"]) if accumulate else None
+    return check_bwd(smoe, x, g, ref, w.tensors["dgates"], xd, gd, dtype, dx_in, dx_in_d)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1000, 200, 6, 3), (517, 72, 64, 8), (300, 136, 13, 1), (64, 64, 8, 8)])
+def test_router_ragged(smoe, dtype, shape):
+    T, d, E, k = shape
+    run_case(smoe, T, d, E, k, dtype, 300 + E)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_accumulate(smoe, dtype):
+    run_case(smoe, 777, 320, 16, 4, dtype, 320, accumulate=True)
+
+
+def test_router_tiny_workload_reproduces_its_routing(smoe):
+    """The tiny fp32 workload (T=256, d=128, E=8, k=2) draws its routing
+    from a gate matrix: the router on that x and G gives the same ids."""
+    w = make_config(1)
+    x = w.f32("x").astype(np.float64)
+    g = w.tensors["gate_w"].astype(np.float64)
+    r, ref = check_fwd(smoe, x, g, w.k, dev_tensor(w.tensors["x"]), dev_tensor(w.tensors["gate_w"]))
+    np.testing.assert_array_equal(ref["expert_idxs"], w.tensors["expert_idxs"])
+
+
+def test_router_single_expert(smoe):
+    """E = k = 1: every token picks expert 0 with gate 1; no gradient."""
+    say("router E=k=1")
+    w = make_router(100, 96, 1, 1, "f32", 331)
+    xd, gd = dev_tensor(w.tensors["x"]), dev_tensor(w.tensors["gate_w"])
+    r = smoe.smoe_router_fwd(xd, gd, 1)
+    assert np.all(r["expert_idxs"].cpu().numpy() == 0)
+    assert np.all(r["gates"].cpu().numpy() == 1.0)
+    dg, dx = smoe.smoe_router_bwd(xd, gd, r["expert_idxs"], r["gates"], dev_tensor(w.tensors["dgates"]))
+    assert np.all(dg.cpu().numpy() == 0.0) and np.all(dx.cpu().numpy() == 0.0)
+
+
+def test_router_no_tokens(smoe):
+    say("router T=0")
+    x = torch.empty((0, 64), device="cuda")
+    g = torch.randn((64, 8), device="cuda")
+    r = smoe.smoe_router_fwd(x, g, 2, want_logits=True)
+    assert r["expert_idxs"].shape == (0, 2) and r["logits"].shape == (0, 8)
+    dg, dx = smoe.smoe_router_bwd(x, g, r["expert_idxs"], r["gates"], torch.empty((0, 2), device="cuda"))
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 64) and np.all(dg.cpu().numpy() == 0.0)
+
+
+def test_router_ties_go_to_lower_expert(smoe):
+    """Equal logits (repeated gate columns): the lower id wins, in order."""
+    say("router ties")
+    T, d, E, k = 200, 64, 8, 4
+    w = make_router(T, d, E, k, "f32", 332)
+    gm = w.tensors["gate_w"].copy()
+    gm[:, 5] = gm[:, 2]
+    gm[:, 7] = gm[:, 2]
+    gm[:, 6] = gm[:, 1]
+    x = w.f32("x").astype(np.float64)
+    r, ref = check_fwd(smoe, x, gm.astype(np.float64), k, dev_tensor(w.tensors["x"]), dev_tensor(gm))
+    idx = r["expert_idxs"].cpu().numpy()
+    # bitwise-equal columns give bitwise-equal fp32 logits: exact tie order
+    for t in range(T):
+        pos = {e: j for j, e in enumerate(idx[t])}
+        for lo, hi in ((2, 5), (2, 7), (5, 7), (1, 6)):
+            if lo in pos and hi in pos:
+                assert pos[lo] < pos[hi], (t, idx[t])
+            assert not (hi in pos and lo not in pos), (t, idx[t])
+
+
+def test_router_deterministic(smoe):
+    say("router determinism")
+    w = make_router(3000, 1024, 16, 2, "bf16", 333)
+    xd, gd = dev_tensor(w.tensors["x"]), dev_tensor(w.tensors["gate_w"])
+    a = smoe.smoe_router_fwd(xd, gd, 2, want_logits=True)
+    b = smoe.smoe_router_fwd(xd, gd, 2, want_logits=True)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+    dgs = dev_tensor(w.tensors["dgates"])
+    dg1, dx1 = smoe.smoe_router_bwd(xd, gd, a["expert_idxs"], a["gates"], dgs)
+    dg2, dx2 = smoe.smoe_router_bwd(xd, gd, a["expert_idxs"], a["gates"], dgs)
+    assert torch.equal(dg1, dg2) and torch.equal(dx1, dx2)
+
+
+@pytest.mark.parametrize("shape", [(16384, 4096, 8, 2), (16384, 1024, 64, 8), (8192, 2048, 16, 4)])
+def test_router_full_size(smoe, shape):
+    """The routers of the Mixtral-shaped, high-granularity and MoA
+    workloads at their full token counts, bf16, in full."""
+    T, d, E, k = shape
+    run_case(smoe, T, d, E, k, "bf16", 340 + E)

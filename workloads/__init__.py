@@ -27,7 +27,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "CONFIGS", "Workload", "bf16_bits", "bf16_bits_to_f32", "make_config",
+    "CONFIGS", "Workload", "bf16_bits", "bf16_bits_to_f32", "make_config", "make_router",
     "make_mlp", "make_pl", "make_moa", "topk_softmax_routing",
     "uniform_distinct_routing", "zipf_routing",
 ]
@@ -237,6 +237,19 @@ def make_moa(T, d, hd, E, k, dtype, cid, w_std=0.02) -> Workload:
     t["dout"] = _normal((T, d), 1.0, (cid, 6), dtype)
     return Workload(f"moa{cid}", "moa", dtype, T, E, k,
                     {"d_model": d, "head_dim": hd}, None, t)
+
+
+def make_router(T, d, E, k, dtype, cid, x_std=1.0) -> Workload:
+    """Router workload: x [T,d] ~ N(0, x_std^2); gate matrix G [d,E] ~
+    N(0, 1/d) (logits of unit scale); upstream dgates [T,k] ~ N(0,1) fp32
+    and an incoming dx [T,d] ~ N(0,1) for the accumulate form."""
+    t: Dict[str, np.ndarray] = {}
+    t["x"] = _normal((T, d), x_std, (cid, 0), dtype)
+    t["gate_w"] = _normal((d, E), d ** -0.5, (cid, 1), dtype)
+    t["dgates"] = _normal((T, k), 1.0, (cid, 2), "f32")
+    t["dx_in"] = _normal((T, d), 1.0, (cid, 3), dtype)
+    return Workload(f"router{cid}", "router", dtype, T, E, k,
+                    {"d_model": d}, None, t)
 
 
 def make_config(cid: int) -> Workload:
