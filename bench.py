@@ -460,7 +460,8 @@ def router_lines(args):
     out = {}
     for name, (T, d, E, k) in shapes.items():
         w = make_router(T, d, E, k, "bf16", 900 + E)
-        x, g, dgs = _dev(w.tensors["x"]), _dev(w.tensors["gate_w"]), _dev(w.tensors["dgates"])
+        x, dgs = _dev(w.tensors["x"]), _dev(w.tensors["dgates"])
+        g = _dev(np.ascontiguousarray(w.tensors["gate_w"].T))   # gate weight [E, d]
         r = smoe.smoe_router_fwd(x, g, k)
         fwd_ms = _event_ms(lambda: smoe.smoe_router_fwd(x, g, k), steps, warmup)
         bwd_ms = _event_ms(lambda: smoe.smoe_router_bwd(x, g, r["expert_idxs"], r["gates"], dgs), steps, warmup)
@@ -473,7 +474,7 @@ def router_lines(args):
     return {"metric": "router fwd+bwd GB/s (supplementary), 1 MI355X",
             "value": m["bytes"] / ((m["fwd_ms"] + m["bwd_ms"]) * 1e-3) / 1e9, "unit": "GB/s",
             "n_gpus": 1, "steps": steps, "warmup": warmup, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "top-k softmax router, bf16: logits x G, top-k, softmax; backward dx, dG; "
+            "config": {"workload": "top-k softmax router, bf16: logits x w^T, top-k, softmax; backward dx, dw; "
                                    "value at T=16384, d_model=4096, E=8, k=2"},
             "peak_GBps": 8000.0, "shapes": out}
 

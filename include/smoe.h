@@ -245,7 +245,10 @@ enum smoe_role {
   SMOE_ROLE_PL_FWD = 12,    /* ParallelLinear forward product               */
   SMOE_ROLE_PL_DX = 13,     /* ParallelLinear dx product                    */
   SMOE_ROLE_PL_DW = 14,     /* ParallelLinear dw product                    */
-  SMOE_ROLE_COUNT = 15
+  SMOE_ROLE_ROUTER_FWD = 15, /* router logits, top-k and softmax            */
+  SMOE_ROLE_ROUTER_DX = 16, /* router dx                                    */
+  SMOE_ROLE_ROUTER_DW = 17, /* router dw product                            */
+  SMOE_ROLE_COUNT = 18
 };
 int smoe_set_role_events(int32_t role, void* start_event, void* stop_event);
 
@@ -253,35 +256,38 @@ int smoe_set_role_events(int32_t role, void* start_event, void* stop_event);
  * smoe_router_fwd - the SMoE router (article "This Machine Learning Research
  * Presents ScatterMoE", body, para. 1: each token goes to k of E experts and
  * its output is their gate-weighted sum):
- *   logits = x g                    x [T, d_model] (dtype), g [d_model, E]
+ *   logits = x w^T            x [T, d_model] (dtype), gate weight w
+ *                             [E, d_model] (dtype; a linear layer's layout)
  *   expert_idxs[t, j] = the j-th largest logit's expert (descending, ties to
  *                      the lower expert id)        int32 [T, k]
  *   gates[t, :] = softmax over the k chosen logits (max subtracted), fp32
  *   logits (fp32 [T, E]) is written if not NULL.
- * Logits accumulate in fp32; a choice between logits closer than their
- * rounding error may differ from an exact evaluation.  1 <= k <= min(E, 8),
- * E <= 64.  expert_idxs and gates are the inputs of the other entry points.
+ * Logits accumulate in fp32 (bf16: on the matrix cores from exact bf16
+ * products); a choice between logits closer than their rounding error may
+ * differ from an exact evaluation.  1 <= k <= min(E, 8), E <= 64.
+ * expert_idxs and gates are the inputs of the other entry points.
  * ------------------------------------------------------------------------ */
-int smoe_router_fwd(const void* x, const void* g, int64_t T, int64_t d_model, int32_t E, int32_t k,
+int smoe_router_fwd(const void* x, const void* w, int64_t T, int64_t d_model, int32_t E, int32_t k,
                     int32_t dtype, int32_t* expert_idxs, float* gates, float* logits, void* stream);
 
 /* ------------------------------------------------------------------------
  * smoe_router_bwd - backward of smoe_router_fwd for upstream dgates [T, k]
  * (fp32; e.g. smoe_mlp_bwd's dgates).  The choice carries no gradient; the
  * softmax gives
- *   dlogits[t, e_j] = g_j (dg_j - sum_i g_i dg_i)   (0 for unchosen experts)
- *   dg_out = x^T dlogits     fp32 [d_model, E], fully written, summed over
+ *   dlogits[t, e_j] = g_j (dg_j - sum_i g_i dg_i)   (0 for unchosen experts;
+ *                            the sum runs over all k choices)
+ *   dw_out = dlogits^T x     fp32 [E, d_model], fully written, summed over
  *                            tokens in a fixed order (deterministic)
- *   dx (+)= dlogits g^T      dtype [T, d_model]: written, or added to what
+ *   dx (+)= dlogits w        dtype [T, d_model]: written, or added to what
  *                            dx holds when accumulate_dx != 0 (to put the
  *                            router's part beside smoe_mlp_bwd's dx)
  * Choices with an expert id outside [0, E) contribute nothing.  Scratch:
  * smoe_router_bwd_workspace_bytes(...).  Limits as smoe_router_fwd.
  * ------------------------------------------------------------------------ */
 size_t smoe_router_bwd_workspace_bytes(int64_t T, int64_t d_model, int32_t E);
-int smoe_router_bwd(const void* x, const void* g, int64_t T, int64_t d_model, int32_t E, int32_t k,
+int smoe_router_bwd(const void* x, const void* w, int64_t T, int64_t d_model, int32_t E, int32_t k,
                     int32_t dtype, const int32_t* expert_idxs, const float* gates, const float* dgates,
-                    float* dg_out, void* dx, int32_t accumulate_dx, void* ws, size_t ws_bytes, void* stream);
+                    float* dw_out, void* dx, int32_t accumulate_dx, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * smoe_probe_mfma_loop - diagnostic (for the caller's measurement of the

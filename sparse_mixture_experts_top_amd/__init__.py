@@ -136,38 +136,38 @@ def smoe_route(expert_idxs: torch.Tensor, E: int) -> Dict[str, torch.Tensor]:
     return out
 
 
-def smoe_router_fwd(x: torch.Tensor, g: torch.Tensor, k: int, want_logits: bool = False) -> Dict[str, torch.Tensor]:
-    """Top-k softmax router: x [T, d], gate matrix g [d, E] -> expert_idxs
-    [T, k] int32, gates [T, k] fp32 (and logits [T, E] fp32)."""
-    _contig(x, g)
+def smoe_router_fwd(x: torch.Tensor, w: torch.Tensor, k: int, want_logits: bool = False) -> Dict[str, torch.Tensor]:
+    """Top-k softmax router: x [T, d], gate weight w [E, d] (logits = x w^T)
+    -> expert_idxs [T, k] int32, gates [T, k] fp32 (and logits [T, E] fp32)."""
+    _contig(x, w)
     T, d = x.shape
-    E = g.shape[1]
+    E = w.shape[0]
     dev = x.device
     out = {"expert_idxs": torch.empty((T, k), dtype=torch.int32, device=dev),
            "gates": torch.empty((T, k), dtype=torch.float32, device=dev)}
     if want_logits:
         out["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
-    _check(lib.smoe_router_fwd(_p(x), _p(g), T, d, E, k, _dtype_code(x), _p(out["expert_idxs"]), _p(out["gates"]),
+    _check(lib.smoe_router_fwd(_p(x), _p(w), T, d, E, k, _dtype_code(x), _p(out["expert_idxs"]), _p(out["gates"]),
                                _p(out.get("logits")), _stream(dev)), "smoe_router_fwd")
     return out
 
 
-def smoe_router_bwd(x, g, expert_idxs, gates, dgates, dx=None, accumulate: bool = False):
-    """Backward of smoe_router_fwd: returns (dg [d, E] fp32, dx [T, d]); with
+def smoe_router_bwd(x, w, expert_idxs, gates, dgates, dx=None, accumulate: bool = False):
+    """Backward of smoe_router_fwd: returns (dw [E, d] fp32, dx [T, d]); with
     accumulate the router's dx is added to the given dx."""
-    _contig(x, g, expert_idxs, gates, dgates, dx)
+    _contig(x, w, expert_idxs, gates, dgates, dx)
     T, d = x.shape
-    E = g.shape[1]
+    E = w.shape[0]
     k = expert_idxs.shape[1]
     dev = x.device
-    dg = torch.empty((d, E), dtype=torch.float32, device=dev)
+    dw = torch.empty((E, d), dtype=torch.float32, device=dev)
     if dx is None:
         dx = torch.empty_like(x)
         accumulate = False
     ws = _ws(lib.smoe_router_bwd_workspace_bytes(T, d, E), dev)
-    _check(lib.smoe_router_bwd(_p(x), _p(g), T, d, E, k, _dtype_code(x), _p(expert_idxs), _p(gates), _p(dgates),
-                               _p(dg), _p(dx), int(accumulate), _p(ws), ws.numel(), _stream(dev)), "smoe_router_bwd")
-    return dg, dx
+    _check(lib.smoe_router_bwd(_p(x), _p(w), T, d, E, k, _dtype_code(x), _p(expert_idxs), _p(gates), _p(dgates),
+                               _p(dw), _p(dx), int(accumulate), _p(ws), ws.numel(), _stream(dev)), "smoe_router_bwd")
+    return dw, dx
 
 
 def smoe_parallel_linear_fwd(x, w, T, k, sorted_scattered_idxs, offsets, x_grouped: bool,
@@ -254,7 +254,7 @@ def smoe_mlp_bwd(dout, x, w1, w2, expert_idxs, gates, act: str, saved, w3=None, 
 
 
 ROLES = ["route", "up", "down", "combine", "dA", "dW2", "dX", "ksum", "dW1", "dW3", "dw_reduce",
-         "dg_reduce", "pl_fwd", "pl_dx", "pl_dw"]
+         "dg_reduce", "pl_fwd", "pl_dx", "pl_dw", "router_fwd", "router_dx", "router_dw"]
 
 
 def smoe_set_role_events(role: str, start=None, stop=None):

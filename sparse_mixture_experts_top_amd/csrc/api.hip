@@ -279,6 +279,28 @@ int run_dw(GemmArgs a, int bf16, float* dw, float* partial, hipStream_t st, int 
   return SMOE_OK;
 }
 
+// Router backward scratch: per-choice dlogits, their dense copy D for the
+// dw product, the single-group offsets and identity row index, the
+// product's [d][ncol] result and its split-K partials.
+struct RouterBwdWs {
+  float* dlog = nullptr;
+  void* D = nullptr;
+  int* offsets = nullptr;
+  int* rows = nullptr;
+  float* tmp = nullptr;
+  float* partial = nullptr;
+};
+void layout_router_bwd(Arena& ar, int64_t T, int64_t d, int E, int bf16, RouterBwdWs& w) {
+  int ep, ncol;
+  gate_dlogit_cols(E, bf16, ep, ncol);
+  w.dlog = static_cast<float*>(ar.take(size_t(T) * 8 * 4));
+  w.D = ar.take(size_t(T) * ncol * (bf16 ? 2 : 4));
+  w.offsets = static_cast<int*>(ar.take(2 * sizeof(int)));
+  w.rows = static_cast<int*>(ar.take(size_t(T) * sizeof(int)));
+  w.tmp = static_cast<float*>(ar.take(size_t(d) * ncol * 4));
+  w.partial = static_cast<float*>(ar.take(dw_partial_bytes(T, 1, d, ncol, bf16)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,46 +331,79 @@ static int check_router(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_
   return SMOE_OK;
 }
 
-int smoe_router_fwd(const void* x, const void* g, int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
+int smoe_router_fwd(const void* x, const void* w, int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
                     int32_t* expert_idxs, float* gates, float* logits, void* stream) {
   SMOE_TRY(check_router(T, d_model, E, k, dtype));
-  SMOE_TRY(need_ptr(g, "g"));
+  SMOE_TRY(need_ptr(w, "w"));
   if (T > 0) {
     SMOE_TRY(need_ptr(x, "x"));
     SMOE_TRY(need_ptr(expert_idxs, "expert_idxs"));
     SMOE_TRY(need_ptr(gates, "gates"));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  SMOE_HIP(launch_gate_fwd(x, g, T, int(d_model), E, k, dtype == SMOE_BF16, expert_idxs, gates, logits, st),
+  RoleTimer t(SMOE_ROLE_ROUTER_FWD, st);
+  SMOE_HIP(launch_gate_fwd(x, w, T, int(d_model), E, k, dtype == SMOE_BF16, expert_idxs, gates, logits, st),
            "router_fwd");
   return ok();
 }
 
 size_t smoe_router_bwd_workspace_bytes(int64_t T, int64_t d_model, int32_t E) {
-  if (T < 0 || d_model < 1 || d_model > INT32_MAX || E < 1) return 0;
-  return gate_bwd_ws_bytes(T, int(d_model), E);
+  if (T < 0 || T > INT32_MAX / 2 || d_model < 1 || d_model > (int64_t(1) << 24) || E < 1 || E > 64) return 0;
+  Arena ar(nullptr);
+  RouterBwdWs w;
+  layout_router_bwd(ar, T, d_model, E, 1, w);
+  const size_t b = ar.used;
+  Arena af(nullptr);
+  layout_router_bwd(af, T, d_model, E, 0, w);
+  return std::max(b, af.used);
 }
 
-int smoe_router_bwd(const void* x, const void* g, int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
-                    const int32_t* expert_idxs, const float* gates, const float* dgates, float* dg_out, void* dx,
+int smoe_router_bwd(const void* x, const void* w, int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
+                    const int32_t* expert_idxs, const float* gates, const float* dgates, float* dw_out, void* dx,
                     int32_t accumulate_dx, void* ws, size_t ws_bytes, void* stream) {
   SMOE_TRY(check_router(T, d_model, E, k, dtype));
-  SMOE_TRY(need_ptr(g, "g"));
-  SMOE_TRY(need_ptr(dg_out, "dg_out"));
-  if (T > 0) {
-    SMOE_TRY(need_ptr(x, "x"));
-    SMOE_TRY(need_ptr(expert_idxs, "expert_idxs"));
-    SMOE_TRY(need_ptr(gates, "gates"));
-    SMOE_TRY(need_ptr(dgates, "dgates"));
-    SMOE_TRY(need_ptr(dx, "dx"));
-    SMOE_TRY(need_ptr(ws, "ws"));
-    const size_t need = smoe_router_bwd_workspace_bytes(T, d_model, E);
-    if (ws_bytes < need) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
-  }
+  SMOE_TRY(check_extent(dtype, T, d_model, "x"));
+  SMOE_TRY(need_ptr(w, "w"));
+  SMOE_TRY(need_ptr(dw_out, "dw_out"));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  SMOE_HIP(launch_gate_bwd(x, g, T, int(d_model), E, k, dtype == SMOE_BF16, expert_idxs, gates, dgates, dg_out, dx,
-                           accumulate_dx, ws, st),
-           "router_bwd");
+  if (T == 0) {
+    SMOE_HIP(launch_zero(dw_out, size_t(d_model) * E * 4, st), "router_bwd");
+    return ok();
+  }
+  SMOE_TRY(need_ptr(x, "x"));
+  SMOE_TRY(need_ptr(expert_idxs, "expert_idxs"));
+  SMOE_TRY(need_ptr(gates, "gates"));
+  SMOE_TRY(need_ptr(dgates, "dgates"));
+  SMOE_TRY(need_ptr(dx, "dx"));
+  SMOE_TRY(need_ptr(ws, "ws"));
+  const size_t need = smoe_router_bwd_workspace_bytes(T, d_model, E);
+  if (ws_bytes < need) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
+  const int bf16 = dtype == SMOE_BF16;
+  Arena ar(ws);
+  RouterBwdWs wl;
+  layout_router_bwd(ar, T, d_model, E, bf16, wl);
+  SMOE_HIP(launch_gate_dlogit(T, E, k, bf16, expert_idxs, gates, dgates, wl.dlog, wl.D, wl.offsets, wl.rows, st),
+           "router_bwd dlogits");
+  {
+    RoleTimer t(SMOE_ROLE_ROUTER_DX, st);
+    SMOE_HIP(launch_gate_dx(w, T, int(d_model), E, k, bf16, expert_idxs, wl.dlog, dx, accumulate_dx, st),
+             "router_bwd dx");
+  }
+  // dw^T [d][ncol] = x^T D as a weight-gradient product over one group of T
+  // rows, then dw[e][c] from its columns
+  int ep, ncol;
+  gate_dlogit_cols(E, bf16, ep, ncol);
+  GemmArgs a = blank_args(wl.offsets, wl.rows, 1, int(T));
+  a.Mo = int(d_model);
+  a.N = ncol;
+  a.a0 = x;
+  a.lda = d_model;
+  a.a_rows = T;
+  a.b0 = wl.D;
+  a.ldb = ncol;
+  a.b_rows = T;
+  SMOE_TRY(run_dw(a, bf16, wl.tmp, wl.partial, st, SMOE_ROLE_ROUTER_DW, "router_bwd dw"));
+  SMOE_HIP(launch_gate_dw_finish(wl.tmp, int(d_model), E, bf16, dw_out, st), "router_bwd dw");
   return ok();
 }
 

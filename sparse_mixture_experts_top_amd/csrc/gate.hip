@@ -1,11 +1,11 @@
-// The SMoE router on the GPU: the gate product logits = x G, each token's k
-// largest logits (descending, ties to the lower expert id) and the softmax
-// over them (article "This Machine Learning Research Presents ScatterMoE",
-// body, para. 1: a token goes to k of E experts and its output is their
-// gate-weighted sum), and the backward of that softmax: dG = x^T dlogits and
-// the router's part of dx = dlogits G^T.  E <= 64 and k <= 8; d is a
-// multiple of 8.  Every pass streams x (or dx) once from HBM; G is small and
-// stays in cache.
+// The SMoE router on the GPU: the gate product logits = x w^T (w [E][d], a
+// linear layer's weight), each token's k largest logits (descending, ties
+// to the lower expert id) and the softmax over them (article "This Machine
+// Learning Research Presents ScatterMoE", body, para. 1: a token goes to k of
+// E experts and its output is their gate-weighted sum), and the backward of
+// that softmax: dw = dlogits^T x and the router's part of dx = dlogits w.
+// E <= 64 and k <= 8; d is a multiple of 8.  Every pass streams x (or dx)
+// once from HBM; w is small and stays in cache.
 #include <algorithm>
 
 #include "common.h"
@@ -18,30 +18,13 @@ constexpr int kGateWaves = kGateThreads / kWave;
 constexpr int kGateMaxK = 8;
 
 // ---- forward -------------------------------------------------------------
-// A wave takes TT = 64 / EMAX tokens at once, so every lane holds 64 partial
-// sums (TT tokens x EMAX experts) and each G value it loads serves TT
-// tokens.  Lane l sums the products of columns 4l..4l+3, 4l+256, ... in
-// column order.
+// The gate weight is w [E][d] (a linear layer's layout: logits = x w^T), so
+// one expert's weights run along d like a token's x.
 
-// G row c into gv (zeros past E); four values per load when E % 4 == 0
-// (rows then start on 16-byte boundaries for fp32, 8-byte for bf16)
-template <class InT, int EMAX>
-SMOE_DEV void load_grow(const InT* __restrict__ gr, int E, bool g4, float (&gv)[EMAX]) {
-  if (g4) {
-    static_for<EMAX / 4>([&](auto q) {
-      constexpr int e0 = decltype(q)::value * 4;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (e0 < E) ld4<InT>(gr + e0, v);
-      gv[e0] = v[0];
-      gv[e0 + 1] = v[1];
-      gv[e0 + 2] = v[2];
-      gv[e0 + 3] = v[3];
-    });
-  } else {
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) gv[e] = e < E ? ld<InT>(gr + e) : 0.f;
-  }
-}
+// fp32 inputs, plain FMA.  A wave takes TT = 64 / EMAX tokens at once, so
+// every lane holds 64 partial sums (TT tokens x EMAX experts) and each w
+// value it loads serves TT tokens.  Lane l sums the products of columns
+// 4l..4l+3, 4l+256, ... in column order.
 
 // Wave-wide sum of 64 per-lane values that leaves lane l with the sum of
 // element l: six exchange rounds, each halving what a lane carries (lanes
@@ -62,12 +45,71 @@ SMOE_DEV float wave_transpose_sum(float (&v)[64]) {
   return v[0];
 }
 
-template <class InT, int EMAX>
-__global__ __launch_bounds__(kGateThreads) void gate_fwd_kernel(const InT* __restrict__ x, const InT* __restrict__ g,
-                                                                int64_t T, int d, int E, int k, int g4,
-                                                                int* __restrict__ idx_out,
-                                                                float* __restrict__ gates_out,
-                                                                float* __restrict__ logits_out) {
+// Top k of the logits of one token held by a group of L adjacent lanes,
+// EL logits per lane (lane p of the group holds experts p*EL .. p*EL+EL-1;
+// experts >= E are absent): k rounds of a group argmax, larger value first,
+// equal values to the lower expert id, the winner leaving the race.  Then
+// the softmax over the chosen logits (max subtracted).  Lane p of the group
+// writes choices p, p+L, ...
+template <int L, int EL>
+SMOE_DEV void group_topk_softmax(const float (&z)[EL], int p, int E, int k, bool real, int64_t t,
+                                 int* __restrict__ idx_out, float* __restrict__ gates_out) {
+  uint32_t gone = 0;
+  float zsel[kGateMaxK];
+  int esel[kGateMaxK];
+#pragma unroll
+  for (int j = 0; j < kGateMaxK; ++j) {
+    zsel[j] = 0.f;
+    esel[j] = 0;
+    if (j < k) {
+      float bv = -INFINITY;
+      int bi = 1 << 30;
+#pragma unroll
+      for (int i = 0; i < EL; ++i) {
+        const int e = p * EL + i;
+        if (e < E && !((gone >> i) & 1u) && (z[i] > bv || bi == (1 << 30))) {
+          bv = z[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < L; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      zsel[j] = bv;
+      esel[j] = bi;
+      const int own = bi - p * EL;
+      if (own >= 0 && own < EL) gone |= 1u << own;
+    }
+  }
+  float w[kGateMaxK], s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kGateMaxK; ++j) {
+    w[j] = j < k ? __expf(zsel[j] - zsel[0]) : 0.f;
+    s += w[j];
+  }
+  if (real) {
+#pragma unroll
+    for (int j = 0; j < kGateMaxK; ++j) {
+      if (j < k && j % L == p) {
+        idx_out[t * k + j] = esel[j];
+        gates_out[t * k + j] = w[j] / s;
+      }
+    }
+  }
+}
+
+template <int EMAX>
+__global__ __launch_bounds__(kGateThreads) void gate_fwd_f32_kernel(const float* __restrict__ x,
+                                                                    const float* __restrict__ wg, int64_t T, int d,
+                                                                    int E, int k, int* __restrict__ idx_out,
+                                                                    float* __restrict__ gates_out,
+                                                                    float* __restrict__ logits_out) {
   constexpr int TT = kWave / EMAX;
   const int lane = lane_id();
   const int64_t wave0 = int64_t(blockIdx.x) * kGateWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -82,73 +124,148 @@ __global__ __launch_bounds__(kGateThreads) void gate_fwd_kernel(const InT* __res
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         if (tt < nt) {
-          ld4<InT>(x + (t0 + tt) * int64_t(d) + c0, xv[tt]);
+          ld4<float>(x + (t0 + tt) * int64_t(d) + c0, xv[tt]);
         } else {
           xv[tt][0] = xv[tt][1] = xv[tt][2] = xv[tt][3] = 0.f;
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float gv[EMAX];
-        load_grow<InT, EMAX>(g + int64_t(c0 + i) * E, E, g4 != 0, gv);
+      for (int e = 0; e < EMAX; ++e) {
+        if (e < E) {
+          float gq[4];
+          ld4<float>(wg + int64_t(e) * d + c0, gq);
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+          for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-          for (int e = 0; e < EMAX; ++e) acc[tt * EMAX + e] += xv[tt][i] * gv[e];
+            for (int i = 0; i < 4; ++i) acc[tt * EMAX + e] += xv[tt][i] * gq[i];
+        }
       }
     }
     // lane l: token t0 + l / EMAX, expert l % EMAX
-    const float z = wave_transpose_sum(acc);
+    const float z[1] = {wave_transpose_sum(acc)};
     const int tt = lane / EMAX, e = lane % EMAX;
-    const int64_t t = t0 + tt;
     const bool real = tt < nt;
-    if (logits_out && real && e < E) logits_out[t * E + e] = z;
-    // k rounds of an argmax within each group of EMAX lanes: larger value
-    // first, equal values to the lower expert id; the winner leaves the race
-    float live = e < E ? z : -INFINITY;
-    float zsel = 0.f, zmax = 0.f;
-    int esel = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = live;
-      int bi = e < E ? e : kWave;
+    if (logits_out && real && e < E) logits_out[(t0 + tt) * E + e] = z[0];
+    group_topk_softmax<EMAX, 1>(z, e, E, k, real, t0 + tt, idx_out, gates_out);
+  }
+}
+
+// bf16 inputs, on the matrix cores: a block takes 32 tokens and all experts
+// (NT tiles of 32), its 4 waves splitting d (wave w takes the 16-wide k
+// steps w, w+4, ...; each wave keeps U steps of loads in flight).  The
+// v_mfma_f32_32x32x16_bf16 fragments come straight from global memory: a
+// lane loads 8 consecutive k of one token row (x) and of one expert row
+// (w).  The wave partials meet in LDS, summed in wave order; then groups of
+// 8 lanes per token pick the top k.
+typedef __bf16 gate_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float gate_f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kGateBT = 32;   // tokens per block
+constexpr int kGateU = 8;     // k steps per wave per batch of loads
+
+SMOE_DEV gate_bf16x8_t load_frag(const uint16_t* p, bool ok) {
+  uint4 v = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+  return __builtin_bit_cast(gate_bf16x8_t, v);
+}
+
+template <int NT>
+__global__ __launch_bounds__(kGateThreads) void gate_fwd_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ wg, int64_t T,
+                                                                     int d, int E, int k, int* __restrict__ idx_out,
+                                                                     float* __restrict__ gates_out,
+                                                                     float* __restrict__ logits_out) {
+  constexpr int EP = 32 * NT;
+  constexpr int PITCH = EP + 1;
+  __shared__ float red[kGateWaves][kGateBT][PITCH];
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int half = lane >> 5;
+  const int nsteps = (d + 15) / 16;
+  for (int64_t t0 = int64_t(blockIdx.x) * kGateBT; t0 < T; t0 += int64_t(gridDim.x) * kGateBT) {
+    const int64_t tok = t0 + (lane & 31);
+    const bool tok_ok = tok < T;
+    const uint16_t* xr = x + (tok_ok ? tok : 0) * int64_t(d) + 8 * half;
+    const uint16_t* wr[NT];
+    bool e_ok[NT];
 #pragma unroll
-      for (int o = EMAX / 2; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (j == 0) zmax = bv;
-      if (e == j) {
-        zsel = bv;
-        esel = bi;
-      }
-      if (e == bi) live = -INFINITY;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = nt * 32 + (lane & 31);
+      e_ok[nt] = e < E;
+      wr[nt] = wg + int64_t(e_ok[nt] ? e : 0) * d + 8 * half;
     }
-    // softmax over the chosen logits (group lanes 0..k-1), max subtracted
-    const float w = e < k ? __expf(zsel - zmax) : 0.f;
-    float s = w;
+    gate_f32x16_t acc[NT];
 #pragma unroll
-    for (int o = EMAX / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
-    if (real && e < k) {
-      idx_out[t * k + e] = esel;
-      gates_out[t * k + e] = w / s;
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
+    for (int s0 = w; s0 < nsteps; s0 += kGateWaves * kGateU) {
+      gate_bf16x8_t a[kGateU], b[kGateU][NT];
+#pragma unroll
+      for (int u = 0; u < kGateU; ++u) {
+        const int kk = 16 * (s0 + kGateWaves * u);
+        const bool k_ok = kk + 8 * half < d;
+        a[u] = load_frag(xr + kk, k_ok && tok_ok);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) b[u][nt] = load_frag(wr[nt] + kk, k_ok && e_ok[nt]);
+      }
+#pragma unroll
+      for (int u = 0; u < kGateU; ++u)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[u][nt], a[u], acc[nt], 0, 0, 0);
     }
+    // lane holds token (lane & 31), experts 32 nt + 8q + 4 half + i in
+    // acc[nt][4q + i]
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[w][lane & 31][32 * nt + 8 * q + 4 * half + i] = acc[nt][4 * q + i];
+    __syncthreads();
+    // 8 lanes per token: lane p of the group sums experts p*EL .. +EL-1
+    constexpr int EL = EP / 8;
+    const int tl = threadIdx.x / 8, p = threadIdx.x % 8;
+    float z[EL];
+#pragma unroll
+    for (int i = 0; i < EL; ++i) {
+      const int e = p * EL + i;
+      z[i] = ((red[0][tl][e] + red[1][tl][e]) + red[2][tl][e]) + red[3][tl][e];
+    }
+    const int64_t t = t0 + tl;
+    const bool real = t < T;
+    if (logits_out && real) {
+#pragma unroll
+      for (int i = 0; i < EL; ++i)
+        if (p * EL + i < E) logits_out[t * E + p * EL + i] = z[i];
+    }
+    group_topk_softmax<8, EL>(z, p, E, k, real, t, idx_out, gates_out);
+    __syncthreads();
   }
 }
 
 // ---- backward ------------------------------------------------------------
-// dlog[t][j] = g_j (dg_j - sum_i g_i dg_i) for choice j of token t (the sum
-// over all k choices), 0 where the expert id is outside [0, E); one thread
-// per token.
-__global__ __launch_bounds__(kGateThreads) void gate_dlogit_kernel(int64_t T, int E, int k,
-                                                                   const int* __restrict__ idx,
+// Per choice j of token t: dlog[t][j] = g_j (dg_j - sum_i g_i dg_i) (the sum
+// over all k choices), 0 where the expert id is outside [0, E).  The same
+// values also go into a dense row-major D [T][ncol] for the dw product:
+// bf16 inputs: D[t][e] = hi, D[t][ep + e] = lo with hi = bf16(v) and
+// lo = bf16(v - hi), so that the bf16 matrix-core product of x with both
+// halves carries v to about 16 significant bits; fp32 inputs: D[t][e] = v.
+// Unchosen entries are 0.  One thread per token; it also writes the
+// product's row index rows[t] = t (the rows are read in place), and thread 0
+// the single-group row offsets {0, T}.
+__global__ __launch_bounds__(kGateThreads) void gate_dlogit_kernel(int64_t T, int E, int k, int ep, int ncol,
+                                                                   int bf16, const int* __restrict__ idx,
                                                                    const float* __restrict__ gates,
                                                                    const float* __restrict__ dgates,
-                                                                   float* __restrict__ dlog) {
-  for (int64_t t = int64_t(blockIdx.x) * kGateThreads + threadIdx.x; t < T; t += int64_t(gridDim.x) * kGateThreads) {
+                                                                   float* __restrict__ dlog, void* __restrict__ D,
+                                                                   int* __restrict__ offsets, int* __restrict__ rows) {
+  const int64_t i0 = int64_t(blockIdx.x) * kGateThreads + threadIdx.x;
+  if (i0 == 0) {
+    offsets[0] = 0;
+    offsets[1] = int(T);
+  }
+  for (int64_t t = i0; t < T; t += int64_t(gridDim.x) * kGateThreads) {
+    rows[t] = int(t);
     float gv[kGateMaxK], dv[kGateMaxK];
     float s = 0.f;
 #pragma unroll
@@ -157,56 +274,84 @@ __global__ __launch_bounds__(kGateThreads) void gate_dlogit_kernel(int64_t T, in
       dv[j] = j < k ? dgates[t * k + j] : 0.f;
       s += gv[j] * dv[j];
     }
+    // clear the row, then place the chosen entries (the same thread writes
+    // both, in order)
+    if (bf16) {
+      uint16_t* row = static_cast<uint16_t*>(D) + t * ncol;
+      for (int c = 0; c < ncol; c += 8) *reinterpret_cast<uint4*>(row + c) = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      float* row = static_cast<float*>(D) + t * ncol;
+      for (int c = 0; c < ncol; c += 4) *reinterpret_cast<float4*>(row + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
     for (int j = 0; j < kGateMaxK; ++j) {
       if (j < k) {
         const int e = idx[t * k + j];
-        dlog[t * k + j] = (e >= 0 && e < E) ? gv[j] * (dv[j] - s) : 0.f;
+        const bool ok = e >= 0 && e < E;
+        const float v = ok ? gv[j] * (dv[j] - s) : 0.f;
+        dlog[t * k + j] = v;
+        if (ok) {
+          if (bf16) {
+            uint16_t* row = static_cast<uint16_t*>(D) + t * ncol;
+            const uint16_t hi = f2bf(v);
+            row[e] = hi;
+            row[ep + e] = f2bf(v - bf2f(hi));
+          } else {
+            static_cast<float*>(D)[t * ncol + e] = v;
+          }
+        }
       }
     }
   }
 }
 
-// Router dx: dx[t][c] (+)= sum_j dlog[t][j] G[c][e_j].  Block (column tile
-// of 256, token chunk): the tile's G rows sit transposed in LDS,
-// Gt[e][c - c0], so a token's k reads are whole LDS rows; lane l of each
-// wave owns columns c0+4l..c0+4l+3, the four waves split the tokens.
+// Router dx: dx[t][c] (+)= sum_j dlog[t][j] w[e_j][c].  Block (column tile
+// of 256, token chunk of 128): the tile's slice of every expert row,
+// w[e][c0 .. c0+255], sits in LDS as fp32, and so do the chunk's expert ids
+// and dlogits; lane l of each wave owns columns c0+4l..c0+4l+3, the four
+// waves take every fourth token.
 constexpr int kDxCols = 4 * kWave;
 constexpr int kDxTokChunk = 128;
-template <class InT>
-__global__ __launch_bounds__(kGateThreads) void gate_dx_kernel(const InT* __restrict__ g, int64_t T, int d, int E,
+template <class InT, int EMAX>
+__global__ __launch_bounds__(kGateThreads) void gate_dx_kernel(const InT* __restrict__ wg, int64_t T, int d, int E,
                                                                int k, const int* __restrict__ idx,
                                                                const float* __restrict__ dlog, InT* __restrict__ dx,
                                                                int accumulate) {
-  extern __shared__ float gt[];   // [E][kDxCols]
+  __shared__ __attribute__((aligned(16))) float ws_tile[EMAX * kDxCols];
+  __shared__ int ch_e[kDxTokChunk * kGateMaxK];
+  __shared__ float ch_v[kDxTokChunk * kGateMaxK];
   const int c0 = blockIdx.x * kDxCols;
   const int ncol = min(kDxCols, d - c0);   // a multiple of 8
-  for (int i = threadIdx.x; i < ncol * E; i += kGateThreads) {
-    const int c = i / E, e = i - c * E;
-    gt[e * kDxCols + c] = ld<InT>(g + int64_t(c0) * E + i);
+  for (int i = threadIdx.x; i < E * kDxCols; i += kGateThreads) {
+    const int e = i / kDxCols, c = i - e * kDxCols;
+    ws_tile[i] = c < ncol ? ld<InT>(wg + int64_t(e) * d + c0 + c) : 0.f;
+  }
+  const int64_t t0 = int64_t(blockIdx.y) * kDxTokChunk;
+  const int nt = int(T - t0 < kDxTokChunk ? T - t0 : kDxTokChunk);
+  for (int i = threadIdx.x; i < nt * k; i += kGateThreads) {
+    const int e = idx[t0 * k + i];
+    const bool ok = e >= 0 && e < E;
+    ch_e[i] = ok ? e : 0;
+    ch_v[i] = ok ? dlog[t0 * k + i] : 0.f;
   }
   __syncthreads();
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t t0 = int64_t(blockIdx.y) * kDxTokChunk;
-  const int64_t t1 = t0 + kDxTokChunk < T ? t0 + kDxTokChunk : T;
   const int cl = 4 * lane;
   const bool mine = cl < ncol;
-  for (int64_t t = t0 + w; t < t1; t += kGateWaves) {
+  for (int tl = w; tl < nt; tl += kGateWaves) {
     float r[4] = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
-      const float dl = dlog[t * k + j];
-      if (e >= 0 && e < E) {
-        const float4 gv = *reinterpret_cast<const float4*>(gt + e * kDxCols + cl);
-        r[0] += dl * gv.x;
-        r[1] += dl * gv.y;
-        r[2] += dl * gv.z;
-        r[3] += dl * gv.w;
-      }
+      const int e = ch_e[tl * k + j];
+      const float dl = ch_v[tl * k + j];
+      const float4 gv = *reinterpret_cast<const float4*>(ws_tile + e * kDxCols + cl);
+      r[0] += dl * gv.x;
+      r[1] += dl * gv.y;
+      r[2] += dl * gv.z;
+      r[3] += dl * gv.w;
     }
     if (mine) {
-      InT* p = dx + t * int64_t(d) + c0 + cl;
+      InT* p = dx + (t0 + tl) * int64_t(d) + c0 + cl;
       if (accumulate) {
         float v[4];
         ld4<InT>(p, v);
@@ -220,156 +365,105 @@ __global__ __launch_bounds__(kGateThreads) void gate_dx_kernel(const InT* __rest
   }
 }
 
-// dG partials: block (column tile of 256, token chunk q) sums x[t][c] dlog
-// into LDS acc[e][c - c0] (a thread per column; each address has one owner,
-// so the adds land in token order), then writes its contiguous slice
-// part[q][c0 .. c0+255][0 .. E).
-constexpr int kDgCols = kGateThreads;
-constexpr int kDgPitch = kDgCols + 1;
-template <class InT>
-__global__ __launch_bounds__(kGateThreads) void gate_dg_partial_kernel(const InT* __restrict__ x, int64_t T, int d,
-                                                                       int E, int k, const int* __restrict__ idx,
-                                                                       const float* __restrict__ dlog, int64_t chunk,
-                                                                       float* __restrict__ part) {
-  extern __shared__ float acc[];   // [E][kDgPitch]
-  const int c0 = blockIdx.x * kDgCols;
-  const int ncol = min(kDgCols, d - c0);
-  const int tid = threadIdx.x;
-  for (int i = tid; i < E * kDgPitch; i += kGateThreads) acc[i] = 0.f;
-  __syncthreads();
-  const int64_t t0 = int64_t(blockIdx.y) * chunk;
-  const int64_t t1 = t0 + chunk < T ? t0 + chunk : T;
-  const bool mine = tid < ncol;
-  const InT* xc = x + c0 + (mine ? tid : 0);
-  float* my = acc + tid;
-  constexpr int U = 8;   // tokens whose x loads are in flight together
-  int64_t t = t0;
-  for (; t + U <= t1; t += U) {
-    float xv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) xv[u] = ld<InT>(xc + (t + u) * int64_t(d));
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      for (int j = 0; j < k; ++j) {
-        const int e = idx[(t + u) * k + j];
-        if (e >= 0 && e < E) my[e * kDgPitch] += xv[u] * dlog[(t + u) * k + j];
-      }
-    }
-  }
-  for (; t < t1; ++t) {
-    const float xv = ld<InT>(xc + t * int64_t(d));
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
-      if (e >= 0 && e < E) my[e * kDgPitch] += xv * dlog[t * k + j];
-    }
-  }
-  __syncthreads();
-  float* out = part + (int64_t(blockIdx.y) * d + c0) * E;
-  for (int i = tid; i < ncol * E; i += kGateThreads) {
-    const int c = i / E, e = i - c * E;
-    out[i] = acc[e * kDgPitch + c];
-  }
-}
-
-// dG[i] = sum over chunks q of part[q][i], in chunk order
-__global__ __launch_bounds__(kGateThreads) void gate_dg_reduce_kernel(const float* __restrict__ part, int chunks,
-                                                                      int64_t n, float* __restrict__ dg) {
+// dw[e][c] from the product's tmp [d][ncol]: tmp[c][e] (+ tmp[c][ep + e]
+// for the bf16 halves)
+__global__ __launch_bounds__(kGateThreads) void gate_dw_finish_kernel(const float* __restrict__ tmp, int d, int E,
+                                                                      int ep, int ncol, int two,
+                                                                      float* __restrict__ dw) {
+  const int64_t n = int64_t(E) * d;
   for (int64_t i = int64_t(blockIdx.x) * kGateThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kGateThreads) {
-    float s = 0.f;
-    for (int q = 0; q < chunks; ++q) s += part[int64_t(q) * n + i];
-    dg[i] = s;
+    const int e = int(i / d);
+    const int64_t c = i - int64_t(e) * d;
+    const float* r = tmp + c * ncol;
+    dw[i] = two ? r[e] + r[ep + e] : r[e];
   }
-}
-
-// Token chunking of the dG partials: enough blocks to fill the chip (about
-// 512), but at most T / (4 E) chunks, so that the partials (chunks * d * E
-// floats) stay well under the size of x.
-static void dg_chunking(int64_t T, int d, int E, int& chunks, int64_t& chunk) {
-  const int64_t colblocks = (d + kDgCols - 1) / kDgCols;
-  int64_t c = (512 + colblocks - 1) / colblocks;
-  c = std::max<int64_t>(std::min<int64_t>(c, T / (4 * int64_t(E))), 1);
-  chunk = std::max<int64_t>((T + c - 1) / c, 1);
-  chunks = int(std::max<int64_t>((T + chunk - 1) / chunk, 1));
-}
-
-static size_t dlog_bytes(int64_t T) { return (size_t(T) * kGateMaxK * 4 + 255) & ~size_t(255); }
-
-// scratch: dlog [T][8] floats, then the partials
-size_t gate_bwd_ws_bytes(int64_t T, int d, int E) {
-  int chunks;
-  int64_t chunk;
-  dg_chunking(T, d, E, chunks, chunk);
-  return dlog_bytes(T) + size_t(chunks) * size_t(d) * size_t(E) * 4;
 }
 
 static unsigned grid_cap(int64_t blocks, int64_t cap) {
   return unsigned(std::min<int64_t>(std::max<int64_t>(blocks, 1), cap));
 }
 
-template <class InT>
-static void go_gate_fwd(const void* x, const void* g, int64_t T, int d, int E, int k, int* idx, float* gates,
-                        float* logits, hipStream_t st) {
-  const InT* xp = static_cast<const InT*>(x);
-  const InT* gp = static_cast<const InT*>(g);
-  const int g4 = E % 4 == 0;
-  const dim3 block(kGateThreads);
-  auto grid = [&](int emax) {
-    const int64_t groups = (T + kWave / emax - 1) / (kWave / emax);
-    return dim3(grid_cap((groups + kGateWaves - 1) / kGateWaves, 8192));
-  };
-  if (E <= 8)
-    hipLaunchKernelGGL((gate_fwd_kernel<InT, 8>), grid(8), block, 0, st, xp, gp, T, d, E, k, g4, idx, gates, logits);
-  else if (E <= 16)
-    hipLaunchKernelGGL((gate_fwd_kernel<InT, 16>), grid(16), block, 0, st, xp, gp, T, d, E, k, g4, idx, gates,
-                       logits);
-  else if (E <= 32)
-    hipLaunchKernelGGL((gate_fwd_kernel<InT, 32>), grid(32), block, 0, st, xp, gp, T, d, E, k, g4, idx, gates,
-                       logits);
-  else
-    hipLaunchKernelGGL((gate_fwd_kernel<InT, 64>), grid(64), block, 0, st, xp, gp, T, d, E, k, g4, idx, gates,
-                       logits);
-}
-
-hipError_t launch_gate_fwd(const void* x, const void* g, int64_t T, int d, int E, int k, int bf16, int* idx,
+hipError_t launch_gate_fwd(const void* x, const void* wg, int64_t T, int d, int E, int k, int bf16, int* idx,
                            float* gates, float* logits, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (bf16) go_gate_fwd<uint16_t>(x, g, T, d, E, k, idx, gates, logits, st);
-  else go_gate_fwd<float>(x, g, T, d, E, k, idx, gates, logits, st);
+  const dim3 block(kGateThreads);
+  if (bf16) {
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    const uint16_t* wp = static_cast<const uint16_t*>(wg);
+    const dim3 grid(grid_cap((T + kGateBT - 1) / kGateBT, 1 << 20));
+    if (E <= 32)
+      hipLaunchKernelGGL((gate_fwd_mfma_kernel<1>), grid, block, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
+    else
+      hipLaunchKernelGGL((gate_fwd_mfma_kernel<2>), grid, block, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
+  } else {
+    const float* xp = static_cast<const float*>(x);
+    const float* wp = static_cast<const float*>(wg);
+    auto grid = [&](int emax) {
+      const int64_t groups = (T + kWave / emax - 1) / (kWave / emax);
+      return dim3(grid_cap((groups + kGateWaves - 1) / kGateWaves, 8192));
+    };
+    if (E <= 8)
+      hipLaunchKernelGGL((gate_fwd_f32_kernel<8>), grid(8), block, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
+    else if (E <= 16)
+      hipLaunchKernelGGL((gate_fwd_f32_kernel<16>), grid(16), block, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
+    else if (E <= 32)
+      hipLaunchKernelGGL((gate_fwd_f32_kernel<32>), grid(32), block, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
+    else
+      hipLaunchKernelGGL((gate_fwd_f32_kernel<64>), grid(64), block, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
+  }
+  return hipGetLastError();
+}
+
+// Columns of the dense dlogits D: ep = E rounded up to 8; bf16 keeps the
+// two halves side by side.
+void gate_dlogit_cols(int E, int bf16, int& ep, int& ncol) {
+  ep = (E + 7) / 8 * 8;
+  ncol = bf16 ? 2 * ep : ep;
+}
+
+hipError_t launch_gate_dlogit(int64_t T, int E, int k, int bf16, const int* idx, const float* gates,
+                              const float* dgates, float* dlog, void* D, int* offsets, int* rows, hipStream_t st) {
+  int ep, ncol;
+  gate_dlogit_cols(E, bf16, ep, ncol);
+  hipLaunchKernelGGL(gate_dlogit_kernel, dim3(grid_cap((T + kGateThreads - 1) / kGateThreads, 4096)),
+                     dim3(kGateThreads), 0, st, T, E, k, ep, ncol, bf16, idx, gates, dgates, dlog, D, offsets, rows);
   return hipGetLastError();
 }
 
 template <class InT>
-static void go_gate_bwd(const void* x, const void* g, int64_t T, int d, int E, int k, const int* idx,
-                        const float* gates, const float* dgates, float* dg, void* dx, int accumulate, void* ws,
-                        hipStream_t st) {
-  const InT* xp = static_cast<const InT*>(x);
-  const InT* gp = static_cast<const InT*>(g);
-  float* dlog = static_cast<float*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + dlog_bytes(T));
-  hipLaunchKernelGGL(gate_dlogit_kernel, dim3(grid_cap((T + kGateThreads - 1) / kGateThreads, 4096)),
-                     dim3(kGateThreads), 0, st, T, E, k, idx, gates, dgates, dlog);
-  const dim3 dxgrid(unsigned((d + kDxCols - 1) / kDxCols), unsigned((T + kDxTokChunk - 1) / kDxTokChunk));
-  hipLaunchKernelGGL((gate_dx_kernel<InT>), dxgrid, dim3(kGateThreads), size_t(E) * kDxCols * 4, st, gp, T, d, E, k,
-                     idx, dlog, static_cast<InT*>(dx), accumulate);
-  int chunks;
-  int64_t chunk;
-  dg_chunking(T, d, E, chunks, chunk);
-  const dim3 pgrid(unsigned((d + kDgCols - 1) / kDgCols), unsigned(chunks));
-  hipLaunchKernelGGL((gate_dg_partial_kernel<InT>), pgrid, dim3(kGateThreads), size_t(E) * kDgPitch * 4, st, xp, T,
-                     d, E, k, idx, dlog, chunk, part);
-  const int64_t n = int64_t(d) * E;
-  hipLaunchKernelGGL(gate_dg_reduce_kernel, dim3(grid_cap((n + kGateThreads - 1) / kGateThreads, 4096)),
-                     dim3(kGateThreads), 0, st, part, chunks, n, dg);
+static void go_gate_dx(const void* wg, int64_t T, int d, int E, int k, const int* idx, const float* dlog, void* dx,
+                       int accumulate, hipStream_t st) {
+  const dim3 grid(unsigned((d + kDxCols - 1) / kDxCols), unsigned((T + kDxTokChunk - 1) / kDxTokChunk));
+  const InT* wp = static_cast<const InT*>(wg);
+  InT* dp = static_cast<InT*>(dx);
+  if (E <= 8)
+    hipLaunchKernelGGL((gate_dx_kernel<InT, 8>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, dlog, dp,
+                       accumulate);
+  else if (E <= 16)
+    hipLaunchKernelGGL((gate_dx_kernel<InT, 16>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, dlog, dp,
+                       accumulate);
+  else if (E <= 32)
+    hipLaunchKernelGGL((gate_dx_kernel<InT, 32>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, dlog, dp,
+                       accumulate);
+  else
+    hipLaunchKernelGGL((gate_dx_kernel<InT, 64>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, dlog, dp,
+                       accumulate);
 }
 
-hipError_t launch_gate_bwd(const void* x, const void* g, int64_t T, int d, int E, int k, int bf16, const int* idx,
-                           const float* gates, const float* dgates, float* dg, void* dx, int accumulate, void* ws,
-                           hipStream_t st) {
-  if (T == 0) return launch_zero(dg, size_t(d) * E * 4, st);
-  if (bf16)
-    go_gate_bwd<uint16_t>(x, g, T, d, E, k, idx, gates, dgates, dg, dx, accumulate, ws, st);
-  else
-    go_gate_bwd<float>(x, g, T, d, E, k, idx, gates, dgates, dg, dx, accumulate, ws, st);
+hipError_t launch_gate_dx(const void* wg, int64_t T, int d, int E, int k, int bf16, const int* idx, const float* dlog,
+                          void* dx, int accumulate, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (bf16) go_gate_dx<uint16_t>(wg, T, d, E, k, idx, dlog, dx, accumulate, st);
+  else go_gate_dx<float>(wg, T, d, E, k, idx, dlog, dx, accumulate, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_dw_finish(const float* tmp, int d, int E, int bf16, float* dw, hipStream_t st) {
+  int ep, ncol;
+  gate_dlogit_cols(E, bf16, ep, ncol);
+  const int64_t n = int64_t(E) * d;
+  hipLaunchKernelGGL(gate_dw_finish_kernel, dim3(grid_cap((n + kGateThreads - 1) / kGateThreads, 4096)),
+                     dim3(kGateThreads), 0, st, tmp, d, E, ep, ncol, bf16, dw);
   return hipGetLastError();
 }
 

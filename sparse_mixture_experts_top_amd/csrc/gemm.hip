@@ -1206,6 +1206,9 @@ int64_t whole_round_tiles(const GemmArgs& a, const GemmPlan& pl) {
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, hipStream_t st) {
   if (pl.grid <= 0) return hipSuccess;
   if (pl.grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  // the bf16 weight-gradient kernel copies row indices for both operands,
+  // gathered or not: it needs a readable index array of M entries
+  if (pl.mode == SEG_K && pl.bf16 && a.sidx == nullptr) return hipErrorInvalidValue;
   if (!dispatch(a, pl, pl.mode == SEG_K ? 1 : pl.out_f32, st)) return hipErrorInvalidConfiguration;
   return hipGetLastError();
 }

@@ -1,33 +1,41 @@
 """smoe_router_fwd / smoe_router_bwd on the GPU against the oracle.
 
-The GPU forms the logits in fp32 from the stored inputs; the oracle in fp64.
-Each logit's error is bounded by the fp32 summation bound
-(ceil(d/64) + 7) * 2^-24 * sum_i |x_i g_ie| (a 64-lane split of the d
-products, each lane summing its share in order, then a 6-level butterfly,
-plus one rounding per product).  A token's choice is unique where the gaps
-between its sorted oracle logits, down to the (k+1)-th, exceed twice that
-bound: there the expert ids must match exactly; elsewhere the GPU's choice
-must be a valid top-k (distinct ids whose oracle logits lie within the bound
-of the sorted ones).  The gates are checked against the softmax of the
-oracle's logits at the GPU's ids.  The backward takes the oracle's forward
-choice as input on both sides; dG is fp32 (tolerance 1e-4 of its RMS), dx is
-stored in the input dtype (bf16: beyond its final rounding)."""
+The oracle reads the gate matrix as G [d, E] (logits = x G); the library
+takes it as w = G^T [E, d] and returns dw = dG^T.  The GPU forms the logits
+in fp32 from the stored inputs, the oracle in fp64.  Each logit's error is
+bounded by (ceil(d/64) + 24) * 2^-24 * sum_i |x_i g_ie|: the products are
+exact (bf16 x bf16, or fp32 rounded once), each lane or matrix-core
+accumulator adds at most ceil(d/64) partial sums in sequence, a matrix-core
+step sums 16 products before adding them, and the final cross-lane or
+cross-wave sums add at most 6 more.  A token's choice is unique where the
+gaps between its sorted oracle logits, down to the (k+1)-th, exceed twice
+that bound: there the expert ids must match exactly; elsewhere the GPU's
+choice must be a valid top-k (distinct ids whose oracle logits lie within
+the bound of the sorted ones).  The gates are checked against the softmax of
+the oracle's logits at the GPU's ids.  The backward takes the oracle's
+forward choice as input on both sides; dw is fp32 (tolerance 1e-4 of its
+RMS), dx is stored in the input dtype (bf16: beyond its final rounding)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from tests.gpu_util import F32_TOL, dev_tensor, host, rel_err, rel_err_stored_bf16, say
-from workloads import make_config, make_router
+from workloads import bf16_bits_to_f32, make_config, make_router
 
 pytestmark = pytest.mark.gpu
 
 U32 = 2.0 ** -24
 
 
+def wt_tensor(g: np.ndarray) -> torch.Tensor:
+    """The oracle's G [d, E] as the library's gate weight w = G^T [E, d]."""
+    return dev_tensor(np.ascontiguousarray(g.T))
+
+
 def logit_bound(x, g):
     d = x.shape[1]
-    return (-(-d // 64) + 7) * U32 * (np.abs(x) @ np.abs(g))
+    return (-(-d // 64) + 24) * U32 * (np.abs(x) @ np.abs(g))
 
 
 def check_fwd(smoe, x, g, k, xd, gd):
@@ -74,8 +82,8 @@ def check_bwd(smoe, x, g, ref_fwd, dgates, xd, gd, dtype, dx_in=None, dx_in_d=No
                                   dx=dx_in_d, accumulate=dx_in_d is not None)
     torch.cuda.synchronize()
     rb = oracle.router_bwd(x, g, idx, gates32.astype(np.float64), dgates.astype(np.float64))
-    e = rel_err(host(dg), rb["dG"])
-    say(f"  dG err {e:.2e}")
+    e = rel_err(host(dg), rb["dG"].T)
+    say(f"  dw err {e:.2e}")
     assert e <= F32_TOL
     want_dx = rb["dx"] + (dx_in if dx_in is not None else 0.0)
     got_dx = host(dx)
@@ -90,7 +98,7 @@ def run_case(smoe, T, d, E, k, dtype, cid, accumulate=False):
     w = make_router(T, d, E, k, dtype, cid)
     x = w.f32("x").astype(np.float64)
     g = w.f32("gate_w").astype(np.float64)
-    xd, gd = dev_tensor(w.tensors["x"]), dev_tensor(w.tensors["gate_w"])
+    xd, gd = dev_tensor(w.tensors["x"]), wt_tensor(w.tensors["gate_w"])
     _, ref = check_fwd(smoe, x, g, k, xd, gd)
     dx_in = w.f32("dx_in").astype(np.float64) if accumulate else None
     dx_in_d = dev_tensor(w.tensors["dx_in"]) if accumulate else None
@@ -115,7 +123,7 @@ def test_router_tiny_workload_reproduces_its_routing(smoe):
     w = make_config(1)
     x = w.f32("x").astype(np.float64)
     g = w.tensors["gate_w"].astype(np.float64)
-    r, ref = check_fwd(smoe, x, g, w.k, dev_tensor(w.tensors["x"]), dev_tensor(w.tensors["gate_w"]))
+    r, ref = check_fwd(smoe, x, g, w.k, dev_tensor(w.tensors["x"]), wt_tensor(w.tensors["gate_w"]))
     np.testing.assert_array_equal(ref["expert_idxs"], w.tensors["expert_idxs"])
 
 
@@ -123,7 +131,7 @@ def test_router_single_expert(smoe):
     """E = k = 1: every token picks expert 0 with gate 1; no gradient."""
     say("router E=k=1")
     w = make_router(100, 96, 1, 1, "f32", 331)
-    xd, gd = dev_tensor(w.tensors["x"]), dev_tensor(w.tensors["gate_w"])
+    xd, gd = dev_tensor(w.tensors["x"]), wt_tensor(w.tensors["gate_w"])
     r = smoe.smoe_router_fwd(xd, gd, 1)
     assert np.all(r["expert_idxs"].cpu().numpy() == 0)
     assert np.all(r["gates"].cpu().numpy() == 1.0)
@@ -134,25 +142,28 @@ def test_router_single_expert(smoe):
 def test_router_no_tokens(smoe):
     say("router T=0")
     x = torch.empty((0, 64), device="cuda")
-    g = torch.randn((64, 8), device="cuda")
+    g = torch.randn((8, 64), device="cuda")
     r = smoe.smoe_router_fwd(x, g, 2, want_logits=True)
     assert r["expert_idxs"].shape == (0, 2) and r["logits"].shape == (0, 8)
     dg, dx = smoe.smoe_router_bwd(x, g, r["expert_idxs"], r["gates"], torch.empty((0, 2), device="cuda"))
     torch.cuda.synchronize()
-    assert dx.shape == (0, 64) and np.all(dg.cpu().numpy() == 0.0)
+    assert dx.shape == (0, 64) and dg.shape == (8, 64) and np.all(dg.cpu().numpy() == 0.0)
 
 
-def test_router_ties_go_to_lower_expert(smoe):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("E", [8, 40])
+def test_router_ties_go_to_lower_expert(smoe, dtype, E):
     """Equal logits (repeated gate columns): the lower id wins, in order."""
-    say("router ties")
-    T, d, E, k = 200, 64, 8, 4
-    w = make_router(T, d, E, k, "f32", 332)
+    say(f"router ties {dtype} E={E}")
+    T, d, k = 200, 64, 4
+    w = make_router(T, d, E, k, dtype, 332)
     gm = w.tensors["gate_w"].copy()
     gm[:, 5] = gm[:, 2]
     gm[:, 7] = gm[:, 2]
     gm[:, 6] = gm[:, 1]
     x = w.f32("x").astype(np.float64)
-    r, ref = check_fwd(smoe, x, gm.astype(np.float64), k, dev_tensor(w.tensors["x"]), dev_tensor(gm))
+    g = bf16_bits_to_f32(gm) if dtype == "bf16" else gm
+    r, ref = check_fwd(smoe, x, g.astype(np.float64), k, dev_tensor(w.tensors["x"]), wt_tensor(gm))
     idx = r["expert_idxs"].cpu().numpy()
     # bitwise-equal columns give bitwise-equal fp32 logits: exact tie order
     for t in range(T):
@@ -166,7 +177,7 @@ def test_router_ties_go_to_lower_expert(smoe):
 def test_router_deterministic(smoe):
     say("router determinism")
     w = make_router(3000, 1024, 16, 2, "bf16", 333)
-    xd, gd = dev_tensor(w.tensors["x"]), dev_tensor(w.tensors["gate_w"])
+    xd, gd = dev_tensor(w.tensors["x"]), wt_tensor(w.tensors["gate_w"])
     a = smoe.smoe_router_fwd(xd, gd, 2, want_logits=True)
     b = smoe.smoe_router_fwd(xd, gd, 2, want_logits=True)
     for n in a:
