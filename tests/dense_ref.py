@@ -8,8 +8,6 @@ import math
 import numpy as np
 import torch
 
-torch.set_default_dtype(torch.float64)
-
 
 def t64(a):
     return torch.tensor(np.asarray(a, dtype=np.float64), dtype=torch.float64)

@@ -141,11 +141,11 @@ def test_router_single_expert(smoe):
 
 def test_router_no_tokens(smoe):
     say("router T=0")
-    x = torch.empty((0, 64), device="cuda")
-    g = torch.randn((8, 64), device="cuda")
+    x = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    g = torch.randn((8, 64), dtype=torch.float32, device="cuda")
     r = smoe.smoe_router_fwd(x, g, 2, want_logits=True)
     assert r["expert_idxs"].shape == (0, 2) and r["logits"].shape == (0, 8)
-    dg, dx = smoe.smoe_router_bwd(x, g, r["expert_idxs"], r["gates"], torch.empty((0, 2), device="cuda"))
+    dg, dx = smoe.smoe_router_bwd(x, g, r["expert_idxs"], r["gates"], torch.empty((0, 2), dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
     assert dx.shape == (0, 64) and dg.shape == (8, 64) and np.all(dg.cpu().numpy() == 0.0)
 
@@ -194,3 +194,33 @@ def test_router_full_size(smoe, shape):
     workloads at their full token counts, bf16, in full."""
     T, d, E, k = shape
     run_case(smoe, T, d, E, k, "bf16", 340 + E)
+
+
+def test_full_chain_tiny_workload(smoe):
+    """The tiny fp32 workload end to end on the GPU: router -> SMoE-MLP
+    forward -> MLP backward -> router backward, the router's dx added to the
+    MLP's; every output against the oracle's same chain."""
+    say("full chain, tiny fp32 workload")
+    w = make_config(1)
+    f = lambda n: w.f32(n).astype(np.float64)
+    x, G, w1, w2, dout = f("x"), w.tensors["gate_w"].astype(np.float64), f("w1"), f("w2"), f("dout")
+    rf = oracle.router_fwd(x, G, w.k)
+    ref_out = oracle.mlp_fwd(x, w1, w2, rf["expert_idxs"], rf["gates"], w.act, storage="f64")
+    mb = oracle.mlp_bwd(x, w1, w2, rf["expert_idxs"], rf["gates"], w.act, dout, storage="f64")
+    rb = oracle.router_bwd(x, G, rf["expert_idxs"], rf["gates"], mb["dgates"])
+
+    xd, wt = dev_tensor(w.tensors["x"]), wt_tensor(w.tensors["gate_w"])
+    w1d, w2d, doutd = dev_tensor(w.tensors["w1"]), dev_tensor(w.tensors["w2"]), dev_tensor(w.tensors["dout"])
+    r = smoe.smoe_router_fwd(xd, wt, w.k)
+    out, saved = smoe.smoe_mlp_fwd(xd, w1d, w2d, r["expert_idxs"], r["gates"], w.act)
+    g = smoe.smoe_mlp_bwd(doutd, xd, w1d, w2d, r["expert_idxs"], r["gates"], w.act, saved)
+    dwg, dx = smoe.smoe_router_bwd(xd, wt, r["expert_idxs"], r["gates"], g["dgates"], dx=g["dx"], accumulate=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(r["expert_idxs"].cpu().numpy(), rf["expert_idxs"])
+    checks = {"out": (out, ref_out), "gates": (r["gates"], rf["gates"]), "dgates": (g["dgates"], mb["dgates"]),
+              "dw1": (g["dw1"], mb["dw1"]), "dw2": (g["dw2"], mb["dw2"]), "dG": (dwg, rb["dG"].T),
+              "dx": (dx, mb["dx"] + rb["dx"])}
+    for n, (got, want) in checks.items():
+        e = rel_err(host(got), want)
+        say(f"  {n} err {e:.2e}")
+        assert e <= F32_TOL, n
