@@ -279,11 +279,10 @@ int run_dw(GemmArgs a, int bf16, float* dw, float* partial, hipStream_t st, int 
   return SMOE_OK;
 }
 
-// Router backward scratch: per-choice dlogits, their dense copy D for the
-// dw product, the single-group offsets and identity row index, the
-// product's [d][ncol] result and its split-K partials.
+// Router backward scratch: the dense dlogits D for the dw product, its
+// single-group offsets and identity row index, the product's [d][ncol]
+// result and its split-K partials.
 struct RouterBwdWs {
-  float* dlog = nullptr;
   void* D = nullptr;
   int* offsets = nullptr;
   int* rows = nullptr;
@@ -293,7 +292,6 @@ struct RouterBwdWs {
 void layout_router_bwd(Arena& ar, int64_t T, int64_t d, int E, int bf16, RouterBwdWs& w) {
   int ep, ncol;
   gate_dlogit_cols(E, bf16, ep, ncol);
-  w.dlog = static_cast<float*>(ar.take(size_t(T) * 8 * 4));
   w.D = ar.take(size_t(T) * ncol * (bf16 ? 2 : 4));
   w.offsets = static_cast<int*>(ar.take(2 * sizeof(int)));
   w.rows = static_cast<int*>(ar.take(size_t(T) * sizeof(int)));
@@ -382,11 +380,10 @@ int smoe_router_bwd(const void* x, const void* w, int64_t T, int64_t d_model, in
   Arena ar(ws);
   RouterBwdWs wl;
   layout_router_bwd(ar, T, d_model, E, bf16, wl);
-  SMOE_HIP(launch_gate_dlogit(T, E, k, bf16, expert_idxs, gates, dgates, wl.dlog, wl.D, wl.offsets, wl.rows, st),
-           "router_bwd dlogits");
   {
     RoleTimer t(SMOE_ROLE_ROUTER_DX, st);
-    SMOE_HIP(launch_gate_dx(w, T, int(d_model), E, k, bf16, expert_idxs, wl.dlog, dx, accumulate_dx, st),
+    SMOE_HIP(launch_gate_dx(w, T, int(d_model), E, k, bf16, expert_idxs, gates, dgates, dx, accumulate_dx, wl.D,
+                            wl.rows, wl.offsets, st),
              "router_bwd dx");
   }
   // dw^T [d][ncol] = x^T D as a weight-gradient product over one group of T

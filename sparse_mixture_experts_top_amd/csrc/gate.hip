@@ -151,14 +151,17 @@ __global__ __launch_bounds__(kGateThreads) void gate_fwd_f32_kernel(const float*
 }
 
 // bf16 inputs, on the matrix cores: a block takes 32 tokens and all experts
-// (NT tiles of 32), its 4 waves splitting d (wave w takes the 16-wide k
-// steps w, w+4, ...; each wave keeps U steps of loads in flight).  The
+// (NT tiles of 32), its 8 waves splitting d (wave w takes the 16-wide k
+// steps w, w+8, ...; each wave keeps U steps of loads in flight, and two
+// blocks share a CU, so 16 waves stream x through each CU).  The
 // v_mfma_f32_32x32x16_bf16 fragments come straight from global memory: a
 // lane loads 8 consecutive k of one token row (x) and of one expert row
 // (w).  The wave partials meet in LDS, summed in wave order; then groups of
-// 8 lanes per token pick the top k.
+// 16 lanes per token pick the top k.
 typedef __bf16 gate_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float gate_f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kFwdThreads = 512;
+constexpr int kFwdWaves = kFwdThreads / kWave;
 constexpr int kGateBT = 32;   // tokens per block
 constexpr int kGateU = 8;     // k steps per wave per batch of loads
 
@@ -168,14 +171,14 @@ SMOE_DEV gate_bf16x8_t load_frag(const uint16_t* p, bool ok) {
 }
 
 template <int NT>
-__global__ __launch_bounds__(kGateThreads) void gate_fwd_mfma_kernel(const uint16_t* __restrict__ x,
-                                                                     const uint16_t* __restrict__ wg, int64_t T,
-                                                                     int d, int E, int k, int* __restrict__ idx_out,
-                                                                     float* __restrict__ gates_out,
-                                                                     float* __restrict__ logits_out) {
+__global__ __launch_bounds__(kFwdThreads) void gate_fwd_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                    const uint16_t* __restrict__ wg, int64_t T, int d,
+                                                                    int E, int k, int* __restrict__ idx_out,
+                                                                    float* __restrict__ gates_out,
+                                                                    float* __restrict__ logits_out) {
   constexpr int EP = 32 * NT;
   constexpr int PITCH = EP + 1;
-  __shared__ float red[kGateWaves][kGateBT][PITCH];
+  __shared__ float red[kFwdWaves][kGateBT][PITCH];
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int half = lane >> 5;
@@ -197,11 +200,11 @@ __global__ __launch_bounds__(kGateThreads) void gate_fwd_mfma_kernel(const uint1
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
-    for (int s0 = w; s0 < nsteps; s0 += kGateWaves * kGateU) {
+    for (int s0 = w; s0 < nsteps; s0 += kFwdWaves * kGateU) {
       gate_bf16x8_t a[kGateU], b[kGateU][NT];
 #pragma unroll
       for (int u = 0; u < kGateU; ++u) {
-        const int kk = 16 * (s0 + kGateWaves * u);
+        const int kk = 16 * (s0 + kFwdWaves * u);
         const bool k_ok = kk + 8 * half < d;
         a[u] = load_frag(xr + kk, k_ok && tok_ok);
 #pragma unroll
@@ -222,14 +225,17 @@ __global__ __launch_bounds__(kGateThreads) void gate_fwd_mfma_kernel(const uint1
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[w][lane & 31][32 * nt + 8 * q + 4 * half + i] = acc[nt][4 * q + i];
     __syncthreads();
-    // 8 lanes per token: lane p of the group sums experts p*EL .. +EL-1
-    constexpr int EL = EP / 8;
-    const int tl = threadIdx.x / 8, p = threadIdx.x % 8;
+    // 16 lanes per token: lane p of the group sums experts p*EL .. +EL-1
+    constexpr int EL = EP / 16;
+    const int tl = threadIdx.x / 16, p = threadIdx.x % 16;
     float z[EL];
 #pragma unroll
     for (int i = 0; i < EL; ++i) {
       const int e = p * EL + i;
-      z[i] = ((red[0][tl][e] + red[1][tl][e]) + red[2][tl][e]) + red[3][tl][e];
+      float v = red[0][tl][e];
+#pragma unroll
+      for (int ww = 1; ww < kFwdWaves; ++ww) v += red[ww][tl][e];
+      z[i] = v;
     }
     const int64_t t = t0 + tl;
     const bool real = t < T;
@@ -238,34 +244,68 @@ __global__ __launch_bounds__(kGateThreads) void gate_fwd_mfma_kernel(const uint1
       for (int i = 0; i < EL; ++i)
         if (p * EL + i < E) logits_out[t * E + p * EL + i] = z[i];
     }
-    group_topk_softmax<8, EL>(z, p, E, k, real, t, idx_out, gates_out);
+    group_topk_softmax<16, EL>(z, p, E, k, real, t, idx_out, gates_out);
     __syncthreads();
   }
 }
 
 // ---- backward ------------------------------------------------------------
-// Per choice j of token t: dlog[t][j] = g_j (dg_j - sum_i g_i dg_i) (the sum
-// over all k choices), 0 where the expert id is outside [0, E).  The same
-// values also go into a dense row-major D [T][ncol] for the dw product:
-// bf16 inputs: D[t][e] = hi, D[t][ep + e] = lo with hi = bf16(v) and
-// lo = bf16(v - hi), so that the bf16 matrix-core product of x with both
-// halves carries v to about 16 significant bits; fp32 inputs: D[t][e] = v.
-// Unchosen entries are 0.  One thread per token; it also writes the
-// product's row index rows[t] = t (the rows are read in place), and thread 0
-// the single-group row offsets {0, T}.
-__global__ __launch_bounds__(kGateThreads) void gate_dlogit_kernel(int64_t T, int E, int k, int ep, int ncol,
-                                                                   int bf16, const int* __restrict__ idx,
-                                                                   const float* __restrict__ gates,
-                                                                   const float* __restrict__ dgates,
-                                                                   float* __restrict__ dlog, void* __restrict__ D,
-                                                                   int* __restrict__ offsets, int* __restrict__ rows) {
-  const int64_t i0 = int64_t(blockIdx.x) * kGateThreads + threadIdx.x;
-  if (i0 == 0) {
+// Router dx: dx[t][c] (+)= sum_j dlog[t][j] w[e_j][c], with
+//   dlog[t][j] = g_j (dg_j - sum_i g_i dg_i)
+// for choice j of token t (the sum over all k choices; 0 where the expert
+// id is outside [0, E)).  Block (column tile of 256, token chunk of 128):
+// the tile's slice of every expert row, w[e][c0 .. c0+255], sits in LDS as
+// fp32, and so do the chunk's expert ids and dlogits, formed in the
+// prologue by one thread per token; lane l of each wave owns columns
+// c0+4l..c0+4l+3, the four waves take every fourth token.
+//
+// The blocks of the first column tile also write what the dw product reads:
+// the dense dlogits D [T][ncol] (bf16 inputs: D[t][e] = hi, D[t][ep + e] =
+// lo with hi = bf16(v), lo = bf16(v - hi), so that the bf16 matrix-core
+// product of x with both halves carries v to about 16 significant bits;
+// fp32 inputs: D[t][e] = v; unchosen entries 0), the identity row index
+// rows[t] = t (its rows are read in place) and the single-group row offsets
+// {0, T}.
+constexpr int kDxCols = 4 * kWave;
+constexpr int kDxTokChunk = 128;
+template <class InT, int EMAX>
+__global__ __launch_bounds__(kGateThreads) void gate_dx_kernel(const InT* __restrict__ wg, int64_t T, int d, int E,
+                                                               int k, const int* __restrict__ idx,
+                                                               const float* __restrict__ gates,
+                                                               const float* __restrict__ dgates, InT* __restrict__ dx,
+                                                               int accumulate, int ep, int ncol_d,
+                                                               InT* __restrict__ D, int* __restrict__ rows,
+                                                               int* __restrict__ offsets) {
+  __shared__ __attribute__((aligned(16))) float ws_tile[EMAX * kDxCols];
+  __shared__ int ch_e[kDxTokChunk * kGateMaxK];
+  __shared__ float ch_v[kDxTokChunk * kGateMaxK];
+  const int c0 = blockIdx.x * kDxCols;
+  const int ncol = min(kDxCols, d - c0);   // a multiple of 8
+  constexpr int VW = sizeof(InT) == 2 ? 8 : 4;   // elements per 16-byte load
+  for (int i = threadIdx.x; i < E * (kDxCols / VW); i += kGateThreads) {
+    const int e = i / (kDxCols / VW), c = (i - e * (kDxCols / VW)) * VW;
+    float v[VW];
+    if (c < ncol) {
+      const InT* src = wg + int64_t(e) * d + c0 + c;
+      ld4<InT>(src, v);
+      if constexpr (VW == 8) ld4<InT>(src + 4, v + 4);
+    } else {
+#pragma unroll
+      for (int q = 0; q < VW; ++q) v[q] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < VW; q += 4)
+      *reinterpret_cast<float4*>(ws_tile + e * kDxCols + c + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+  }
+  const int64_t t0 = int64_t(blockIdx.y) * kDxTokChunk;
+  const int nt = int(T - t0 < kDxTokChunk ? T - t0 : kDxTokChunk);
+  const bool first = blockIdx.x == 0;
+  if (first && blockIdx.y == 0 && threadIdx.x == 0) {
     offsets[0] = 0;
     offsets[1] = int(T);
   }
-  for (int64_t t = i0; t < T; t += int64_t(gridDim.x) * kGateThreads) {
-    rows[t] = int(t);
+  for (int i = threadIdx.x; i < nt; i += kGateThreads) {
+    const int64_t t = t0 + i;
     float gv[kGateMaxK], dv[kGateMaxK];
     float s = 0.f;
 #pragma unroll
@@ -274,14 +314,11 @@ __global__ __launch_bounds__(kGateThreads) void gate_dlogit_kernel(int64_t T, in
       dv[j] = j < k ? dgates[t * k + j] : 0.f;
       s += gv[j] * dv[j];
     }
-    // clear the row, then place the chosen entries (the same thread writes
-    // both, in order)
-    if (bf16) {
-      uint16_t* row = static_cast<uint16_t*>(D) + t * ncol;
-      for (int c = 0; c < ncol; c += 8) *reinterpret_cast<uint4*>(row + c) = make_uint4(0u, 0u, 0u, 0u);
-    } else {
-      float* row = static_cast<float*>(D) + t * ncol;
-      for (int c = 0; c < ncol; c += 4) *reinterpret_cast<float4*>(row + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    InT* drow = D + t * ncol_d;
+    if (first) {
+      rows[t] = int(t);
+      for (int c = 0; c < ncol_d; c += 16 / int(sizeof(InT)))
+        *reinterpret_cast<uint4*>(drow + c) = make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int j = 0; j < kGateMaxK; ++j) {
@@ -289,50 +326,19 @@ __global__ __launch_bounds__(kGateThreads) void gate_dlogit_kernel(int64_t T, in
         const int e = idx[t * k + j];
         const bool ok = e >= 0 && e < E;
         const float v = ok ? gv[j] * (dv[j] - s) : 0.f;
-        dlog[t * k + j] = v;
-        if (ok) {
-          if (bf16) {
-            uint16_t* row = static_cast<uint16_t*>(D) + t * ncol;
+        ch_e[i * k + j] = ok ? e : 0;
+        ch_v[i * k + j] = v;
+        if (first && ok) {
+          if constexpr (sizeof(InT) == 2) {
             const uint16_t hi = f2bf(v);
-            row[e] = hi;
-            row[ep + e] = f2bf(v - bf2f(hi));
+            drow[e] = hi;
+            drow[ep + e] = f2bf(v - bf2f(hi));
           } else {
-            static_cast<float*>(D)[t * ncol + e] = v;
+            drow[e] = v;
           }
         }
       }
     }
-  }
-}
-
-// Router dx: dx[t][c] (+)= sum_j dlog[t][j] w[e_j][c].  Block (column tile
-// of 256, token chunk of 128): the tile's slice of every expert row,
-// w[e][c0 .. c0+255], sits in LDS as fp32, and so do the chunk's expert ids
-// and dlogits; lane l of each wave owns columns c0+4l..c0+4l+3, the four
-// waves take every fourth token.
-constexpr int kDxCols = 4 * kWave;
-constexpr int kDxTokChunk = 128;
-template <class InT, int EMAX>
-__global__ __launch_bounds__(kGateThreads) void gate_dx_kernel(const InT* __restrict__ wg, int64_t T, int d, int E,
-                                                               int k, const int* __restrict__ idx,
-                                                               const float* __restrict__ dlog, InT* __restrict__ dx,
-                                                               int accumulate) {
-  __shared__ __attribute__((aligned(16))) float ws_tile[EMAX * kDxCols];
-  __shared__ int ch_e[kDxTokChunk * kGateMaxK];
-  __shared__ float ch_v[kDxTokChunk * kGateMaxK];
-  const int c0 = blockIdx.x * kDxCols;
-  const int ncol = min(kDxCols, d - c0);   // a multiple of 8
-  for (int i = threadIdx.x; i < E * kDxCols; i += kGateThreads) {
-    const int e = i / kDxCols, c = i - e * kDxCols;
-    ws_tile[i] = c < ncol ? ld<InT>(wg + int64_t(e) * d + c0 + c) : 0.f;
-  }
-  const int64_t t0 = int64_t(blockIdx.y) * kDxTokChunk;
-  const int nt = int(T - t0 < kDxTokChunk ? T - t0 : kDxTokChunk);
-  for (int i = threadIdx.x; i < nt * k; i += kGateThreads) {
-    const int e = idx[t0 * k + i];
-    const bool ok = e >= 0 && e < E;
-    ch_e[i] = ok ? e : 0;
-    ch_v[i] = ok ? dlog[t0 * k + i] : 0.f;
   }
   __syncthreads();
   const int lane = lane_id();
@@ -390,11 +396,11 @@ hipError_t launch_gate_fwd(const void* x, const void* wg, int64_t T, int d, int 
   if (bf16) {
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const uint16_t* wp = static_cast<const uint16_t*>(wg);
-    const dim3 grid(grid_cap((T + kGateBT - 1) / kGateBT, 1 << 20));
+    const dim3 grid(grid_cap((T + kGateBT - 1) / kGateBT, 1 << 20)), fblock(kFwdThreads);
     if (E <= 32)
-      hipLaunchKernelGGL((gate_fwd_mfma_kernel<1>), grid, block, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
+      hipLaunchKernelGGL((gate_fwd_mfma_kernel<1>), grid, fblock, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
     else
-      hipLaunchKernelGGL((gate_fwd_mfma_kernel<2>), grid, block, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
+      hipLaunchKernelGGL((gate_fwd_mfma_kernel<2>), grid, fblock, 0, st, xp, wp, T, d, E, k, idx, gates, logits);
   } else {
     const float* xp = static_cast<const float*>(x);
     const float* wp = static_cast<const float*>(wg);
@@ -421,40 +427,32 @@ void gate_dlogit_cols(int E, int bf16, int& ep, int& ncol) {
   ncol = bf16 ? 2 * ep : ep;
 }
 
-hipError_t launch_gate_dlogit(int64_t T, int E, int k, int bf16, const int* idx, const float* gates,
-                              const float* dgates, float* dlog, void* D, int* offsets, int* rows, hipStream_t st) {
-  int ep, ncol;
-  gate_dlogit_cols(E, bf16, ep, ncol);
-  hipLaunchKernelGGL(gate_dlogit_kernel, dim3(grid_cap((T + kGateThreads - 1) / kGateThreads, 4096)),
-                     dim3(kGateThreads), 0, st, T, E, k, ep, ncol, bf16, idx, gates, dgates, dlog, D, offsets, rows);
-  return hipGetLastError();
-}
-
 template <class InT>
-static void go_gate_dx(const void* wg, int64_t T, int d, int E, int k, const int* idx, const float* dlog, void* dx,
-                       int accumulate, hipStream_t st) {
+static void go_gate_dx(const void* wg, int64_t T, int d, int E, int k, const int* idx, const float* gates,
+                       const float* dgates, void* dx, int accumulate, void* D, int* rows, int* offsets,
+                       hipStream_t st) {
+  int ep, ncol;
+  gate_dlogit_cols(E, sizeof(InT) == 2, ep, ncol);
   const dim3 grid(unsigned((d + kDxCols - 1) / kDxCols), unsigned((T + kDxTokChunk - 1) / kDxTokChunk));
   const InT* wp = static_cast<const InT*>(wg);
   InT* dp = static_cast<InT*>(dx);
-  if (E <= 8)
-    hipLaunchKernelGGL((gate_dx_kernel<InT, 8>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, dlog, dp,
-                       accumulate);
-  else if (E <= 16)
-    hipLaunchKernelGGL((gate_dx_kernel<InT, 16>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, dlog, dp,
-                       accumulate);
-  else if (E <= 32)
-    hipLaunchKernelGGL((gate_dx_kernel<InT, 32>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, dlog, dp,
-                       accumulate);
-  else
-    hipLaunchKernelGGL((gate_dx_kernel<InT, 64>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, dlog, dp,
-                       accumulate);
+  InT* Dp = static_cast<InT*>(D);
+#define SMOE_GO_DX(EM)                                                                                            \
+  hipLaunchKernelGGL((gate_dx_kernel<InT, EM>), grid, dim3(kGateThreads), 0, st, wp, T, d, E, k, idx, gates, dgates, \
+                     dp, accumulate, ep, ncol, Dp, rows, offsets)
+  if (E <= 8) SMOE_GO_DX(8);
+  else if (E <= 16) SMOE_GO_DX(16);
+  else if (E <= 32) SMOE_GO_DX(32);
+  else SMOE_GO_DX(64);
+#undef SMOE_GO_DX
 }
 
-hipError_t launch_gate_dx(const void* wg, int64_t T, int d, int E, int k, int bf16, const int* idx, const float* dlog,
-                          void* dx, int accumulate, hipStream_t st) {
+hipError_t launch_gate_dx(const void* wg, int64_t T, int d, int E, int k, int bf16, const int* idx,
+                          const float* gates, const float* dgates, void* dx, int accumulate, void* D, int* rows,
+                          int* offsets, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (bf16) go_gate_dx<uint16_t>(wg, T, d, E, k, idx, dlog, dx, accumulate, st);
-  else go_gate_dx<float>(wg, T, d, E, k, idx, dlog, dx, accumulate, st);
+  if (bf16) go_gate_dx<uint16_t>(wg, T, d, E, k, idx, gates, dgates, dx, accumulate, D, rows, offsets, st);
+  else go_gate_dx<float>(wg, T, d, E, k, idx, gates, dgates, dx, accumulate, D, rows, offsets, st);
   return hipGetLastError();
 }
 

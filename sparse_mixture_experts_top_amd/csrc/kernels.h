@@ -115,18 +115,16 @@ bool plan_gemm(GemmArgs& a, GemmPlan& plan, int mode, int epi, int dual, int bf1
 int64_t whole_round_tiles(const GemmArgs& a, const GemmPlan& plan);
 
 // Router (gate.hip): top-k softmax gates from logits = x w^T (w [E][d]);
-// the backward's pieces: per-choice dlogits (and their dense copy D
-// [T][ncol] for the dw product, with the single-group offsets {0, T} and
-// the identity row index rows[t] = t the product reads), the
-// router's dx (written or added), and dw [E][d] from the product's
-// [d][ncol] result.
+// the backward's pieces: the router's dx (written or added) from the
+// per-choice dlogits, which it also leaves as a dense D [T][ncol] for the dw
+// product together with that product's identity row index and single-group
+// offsets {0, T}; and dw [E][d] from the product's [d][ncol] result.
 hipError_t launch_gate_fwd(const void* x, const void* wg, int64_t T, int d, int E, int k, int bf16, int* idx,
                            float* gates, float* logits, hipStream_t st);
 void gate_dlogit_cols(int E, int bf16, int& ep, int& ncol);
-hipError_t launch_gate_dlogit(int64_t T, int E, int k, int bf16, const int* idx, const float* gates,
-                              const float* dgates, float* dlog, void* D, int* offsets, int* rows, hipStream_t st);
-hipError_t launch_gate_dx(const void* wg, int64_t T, int d, int E, int k, int bf16, const int* idx, const float* dlog,
-                          void* dx, int accumulate, hipStream_t st);
+hipError_t launch_gate_dx(const void* wg, int64_t T, int d, int E, int k, int bf16, const int* idx,
+                          const float* gates, const float* dgates, void* dx, int accumulate, void* D, int* rows,
+                          int* offsets, hipStream_t st);
 hipError_t launch_gate_dw_finish(const float* tmp, int d, int E, int bf16, float* dw, hipStream_t st);
 
 // Matrix-core rate probe (probe.hip): blocks x 256 threads, each wave
