@@ -1,6 +1,6 @@
 """Plain fp64 CPU oracle: routing indices, ParallelLinear (four layouts),
-top-k combine, SMoE-MLP (GELU / SwiGLU), the top-k softmax router and their
-backward passes.
+top-k combine, SMoE-MLP (GELU / SwiGLU), the top-k softmax router, the
+Mixture-of-Attention core over grouped queries, and their backward passes.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow and obvious on
 purpose: loops over tokens t and their k choices j, one vector-matrix product
@@ -39,6 +39,7 @@ __all__ = [
     "bf16_round", "route", "grouped_position", "parallel_linear_fwd",
     "parallel_linear_bwd", "mlp_fwd", "mlp_bwd", "mlp_dw_cols",
     "gelu", "gelu_grad", "silu", "silu_grad", "router_fwd", "router_bwd",
+    "moa_attention_fwd", "moa_attention_bwd",
 ]
 
 
@@ -449,3 +450,73 @@ def router_bwd(x, g, expert_idxs, gates, dgates) -> Dict[str, np.ndarray]:
         dg += np.outer(x[t], dlogits[t])
         dx[t] = g @ dlogits[t]
     return {"dlogits": dlogits, "dG": dg, "dx": dx}
+
+
+# --------------------------------------------------------------------------
+# Mixture-of-Attention core
+# --------------------------------------------------------------------------
+def _moa_rows(sorted_scattered_idxs, k: int, seq_len: int, r: int):
+    """Grouped query row r belongs to token t = s_r // k (its assignment's
+    token); the token is position t % S of sequence t // S; it attends to
+    the keys of its own sequence up to and including its own position."""
+    t = int(sorted_scattered_idxs[r]) // k
+    lo = (t // seq_len) * seq_len
+    return t, lo
+
+
+def moa_attention_fwd(q, kk, v, sorted_scattered_idxs, k: int, seq_len: int) -> Dict[str, np.ndarray]:
+    """Attention of grouped expert queries against shared keys and values
+    ([ART] para. 4: ScatterMoE runs Mixture-of-Attention, whose experts are
+    attention heads, with the same grouped products; the head experts
+    share K and V).  Readings: query row r (grouped order, as the Q
+    projection's scattered-in / grouped-out product leaves it) is token
+    t = s_r // k's query for its expert head; it attends causally within
+    its sequence (keys t' with t' // S == t // S and t' <= t); scale
+    1/sqrt(hd); the output row stays in grouped order, as the O
+    projection's grouped-in input.
+
+    q [M, hd] grouped, kk and v [T, hd] token order (T = B*S) -> o [M, hd],
+    lse [M] = log sum_t' exp(score) (the softmax normaliser)."""
+    q = _as64(q)
+    kk = _as64(kk)
+    v = _as64(v)
+    M, hd = q.shape
+    scale = 1.0 / math.sqrt(hd)
+    o = np.empty((M, hd))
+    lse = np.empty(M)
+    for r in range(M):
+        t, lo = _moa_rows(sorted_scattered_idxs, k, seq_len, r)
+        z = (kk[lo:t + 1] @ q[r]) * scale
+        m = z.max()
+        w = np.exp(z - m)
+        o[r] = (w @ v[lo:t + 1]) / w.sum()
+        lse[r] = m + math.log(w.sum())
+    return {"o": o, "lse": lse}
+
+
+def moa_attention_bwd(q, kk, v, sorted_scattered_idxs, k: int, seq_len: int, do) -> Dict[str, np.ndarray]:
+    """Backward of moa_attention_fwd for upstream do [M, hd]: with
+    p = softmax(z) over row r's keys and dp_t' = do_r . v_t',
+      dz = p * (dp - sum p dp),  dq_r = scale * dz @ K,
+      dK[t'] += scale * dz_t' q_r,  dV[t'] += p_t' do_r
+    (the keys and values gather gradient from every row that reads them)."""
+    q = _as64(q)
+    kk = _as64(kk)
+    v = _as64(v)
+    do = _as64(do)
+    M, hd = q.shape
+    scale = 1.0 / math.sqrt(hd)
+    dq = np.empty_like(q)
+    dk = np.zeros_like(kk)
+    dv = np.zeros_like(v)
+    for r in range(M):
+        t, lo = _moa_rows(sorted_scattered_idxs, k, seq_len, r)
+        z = (kk[lo:t + 1] @ q[r]) * scale
+        w = np.exp(z - z.max())
+        p = w / w.sum()
+        dp = v[lo:t + 1] @ do[r]
+        dz = p * (dp - p @ dp)
+        dq[r] = scale * (dz @ kk[lo:t + 1])
+        dk[lo:t + 1] += scale * np.outer(dz, q[r])
+        dv[lo:t + 1] += np.outer(p, do[r])
+    return {"dq": dq, "dk": dk, "dv": dv}
