@@ -494,16 +494,22 @@ def moa_attention_fwd(q, kk, v, sorted_scattered_idxs, k: int, seq_len: int) -> 
     return {"o": o, "lse": lse}
 
 
-def moa_attention_bwd(q, kk, v, sorted_scattered_idxs, k: int, seq_len: int, do) -> Dict[str, np.ndarray]:
+def moa_attention_bwd(q, kk, v, sorted_scattered_idxs, k: int, seq_len: int, do,
+                      o=None) -> Dict[str, np.ndarray]:
     """Backward of moa_attention_fwd for upstream do [M, hd]: with
-    p = softmax(z) over row r's keys and dp_t' = do_r . v_t',
-      dz = p * (dp - sum p dp),  dq_r = scale * dz @ K,
+    p = softmax(z) over row r's keys, dp_t' = do_r . v_t' and
+    D_r = sum p dp (= do_r . o_r),
+      dz = p * (dp - D_r),  dq_r = scale * dz @ K,
       dK[t'] += scale * dz_t' q_r,  dV[t'] += p_t' do_r
-    (the keys and values gather gradient from every row that reads them)."""
+    (the keys and values gather gradient from every row that reads them).
+    With ``o`` (the forward's output as stored, e.g. rounded to bf16), D_r
+    is do_r . o_r from it: the one place the backward reads the stored
+    output; with the exact o this is the same sum."""
     q = _as64(q)
     kk = _as64(kk)
     v = _as64(v)
     do = _as64(do)
+    o = None if o is None else _as64(o)
     M, hd = q.shape
     scale = 1.0 / math.sqrt(hd)
     dq = np.empty_like(q)
@@ -515,7 +521,8 @@ def moa_attention_bwd(q, kk, v, sorted_scattered_idxs, k: int, seq_len: int, do)
         w = np.exp(z - z.max())
         p = w / w.sum()
         dp = v[lo:t + 1] @ do[r]
-        dz = p * (dp - p @ dp)
+        D = p @ dp if o is None else do[r] @ o[r]
+        dz = p * (dp - D)
         dq[r] = scale * (dz @ kk[lo:t + 1])
         dk[lo:t + 1] += scale * np.outer(dz, q[r])
         dv[lo:t + 1] += np.outer(p, do[r])

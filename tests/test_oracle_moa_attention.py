@@ -8,6 +8,8 @@
   with autograd for the gradients; the normaliser against torch.logsumexp.
 * Permuting the grouped rows permutes o and dq and leaves dK and dV alone;
   a row at its sequence's first position returns that position's value.
+* The backward given the forward's exact o (D_r = do_r . o_r) equals the
+  backward that forms D_r = sum p dp itself.
 """
 import math
 
@@ -93,3 +95,12 @@ def test_row_permutation_and_first_position():
         t = int(sidx[r]) // k
         if t % S == 0:
             np.testing.assert_array_equal(f["o"][r], v[t])
+
+
+def test_backward_from_exact_stored_output_is_the_same():
+    q, kk, v, do, sidx, k, S = _setup(seed=4)
+    f = oracle.moa_attention_fwd(q, kk, v, sidx, k, S)
+    a = oracle.moa_attention_bwd(q, kk, v, sidx, k, S, do)
+    b = oracle.moa_attention_bwd(q, kk, v, sidx, k, S, do, o=f["o"])
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(b[n], a[n], rtol=1e-10, atol=1e-12)
