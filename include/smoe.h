@@ -248,7 +248,10 @@ enum smoe_role {
   SMOE_ROLE_ROUTER_FWD = 15, /* router logits, top-k and softmax            */
   SMOE_ROLE_ROUTER_DX = 16, /* router dx                                    */
   SMOE_ROLE_ROUTER_DW = 17, /* router dw product                            */
-  SMOE_ROLE_COUNT = 18
+  SMOE_ROLE_ATTN_FWD = 18,  /* MoA attention forward                        */
+  SMOE_ROLE_ATTN_DQ = 19,   /* MoA attention dq                             */
+  SMOE_ROLE_ATTN_DKV = 20,  /* MoA attention dk, dv                         */
+  SMOE_ROLE_COUNT = 21
 };
 int smoe_set_role_events(int32_t role, void* start_event, void* stop_event);
 
@@ -288,6 +291,46 @@ size_t smoe_router_bwd_workspace_bytes(int64_t T, int64_t d_model, int32_t E);
 int smoe_router_bwd(const void* x, const void* w, int64_t T, int64_t d_model, int32_t E, int32_t k,
                     int32_t dtype, const int32_t* expert_idxs, const float* gates, const float* dgates,
                     float* dw_out, void* dx, int32_t accumulate_dx, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * smoe_moa_attention_fwd - the Mixture-of-Attention core (article "This
+ * Machine Learning Research Presents ScatterMoE", body, para. 4: the head
+ * experts of MoA run on the same grouped products, with no extra memory):
+ * grouped query rows against keys and values shared by all experts.
+ *   q [T*k, head_dim] in grouped order (row r = assignment
+ *     sorted_scattered_idxs[r], as smoe_parallel_linear_fwd writes it
+ *     scattered-in / grouped-out); row r is token t = s_r / k's query for
+ *     its expert head
+ *   k, v [T, head_dim] token order, T = B * seq_len tokens (B sequences)
+ *   o[r] = softmax_t'(q_r . k_t' / sqrt(head_dim)) v over the keys t' of
+ *     t's sequence with t' <= t (causal); o [T*k, head_dim], grouped order
+ *   lse[r] = log sum_t' exp(q_r . k_t' / sqrt(head_dim)), fp32 [T*k] (the
+ *     backward's input)
+ * bf16 only (SMOE_ERR_UNSUPPORTED otherwise), head_dim 128; fp32
+ * accumulation, the probabilities enter the P v product in bf16.
+ * ------------------------------------------------------------------------ */
+int smoe_moa_attention_fwd(const void* q, const void* k_, const void* v, const int32_t* sorted_scattered_idxs,
+                           int64_t T, int32_t k, int64_t seq_len, int64_t head_dim, int32_t dtype, void* o, float* lse,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * smoe_moa_attention_bwd - backward of smoe_moa_attention_fwd for upstream
+ * dout [T*k, head_dim] (grouped order).  With p the row's probabilities
+ * (recomputed from lse) and D_r = dout_r . o_r:
+ *   dz = p (dout_r . v_t' - D_r)          (gradient of the scaled score)
+ *   dq_r = dz k / sqrt(head_dim)          [T*k, head_dim], grouped order
+ *   dk_t' = sum over rows of dz q_r / sqrt(head_dim),  dv_t' = sum p dout_r
+ *                                          [T, head_dim] each
+ * dk and dv are summed over every row that reads them in a fixed order
+ * (deterministic).  Outputs in the input dtype (bf16), fp32 accumulation.
+ * Scratch: smoe_moa_attention_bwd_workspace_bytes(...).  Limits as the
+ * forward.
+ * ------------------------------------------------------------------------ */
+size_t smoe_moa_attention_bwd_workspace_bytes(int64_t T, int32_t k, int64_t seq_len, int64_t head_dim);
+int smoe_moa_attention_bwd(const void* q, const void* k_, const void* v, const int32_t* sorted_scattered_idxs,
+                           int64_t T, int32_t k, int64_t seq_len, int64_t head_dim, int32_t dtype, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * smoe_probe_mfma_loop - diagnostic (for the caller's measurement of the

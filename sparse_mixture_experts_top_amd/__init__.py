@@ -22,7 +22,8 @@ __all__ = [
     "LIB_PATH", "SmoeError", "lib", "smoe_route", "smoe_parallel_linear_fwd",
     "smoe_parallel_linear_bwd", "smoe_mlp_fwd", "smoe_mlp_bwd", "saved_views",
     "header_functions", "F32", "BF16", "ACT_GELU", "ACT_SWIGLU", "ROLES", "smoe_set_role_events",
-    "smoe_probe_mfma_loop", "smoe_router_fwd", "smoe_router_bwd",
+    "smoe_probe_mfma_loop", "smoe_router_fwd", "smoe_router_bwd", "smoe_moa_attention_fwd",
+    "smoe_moa_attention_bwd",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +64,10 @@ _SIGS = {
     "smoe_router_bwd_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "smoe_router_bwd": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
                                        _vp, _sz, _vp]),
+    "smoe_moa_attention_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "smoe_moa_attention_bwd_workspace_bytes": (_sz, [_i64, _i32, _i64, _i64]),
+    "smoe_moa_attention_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _i32, _vp, _vp, _vp,
+                                              _vp, _vp, _vp, _vp, _sz, _vp]),
     "smoe_mlp_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32,
                                     _i32, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -170,6 +175,35 @@ def smoe_router_bwd(x, w, expert_idxs, gates, dgates, dx=None, accumulate: bool 
     return dw, dx
 
 
+def smoe_moa_attention_fwd(q, k_, v, sorted_scattered_idxs, k: int, seq_len: int):
+    """Mixture-of-Attention core: grouped queries q [T*k, hd] against shared
+    k_, v [T, hd] (causal within sequences of seq_len tokens) -> (o [T*k, hd]
+    grouped, lse [T*k] fp32)."""
+    _contig(q, k_, v, sorted_scattered_idxs)
+    T, hd = k_.shape
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0],), dtype=torch.float32, device=dev)
+    _check(lib.smoe_moa_attention_fwd(_p(q), _p(k_), _p(v), _p(sorted_scattered_idxs), T, k, seq_len, hd,
+                                      _dtype_code(q), _p(o), _p(lse), _stream(dev)), "smoe_moa_attention_fwd")
+    return o, lse
+
+
+def smoe_moa_attention_bwd(q, k_, v, sorted_scattered_idxs, k: int, seq_len: int, o, lse, dout):
+    """Backward of smoe_moa_attention_fwd: returns (dq [T*k, hd], dk, dv [T, hd])."""
+    _contig(q, k_, v, sorted_scattered_idxs, o, lse, dout)
+    T, hd = k_.shape
+    dev = q.device
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k_)
+    dv = torch.empty_like(v)
+    ws = _ws(lib.smoe_moa_attention_bwd_workspace_bytes(T, k, seq_len, hd), dev)
+    _check(lib.smoe_moa_attention_bwd(_p(q), _p(k_), _p(v), _p(sorted_scattered_idxs), T, k, seq_len, hd,
+                                      _dtype_code(q), _p(o), _p(lse), _p(dout), _p(dq), _p(dk), _p(dv), _p(ws),
+                                      ws.numel(), _stream(dev)), "smoe_moa_attention_bwd")
+    return dq, dk, dv
+
+
 def smoe_parallel_linear_fwd(x, w, T, k, sorted_scattered_idxs, offsets, x_grouped: bool,
                              y_grouped: bool, gates=None):
     """scatter2scatter forward; returns y ([T*k, d_out], or [T, d_out] with gates)."""
@@ -254,7 +288,8 @@ def smoe_mlp_bwd(dout, x, w1, w2, expert_idxs, gates, act: str, saved, w3=None, 
 
 
 ROLES = ["route", "up", "down", "combine", "dA", "dW2", "dX", "ksum", "dW1", "dW3", "dw_reduce",
-         "dg_reduce", "pl_fwd", "pl_dx", "pl_dw", "router_fwd", "router_dx", "router_dw"]
+         "dg_reduce", "pl_fwd", "pl_dx", "pl_dw", "router_fwd", "router_dx", "router_dw", "attn_fwd",
+         "attn_dq", "attn_dkv"]
 
 
 def smoe_set_role_events(role: str, start=None, stop=None):

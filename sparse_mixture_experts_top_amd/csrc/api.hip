@@ -404,6 +404,91 @@ int smoe_router_bwd(const void* x, const void* w, int64_t T, int64_t d_model, in
   return ok();
 }
 
+// ------------------------------------------------------- MoA attention --
+static int check_attn(int64_t T, int32_t k, int64_t seq_len, int64_t head_dim, int32_t dtype) {
+  if (dtype != SMOE_F32 && dtype != SMOE_BF16) return fail(SMOE_ERR_DTYPE, "dtype %d is not SMOE_F32/SMOE_BF16", dtype);
+  if (dtype != SMOE_BF16) return fail(SMOE_ERR_UNSUPPORTED, "attention: bf16 only");
+  if (head_dim != 128) return fail(SMOE_ERR_UNSUPPORTED, "attention: head_dim=%lld (128 supported)", (long long)head_dim);
+  if (k < 1 || k > 1024) return fail(SMOE_ERR_SHAPE, "k=%d out of range", k);
+  if (T < 0 || seq_len < 1 || T % seq_len != 0)
+    return fail(SMOE_ERR_SHAPE, "T=%lld must be a multiple of seq_len=%lld", (long long)T, (long long)seq_len);
+  if (T * k > INT32_MAX / 2) return fail(SMOE_ERR_SHAPE, "T*k=%lld too large", (long long)(T * k));
+  return SMOE_OK;
+}
+
+int smoe_moa_attention_fwd(const void* q, const void* k_, const void* v, const int32_t* sorted_scattered_idxs,
+                           int64_t T, int32_t k, int64_t seq_len, int64_t head_dim, int32_t dtype, void* o, float* lse,
+                           void* stream) {
+  SMOE_TRY(check_attn(T, k, seq_len, head_dim, dtype));
+  if (T == 0) return ok();
+  SMOE_TRY(need_ptr(q, "q"));
+  SMOE_TRY(need_ptr(k_, "k"));
+  SMOE_TRY(need_ptr(v, "v"));
+  SMOE_TRY(need_ptr(sorted_scattered_idxs, "sorted_scattered_idxs"));
+  SMOE_TRY(need_ptr(o, "o"));
+  SMOE_TRY(need_ptr(lse, "lse"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  RoleTimer t(SMOE_ROLE_ATTN_FWD, st);
+  SMOE_HIP(launch_attn_fwd(q, k_, v, sorted_scattered_idxs, T * k, T, k, seq_len, o, lse, st), "moa_attention_fwd");
+  return ok();
+}
+
+struct AttnBwdWs {
+  float* D = nullptr;
+  int* tile_lo = nullptr;
+  int* tile_hi = nullptr;
+  float* pdk = nullptr;
+  float* pdv = nullptr;
+};
+static void layout_attn_bwd(Arena& ar, int64_t T, int64_t M, AttnBwdWs& w) {
+  const int64_t ntiles = (M + 31) / 32;
+  const size_t part = size_t(attn_query_splits(T)) * size_t(T) * 128 * 4;
+  w.D = static_cast<float*>(ar.take(size_t(M) * 4));
+  w.tile_lo = static_cast<int*>(ar.take(size_t(ntiles) * 4));
+  w.tile_hi = static_cast<int*>(ar.take(size_t(ntiles) * 4));
+  w.pdk = static_cast<float*>(ar.take(part));
+  w.pdv = static_cast<float*>(ar.take(part));
+}
+
+size_t smoe_moa_attention_bwd_workspace_bytes(int64_t T, int32_t k, int64_t seq_len, int64_t head_dim) {
+  if (T < 0 || k < 1 || seq_len < 1 || head_dim != 128 || T * k > INT32_MAX / 2) return 0;
+  Arena ar(nullptr);
+  AttnBwdWs w;
+  layout_attn_bwd(ar, T, T * k, w);
+  return ar.used;
+}
+
+int smoe_moa_attention_bwd(const void* q, const void* k_, const void* v, const int32_t* sorted_scattered_idxs,
+                           int64_t T, int32_t k, int64_t seq_len, int64_t head_dim, int32_t dtype, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                           size_t ws_bytes, void* stream) {
+  SMOE_TRY(check_attn(T, k, seq_len, head_dim, dtype));
+  if (T == 0) return ok();
+  SMOE_TRY(need_ptr(q, "q"));
+  SMOE_TRY(need_ptr(k_, "k"));
+  SMOE_TRY(need_ptr(v, "v"));
+  SMOE_TRY(need_ptr(sorted_scattered_idxs, "sorted_scattered_idxs"));
+  SMOE_TRY(need_ptr(o, "o"));
+  SMOE_TRY(need_ptr(lse, "lse"));
+  SMOE_TRY(need_ptr(dout, "dout"));
+  SMOE_TRY(need_ptr(dq, "dq"));
+  SMOE_TRY(need_ptr(dk, "dk"));
+  SMOE_TRY(need_ptr(dv, "dv"));
+  SMOE_TRY(need_ptr(ws, "ws"));
+  const size_t need = smoe_moa_attention_bwd_workspace_bytes(T, k, seq_len, head_dim);
+  if (ws_bytes < need) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Arena ar(ws);
+  AttnBwdWs wl;
+  layout_attn_bwd(ar, T, T * k, wl);
+  SMOE_HIP(launch_attn_bwd(q, k_, v, sorted_scattered_idxs, T * k, T, k, seq_len, o, lse, dout, dq, dk, dv, wl.D,
+                           wl.tile_lo, wl.tile_hi, wl.pdk, wl.pdv, st, g_role_ev[SMOE_ROLE_ATTN_DQ][0],
+                           g_role_ev[SMOE_ROLE_ATTN_DQ][1], g_role_ev[SMOE_ROLE_ATTN_DKV][0],
+                           g_role_ev[SMOE_ROLE_ATTN_DKV][1]),
+           "moa_attention_bwd");
+  return ok();
+}
+
 int smoe_probe_mfma_loop(float* out, int32_t blocks, int32_t iters, void* stream) {
   SMOE_TRY(need_ptr(out, "out"));
   if (blocks < 1 || iters < 1) return fail(SMOE_ERR_SHAPE, "blocks=%d and iters=%d must be positive", blocks, iters);

@@ -1,0 +1,633 @@
+// Mixture-of-Attention core on the matrix cores (article "This Machine
+// Learning Research Presents ScatterMoE", body, para. 4: the head experts
+// of Mixture-of-Attention run on the same grouped products, with no extra
+// memory).  Query row r is in grouped order (as the scattered-in /
+// grouped-out Q projection writes it) and belongs to token t = s_r / k; it
+// attends causally within its sequence (keys t' of the same sequence with
+// t' <= t, sequences of S tokens) to keys and values shared by all experts;
+// the output row stays in grouped order, ready for the grouped-in O
+// projection.  bf16 operands, fp32 accumulation, head_dim 128.
+//
+// Matrix-core layout.  v_mfma_f32_32x32x16_bf16 is issued with the
+// 32-row "column" operand first, as in the grouped products, so a lane ends
+// up holding one row (lane & 31) of the result and columns 8q + 4h + i
+// (h = lane >> 5) in acc[4q + i].  The scores of a 32-key block are formed
+// with the key rows loaded in the order pi(c) (bits 2 and 3 of the column
+// index swapped): a lane's scores for k-step s of the following product then
+// cover keys 16s + 8h + 0..7 in register order, which is exactly the A
+// operand layout that product needs, so the probabilities feed P V (and, in
+// the backward, dS K) with no shuffle.  V (and the backward's other
+// right-hand operands) are read from LDS with gfx950's transposing read.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace smoe {
+
+typedef __bf16 at_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float at_f32x16_t __attribute__((ext_vector_type(16)));
+typedef short at_i16x4_t __attribute__((ext_vector_type(4)));
+typedef short at_i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void at_lds_void_t;
+typedef __attribute__((address_space(3))) at_i16x4_t at_lds_i16x4_t;
+
+constexpr int kHD = 128;          // head dim
+constexpr int kRowB = kHD * 2;    // bytes per row of a bf16 tile
+constexpr int kKB = 32;           // keys per block
+constexpr int kAttnThreads = 256;
+constexpr int kAttnRows = 128;    // query rows per block (32 per wave)
+
+SMOE_DEV int key_perm(int c) { return (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1); }
+
+// Row tiles [32 rows][128] bf16 in LDS, 16 chunks of 16 bytes per row.
+// Row-read layout (a lane reads one row's chunk): chunk c of row r at
+// c ^ (r & 15), so 16 consecutive rows put a given chunk on 16 distinct
+// bank groups.  Transposing-read layout (a lane gathers one column over 4
+// rows): chunk c at c ^ ((r & 3) << 2).
+SMOE_DEV int swz_row(int r) { return r & 15; }
+SMOE_DEV int swz_tr(int r) { return (r & 3) << 2; }
+
+// 8 consecutive head-dim values of tile row `row`, k-step s, half h, from a
+// row-read (TR = false) or transposing-read (TR = true) layout tile
+template <bool TR = false>
+SMOE_DEV at_bf16x8_t row_frag(const char* tile, int row, int s, int h) {
+  const int c = (2 * s + h) ^ (TR ? swz_tr(row) : swz_row(row));
+  return *reinterpret_cast<const at_bf16x8_t*>(tile + row * kRowB + (c << 4));
+}
+
+// MFMA operand from a transposing-layout tile [k-rows][128 cols]: lane gets
+// column m0 + (lane & 31) at k-rows 16s + 8h + 0..7 (h = lane >> 5).  Within
+// each 16-lane group, lane i addresses k-row kb + (i >> 2), columns
+// mb + 4 (i & 3) .. +3 and receives column mb + i at k-rows kb .. kb+3.
+SMOE_DEV at_bf16x8_t tr_frag(const char* tile, int m0, int s, int lane) {
+  const int grp = lane >> 4, i = lane & 15;
+  const int mn = m0 + 16 * (grp & 1) + 4 * (i & 3);
+  const int kr = 16 * s + 8 * (grp >> 1) + (i >> 2);
+  const int c = mn >> 3, within = (mn & 7) * 2;
+  const char* p0 = tile + kr * kRowB + ((c ^ swz_tr(kr)) << 4) + within;
+  const char* p1 = tile + (kr + 4) * kRowB + ((c ^ swz_tr(kr + 4)) << 4) + within;
+  const at_i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4_t*)(const at_lds_void_t*)p0);
+  const at_i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4_t*)(const at_lds_void_t*)p1);
+  const at_i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(at_bf16x8_t, v);
+}
+
+// bf16 A operands of k-step s from a lane's 16 accumulator values (keys or
+// queries in the pi order, see the file comment), as two halves hi =
+// bf16(v) and lo = bf16(v - hi): the product with both carries v to about
+// 16 significant bits (one bf16 rounding of the probabilities alone would
+// cost up to 2^-9 of each term)
+SMOE_DEV void acc_frags(const float (&p)[16], int s, at_bf16x8_t& hi, at_bf16x8_t& lo) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float v = p[8 * s + m];
+    const __bf16 b = static_cast<__bf16>(v);
+    hi[m] = b;
+    lo[m] = static_cast<__bf16>(v - static_cast<float>(b));
+  }
+}
+
+// A 32-row tile (rows row0 .. row0+31 of a [n][128] tensor, zeros past n)
+// moved by 256 threads: two 16-byte pieces per thread, held in registers
+// between the load and the LDS store so the load can run ahead.
+struct TileRegs {
+  uint4 v[2];
+};
+SMOE_DEV void tile_load(TileRegs& r, const uint16_t* src, int64_t row0, int64_t n) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = threadIdx.x + u * kAttnThreads;
+    const int row = i >> 4, c = i & 15;
+    const int64_t g = row0 + row;
+    r.v[u] = g < n ? *reinterpret_cast<const uint4*>(src + g * kHD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+template <bool TR>
+SMOE_DEV void tile_store(const TileRegs& r, char* tile) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = threadIdx.x + u * kAttnThreads;
+    const int row = i >> 4, c = i & 15;
+    const int pc = c ^ (TR ? swz_tr(row) : swz_row(row));
+    *reinterpret_cast<uint4*>(tile + row * kRowB + (pc << 4)) = r.v[u];
+  }
+}
+
+// Block-wide [min lo, max t] over the block's rows (t = -1, lo = big for
+// rows past M); every thread gets the result.
+SMOE_DEV void block_range(int lo, int t, int* red, int& blo, int& bhi) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o, kWave));
+    t = max(t, __shfl_xor(t, o, kWave));
+  }
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    red[2 * w] = lo;
+    red[2 * w + 1] = t;
+  }
+  __syncthreads();
+  blo = red[0];
+  bhi = red[1];
+#pragma unroll
+  for (int i = 1; i < kAttnThreads / kWave; ++i) {
+    blo = min(blo, red[2 * i]);
+    bhi = max(bhi, red[2 * i + 1]);
+  }
+}
+
+// ---- forward ---------------------------------------------------------------
+// Block: 128 query rows, wave w owns rows 32w .. 32w+31 (lane: row lane & 31).
+// Key blocks of 32 run from the block's lowest sequence start to its highest
+// token; K and V tiles are shared through LDS, the next pair loading into
+// registers while the current one is used.  Online softmax in base 2.
+__global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ kk,
+                                                                const uint16_t* __restrict__ v,
+                                                                const int* __restrict__ sidx, int64_t M, int64_t T,
+                                                                int ktop, int64_t S, uint16_t* __restrict__ o,
+                                                                float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) char ks[kKB * kRowB];
+  __shared__ __attribute__((aligned(16))) char vs[kKB * kRowB];
+  __shared__ int red[2 * kAttnThreads / kWave];
+  const int lane = lane_id(), h = lane >> 5;
+  const int w = threadIdx.x / kWave;
+  const int64_t r = int64_t(blockIdx.x) * kAttnRows + 32 * w + (lane & 31);
+  const bool real = r < M;
+  const int t = real ? sidx[r] / ktop : -1;
+  const int lo = real ? int(int64_t(t) / S * S) : 0x7fffffff;
+  int blo, bhi;
+  block_range(lo, t, red, blo, bhi);
+  // this wave's own range
+  int wlo = lo, whi = t;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    wlo = min(wlo, __shfl_xor(wlo, off, kWave));
+    whi = max(whi, __shfl_xor(whi, off, kWave));
+  }
+  if (bhi < 0) return;   // no real rows (uniform over the block)
+
+  at_bf16x8_t qf[8];
+  const uint16_t* qr = q + (real ? r : 0) * kHD + 8 * h;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    uint4 x = real ? *reinterpret_cast<const uint4*>(qr + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
+    qf[s] = __builtin_bit_cast(at_bf16x8_t, x);
+  }
+  at_f32x16_t acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
+  const float sl2 = 1.4426950408889634f / sqrtf(float(kHD));   // scale * log2(e)
+  float m2 = -INFINITY, l = 0.f;
+
+  const int kb_first = blo / kKB * kKB;
+  TileRegs kr, vr;
+  tile_load(kr, kk, kb_first, T);
+  tile_load(vr, v, kb_first, T);
+  for (int kb0 = kb_first; kb0 <= bhi; kb0 += kKB) {
+    __syncthreads();
+    tile_store<false>(kr, ks);
+    tile_store<true>(vr, vs);
+    __syncthreads();
+    if (kb0 + kKB <= bhi) {
+      tile_load(kr, kk, kb0 + kKB, T);
+      tile_load(vr, v, kb0 + kKB, T);
+    }
+    if (kb0 > whi || kb0 + kKB <= wlo) continue;   // nothing for this wave
+    // scores for keys kb0 + pi(c)
+    at_f32x16_t sc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+    const int krow = key_perm(lane & 31);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s, h), qf[s], sc, 0, 0, 0);
+    float z[16];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
+        const bool ok = key >= lo && key <= t;
+        const float zz = ok ? sc[4 * q4 + i] * sl2 : -INFINITY;
+        z[4 * q4 + i] = zz;
+        bm = fmaxf(bm, zz);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+    const float mn = fmaxf(m2, bm);
+    const float alpha = mn == -INFINITY ? 1.f : exp2f(m2 - mn);
+    float p[16], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = mn == -INFINITY ? 0.f : exp2f(z[i] - mn);
+      ps += p[i];
+    }
+    ps += __shfl_xor(ps, 32, kWave);
+    l = alpha * l + ps;
+    m2 = mn;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nt][i] *= alpha;
+    at_bf16x8_t a0h, a0l, a1h, a1l;
+    acc_frags(p, 0, a0h, a0l);
+    acc_frags(p, 1, a1h, a1l);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const at_bf16x8_t v0 = tr_frag(vs, 32 * nt, 0, lane), v1 = tr_frag(vs, 32 * nt, 1, lane);
+      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0h, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0l, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1h, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1l, acc[nt], 0, 0, 0);
+    }
+  }
+  if (!real) return;
+  const float inv = 1.f / l;
+  uint16_t* orow = o + r * kHD;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float vals[4] = {acc[nt][4 * q4] * inv, acc[nt][4 * q4 + 1] * inv, acc[nt][4 * q4 + 2] * inv,
+                             acc[nt][4 * q4 + 3] * inv};
+      *reinterpret_cast<uint2*>(orow + 32 * nt + 8 * q4 + 4 * h) = pack4_bf16(vals);
+    }
+  if (h == 0) lse[r] = m2 * 0.69314718055994531f + logf(l);
+}
+
+hipError_t launch_attn_fwd(const void* q, const void* kk, const void* v, const int* sidx, int64_t M, int64_t T,
+                           int ktop, int64_t S, void* o, float* lse, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const unsigned grid = unsigned((M + kAttnRows - 1) / kAttnRows);
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(grid), dim3(kAttnThreads), 0, st, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(kk), static_cast<const uint16_t*>(v), sidx, M, T, ktop, S,
+                     static_cast<uint16_t*>(o), lse);
+  return hipGetLastError();
+}
+
+// ---- backward ----------------------------------------------------------
+// With p the probabilities of row r (recomputed from lse), dp_t' = do_r . v_t'
+// and D_r = do_r . o_r (= sum_t' p dp): dz = p (dp - D_r) is the gradient of
+// the scaled score; dq_r = scale dz K, dK += scale dz^T q, dV += p^T do.
+
+// D_r, and each 32-row query tile's [lowest sequence start, highest token]
+// (one wave per tile; two lanes per row, 64 head-dim values each)
+__global__ __launch_bounds__(kAttnThreads) void attn_bwd_prep_kernel(const uint16_t* __restrict__ o,
+                                                                     const uint16_t* __restrict__ dout,
+                                                                     const int* __restrict__ sidx, int64_t M,
+                                                                     int ktop, int64_t S, float* __restrict__ D,
+                                                                     int* __restrict__ tile_lo,
+                                                                     int* __restrict__ tile_hi, int64_t ntiles) {
+  const int lane = lane_id();
+  const int64_t tile = int64_t(blockIdx.x) * (kAttnThreads / kWave) + threadIdx.x / kWave;
+  if (tile >= ntiles) return;
+  const int64_t r = tile * 32 + (lane >> 1);
+  const int half = lane & 1;
+  const bool real = r < M;
+  float sum = 0.f;
+  if (real) {
+    const uint4* a = reinterpret_cast<const uint4*>(o + r * kHD + 64 * half);
+    const uint4* b = reinterpret_cast<const uint4*>(dout + r * kHD + 64 * half);
+#pragma unroll 2
+    for (int c = 0; c < 8; ++c) {
+      const uint4 x = a[c], y = b[c];
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+      for (int j = 0; j < 4; ++j) {
+        sum += __uint_as_float(xs[j] << 16) * __uint_as_float(ys[j] << 16);
+        sum += __uint_as_float(xs[j] & 0xffff0000u) * __uint_as_float(ys[j] & 0xffff0000u);
+      }
+    }
+  }
+  sum += __shfl_xor(sum, 1, kWave);
+  if (real && half == 0) D[r] = sum;
+  int t = real ? sidx[r] / ktop : -1;
+  int lo = real ? int(int64_t(t) / S * S) : 0x7fffffff;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off, kWave));
+    t = max(t, __shfl_xor(t, off, kWave));
+  }
+  if (lane == 0) {
+    tile_lo[tile] = lo;
+    tile_hi[tile] = t;
+  }
+}
+
+// dq: blocks of 128 query rows as in the forward; per key block the scores
+// (keys in the pi order) and dp = do V^T (V rows in the same order) give
+// dz in the A operand layout of dz K, K read back transposed from LDS.
+__global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ kk,
+                                                               const uint16_t* __restrict__ v,
+                                                               const int* __restrict__ sidx, int64_t M, int64_t T,
+                                                               int ktop, int64_t S, const float* __restrict__ lse,
+                                                               const float* __restrict__ D,
+                                                               const uint16_t* __restrict__ dout,
+                                                               uint16_t* __restrict__ dq) {
+  __shared__ __attribute__((aligned(16))) char ks[kKB * kRowB];
+  __shared__ __attribute__((aligned(16))) char vs[kKB * kRowB];
+  __shared__ int red[2 * kAttnThreads / kWave];
+  const int lane = lane_id(), h = lane >> 5;
+  const int w = threadIdx.x / kWave;
+  const int64_t r = int64_t(blockIdx.x) * kAttnRows + 32 * w + (lane & 31);
+  const bool real = r < M;
+  const int t = real ? sidx[r] / ktop : -1;
+  const int lo = real ? int(int64_t(t) / S * S) : 0x7fffffff;
+  int blo, bhi;
+  block_range(lo, t, red, blo, bhi);
+  int wlo = lo, whi = t;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    wlo = min(wlo, __shfl_xor(wlo, off, kWave));
+    whi = max(whi, __shfl_xor(whi, off, kWave));
+  }
+  if (bhi < 0) return;
+  const float l2e = 1.4426950408889634f;
+  const float sl2 = l2e / sqrtf(float(kHD));
+  const float lse2 = real ? lse[r] * l2e : 0.f;
+  const float Dr = real ? D[r] : 0.f;
+  at_bf16x8_t qf[8], df[8];
+  const uint16_t* qr = q + (real ? r : 0) * kHD + 8 * h;
+  const uint16_t* dr = dout + (real ? r : 0) * kHD + 8 * h;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    uint4 a = real ? *reinterpret_cast<const uint4*>(qr + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
+    uint4 b = real ? *reinterpret_cast<const uint4*>(dr + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
+    qf[s] = __builtin_bit_cast(at_bf16x8_t, a);
+    df[s] = __builtin_bit_cast(at_bf16x8_t, b);
+  }
+  at_f32x16_t acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
+  const int kb_first = blo / kKB * kKB;
+  TileRegs kr, vr;
+  tile_load(kr, kk, kb_first, T);
+  tile_load(vr, v, kb_first, T);
+  for (int kb0 = kb_first; kb0 <= bhi; kb0 += kKB) {
+    __syncthreads();
+    tile_store<true>(kr, ks);
+    tile_store<false>(vr, vs);
+    __syncthreads();
+    if (kb0 + kKB <= bhi) {
+      tile_load(kr, kk, kb0 + kKB, T);
+      tile_load(vr, v, kb0 + kKB, T);
+    }
+    if (kb0 > whi || kb0 + kKB <= wlo) continue;
+    at_f32x16_t sc, dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+    const int krow = key_perm(lane & 31);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(ks, krow, s, h), qf[s], sc, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<false>(vs, krow, s, h), df[s], dp, 0, 0, 0);
+    }
+    float ds[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
+        const bool ok = key >= lo && key <= t;
+        const float p = ok ? exp2f(sc[4 * q4 + i] * sl2 - lse2) : 0.f;
+        ds[4 * q4 + i] = p * (dp[4 * q4 + i] - Dr);
+      }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      at_bf16x8_t ah, al;
+      acc_frags(ds, s, ah, al);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const at_bf16x8_t kf = tr_frag(ks, 32 * nt, s, lane);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, ah, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, al, acc[nt], 0, 0, 0);
+      }
+    }
+  }
+  if (!real) return;
+  const float scale = 1.f / sqrtf(float(kHD));
+  uint16_t* out = dq + r * kHD;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float vals[4] = {acc[nt][4 * q4] * scale, acc[nt][4 * q4 + 1] * scale, acc[nt][4 * q4 + 2] * scale,
+                             acc[nt][4 * q4 + 3] * scale};
+      *reinterpret_cast<uint2*>(out + 32 * nt + 8 * q4 + 4 * h) = pack4_bf16(vals);
+    }
+}
+
+// dK, dV: block (128 keys, query split q), wave w owns keys 32w .. 32w+31 of
+// the block (lane: key lane & 31, its K and V rows in registers).  The block
+// walks the query tiles q, q + QS, ... whose key range meets its keys, each
+// tile's q and do rows shared through LDS (the next relevant tile loading
+// into registers meanwhile).  Transposed scores (queries in the pi order)
+// and dp^T give p^T and dz^T in the A operand layout of p^T do and dz^T q.
+// Partial sums per split, fp32: part[q][key][128] (dK, then dV).
+__global__ __launch_bounds__(kAttnThreads) void attn_dkv_kernel(const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ kk,
+                                                                const uint16_t* __restrict__ v,
+                                                                const int* __restrict__ sidx, int64_t M, int64_t T,
+                                                                int ktop, int64_t S, const float* __restrict__ lse,
+                                                                const float* __restrict__ D,
+                                                                const uint16_t* __restrict__ dout,
+                                                                const int* __restrict__ tile_lo,
+                                                                const int* __restrict__ tile_hi, int64_t ntiles,
+                                                                int QS, float* __restrict__ pdk,
+                                                                float* __restrict__ pdv) {
+  __shared__ __attribute__((aligned(16))) char qs[32 * kRowB];
+  __shared__ __attribute__((aligned(16))) char dos[32 * kRowB];
+  __shared__ int q_lo[32], q_t[32];
+  __shared__ float q_lse2[32], q_D[32];
+  const int lane = lane_id(), h = lane >> 5;
+  const int w = threadIdx.x / kWave;
+  const int64_t k0 = int64_t(blockIdx.x) * kAttnRows;
+  const int64_t k1 = min(T, k0 + kAttnRows) - 1;
+  const int64_t kw0 = k0 + 32 * w;
+  const int64_t key = kw0 + (lane & 31);
+  const int split = blockIdx.y;
+  const float l2e = 1.4426950408889634f;
+  const float sl2 = l2e / sqrtf(float(kHD));
+  at_bf16x8_t kf[8], vf[8];
+  {
+    const bool ok = key < T;
+    const uint16_t* kr = kk + (ok ? key : 0) * kHD + 8 * h;
+    const uint16_t* vr = v + (ok ? key : 0) * kHD + 8 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 a = ok ? *reinterpret_cast<const uint4*>(kr + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
+      uint4 b = ok ? *reinterpret_cast<const uint4*>(vr + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
+      kf[s] = __builtin_bit_cast(at_bf16x8_t, a);
+      vf[s] = __builtin_bit_cast(at_bf16x8_t, b);
+    }
+  }
+  at_f32x16_t adk[4], adv[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) adk[nt][i] = adv[nt][i] = 0.f;
+
+  // next query tile at or after i (step QS) whose range meets [k0, k1]
+  auto next_tile = [&](int64_t i) -> int64_t {
+    for (; i < ntiles; i += QS)
+      if (tile_hi[i] >= k0 && tile_lo[i] <= k1) return i;
+    return ntiles;
+  };
+  // per-row values of a query tile, one row per thread 0..31
+  int pr_lo = 0x7fffffff, pr_t = -1;
+  float pr_lse2 = 0.f, pr_D = 0.f;
+  auto row_load = [&](int64_t i) {
+    if (threadIdx.x < 32) {
+      const int64_t r = i * 32 + threadIdx.x;
+      if (r < M) {
+        pr_t = sidx[r] / ktop;
+        pr_lo = int(int64_t(pr_t) / S * S);
+        pr_lse2 = lse[r] * l2e;
+        pr_D = D[r];
+      } else {
+        pr_t = -1;
+        pr_lo = 0x7fffffff;
+        pr_lse2 = 0.f;
+        pr_D = 0.f;
+      }
+    }
+  };
+  int64_t i = next_tile(split);
+  TileRegs qr, dr;
+  if (i < ntiles) {
+    tile_load(qr, q, i * 32, M);
+    tile_load(dr, dout, i * 32, M);
+    row_load(i);
+  }
+  while (i < ntiles) {
+    __syncthreads();
+    tile_store<true>(qr, qs);
+    tile_store<true>(dr, dos);
+    if (threadIdx.x < 32) {
+      q_lo[threadIdx.x] = pr_lo;
+      q_t[threadIdx.x] = pr_t;
+      q_lse2[threadIdx.x] = pr_lse2;
+      q_D[threadIdx.x] = pr_D;
+    }
+    const int tlo = tile_lo[i], thi = tile_hi[i];
+    __syncthreads();
+    const int64_t inext = next_tile(i + QS);
+    if (inext < ntiles) {
+      tile_load(qr, q, inext * 32, M);
+      tile_load(dr, dout, inext * 32, M);
+      row_load(inext);
+    }
+    if (!(thi < kw0 || tlo > kw0 + 31)) {
+      at_f32x16_t sc, dp;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc[j] = dp[j] = 0.f;
+      const int qrow = key_perm(lane & 31);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(qs, qrow, s, h), kf[s], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(dos, qrow, s, h), vf[s], dp, 0, 0, 0);
+      }
+      float pt[16], dz[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qi = key_perm(8 * q4 + 4 * h + j);
+          const bool ok = key >= q_lo[qi] && key <= q_t[qi];
+          const float p = ok ? exp2f(sc[4 * q4 + j] * sl2 - q_lse2[qi]) : 0.f;
+          pt[4 * q4 + j] = p;
+          dz[4 * q4 + j] = p * (dp[4 * q4 + j] - q_D[qi]);
+        }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        at_bf16x8_t ph, pl, zh, zl;
+        acc_frags(pt, s, ph, pl);
+        acc_frags(dz, s, zh, zl);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const at_bf16x8_t fo = tr_frag(dos, 32 * nt, s, lane);
+          const at_bf16x8_t fq = tr_frag(qs, 32 * nt, s, lane);
+          adv[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo, ph, adv[nt], 0, 0, 0);
+          adv[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo, pl, adv[nt], 0, 0, 0);
+          adk[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq, zh, adk[nt], 0, 0, 0);
+          adk[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq, zl, adk[nt], 0, 0, 0);
+        }
+      }
+    }
+    i = inext;
+  }
+  if (key >= T) return;
+  const float scale = 1.f / sqrtf(float(kHD));
+  float* ok_ = pdk + (int64_t(split) * T + key) * kHD;
+  float* ov_ = pdv + (int64_t(split) * T + key) * kHD;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int c = 32 * nt + 8 * q4 + 4 * h;
+      *reinterpret_cast<float4*>(ok_ + c) = make_float4(adk[nt][4 * q4] * scale, adk[nt][4 * q4 + 1] * scale,
+                                                        adk[nt][4 * q4 + 2] * scale, adk[nt][4 * q4 + 3] * scale);
+      *reinterpret_cast<float4*>(ov_ + c) =
+          make_float4(adv[nt][4 * q4], adv[nt][4 * q4 + 1], adv[nt][4 * q4 + 2], adv[nt][4 * q4 + 3]);
+    }
+}
+
+// dK, dV [T][128] in bf16 from the QS partials, summed in split order
+__global__ __launch_bounds__(kAttnThreads) void attn_dkv_reduce_kernel(const float* __restrict__ pdk,
+                                                                       const float* __restrict__ pdv, int QS,
+                                                                       int64_t n, uint16_t* __restrict__ dk,
+                                                                       uint16_t* __restrict__ dv) {
+  for (int64_t i = (int64_t(blockIdx.x) * kAttnThreads + threadIdx.x) * 4; i < n;
+       i += int64_t(gridDim.x) * kAttnThreads * 4) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < QS; ++sp) {
+      const float4 x = *reinterpret_cast<const float4*>(pdk + int64_t(sp) * n + i);
+      const float4 y = *reinterpret_cast<const float4*>(pdv + int64_t(sp) * n + i);
+      a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w;
+      b[0] += y.x; b[1] += y.y; b[2] += y.z; b[3] += y.w;
+    }
+    *reinterpret_cast<uint2*>(dk + i) = pack4_bf16(a);
+    *reinterpret_cast<uint2*>(dv + i) = pack4_bf16(b);
+  }
+}
+
+// query splits of the dK/dV pass: about 512 blocks in all, at most 16
+int attn_query_splits(int64_t T) {
+  const int64_t kb = (T + kAttnRows - 1) / kAttnRows;
+  return int(std::min<int64_t>(16, std::max<int64_t>(1, (512 + kb - 1) / std::max<int64_t>(kb, 1))));
+}
+
+hipError_t launch_attn_bwd(const void* q, const void* kk, const void* v, const int* sidx, int64_t M, int64_t T,
+                           int ktop, int64_t S, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, float* D, int* tile_lo, int* tile_hi, float* pdk, float* pdv, hipStream_t st,
+                           hipEvent_t dq_start, hipEvent_t dq_stop, hipEvent_t dkv_start, hipEvent_t dkv_stop) {
+  if (M == 0) return hipSuccess;
+  const uint16_t* qp = static_cast<const uint16_t*>(q);
+  const uint16_t* kp = static_cast<const uint16_t*>(kk);
+  const uint16_t* vp = static_cast<const uint16_t*>(v);
+  const uint16_t* dp = static_cast<const uint16_t*>(dout);
+  const int64_t ntiles = (M + 31) / 32;
+  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(unsigned((ntiles + 3) / 4)), dim3(kAttnThreads), 0, st,
+                     static_cast<const uint16_t*>(o), dp, sidx, M, ktop, S, D, tile_lo, tile_hi, ntiles);
+  if (dq_start) (void)hipEventRecord(dq_start, st);
+  hipLaunchKernelGGL(attn_dq_kernel, dim3(unsigned((M + kAttnRows - 1) / kAttnRows)), dim3(kAttnThreads), 0, st, qp,
+                     kp, vp, sidx, M, T, ktop, S, lse, D, dp, static_cast<uint16_t*>(dq));
+  if (dq_stop) (void)hipEventRecord(dq_stop, st);
+  const int QS = attn_query_splits(T);
+  if (dkv_start) (void)hipEventRecord(dkv_start, st);
+  hipLaunchKernelGGL(attn_dkv_kernel, dim3(unsigned((T + kAttnRows - 1) / kAttnRows), unsigned(QS)),
+                     dim3(kAttnThreads), 0, st, qp, kp, vp, sidx, M, T, ktop, S, lse, D, dp, tile_lo, tile_hi, ntiles,
+                     QS, pdk, pdv);
+  if (dkv_stop) (void)hipEventRecord(dkv_stop, st);
+  const int64_t n = T * kHD;
+  hipLaunchKernelGGL(attn_dkv_reduce_kernel, dim3(unsigned(std::min<int64_t>((n / 4 + kAttnThreads - 1) / kAttnThreads, 4096))),
+                     dim3(kAttnThreads), 0, st, pdk, pdv, QS, n, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
+  return hipGetLastError();
+}
+
+}  // namespace smoe

@@ -127,6 +127,18 @@ hipError_t launch_gate_dx(const void* wg, int64_t T, int d, int E, int k, int bf
                           int* offsets, hipStream_t st);
 hipError_t launch_gate_dw_finish(const float* tmp, int d, int E, int bf16, float* dw, hipStream_t st);
 
+// Mixture-of-Attention core (attn.hip), bf16, head_dim 128: o and lse of
+// grouped query rows against shared K/V, causal within sequences of S.
+hipError_t launch_attn_fwd(const void* q, const void* kk, const void* v, const int* sidx, int64_t M, int64_t T,
+                           int ktop, int64_t S, void* o, float* lse, hipStream_t st);
+// backward: D [M], per-32-row query tile ranges [ceil(M/32)] x 2, and fp32
+// dK/dV partials [attn_query_splits(T)][T][128] each
+int attn_query_splits(int64_t T);
+hipError_t launch_attn_bwd(const void* q, const void* kk, const void* v, const int* sidx, int64_t M, int64_t T,
+                           int ktop, int64_t S, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, float* D, int* tile_lo, int* tile_hi, float* pdk, float* pdv, hipStream_t st,
+                           hipEvent_t dq_start, hipEvent_t dq_stop, hipEvent_t dkv_start, hipEvent_t dkv_stop);
+
 // Matrix-core rate probe (probe.hip): blocks x 256 threads, each wave
 // iters rounds of 16 bf16 32x32x16 multiplies on registers.
 hipError_t launch_mfma_loop(float* out, int blocks, int iters, hipStream_t st);

@@ -1,0 +1,101 @@
+"""smoe_moa_attention_fwd and _bwd on the GPU against the oracle: grouped
+query rows of several expert heads against shared K/V, causal within each
+sequence.  bf16 inputs; o, dq, dk, dv are stored in bf16 and held to 2e-2
+of their RMS beyond that final rounding; lse (fp32, from exact bf16
+products summed in fp32) to 1e-3 absolute.  The routing arrays are the
+oracle's.  The backward is given the oracle's forward (o rounded to bf16,
+as the forward stores it, and lse); D_r = do_r . o_r comes from that stored
+o on both sides."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import BF16_TOL, dev_tensor, host, rel_err, rel_err_stored_bf16, say
+from workloads import make_moa_attention
+
+pytestmark = pytest.mark.gpu
+
+
+def setup(B, S, E, k, cid, hd=128):
+    w = make_moa_attention(B, S, hd, E, k, "bf16", cid)
+    sidx = oracle.route(w.tensors["expert_idxs"], E)["sorted_scattered_idxs"].astype(np.int32)
+    f = {n: w.f32(n).astype(np.float64) for n in ("q", "k", "v", "do")}
+    d = {n: dev_tensor(w.tensors[n]) for n in ("q", "k", "v", "do")}
+    d["sidx"] = torch.from_numpy(sidx).cuda()
+    return w, sidx, f, d
+
+
+def check_fwd(smoe, w, sidx, f, d, rows=None):
+    S = w.dims["seq_len"]
+    o, lse = smoe.smoe_moa_attention_fwd(d["q"], d["k"], d["v"], d["sidx"], w.k, S)
+    torch.cuda.synchronize()
+    rows = np.arange(sidx.shape[0]) if rows is None else rows
+    ref = oracle.moa_attention_fwd(f["q"][rows], f["k"], f["v"], sidx[rows], w.k, S)
+    e = rel_err_stored_bf16(host(o)[rows], ref["o"])
+    el = float(np.abs(host(lse)[rows] - ref["lse"]).max())
+    say(f"  o err {e:.2e}  lse max abs err {el:.2e}")
+    assert e <= BF16_TOL
+    assert el <= 1e-3
+    return o, lse
+
+
+@pytest.mark.parametrize("shape", [(2, 100, 4, 2), (3, 64, 1, 1), (1, 333, 6, 3)])
+def test_attention_fwd_ragged(smoe, shape):
+    B, S, E, k = shape
+    say(f"moa attention fwd B={B} S={S} E={E} k={k}")
+    w, sidx, f, d = setup(B, S, E, k, 400 + S)
+    check_fwd(smoe, w, sidx, f, d)
+
+
+def test_attention_fwd_full_size(smoe):
+    """The MoA workload's shape: 2 sequences of 4096, 16 heads of 128, k=4;
+    2048 sampled rows (rows are independent in the forward) and every row's
+    lse."""
+    say("moa attention fwd full size")
+    w, sidx, f, d = setup(2, 4096, 16, 4, 410)
+    rows = np.sort(np.random.default_rng(3).choice(sidx.shape[0], 2048, replace=False))
+    o1, l1 = check_fwd(smoe, w, sidx, f, d, rows)
+    o2, l2 = smoe.smoe_moa_attention_fwd(d["q"], d["k"], d["v"], d["sidx"], w.k, 4096)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def bf16_dev(a: np.ndarray) -> torch.Tensor:
+    """fp64 values -> bf16 tensor on the GPU (round to nearest even)."""
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).cuda()
+
+
+def check_bwd(smoe, w, sidx, f, d):
+    """The GPU backward from the oracle's forward (o rounded to bf16, lse)."""
+    S = w.dims["seq_len"]
+    ref = oracle.moa_attention_fwd(f["q"], f["k"], f["v"], sidx, w.k, S)
+    o = bf16_dev(ref["o"])
+    # D_r = do_r . o_r from the output as stored (bf16), as the GPU reads it
+    rb = oracle.moa_attention_bwd(f["q"], f["k"], f["v"], sidx, w.k, S, f["do"], o=host(o))
+    lse = torch.from_numpy(ref["lse"].astype(np.float32)).cuda()
+    dq, dk, dv = smoe.smoe_moa_attention_bwd(d["q"], d["k"], d["v"], d["sidx"], w.k, S, o, lse, d["do"])
+    torch.cuda.synchronize()
+    for n, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        e = rel_err_stored_bf16(host(got), rb[n])
+        say(f"  {n} err {e:.2e}")
+        assert e <= BF16_TOL, n
+    return dq, dk, dv, o, lse
+
+
+@pytest.mark.parametrize("shape", [(2, 100, 4, 2), (3, 64, 1, 1), (1, 333, 6, 3)])
+def test_attention_bwd_ragged(smoe, shape):
+    B, S, E, k = shape
+    say(f"moa attention bwd B={B} S={S} E={E} k={k}")
+    w, sidx, f, d = setup(B, S, E, k, 420 + S)
+    check_bwd(smoe, w, sidx, f, d)
+
+
+def test_attention_bwd_full_size(smoe):
+    """The MoA workload's shape, every row; two runs bitwise equal."""
+    say("moa attention bwd full size")
+    w, sidx, f, d = setup(2, 4096, 16, 4, 430)
+    dq, dk, dv, o, lse = check_bwd(smoe, w, sidx, f, d)
+    dq2, dk2, dv2 = smoe.smoe_moa_attention_bwd(d["q"], d["k"], d["v"], d["sidx"], w.k, 4096, o, lse, d["do"])
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)

@@ -27,7 +27,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "CONFIGS", "Workload", "bf16_bits", "bf16_bits_to_f32", "make_config", "make_router",
+    "CONFIGS", "Workload", "bf16_bits", "bf16_bits_to_f32", "make_config", "make_router", "make_moa_attention",
     "make_mlp", "make_pl", "make_moa", "topk_softmax_routing",
     "uniform_distinct_routing", "zipf_routing",
 ]
@@ -250,6 +250,24 @@ def make_router(T, d, E, k, dtype, cid, x_std=1.0) -> Workload:
     t["dx_in"] = _normal((T, d), 1.0, (cid, 3), dtype)
     return Workload(f"router{cid}", "router", dtype, T, E, k,
                     {"d_model": d}, None, t)
+
+
+def make_moa_attention(B, S, hd, E, k, dtype, cid) -> Workload:
+    """Mixture-of-Attention core workload: B sequences of S tokens; grouped
+    queries q [T*k, hd] ~ N(0,1) (the Q projection's grouped output), shared
+    keys and values [T, hd] ~ N(0,1) (dense, as the MoA workload gives
+    them), top-k softmax routing over N(0,1) logits [T, E], upstream do
+    [T*k, hd] ~ N(0,1)."""
+    T = B * S
+    t: Dict[str, np.ndarray] = {}
+    t["q"] = _normal((T * k, hd), 1.0, (cid, 0), dtype)
+    t["k"] = _normal((T, hd), 1.0, (cid, 1), dtype)
+    t["v"] = _normal((T, hd), 1.0, (cid, 2), dtype)
+    logits = _rng(cid, 3).standard_normal((T, E), dtype=np.float32)
+    t["expert_idxs"], t["gates"] = topk_softmax_routing(logits, k)
+    t["do"] = _normal((T * k, hd), 1.0, (cid, 4), dtype)
+    return Workload(f"moa_attn{cid}", "moa_attn", dtype, T, E, k,
+                    {"seq_len": S, "head_dim": hd, "batch": B}, None, t)
 
 
 def make_config(cid: int) -> Workload:
