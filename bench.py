@@ -172,11 +172,12 @@ def parse():
                     help="also run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl", "router"],
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl", "router", "attention"],
                     help="mixtral (the measured line); the others print supplementary lines: "
                          "granular = high-granularity Zipf SMoE-MLP, moa = Mixture-of-Attention "
                          "projections, pl = single ParallelLinear in its four layouts, router = the "
-                         "top-k softmax router forward and backward at the three workloads' shapes")
+                         "top-k softmax router forward and backward at the three workloads' shapes, "
+                         "attention = the Mixture-of-Attention core at the MoA workload's shape")
     return ap.parse_args()
 
 
@@ -363,6 +364,8 @@ def supplementary(args):
     steps, warmup = args.steps, args.warmup
     if args.workload == "router":
         return router_lines(args)
+    if args.workload == "attention":
+        return attention_line(args)
     if args.workload == "granular":
         w = make_config(4)
         T, k, E = w.T, w.k, w.E
@@ -477,6 +480,50 @@ def router_lines(args):
             "config": {"workload": "top-k softmax router, bf16: logits x w^T, top-k, softmax; backward dx, dw; "
                                    "value at T=16384, d_model=4096, E=8, k=2"},
             "peak_GBps": 8000.0, "shapes": out}
+
+
+def attention_line(args):
+    """Mixture-of-Attention core, forward and backward, at the MoA workload's
+    shape (2 sequences of 4096 tokens, 16 head experts of 128, k = 4, bf16).
+    Algorithmic FLOP over the causal pairs (row r, key t'), n pairs in all:
+    forward 4 * hd * n (q k^T and p v), backward 10 * hd * n (scores again,
+    dp, dq, dk, dv)."""
+    import torch
+    import sparse_mixture_experts_top_amd as smoe
+    from workloads import make_moa_attention
+    steps, warmup = args.steps, args.warmup
+    B, S, hd, E, k = 2, 4096, 128, 16, 4
+    w = make_moa_attention(B, S, hd, E, k, "bf16", 950)
+    t = {n: _dev(w.tensors[n]) for n in ("q", "k", "v", "do")}
+    rt = smoe.smoe_route(_dev(w.tensors["expert_idxs"]), E)
+    sidx = rt["sorted_scattered_idxs"]
+    pairs = k * B * S * (S + 1) // 2
+    fl_f, fl_b = 4.0 * hd * pairs, 10.0 * hd * pairs
+    o, lse = smoe.smoe_moa_attention_fwd(t["q"], t["k"], t["v"], sidx, k, S)
+    fwd_ms = _event_ms(lambda: smoe.smoe_moa_attention_fwd(t["q"], t["k"], t["v"], sidx, k, S), steps, warmup)
+    bwd_ms = _event_ms(lambda: smoe.smoe_moa_attention_bwd(t["q"], t["k"], t["v"], sidx, k, S, o, lse, t["do"]),
+                       steps, warmup)
+    roles = ["attn_fwd", "attn_dq", "attn_dkv"]
+    evs = {r: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for r in roles}
+    for r in roles:
+        smoe.smoe_set_role_events(r, *evs[r])
+    smoe.smoe_moa_attention_fwd(t["q"], t["k"], t["v"], sidx, k, S)
+    smoe.smoe_moa_attention_bwd(t["q"], t["k"], t["v"], sidx, k, S, o, lse, t["do"])
+    torch.cuda.synchronize()
+    for r in roles:
+        smoe.smoe_set_role_events(r, None, None)
+    kms = {r: evs[r][0].elapsed_time(evs[r][1]) for r in roles}
+    tf = (fl_f + fl_b) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+    fwd_tf = fl_f / (kms["attn_fwd"] * 1e-3) / 1e12
+    return {"metric": "MoA attention core fwd+bwd TFLOP/s (supplementary), 1 MI355X", "value": tf,
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "Mixture-of-Attention core: 2 sequences x 4096 tokens, 16 head experts of 128, "
+                                   "k=4, grouped queries against shared K/V, causal, bf16"},
+            "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "fwd_tflops": fl_f / (fwd_ms * 1e-3) / 1e12,
+            "bwd_tflops": fl_b / (bwd_ms * 1e-3) / 1e12, "kernels_ms_last_launch": kms,
+            "roofline": {"bound": "mfma", "kernel": "attn_fwd", "achieved": fwd_tf, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": fwd_tf / PEAK_BF16_TFLOPS, "traffic": None,
+                         "flop_per_launch": fl_f, "avg_launch_ms": kms["attn_fwd"]}}
 
 
 if __name__ == "__main__":
