@@ -138,33 +138,52 @@ SMOE_DEV void block_range(int lo, int t, int* red, int& blo, int& bhi) {
 }
 
 // ---- forward ---------------------------------------------------------------
-// Block: 128 query rows, wave w owns rows 32w .. 32w+31 (lane: row lane & 31).
-// Key blocks of 32 run from the block's lowest sequence start to its highest
-// token; K and V tiles are shared through LDS, the next pair loading into
-// registers while the current one is used.  Online softmax in base 2.
-__global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(const uint16_t* __restrict__ q,
-                                                                const uint16_t* __restrict__ kk,
-                                                                const uint16_t* __restrict__ v,
-                                                                const int* __restrict__ sidx, int64_t M, int64_t T,
-                                                                int ktop, int64_t S, uint16_t* __restrict__ o,
-                                                                float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) char ks[kKB * kRowB];
-  __shared__ __attribute__((aligned(16))) char vs[kKB * kRowB];
-  __shared__ int red[2 * kAttnThreads / kWave];
+// Block: 128 query rows and 8 waves, wave w = (row tile w & 3, key half
+// w >> 2); lane: row lane & 31 of its tile.  Per step of 64 keys the block
+// stages two 32-key K and V tiles in LDS and each wave takes the tile of its
+// half, so K and V cross from L2 once per 128 rows.  Each wave keeps its own
+// online-softmax state (base 2); at the end the second half's state goes
+// through LDS to the first: O = (2^(m0-M) O0 + 2^(m1-M) O1) / (2^(m0-M) l0 +
+// 2^(m1-M) l1).
+constexpr int kFwdThreads = 512;
+constexpr int kFwdWaves = kFwdThreads / kWave;
+constexpr int kFwdRows = 128;
+constexpr int kStepKeys = 2 * kKB;   // keys staged per step
+__global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ kk,
+                                                               const uint16_t* __restrict__ v,
+                                                               const int* __restrict__ sidx, int64_t M, int64_t T,
+                                                               int ktop, int64_t S, uint16_t* __restrict__ o,
+                                                               float* __restrict__ lse) {
+  // staging: K tiles [2][32 rows], V tiles [2][32 rows]; merge: the second
+  // half's O as [row tile][16 float4 slots][64 lanes]
+  __shared__ __attribute__((aligned(16))) char smem[4 * 16 * kWave * 16];
+  __shared__ float st_m[4][kWave], st_l[4][kWave];
+  __shared__ int red[2 * kFwdWaves];
   const int lane = lane_id(), h = lane >> 5;
   const int w = threadIdx.x / kWave;
-  const int64_t r = int64_t(blockIdx.x) * kAttnRows + 32 * w + (lane & 31);
+  const int rt = w & 3, kh = w >> 2;
+  const int64_t r = int64_t(blockIdx.x) * kFwdRows + 32 * rt + (lane & 31);
   const bool real = r < M;
   const int t = real ? sidx[r] / ktop : -1;
   const int lo = real ? int(int64_t(t) / S * S) : 0x7fffffff;
-  int blo, bhi;
-  block_range(lo, t, red, blo, bhi);
-  // this wave's own range
+  // block and row-tile ranges
   int wlo = lo, whi = t;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     wlo = min(wlo, __shfl_xor(wlo, off, kWave));
     whi = max(whi, __shfl_xor(whi, off, kWave));
+  }
+  if (lane == 0) {
+    red[2 * w] = wlo;
+    red[2 * w + 1] = whi;
+  }
+  __syncthreads();
+  int blo = red[0], bhi = red[1];
+#pragma unroll
+  for (int i = 1; i < kFwdWaves; ++i) {
+    blo = min(blo, red[2 * i]);
+    bhi = max(bhi, red[2 * i + 1]);
   }
   if (bhi < 0) return;   // no real rows (uniform over the block)
 
@@ -182,28 +201,49 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(const uint16_t* 
     for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf(float(kHD));   // scale * log2(e)
   float m2 = -INFINITY, l = 0.f;
+  char* ktiles = smem;
+  char* vtiles = smem + kStepKeys * kRowB;
+  const char* ks = ktiles + kh * kKB * kRowB;
+  const char* vs = vtiles + kh * kKB * kRowB;
+  const int krow = key_perm(lane & 31);
 
-  const int kb_first = blo / kKB * kKB;
-  TileRegs kr, vr;
-  tile_load(kr, kk, kb_first, T);
-  tile_load(vr, v, kb_first, T);
-  for (int kb0 = kb_first; kb0 <= bhi; kb0 += kKB) {
-    __syncthreads();
-    tile_store<false>(kr, ks);
-    tile_store<true>(vr, vs);
-    __syncthreads();
-    if (kb0 + kKB <= bhi) {
-      tile_load(kr, kk, kb0 + kKB, T);
-      tile_load(vr, v, kb0 + kKB, T);
+  // 64 keys of K and V per step, two 16-byte pieces of each per thread,
+  // loaded one step ahead into registers
+  uint4 kv[2], vv[2];
+  auto step_load = [&](int sb) SMOE_INL {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = threadIdx.x + u * kFwdThreads;   // 0 .. 1023: 64 rows x 16 chunks
+      const int64_t g = int64_t(sb) + (i >> 4);
+      const bool ok = g < T;
+      kv[u] = ok ? *reinterpret_cast<const uint4*>(kk + g * kHD + (i & 15) * 8) : make_uint4(0u, 0u, 0u, 0u);
+      vv[u] = ok ? *reinterpret_cast<const uint4*>(v + g * kHD + (i & 15) * 8) : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (kb0 > whi || kb0 + kKB <= wlo) continue;   // nothing for this wave
-    // scores for keys kb0 + pi(c)
-    at_f32x16_t sc;
+  };
+  step_load(blo / kKB * kKB);
+  for (int sb0 = blo / kKB * kKB; sb0 <= bhi; sb0 += kStepKeys) {
+    __syncthreads();
+    // K in the row-read layout, V in the transposing layout
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-    const int krow = key_perm(lane & 31);
+    for (int u = 0; u < 2; ++u) {
+      const int i = threadIdx.x + u * kFwdThreads;
+      const int row = i >> 4, c = i & 15, tr = row & 31;
+      *reinterpret_cast<uint4*>(ktiles + row * kRowB + ((c ^ swz_row(tr)) << 4)) = kv[u];
+      *reinterpret_cast<uint4*>(vtiles + row * kRowB + ((c ^ swz_tr(tr)) << 4)) = vv[u];
+    }
+    __syncthreads();
+    if (sb0 + kStepKeys <= bhi) step_load(sb0 + kStepKeys);
+    const int kb0 = sb0 + kKB * kh;
+    if (kb0 > whi || kb0 + kKB <= wlo) continue;   // nothing for this wave (uniform)
+    // scores for keys kb0 + pi(c), two accumulation chains
+    at_f32x16_t sa, sb;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s, h), qf[s], sc, 0, 0, 0);
+    for (int i = 0; i < 16; ++i) sa[i] = sb[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s, h), qf[s], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s + 1, h), qf[s + 1], sb, 0, 0, 0);
+    }
     float z[16];
     float bm = -INFINITY;
 #pragma unroll
@@ -212,17 +252,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(const uint16_t* 
       for (int i = 0; i < 4; ++i) {
         const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
         const bool ok = key >= lo && key <= t;
-        const float zz = ok ? sc[4 * q4 + i] * sl2 : -INFINITY;
+        const float zz = ok ? (sa[4 * q4 + i] + sb[4 * q4 + i]) * sl2 : -INFINITY;
         z[4 * q4 + i] = zz;
         bm = fmaxf(bm, zz);
       }
     bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+    // a row with no key so far keeps m = -inf, l = 0 and a zero O
     const float mn = fmaxf(m2, bm);
-    const float alpha = mn == -INFINITY ? 1.f : exp2f(m2 - mn);
+    const bool none = mn == -INFINITY;
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
     float p[16], ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p[i] = mn == -INFINITY ? 0.f : exp2f(z[i] - mn);
+      p[i] = none ? 0.f : __builtin_amdgcn_exp2f(z[i] - mn);
       ps += p[i];
     }
     ps += __shfl_xor(ps, 32, kWave);
@@ -239,30 +281,50 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(const uint16_t* 
     for (int nt = 0; nt < 4; ++nt) {
       const at_bf16x8_t v0 = tr_frag(vs, 32 * nt, 0, lane), v1 = tr_frag(vs, 32 * nt, 1, lane);
       acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0h, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0l, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1h, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0l, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1l, acc[nt], 0, 0, 0);
     }
   }
-  if (!real) return;
-  const float inv = 1.f / l;
+  // the second key half hands its state to the first
+  __syncthreads();
+  float4* slots = reinterpret_cast<float4*>(smem) + rt * 16 * kWave;
+  if (kh == 1) {
+    st_m[rt][lane] = m2;
+    st_l[rt][lane] = l;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        slots[(4 * nt + q4) * kWave + lane] =
+            make_float4(acc[nt][4 * q4], acc[nt][4 * q4 + 1], acc[nt][4 * q4 + 2], acc[nt][4 * q4 + 3]);
+  }
+  __syncthreads();
+  if (kh == 1 || !real) return;
+  const float m1 = st_m[rt][lane], l1 = st_l[rt][lane];
+  const float mx = fmaxf(m2, m1);
+  const float f0 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mx);
+  const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+  const float L = f0 * l + f1 * l1;
+  const float inv = 1.f / L;
   uint16_t* orow = o + r * kHD;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float vals[4] = {acc[nt][4 * q4] * inv, acc[nt][4 * q4 + 1] * inv, acc[nt][4 * q4 + 2] * inv,
-                             acc[nt][4 * q4 + 3] * inv};
+      const float4 x = slots[(4 * nt + q4) * kWave + lane];
+      const float vals[4] = {(f0 * acc[nt][4 * q4] + f1 * x.x) * inv, (f0 * acc[nt][4 * q4 + 1] + f1 * x.y) * inv,
+                             (f0 * acc[nt][4 * q4 + 2] + f1 * x.z) * inv, (f0 * acc[nt][4 * q4 + 3] + f1 * x.w) * inv};
       *reinterpret_cast<uint2*>(orow + 32 * nt + 8 * q4 + 4 * h) = pack4_bf16(vals);
     }
-  if (h == 0) lse[r] = m2 * 0.69314718055994531f + logf(l);
+  if (h == 0) lse[r] = mx * 0.69314718055994531f + logf(L);
 }
 
 hipError_t launch_attn_fwd(const void* q, const void* kk, const void* v, const int* sidx, int64_t M, int64_t T,
                            int ktop, int64_t S, void* o, float* lse, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const unsigned grid = unsigned((M + kAttnRows - 1) / kAttnRows);
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(grid), dim3(kAttnThreads), 0, st, static_cast<const uint16_t*>(q),
+  const unsigned grid = unsigned((M + kFwdRows - 1) / kFwdRows);
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(grid), dim3(kFwdThreads), 0, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(kk), static_cast<const uint16_t*>(v), sidx, M, T, ktop, S,
                      static_cast<uint16_t*>(o), lse);
   return hipGetLastError();
