@@ -99,3 +99,49 @@ def test_attention_bwd_full_size(smoe):
     dq2, dk2, dv2 = smoe.smoe_moa_attention_bwd(d["q"], d["k"], d["v"], d["sidx"], w.k, 4096, o, lse, d["do"])
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+def test_moa_layer_chain(smoe):
+    """A whole Mixture-of-Attention layer on the GPU: Q projection
+    (scattered-in, grouped-out) -> attention core -> O projection (grouped-in,
+    scattered-out, combined with the gates), then the backward through all
+    three.  The oracle runs the same chain, rounding to bf16 where the GPU
+    stores bf16 (q, o, d o, dq)."""
+    from workloads import make_moa_layer
+    B, S, d, hd, E, k = 2, 96, 256, 128, 4, 2
+    say(f"MoA layer chain B={B} S={S} d={d} E={E} k={k}")
+    w = make_moa_layer(B, S, d, hd, E, k, "bf16", 440, w_std=0.06)
+    T = w.T
+    f = {n: w.f32(n).astype(np.float64) for n in ("x", "wq", "wo", "k", "v", "dout")}
+    idx, gates = w.tensors["expert_idxs"], w.tensors["gates"].astype(np.float64)
+    sidx = oracle.route(idx, E)["sorted_scattered_idxs"]
+    bf = oracle.bf16_round
+    qg = bf(oracle.parallel_linear_fwd(f["x"], f["wq"], idx, False, True))
+    att = oracle.moa_attention_fwd(qg, f["k"], f["v"], sidx, k, S)
+    og = bf(att["o"])
+    ref_out = oracle.parallel_linear_fwd(og, f["wo"], idx, True, False, gates=gates)
+    d_og, ref_dwo, ref_dg = oracle.parallel_linear_bwd(og, f["wo"], idx, True, False, f["dout"], gates=gates,
+                                                       storage="bf16")
+    d_og = bf(d_og)
+    ab = oracle.moa_attention_bwd(qg, f["k"], f["v"], sidx, k, S, d_og, o=og)
+    ref_dx, ref_dwq, _ = oracle.parallel_linear_bwd(f["x"], f["wq"], idx, False, True, bf(ab["dq"]),
+                                                    storage="bf16")
+
+    dd = {n: dev_tensor(w.tensors[n]) for n in ("x", "wq", "wo", "k", "v", "dout", "expert_idxs", "gates")}
+    rt = smoe.smoe_route(dd["expert_idxs"], E)
+    s, off = rt["sorted_scattered_idxs"], rt["offsets"]
+    q = smoe.smoe_parallel_linear_fwd(dd["x"], dd["wq"], T, k, s, off, False, True)
+    o, lse = smoe.smoe_moa_attention_fwd(q, dd["k"], dd["v"], s, k, S)
+    out = smoe.smoe_parallel_linear_fwd(o, dd["wo"], T, k, s, off, True, False, dd["gates"])
+    do, dwo, dg = smoe.smoe_parallel_linear_bwd(o, dd["wo"], T, k, s, off, True, False, dd["dout"], dd["gates"],
+                                                need_dgates=True)
+    dq, dk, dv = smoe.smoe_moa_attention_bwd(q, dd["k"], dd["v"], s, k, S, o, lse, do)
+    dx, dwq, _ = smoe.smoe_parallel_linear_bwd(dd["x"], dd["wq"], T, k, s, off, False, True, dq)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s.cpu().numpy(), sidx)
+    for n, got, want, stored in (("out", out, ref_out, True), ("dx", dx, ref_dx, True), ("dk", dk, ab["dk"], True),
+                                 ("dv", dv, ab["dv"], True), ("dwq", dwq, ref_dwq, False),
+                                 ("dwo", dwo, ref_dwo, False), ("dgates", dg, ref_dg, False)):
+        e = rel_err_stored_bf16(host(got), want) if stored else rel_err(host(got), want)
+        say(f"  {n} err {e:.2e}")
+        assert e <= BF16_TOL, n

@@ -27,7 +27,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "CONFIGS", "Workload", "bf16_bits", "bf16_bits_to_f32", "make_config", "make_router", "make_moa_attention",
+    "CONFIGS", "Workload", "bf16_bits", "bf16_bits_to_f32", "make_config", "make_router", "make_moa_attention", "make_moa_layer",
     "make_mlp", "make_pl", "make_moa", "topk_softmax_routing",
     "uniform_distinct_routing", "zipf_routing",
 ]
@@ -268,6 +268,25 @@ def make_moa_attention(B, S, hd, E, k, dtype, cid) -> Workload:
     t["do"] = _normal((T * k, hd), 1.0, (cid, 4), dtype)
     return Workload(f"moa_attn{cid}", "moa_attn", dtype, T, E, k,
                     {"seq_len": S, "head_dim": hd, "batch": B}, None, t)
+
+
+def make_moa_layer(B, S, d, hd, E, k, dtype, cid, w_std=0.02) -> Workload:
+    """A whole Mixture-of-Attention layer: x [T, d] ~ N(0,1); per-head-expert
+    Wq [E, d, hd] and Wo [E, hd, d] ~ N(0, w_std^2); shared keys and values
+    [T, hd] ~ N(0,1); top-k softmax routing over N(0,1) logits; upstream
+    dout [T, d] ~ N(0,1).  T = B * S."""
+    T = B * S
+    t: Dict[str, np.ndarray] = {}
+    t["x"] = _normal((T, d), 1.0, (cid, 0), dtype)
+    t["wq"] = _normal((E, d, hd), w_std, (cid, 1), dtype)
+    t["wo"] = _normal((E, hd, d), w_std, (cid, 2), dtype)
+    t["k"] = _normal((T, hd), 1.0, (cid, 3), dtype)
+    t["v"] = _normal((T, hd), 1.0, (cid, 4), dtype)
+    logits = _rng(cid, 5).standard_normal((T, E), dtype=np.float32)
+    t["expert_idxs"], t["gates"] = topk_softmax_routing(logits, k)
+    t["dout"] = _normal((T, d), 1.0, (cid, 6), dtype)
+    return Workload(f"moa_layer{cid}", "moa_layer", dtype, T, E, k,
+                    {"seq_len": S, "batch": B, "d_model": d, "head_dim": hd}, None, t)
 
 
 def make_config(cid: int) -> Workload:
