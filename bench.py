@@ -515,12 +515,34 @@ def attention_line(args):
     kms = {r: evs[r][0].elapsed_time(evs[r][1]) for r in roles}
     tf = (fl_f + fl_b) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
     fwd_tf = fl_f / (kms["attn_fwd"] * 1e-3) / 1e12
+    # the whole layer: Q projection -> attention -> O projection with the
+    # combine, forward and backward (2048-wide model, as the MoA workload)
+    from workloads import make_moa_layer
+    lw = make_moa_layer(B, S, 2048, hd, E, k, "bf16", 951)
+    L = {n: _dev(lw.tensors[n]) for n in ("x", "wq", "wo", "k", "v", "dout", "expert_idxs", "gates")}
+    T = lw.T
+
+    def layer():
+        rt2 = smoe.smoe_route(L["expert_idxs"], E)
+        s2, off2 = rt2["sorted_scattered_idxs"], rt2["offsets"]
+        qg = smoe.smoe_parallel_linear_fwd(L["x"], L["wq"], T, k, s2, off2, False, True)
+        og, lse2 = smoe.smoe_moa_attention_fwd(qg, L["k"], L["v"], s2, k, S)
+        smoe.smoe_parallel_linear_fwd(og, L["wo"], T, k, s2, off2, True, False, L["gates"])
+        dog, _, _ = smoe.smoe_parallel_linear_bwd(og, L["wo"], T, k, s2, off2, True, False, L["dout"], L["gates"],
+                                                  need_dgates=True)
+        dqg, _, _ = smoe.smoe_moa_attention_bwd(qg, L["k"], L["v"], s2, k, S, og, lse2, dog)
+        smoe.smoe_parallel_linear_bwd(L["x"], L["wq"], T, k, s2, off2, False, True, dqg)
+
+    layer_ms = _event_ms(layer, steps, warmup)
     return {"metric": "MoA attention core fwd+bwd TFLOP/s (supplementary), 1 MI355X", "value": tf,
             "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "Mixture-of-Attention core: 2 sequences x 4096 tokens, 16 head experts of 128, "
                                    "k=4, grouped queries against shared K/V, causal, bf16"},
             "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "fwd_tflops": fl_f / (fwd_ms * 1e-3) / 1e12,
             "bwd_tflops": fl_b / (bwd_ms * 1e-3) / 1e12, "kernels_ms_last_launch": kms,
+            "moa_layer": {"ms_per_step": layer_ms, "tokens_per_s": T / (layer_ms * 1e-3),
+                          "what": "route + Q projection + attention core + O projection with the combine, "
+                                  "forward and backward, d_model=2048"},
             "roofline": {"bound": "mfma", "kernel": "attn_fwd", "achieved": fwd_tf, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": fwd_tf / PEAK_BF16_TFLOPS, "traffic": None,
                          "flop_per_launch": fl_f, "avg_launch_ms": kms["attn_fwd"]}}
