@@ -172,12 +172,14 @@ def parse():
                     help="also run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl", "router", "attention"],
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl", "router", "attention", "sparsity"],
                     help="mixtral (the measured line); the others print supplementary lines: "
                          "granular = high-granularity Zipf SMoE-MLP, moa = Mixture-of-Attention "
                          "projections, pl = single ParallelLinear in its four layouts, router = the "
                          "top-k softmax router forward and backward at the three workloads' shapes, "
-                         "attention = the Mixture-of-Attention core at the MoA workload's shape")
+                         "attention = the Mixture-of-Attention core at the MoA workload's shape, "
+                         "sparsity = SMoE-MLP at fixed E with k swept, each beside a dense MLP of the same "
+                         "active FLOPs, and the memory footprint of the Mixtral-shaped step")
     return ap.parse_args()
 
 
@@ -366,6 +368,8 @@ def supplementary(args):
         return router_lines(args)
     if args.workload == "attention":
         return attention_line(args)
+    if args.workload == "sparsity":
+        return sparsity_line(args)
     if args.workload == "granular":
         w = make_config(4)
         T, k, E = w.T, w.k, w.E
@@ -480,6 +484,53 @@ def router_lines(args):
             "config": {"workload": "top-k softmax router, bf16: logits x w^T, top-k, softmax; backward dx, dw; "
                                    "value at T=16384, d_model=4096, E=8, k=2"},
             "peak_GBps": 8000.0, "shapes": out}
+
+
+def sparsity_line(args):
+    """SMoE-MLP fwd+bwd at fixed E = 16 (T=16384, d_model=1024, d_ff=1024 per
+    expert, GELU, bf16) with k = 1, 2, 4, 8, 16, each timed beside a dense
+    MLP of the same active FLOPs (this library's own path with E = 1, k = 1
+    and d_ff * k hidden units).  Also the memory footprint of the
+    Mixtral-shaped step from the library's size functions, beside the
+    grouped input copy a copy-based design would add."""
+    import sparse_mixture_experts_top_amd as smoe
+    from workloads import make_mlp
+    steps, warmup = args.steps, args.warmup
+    T, d, f, E = 16384, 1024, 1024, 16
+    pts = []
+    for k in (1, 2, 4, 8, 16):
+        row = {"k": k}
+        for kind, (EE, kk, ff) in (("smoe", (E, k, f)), ("dense", (1, 1, f * k))):
+            w = make_mlp(T, d, ff, EE, kk, "gelu", "bf16", 960 + 2 * k + (kind == "dense"), routing="softmax",
+                         w_std=0.02)
+            t = {n: _dev(w.tensors[n]) for n in ("x", "w1", "w2", "expert_idxs", "gates", "dout")}
+
+            def step():
+                out, saved = smoe.smoe_mlp_fwd(t["x"], t["w1"], t["w2"], t["expert_idxs"], t["gates"], "gelu")
+                smoe.smoe_mlp_bwd(t["dout"], t["x"], t["w1"], t["w2"], t["expert_idxs"], t["gates"], "gelu", saved)
+
+            ms = _event_ms(step, steps, warmup)
+            fl = sum(gemm_flops(T, kk, d, ff, "gelu").values())
+            row[kind] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3), "tflops": fl / (ms * 1e-3) / 1e12}
+            del t, w
+        row["smoe_over_dense"] = row["dense"]["ms"] / row["smoe"]["ms"]
+        pts.append(row)
+    # memory footprint of the Mixtral-shaped step (bytes)
+    Tm, km, Em, dm, fm = 16384, 2, 8, 4096, 14336
+    a, bf = smoe.ACT_SWIGLU, smoe.BF16
+    mem = {"saved": smoe.lib.smoe_mlp_saved_bytes(Tm, km, Em, dm, fm, a, bf),
+           "fwd_workspace": smoe.lib.smoe_mlp_fwd_workspace_bytes(Tm, km, Em, dm, fm, a, bf),
+           "bwd_workspace": smoe.lib.smoe_mlp_bwd_workspace_bytes(Tm, km, Em, dm, fm, a, bf),
+           "grouped_input_copy_avoided": Tm * km * dm * 2,
+           "what": "Mixtral-shaped step; saved holds the routing arrays and h1, h3 (a is recomputed); the "
+                   "scattered-in products read x in place, so no grouped copy of x (T*k*d_model*2 bytes) exists"}
+    best = max(p["smoe_over_dense"] for p in pts)
+    return {"metric": "SMoE-MLP over dense MLP of equal active FLOPs, time ratio (supplementary), 1 MI355X",
+            "value": pts[1]["smoe_over_dense"], "unit": "x (dense ms / SMoE ms at k=2)", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "SMoE-MLP fwd+bwd, T=16384, d_model=1024, d_ff=1024 per expert, E=16, GELU, "
+                                   "k swept 1..16; dense twin E=1, k=1, d_ff=1024*k"},
+            "points": pts, "best_ratio": best, "memory_bytes": mem}
 
 
 def attention_line(args):
