@@ -484,61 +484,76 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const uint16_t* _
     }
 }
 
-// dK, dV: block (128 keys, query split q), wave w owns keys 32w .. 32w+31 of
-// the block (lane: key lane & 31, its K and V rows in registers).  The block
-// walks the query tiles q, q + QS, ... whose key range meets its keys, each
-// tile's q and do rows shared through LDS (the next relevant tile loading
-// into registers meanwhile).  Transposed scores (queries in the pi order)
-// and dp^T give p^T and dz^T in the A operand layout of p^T do and dz^T q.
-// Partial sums per split, fp32: part[q][key][128] (dK, then dV).
-__global__ __launch_bounds__(kAttnThreads) void attn_dkv_kernel(const uint16_t* __restrict__ q,
-                                                                const uint16_t* __restrict__ kk,
-                                                                const uint16_t* __restrict__ v,
-                                                                const int* __restrict__ sidx, int64_t M, int64_t T,
-                                                                int ktop, int64_t S, const float* __restrict__ lse,
-                                                                const float* __restrict__ D,
-                                                                const uint16_t* __restrict__ dout,
-                                                                const int* __restrict__ tile_lo,
-                                                                const int* __restrict__ tile_hi, int64_t ntiles,
-                                                                int QS, float* __restrict__ pdk,
-                                                                float* __restrict__ pdv) {
+// dK, dV: block (128 keys, query split q) of 8 waves, wave w = (key tile
+// w & 3, head-dim half w >> 2); lane: key lane & 31 of its tile, its K and V
+// rows in registers.  The block walks the query tiles q, q + QS, ... whose
+// key range meets its keys, each tile's q and do rows shared through LDS
+// (the next relevant tile loading into registers meanwhile).  Transposed
+// scores (queries in the pi order) and dp^T give p^T and dz^T in the A
+// operand layout of p^T do and dz^T q; each wave forms the columns of its
+// head-dim half.  Partial sums per split, fp32: part[q][key][128].
+constexpr int kDkvThreads = 512;
+__global__ __launch_bounds__(kDkvThreads) void attn_dkv_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ kk,
+                                                               const uint16_t* __restrict__ v,
+                                                               const int* __restrict__ sidx, int64_t M, int64_t T,
+                                                               int ktop, int64_t S, const float* __restrict__ lse,
+                                                               const float* __restrict__ D,
+                                                               const uint16_t* __restrict__ dout,
+                                                               const int* __restrict__ tile_lo,
+                                                               const int* __restrict__ tile_hi, int64_t ntiles,
+                                                               int QS, float* __restrict__ pdk,
+                                                               float* __restrict__ pdv) {
   __shared__ __attribute__((aligned(16))) char qs[32 * kRowB];
   __shared__ __attribute__((aligned(16))) char dos[32 * kRowB];
+  __shared__ __attribute__((aligned(16))) char kall[kAttnRows * kRowB];   // the block's K rows
+  __shared__ __attribute__((aligned(16))) char vall[kAttnRows * kRowB];   // and V rows
   __shared__ int q_lo[32], q_t[32];
   __shared__ float q_lse2[32], q_D[32];
   const int lane = lane_id(), h = lane >> 5;
   const int w = threadIdx.x / kWave;
+  const int kt = w & 3, hh = w >> 2;
   const int64_t k0 = int64_t(blockIdx.x) * kAttnRows;
   const int64_t k1 = min(T, k0 + kAttnRows) - 1;
-  const int64_t kw0 = k0 + 32 * w;
+  const int64_t kw0 = k0 + 32 * kt;
   const int64_t key = kw0 + (lane & 31);
   const int split = blockIdx.y;
   const float l2e = 1.4426950408889634f;
   const float sl2 = l2e / sqrtf(float(kHD));
-  at_bf16x8_t kf[8], vf[8];
-  {
-    const bool ok = key < T;
-    const uint16_t* kr = kk + (ok ? key : 0) * kHD + 8 * h;
-    const uint16_t* vr = v + (ok ? key : 0) * kHD + 8 * h;
+  // the block's 128 K and V rows, row-read layout (rows past T zero)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      uint4 a = ok ? *reinterpret_cast<const uint4*>(kr + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
-      uint4 b = ok ? *reinterpret_cast<const uint4*>(vr + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
-      kf[s] = __builtin_bit_cast(at_bf16x8_t, a);
-      vf[s] = __builtin_bit_cast(at_bf16x8_t, b);
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int i = threadIdx.x + u * kDkvThreads;   // 0 .. 2047: 128 rows x 16 chunks
+    const int row = i >> 4, c = i & 15;
+    const int64_t g = k0 + row;
+    const bool ok = g < T;
+    const int pc = c ^ swz_row(row & 31);
+    *reinterpret_cast<uint4*>(kall + row * kRowB + (pc << 4)) =
+        ok ? *reinterpret_cast<const uint4*>(kk + g * kHD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(vall + row * kRowB + (pc << 4)) =
+        ok ? *reinterpret_cast<const uint4*>(v + g * kHD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
-  at_f32x16_t adk[4], adv[4];
+  const char* kmine = kall + kt * 32 * kRowB;
+  const char* vmine = vall + kt * 32 * kRowB;
+  at_f32x16_t adk[2], adv[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) adk[nt][i] = adv[nt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) adk[n][i] = adv[n][i] = 0.f;
 
   // next query tile at or after i (step QS) whose range meets [k0, k1]
   auto next_tile = [&](int64_t i) -> int64_t {
     for (; i < ntiles; i += QS)
       if (tile_hi[i] >= k0 && tile_lo[i] <= k1) return i;
     return ntiles;
+  };
+  // a query tile's q and do rows: one 16-byte piece of each per thread
+  uint4 qv, dv_;
+  auto piece_load = [&](int64_t i) {
+    const int row = threadIdx.x >> 4, c = threadIdx.x & 15;
+    const int64_t g = i * 32 + row;
+    qv = g < M ? *reinterpret_cast<const uint4*>(q + g * kHD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+    dv_ = g < M ? *reinterpret_cast<const uint4*>(dout + g * kHD + c * 8) : make_uint4(0u, 0u, 0u, 0u);
   };
   // per-row values of a query tile, one row per thread 0..31
   int pr_lo = 0x7fffffff, pr_t = -1;
@@ -560,16 +575,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkv_kernel(const uint16_t* 
     }
   };
   int64_t i = next_tile(split);
-  TileRegs qr, dr;
   if (i < ntiles) {
-    tile_load(qr, q, i * 32, M);
-    tile_load(dr, dout, i * 32, M);
+    piece_load(i);
     row_load(i);
   }
   while (i < ntiles) {
     __syncthreads();
-    tile_store<true>(qr, qs);
-    tile_store<true>(dr, dos);
+    {
+      const int row = threadIdx.x >> 4, c = threadIdx.x & 15;
+      const int pc = c ^ swz_tr(row);
+      *reinterpret_cast<uint4*>(qs + row * kRowB + (pc << 4)) = qv;
+      *reinterpret_cast<uint4*>(dos + row * kRowB + (pc << 4)) = dv_;
+    }
     if (threadIdx.x < 32) {
       q_lo[threadIdx.x] = pr_lo;
       q_t[threadIdx.x] = pr_t;
@@ -580,8 +597,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkv_kernel(const uint16_t* 
     __syncthreads();
     const int64_t inext = next_tile(i + QS);
     if (inext < ntiles) {
-      tile_load(qr, q, inext * 32, M);
-      tile_load(dr, dout, inext * 32, M);
+      piece_load(inext);
       row_load(inext);
     }
     if (!(thi < kw0 || tlo > kw0 + 31)) {
@@ -591,8 +607,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkv_kernel(const uint16_t* 
       const int qrow = key_perm(lane & 31);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(qs, qrow, s, h), kf[s], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(dos, qrow, s, h), vf[s], dp, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(qs, qrow, s, h),
+                                                     row_frag<false>(kmine, lane & 31, s, h), sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(dos, qrow, s, h),
+                                                     row_frag<false>(vmine, lane & 31, s, h), dp, 0, 0, 0);
       }
       float pt[16], dz[16];
 #pragma unroll
@@ -601,7 +619,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkv_kernel(const uint16_t* 
         for (int j = 0; j < 4; ++j) {
           const int qi = key_perm(8 * q4 + 4 * h + j);
           const bool ok = key >= q_lo[qi] && key <= q_t[qi];
-          const float p = ok ? exp2f(sc[4 * q4 + j] * sl2 - q_lse2[qi]) : 0.f;
+          const float p = ok ? __builtin_amdgcn_exp2f(sc[4 * q4 + j] * sl2 - q_lse2[qi]) : 0.f;
           pt[4 * q4 + j] = p;
           dz[4 * q4 + j] = p * (dp[4 * q4 + j] - q_D[qi]);
         }
@@ -611,13 +629,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkv_kernel(const uint16_t* 
         acc_frags(pt, s, ph, pl);
         acc_frags(dz, s, zh, zl);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int n = 0; n < 2; ++n) {
+          const int nt = 2 * hh + n;
           const at_bf16x8_t fo = tr_frag(dos, 32 * nt, s, lane);
           const at_bf16x8_t fq = tr_frag(qs, 32 * nt, s, lane);
-          adv[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo, ph, adv[nt], 0, 0, 0);
-          adv[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo, pl, adv[nt], 0, 0, 0);
-          adk[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq, zh, adk[nt], 0, 0, 0);
-          adk[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq, zl, adk[nt], 0, 0, 0);
+          adv[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo, ph, adv[n], 0, 0, 0);
+          adk[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq, zh, adk[n], 0, 0, 0);
+          adv[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo, pl, adv[n], 0, 0, 0);
+          adk[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq, zl, adk[n], 0, 0, 0);
         }
       }
     }
@@ -628,14 +647,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkv_kernel(const uint16_t* 
   float* ok_ = pdk + (int64_t(split) * T + key) * kHD;
   float* ov_ = pdv + (int64_t(split) * T + key) * kHD;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int n = 0; n < 2; ++n)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int c = 32 * nt + 8 * q4 + 4 * h;
-      *reinterpret_cast<float4*>(ok_ + c) = make_float4(adk[nt][4 * q4] * scale, adk[nt][4 * q4 + 1] * scale,
-                                                        adk[nt][4 * q4 + 2] * scale, adk[nt][4 * q4 + 3] * scale);
+      const int c = 32 * (2 * hh + n) + 8 * q4 + 4 * h;
+      *reinterpret_cast<float4*>(ok_ + c) = make_float4(adk[n][4 * q4] * scale, adk[n][4 * q4 + 1] * scale,
+                                                        adk[n][4 * q4 + 2] * scale, adk[n][4 * q4 + 3] * scale);
       *reinterpret_cast<float4*>(ov_ + c) =
-          make_float4(adv[nt][4 * q4], adv[nt][4 * q4 + 1], adv[nt][4 * q4 + 2], adv[nt][4 * q4 + 3]);
+          make_float4(adv[n][4 * q4], adv[n][4 * q4 + 1], adv[n][4 * q4 + 2], adv[n][4 * q4 + 3]);
     }
 }
 
@@ -683,7 +702,7 @@ hipError_t launch_attn_bwd(const void* q, const void* kk, const void* v, const i
   const int QS = attn_query_splits(T);
   if (dkv_start) (void)hipEventRecord(dkv_start, st);
   hipLaunchKernelGGL(attn_dkv_kernel, dim3(unsigned((T + kAttnRows - 1) / kAttnRows), unsigned(QS)),
-                     dim3(kAttnThreads), 0, st, qp, kp, vp, sidx, M, T, ktop, S, lse, D, dp, tile_lo, tile_hi, ntiles,
+                     dim3(kDkvThreads), 0, st, qp, kp, vp, sidx, M, T, ktop, S, lse, D, dp, tile_lo, tile_hi, ntiles,
                      QS, pdk, pdv);
   if (dkv_stop) (void)hipEventRecord(dkv_stop, st);
   const int64_t n = T * kHD;
