@@ -378,33 +378,46 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_prep_kernel(const uint1
   }
 }
 
-// dq: blocks of 128 query rows as in the forward; per key block the scores
-// (keys in the pi order) and dp = do V^T (V rows in the same order) give
-// dz in the A operand layout of dz K, K read back transposed from LDS.
-__global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ kk,
-                                                               const uint16_t* __restrict__ v,
-                                                               const int* __restrict__ sidx, int64_t M, int64_t T,
-                                                               int ktop, int64_t S, const float* __restrict__ lse,
-                                                               const float* __restrict__ D,
-                                                               const uint16_t* __restrict__ dout,
-                                                               uint16_t* __restrict__ dq) {
-  __shared__ __attribute__((aligned(16))) char ks[kKB * kRowB];
-  __shared__ __attribute__((aligned(16))) char vs[kKB * kRowB];
-  __shared__ int red[2 * kAttnThreads / kWave];
+// dq: blocks of 128 query rows in 8 waves, wave w = (row tile w & 3, key
+// half w >> 2), as in the forward; per step of 64 keys the scores (keys in
+// the pi order) and dp = do V^T (V rows in the same order) give dz in the A
+// operand layout of dz K, K read back transposed from LDS.  The two halves'
+// dq partials are added through LDS at the end.
+__global__ __launch_bounds__(kFwdThreads) void attn_dq_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ kk,
+                                                              const uint16_t* __restrict__ v,
+                                                              const int* __restrict__ sidx, int64_t M, int64_t T,
+                                                              int ktop, int64_t S, const float* __restrict__ lse,
+                                                              const float* __restrict__ D,
+                                                              const uint16_t* __restrict__ dout,
+                                                              uint16_t* __restrict__ dq) {
+  // staging: K tiles [2][32] (transposing layout), V tiles [2][32] (row-read
+  // layout); merge: the second half's dq as [row tile][16 float4][64 lanes]
+  __shared__ __attribute__((aligned(16))) char smem[4 * 16 * kWave * 16];
+  __shared__ int red[2 * kFwdWaves];
   const int lane = lane_id(), h = lane >> 5;
   const int w = threadIdx.x / kWave;
-  const int64_t r = int64_t(blockIdx.x) * kAttnRows + 32 * w + (lane & 31);
+  const int rt = w & 3, kh = w >> 2;
+  const int64_t r = int64_t(blockIdx.x) * kFwdRows + 32 * rt + (lane & 31);
   const bool real = r < M;
   const int t = real ? sidx[r] / ktop : -1;
   const int lo = real ? int(int64_t(t) / S * S) : 0x7fffffff;
-  int blo, bhi;
-  block_range(lo, t, red, blo, bhi);
   int wlo = lo, whi = t;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     wlo = min(wlo, __shfl_xor(wlo, off, kWave));
     whi = max(whi, __shfl_xor(whi, off, kWave));
+  }
+  if (lane == 0) {
+    red[2 * w] = wlo;
+    red[2 * w + 1] = whi;
+  }
+  __syncthreads();
+  int blo = red[0], bhi = red[1];
+#pragma unroll
+  for (int i = 1; i < kFwdWaves; ++i) {
+    blo = min(blo, red[2 * i]);
+    bhi = max(bhi, red[2 * i + 1]);
   }
   if (bhi < 0) return;
   const float l2e = 1.4426950408889634f;
@@ -426,24 +439,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const uint16_t* _
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
-  const int kb_first = blo / kKB * kKB;
-  TileRegs kr, vr;
-  tile_load(kr, kk, kb_first, T);
-  tile_load(vr, v, kb_first, T);
-  for (int kb0 = kb_first; kb0 <= bhi; kb0 += kKB) {
-    __syncthreads();
-    tile_store<true>(kr, ks);
-    tile_store<false>(vr, vs);
-    __syncthreads();
-    if (kb0 + kKB <= bhi) {
-      tile_load(kr, kk, kb0 + kKB, T);
-      tile_load(vr, v, kb0 + kKB, T);
+  char* ktiles = smem;
+  char* vtiles = smem + kStepKeys * kRowB;
+  const char* ks = ktiles + kh * kKB * kRowB;
+  const char* vs = vtiles + kh * kKB * kRowB;
+  const int krow = key_perm(lane & 31);
+  uint4 kv[2], vv[2];
+  auto step_load = [&](int sb) SMOE_INL {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = threadIdx.x + u * kFwdThreads;
+      const int64_t g = int64_t(sb) + (i >> 4);
+      const bool ok = g < T;
+      kv[u] = ok ? *reinterpret_cast<const uint4*>(kk + g * kHD + (i & 15) * 8) : make_uint4(0u, 0u, 0u, 0u);
+      vv[u] = ok ? *reinterpret_cast<const uint4*>(v + g * kHD + (i & 15) * 8) : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (kb0 > whi || kb0 + kKB <= wlo) continue;
+  };
+  step_load(blo / kKB * kKB);
+  for (int sb0 = blo / kKB * kKB; sb0 <= bhi; sb0 += kStepKeys) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = threadIdx.x + u * kFwdThreads;
+      const int row = i >> 4, c = i & 15, tr = row & 31;
+      *reinterpret_cast<uint4*>(ktiles + row * kRowB + ((c ^ swz_tr(tr)) << 4)) = kv[u];
+      *reinterpret_cast<uint4*>(vtiles + row * kRowB + ((c ^ swz_row(tr)) << 4)) = vv[u];
+    }
+    __syncthreads();
+    if (sb0 + kStepKeys <= bhi) step_load(sb0 + kStepKeys);
+    const int kb0 = sb0 + kKB * kh;
+    if (kb0 > whi || kb0 + kKB <= wlo) continue;   // nothing for this wave (uniform)
     at_f32x16_t sc, dp;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
-    const int krow = key_perm(lane & 31);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(ks, krow, s, h), qf[s], sc, 0, 0, 0);
@@ -456,7 +484,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const uint16_t* _
       for (int i = 0; i < 4; ++i) {
         const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
         const bool ok = key >= lo && key <= t;
-        const float p = ok ? exp2f(sc[4 * q4 + i] * sl2 - lse2) : 0.f;
+        const float p = ok ? __builtin_amdgcn_exp2f(sc[4 * q4 + i] * sl2 - lse2) : 0.f;
         ds[4 * q4 + i] = p * (dp[4 * q4 + i] - Dr);
       }
 #pragma unroll
@@ -471,15 +499,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const uint16_t* _
       }
     }
   }
-  if (!real) return;
+  // the second key half adds its partial to the first
+  __syncthreads();
+  float4* slots = reinterpret_cast<float4*>(smem) + rt * 16 * kWave;
+  if (kh == 1) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        slots[(4 * nt + q4) * kWave + lane] =
+            make_float4(acc[nt][4 * q4], acc[nt][4 * q4 + 1], acc[nt][4 * q4 + 2], acc[nt][4 * q4 + 3]);
+  }
+  __syncthreads();
+  if (kh == 1 || !real) return;
   const float scale = 1.f / sqrtf(float(kHD));
   uint16_t* out = dq + r * kHD;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float vals[4] = {acc[nt][4 * q4] * scale, acc[nt][4 * q4 + 1] * scale, acc[nt][4 * q4 + 2] * scale,
-                             acc[nt][4 * q4 + 3] * scale};
+      const float4 x = slots[(4 * nt + q4) * kWave + lane];
+      const float vals[4] = {(acc[nt][4 * q4] + x.x) * scale, (acc[nt][4 * q4 + 1] + x.y) * scale,
+                             (acc[nt][4 * q4 + 2] + x.z) * scale, (acc[nt][4 * q4 + 3] + x.w) * scale};
       *reinterpret_cast<uint2*>(out + 32 * nt + 8 * q4 + 4 * h) = pack4_bf16(vals);
     }
 }
@@ -696,7 +737,7 @@ hipError_t launch_attn_bwd(const void* q, const void* kk, const void* v, const i
   hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(unsigned((ntiles + 3) / 4)), dim3(kAttnThreads), 0, st,
                      static_cast<const uint16_t*>(o), dp, sidx, M, ktop, S, D, tile_lo, tile_hi, ntiles);
   if (dq_start) (void)hipEventRecord(dq_start, st);
-  hipLaunchKernelGGL(attn_dq_kernel, dim3(unsigned((M + kAttnRows - 1) / kAttnRows)), dim3(kAttnThreads), 0, st, qp,
+  hipLaunchKernelGGL(attn_dq_kernel, dim3(unsigned((M + kFwdRows - 1) / kFwdRows)), dim3(kFwdThreads), 0, st, qp,
                      kp, vp, sidx, M, T, ktop, S, lse, D, dp, static_cast<uint16_t*>(dq));
   if (dq_stop) (void)hipEventRecord(dq_stop, st);
   const int QS = attn_query_splits(T);
