@@ -153,3 +153,30 @@ def test_router_rejects_bad_arguments():
     assert b(wsb=ws - 1) == 4
     assert b(E=100) == 5
     assert b(dx=NULL) == 1
+
+
+def test_attention_rejects_bad_arguments():
+    fwd, bwd = lib.smoe_moa_attention_fwd, lib.smoe_moa_attention_bwd
+
+    def f(T=256, k=2, S=128, hd=128, dtype=smoe.BF16, q=_fake()):
+        return fwd(q, _fake(), _fake(), _fake(), T, k, S, hd, dtype, _fake(), _fake(), NULL)
+
+    assert f(dtype=smoe.F32) == 5                    # bf16 only
+    assert f(dtype=9) == 3
+    assert f(hd=64) == 5                             # head_dim 128 only
+    assert f(T=200, S=128) == 2                      # T not a multiple of seq_len
+    assert f(S=0) == 2
+    assert f(k=0) == 2
+    assert f(q=NULL) == 1
+    assert f(q=_fake(4104)) == 2                     # misaligned
+    assert f(T=0) == 0                               # nothing to do
+    ws = lib.smoe_moa_attention_bwd_workspace_bytes(256, 2, 128, 128)
+    assert ws >= 256 * 2 * 4 + 2 * 256 * 128 * 4
+    assert lib.smoe_moa_attention_bwd_workspace_bytes(256, 2, 128, 64) == 0
+
+    def b(wsb=ws, dq=_fake()):
+        return bwd(_fake(), _fake(), _fake(), _fake(), 256, 2, 128, 128, smoe.BF16, _fake(), _fake(), _fake(), dq,
+                   _fake(), _fake(), _fake(), wsb, NULL)
+
+    assert b(wsb=ws - 1) == 4
+    assert b(dq=NULL) == 1
