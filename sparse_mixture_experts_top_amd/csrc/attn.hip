@@ -168,11 +168,13 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(const uint16_t* _
   const int t = real ? sidx[r] / ktop : -1;
   const int lo = real ? int(int64_t(t) / S * S) : 0x7fffffff;
   // block and row-tile ranges
-  int wlo = lo, whi = t;
+  int wlo = lo, whi = t, wlo_max = real ? lo : -1, whi_min = real ? t : 0x7fffffff;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     wlo = min(wlo, __shfl_xor(wlo, off, kWave));
     whi = max(whi, __shfl_xor(whi, off, kWave));
+    wlo_max = max(wlo_max, __shfl_xor(wlo_max, off, kWave));
+    whi_min = min(whi_min, __shfl_xor(whi_min, off, kWave));
   }
   if (lane == 0) {
     red[2 * w] = wlo;
@@ -246,34 +248,51 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(const uint16_t* _
     }
     float z[16];
     float bm = -INFINITY;
+    // a tile inside every row's range of this wave needs no mask (uniform)
+    const bool inner = kb0 >= wlo_max && kb0 + kKB - 1 <= whi_min;
+    if (inner) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
-        const bool ok = key >= lo && key <= t;
-        const float zz = ok ? (sa[4 * q4 + i] + sb[4 * q4 + i]) * sl2 : -INFINITY;
-        z[4 * q4 + i] = zz;
-        bm = fmaxf(bm, zz);
+      for (int i = 0; i < 16; ++i) {
+        z[i] = (sa[i] + sb[i]) * sl2;
+        bm = fmaxf(bm, z[i]);
       }
+    } else {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
+          const bool ok = key >= lo && key <= t;
+          const float zz = ok ? (sa[4 * q4 + i] + sb[4 * q4 + i]) * sl2 : -INFINITY;
+          z[4 * q4 + i] = zz;
+          bm = fmaxf(bm, zz);
+        }
+    }
     bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-    // a row with no key so far keeps m = -inf, l = 0 and a zero O
-    const float mn = fmaxf(m2, bm);
-    const bool none = mn == -INFINITY;
-    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
+    // The reference m2 moves only when a row's max exceeds it by more than
+    // 8 (base 2), so the probabilities stay below 2^8 and O and l are
+    // rescaled only on those steps (for the whole wave, when any row
+    // needs it).  A row with no key so far keeps m = -inf, l = 0, O = 0.
+    const bool grow = bm > m2 + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mn = fmaxf(m2, bm);
+      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
+      l *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nt][i] *= alpha;
+      m2 = mn;
+    }
+    const bool none = m2 == -INFINITY;
     float p[16], ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p[i] = none ? 0.f : __builtin_amdgcn_exp2f(z[i] - mn);
+      p[i] = none ? 0.f : __builtin_amdgcn_exp2f(z[i] - m2);
       ps += p[i];
     }
     ps += __shfl_xor(ps, 32, kWave);
-    l = alpha * l + ps;
-    m2 = mn;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[nt][i] *= alpha;
+    l += ps;
     at_bf16x8_t a0h, a0l, a1h, a1l;
     acc_frags(p, 0, a0h, a0l);
     acc_frags(p, 1, a1h, a1l);
