@@ -17,7 +17,10 @@
  * Summary), with no padded or copied grouped input (catalogue record
  * "Scattered Mixture-of-Experts Implementation", abstract).  The backward
  * pass runs through the same machinery and yields per-expert weight
- * gradients (article, para. 4).
+ * gradients (article, para. 4).  Around that path the library also exports
+ * the router that produces the expert choices and gates (smoe_router_*)
+ * and the Mixture-of-Attention core between the Q and O projections
+ * (smoe_moa_attention_*), each with its backward.
  *
  * Conventions for every entry point.
  *  - Pointers to tensors are DEVICE pointers owned by the caller.  The
