@@ -444,8 +444,8 @@ static void layout_attn_bwd(Arena& ar, int64_t T, int64_t M, AttnBwdWs& w) {
   const int64_t ntiles = (M + 31) / 32;
   const size_t part = size_t(attn_query_splits(T)) * size_t(T) * 128 * 4;
   w.D = static_cast<float*>(ar.take(size_t(M) * 4));
-  w.tile_lo = static_cast<int*>(ar.take(size_t(ntiles) * 4));
-  w.tile_hi = static_cast<int*>(ar.take(size_t(ntiles) * 4));
+  w.tile_lo = static_cast<int*>(ar.take(size_t(ntiles) * 8));   // two values per tile
+  w.tile_hi = static_cast<int*>(ar.take(size_t(ntiles) * 8));
   w.pdk = static_cast<float*>(ar.take(part));
   w.pdv = static_cast<float*>(ar.take(part));
 }

@@ -362,6 +362,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_prep_kernel(const uint1
                                                                      int ktop, int64_t S, float* __restrict__ D,
                                                                      int* __restrict__ tile_lo,
                                                                      int* __restrict__ tile_hi, int64_t ntiles) {
+  // tile_lo / tile_hi hold, per tile: [0, ntiles) the lowest sequence start
+  // and the highest token, [ntiles, 2 ntiles) the highest sequence start and
+  // the lowest token (a key inside both of the latter is in every row's range)
   const int lane = lane_id();
   const int64_t tile = int64_t(blockIdx.x) * (kAttnThreads / kWave) + threadIdx.x / kWave;
   if (tile >= ntiles) return;
@@ -386,14 +389,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bwd_prep_kernel(const uint1
   if (real && half == 0) D[r] = sum;
   int t = real ? sidx[r] / ktop : -1;
   int lo = real ? int(int64_t(t) / S * S) : 0x7fffffff;
+  int lo_max = real ? lo : -1, t_min = real ? t : 0x7fffffff;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     lo = min(lo, __shfl_xor(lo, off, kWave));
     t = max(t, __shfl_xor(t, off, kWave));
+    lo_max = max(lo_max, __shfl_xor(lo_max, off, kWave));
+    t_min = min(t_min, __shfl_xor(t_min, off, kWave));
   }
   if (lane == 0) {
     tile_lo[tile] = lo;
     tile_hi[tile] = t;
+    tile_lo[ntiles + tile] = lo_max;
+    tile_hi[ntiles + tile] = t_min;
   }
 }
 
@@ -421,11 +429,13 @@ __global__ __launch_bounds__(kFwdThreads) void attn_dq_kernel(const uint16_t* __
   const bool real = r < M;
   const int t = real ? sidx[r] / ktop : -1;
   const int lo = real ? int(int64_t(t) / S * S) : 0x7fffffff;
-  int wlo = lo, whi = t;
+  int wlo = lo, whi = t, wlo_max = real ? lo : -1, whi_min = real ? t : 0x7fffffff;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     wlo = min(wlo, __shfl_xor(wlo, off, kWave));
     whi = max(whi, __shfl_xor(whi, off, kWave));
+    wlo_max = max(wlo_max, __shfl_xor(wlo_max, off, kWave));
+    whi_min = min(whi_min, __shfl_xor(whi_min, off, kWave));
   }
   if (lane == 0) {
     red[2 * w] = wlo;
@@ -497,15 +507,20 @@ __global__ __launch_bounds__(kFwdThreads) void attn_dq_kernel(const uint16_t* __
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<false>(vs, krow, s, h), df[s], dp, 0, 0, 0);
     }
     float ds[16];
+    if (kb0 >= wlo_max && kb0 + kKB - 1 <= whi_min) {   // inside every row's range (uniform)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
+      for (int i = 0; i < 16; ++i) ds[i] = __builtin_amdgcn_exp2f(sc[i] * sl2 - lse2) * (dp[i] - Dr);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
-        const bool ok = key >= lo && key <= t;
-        const float p = ok ? __builtin_amdgcn_exp2f(sc[4 * q4 + i] * sl2 - lse2) : 0.f;
-        ds[4 * q4 + i] = p * (dp[4 * q4 + i] - Dr);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
+          const bool ok = key >= lo && key <= t;
+          const float p = ok ? __builtin_amdgcn_exp2f(sc[4 * q4 + i] * sl2 - lse2) : 0.f;
+          ds[4 * q4 + i] = p * (dp[4 * q4 + i] - Dr);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       at_bf16x8_t ah, al;
@@ -654,6 +669,7 @@ __global__ __launch_bounds__(kDkvThreads) void attn_dkv_kernel(const uint16_t* _
       q_D[threadIdx.x] = pr_D;
     }
     const int tlo = tile_lo[i], thi = tile_hi[i];
+    const int tlo_max = tile_lo[ntiles + i], thi_min = tile_hi[ntiles + i];
     __syncthreads();
     const int64_t inext = next_tile(i + QS);
     if (inext < ntiles) {
@@ -673,12 +689,14 @@ __global__ __launch_bounds__(kDkvThreads) void attn_dkv_kernel(const uint16_t* _
                                                      row_frag<false>(vmine, lane & 31, s, h), dp, 0, 0, 0);
       }
       float pt[16], dz[16];
+      // the wave's keys inside every row's range need no mask (uniform)
+      const bool inner = kw0 >= tlo_max && kw0 + 31 <= thi_min;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int qi = key_perm(8 * q4 + 4 * h + j);
-          const bool ok = key >= q_lo[qi] && key <= q_t[qi];
+          const bool ok = inner || (key >= q_lo[qi] && key <= q_t[qi]);
           const float p = ok ? __builtin_amdgcn_exp2f(sc[4 * q4 + j] * sl2 - q_lse2[qi]) : 0.f;
           pt[4 * q4 + j] = p;
           dz[4 * q4 + j] = p * (dp[4 * q4 + j] - q_D[qi]);

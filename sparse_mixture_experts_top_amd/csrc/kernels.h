@@ -131,7 +131,7 @@ hipError_t launch_gate_dw_finish(const float* tmp, int d, int E, int bf16, float
 // grouped query rows against shared K/V, causal within sequences of S.
 hipError_t launch_attn_fwd(const void* q, const void* kk, const void* v, const int* sidx, int64_t M, int64_t T,
                            int ktop, int64_t S, void* o, float* lse, hipStream_t st);
-// backward: D [M], per-32-row query tile ranges [ceil(M/32)] x 2, and fp32
+// backward: D [M], per-32-row query tile ranges [ceil(M/32)] x 4, and fp32
 // dK/dV partials [attn_query_splits(T)][T][128] each
 int attn_query_splits(int64_t T);
 hipError_t launch_attn_bwd(const void* q, const void* kk, const void* v, const int* sidx, int64_t M, int64_t T,
