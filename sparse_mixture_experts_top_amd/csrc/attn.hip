@@ -246,6 +246,13 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(const uint16_t* _
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s, h), qf[s], sa, 0, 0, 0);
       sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s + 1, h), qf[s + 1], sb, 0, 0, 0);
     }
+    // V fragments now, so their LDS reads overlap the softmax below
+    at_bf16x8_t vfr[4][2];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      vfr[nt][0] = tr_frag(vs, 32 * nt, 0, lane);
+      vfr[nt][1] = tr_frag(vs, 32 * nt, 1, lane);
+    }
     float z[16];
     float bm = -INFINITY;
     // a tile inside every row's range of this wave needs no mask (uniform)
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(const uint16_t* _
     acc_frags(p, 1, a1h, a1l);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const at_bf16x8_t v0 = tr_frag(vs, 32 * nt, 0, lane), v1 = tr_frag(vs, 32 * nt, 1, lane);
+      const at_bf16x8_t v0 = vfr[nt][0], v1 = vfr[nt][1];
       acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0h, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1h, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0l, acc[nt], 0, 0, 0);
