@@ -590,6 +590,7 @@ __global__ __launch_bounds__(kDkvThreads) void attn_dkv_kernel(const uint16_t* _
   __shared__ __attribute__((aligned(16))) char dos[32 * kRowB];
   __shared__ __attribute__((aligned(16))) char kall[kAttnRows * kRowB];   // the block's K rows
   __shared__ __attribute__((aligned(16))) char vall[kAttnRows * kRowB];   // and V rows
+  __shared__ float4 xch[4][2][4 * kWave];   // per key tile: p (from half 0), dp (from half 1)
   __shared__ int q_lo[32], q_t[32];
   __shared__ float q_lse2[32], q_D[32];
   const int lane = lane_id(), h = lane >> 5;
@@ -683,30 +684,63 @@ __global__ __launch_bounds__(kDkvThreads) void attn_dkv_kernel(const uint16_t* _
       piece_load(inext);
       row_load(inext);
     }
-    if (!(thi < kw0 || tlo > kw0 + 31)) {
-      at_f32x16_t sc, dp;
+    // half 0 forms p^T, half 1 dp^T; they swap them through LDS
+    const bool active = !(thi < kw0 || tlo > kw0 + 31);   // uniform per key tile
+    float pt[16], dz[16];
+    if (active) {
+      at_f32x16_t acc_;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sc[j] = dp[j] = 0.f;
+      for (int j = 0; j < 16; ++j) acc_[j] = 0.f;
       const int qrow = key_perm(lane & 31);
+      const char* src = hh == 0 ? qs : dos;
+      const char* mine = hh == 0 ? kmine : vmine;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(qs, qrow, s, h),
-                                                     row_frag<false>(kmine, lane & 31, s, h), sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(dos, qrow, s, h),
-                                                     row_frag<false>(vmine, lane & 31, s, h), dp, 0, 0, 0);
+      for (int s = 0; s < 8; ++s)
+        acc_ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<true>(src, qrow, s, h),
+                                                       row_frag<false>(mine, lane & 31, s, h), acc_, 0, 0, 0);
+      float mineval[16];
+      if (hh == 0) {
+        const bool inner = kw0 >= tlo_max && kw0 + 31 <= thi_min;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int qi = key_perm(8 * q4 + 4 * h + j);
+            const bool ok = inner || (key >= q_lo[qi] && key <= q_t[qi]);
+            mineval[4 * q4 + j] = ok ? __builtin_amdgcn_exp2f(acc_[4 * q4 + j] * sl2 - q_lse2[qi]) : 0.f;
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mineval[j] = acc_[j];
       }
-      float pt[16], dz[16];
-      // the wave's keys inside every row's range need no mask (uniform)
-      const bool inner = kw0 >= tlo_max && kw0 + 31 <= thi_min;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        xch[kt][hh][q4 * kWave + lane] =
+            make_float4(mineval[4 * q4], mineval[4 * q4 + 1], mineval[4 * q4 + 2], mineval[4 * q4 + 3]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pt[j] = mineval[j];
+    }
+    __syncthreads();
+    if (active) {
+      float other[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = xch[kt][1 - hh][q4 * kWave + lane];
+        other[4 * q4] = x.x;
+        other[4 * q4 + 1] = x.y;
+        other[4 * q4 + 2] = x.z;
+        other[4 * q4 + 3] = x.w;
+      }
+      // pt: p^T, dz = p (dp - D)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int qi = key_perm(8 * q4 + 4 * h + j);
-          const bool ok = inner || (key >= q_lo[qi] && key <= q_t[qi]);
-          const float p = ok ? __builtin_amdgcn_exp2f(sc[4 * q4 + j] * sl2 - q_lse2[qi]) : 0.f;
+          const float p = hh == 0 ? pt[4 * q4 + j] : other[4 * q4 + j];
+          const float dpv = hh == 0 ? other[4 * q4 + j] : pt[4 * q4 + j];
           pt[4 * q4 + j] = p;
-          dz[4 * q4 + j] = p * (dp[4 * q4 + j] - q_D[qi]);
+          dz[4 * q4 + j] = p * (dpv - q_D[qi]);
         }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
