@@ -253,7 +253,8 @@ __global__ __launch_bounds__(kFwdThreads) void gate_fwd_mfma_kernel(const uint16
 // Router dx: dx[t][c] (+)= sum_j dlog[t][j] w[e_j][c], with
 //   dlog[t][j] = g_j (dg_j - sum_i g_i dg_i)
 // for choice j of token t (the sum over all k choices; 0 where the expert
-// id is outside [0, E)).  Block (column tile of 256, token chunk of 128):
+// id is outside [0, E)).  Block (column tile of 256, token chunks of 128,
+// strided by the grid's y extent):
 // the tile's slice of every expert row, w[e][c0 .. c0+255], sits in LDS as
 // fp32, and so do the chunk's expert ids and dlogits, formed in the
 // prologue by one thread per token; lane l of each wave owns columns
@@ -297,76 +298,79 @@ __global__ __launch_bounds__(kGateThreads) void gate_dx_kernel(const InT* __rest
     for (int q = 0; q < VW; q += 4)
       *reinterpret_cast<float4*>(ws_tile + e * kDxCols + c + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
   }
-  const int64_t t0 = int64_t(blockIdx.y) * kDxTokChunk;
-  const int nt = int(T - t0 < kDxTokChunk ? T - t0 : kDxTokChunk);
   const bool first = blockIdx.x == 0;
   if (first && blockIdx.y == 0 && threadIdx.x == 0) {
     offsets[0] = 0;
     offsets[1] = int(T);
   }
-  for (int i = threadIdx.x; i < nt; i += kGateThreads) {
-    const int64_t t = t0 + i;
-    float gv[kGateMaxK], dv[kGateMaxK];
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < kGateMaxK; ++j) {
-      gv[j] = j < k ? gates[t * k + j] : 0.f;
-      dv[j] = j < k ? dgates[t * k + j] : 0.f;
-      s += gv[j] * dv[j];
-    }
-    InT* drow = D + t * ncol_d;
-    if (first) {
-      rows[t] = int(t);
-      for (int c = 0; c < ncol_d; c += 16 / int(sizeof(InT)))
-        *reinterpret_cast<uint4*>(drow + c) = make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int j = 0; j < kGateMaxK; ++j) {
-      if (j < k) {
-        const int e = idx[t * k + j];
-        const bool ok = e >= 0 && e < E;
-        const float v = ok ? gv[j] * (dv[j] - s) : 0.f;
-        ch_e[i * k + j] = ok ? e : 0;
-        ch_v[i * k + j] = v;
-        if (first && ok) {
-          if constexpr (sizeof(InT) == 2) {
-            const uint16_t hi = f2bf(v);
-            drow[e] = hi;
-            drow[ep + e] = f2bf(v - bf2f(hi));
-          } else {
-            drow[e] = v;
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int cl = 4 * lane;
   const bool mine = cl < ncol;
-  for (int tl = w; tl < nt; tl += kGateWaves) {
-    float r[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int e = ch_e[tl * k + j];
-      const float dl = ch_v[tl * k + j];
-      const float4 gv = *reinterpret_cast<const float4*>(ws_tile + e * kDxCols + cl);
-      r[0] += dl * gv.x;
-      r[1] += dl * gv.y;
-      r[2] += dl * gv.z;
-      r[3] += dl * gv.w;
-    }
-    if (mine) {
-      InT* p = dx + (t0 + tl) * int64_t(d) + c0 + cl;
-      if (accumulate) {
-        float v[4];
-        ld4<InT>(p, v);
-        r[0] = v[0] + r[0];
-        r[1] = v[1] + r[1];
-        r[2] = v[2] + r[2];
-        r[3] = v[3] + r[3];
+  // token chunks y, y + gridDim.y, ... (the grid's y extent is capped)
+  for (int64_t t0 = int64_t(blockIdx.y) * kDxTokChunk; t0 < T; t0 += int64_t(gridDim.y) * kDxTokChunk) {
+    const int nt = int(T - t0 < kDxTokChunk ? T - t0 : kDxTokChunk);
+    __syncthreads();   // the previous chunk's choices are no longer read
+    for (int i = threadIdx.x; i < nt; i += kGateThreads) {
+      const int64_t t = t0 + i;
+      float gv[kGateMaxK], dv[kGateMaxK];
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < kGateMaxK; ++j) {
+        gv[j] = j < k ? gates[t * k + j] : 0.f;
+        dv[j] = j < k ? dgates[t * k + j] : 0.f;
+        s += gv[j] * dv[j];
       }
-      st4<InT>(p, r);
+      InT* drow = D + t * ncol_d;
+      if (first) {
+        rows[t] = int(t);
+        for (int c = 0; c < ncol_d; c += 16 / int(sizeof(InT)))
+          *reinterpret_cast<uint4*>(drow + c) = make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < kGateMaxK; ++j) {
+        if (j < k) {
+          const int e = idx[t * k + j];
+          const bool ok = e >= 0 && e < E;
+          const float v = ok ? gv[j] * (dv[j] - s) : 0.f;
+          ch_e[i * k + j] = ok ? e : 0;
+          ch_v[i * k + j] = v;
+          if (first && ok) {
+            if constexpr (sizeof(InT) == 2) {
+              const uint16_t hi = f2bf(v);
+              drow[e] = hi;
+              drow[ep + e] = f2bf(v - bf2f(hi));
+            } else {
+              drow[e] = v;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (int tl = w; tl < nt; tl += kGateWaves) {
+      float r[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < k; ++j) {
+        const int e = ch_e[tl * k + j];
+        const float dl = ch_v[tl * k + j];
+        const float4 gv = *reinterpret_cast<const float4*>(ws_tile + e * kDxCols + cl);
+        r[0] += dl * gv.x;
+        r[1] += dl * gv.y;
+        r[2] += dl * gv.z;
+        r[3] += dl * gv.w;
+      }
+      if (mine) {
+        InT* p = dx + (t0 + tl) * int64_t(d) + c0 + cl;
+        if (accumulate) {
+          float v[4];
+          ld4<InT>(p, v);
+          r[0] = v[0] + r[0];
+          r[1] = v[1] + r[1];
+          r[2] = v[2] + r[2];
+          r[3] = v[3] + r[3];
+        }
+        st4<InT>(p, r);
+      }
     }
   }
 }
@@ -433,7 +437,8 @@ static void go_gate_dx(const void* wg, int64_t T, int d, int E, int k, const int
                        hipStream_t st) {
   int ep, ncol;
   gate_dlogit_cols(E, sizeof(InT) == 2, ep, ncol);
-  const dim3 grid(unsigned((d + kDxCols - 1) / kDxCols), unsigned((T + kDxTokChunk - 1) / kDxTokChunk));
+  const dim3 grid(unsigned((d + kDxCols - 1) / kDxCols),
+                  unsigned(std::min<int64_t>((T + kDxTokChunk - 1) / kDxTokChunk, 65535)));
   const InT* wp = static_cast<const InT*>(wg);
   InT* dp = static_cast<InT*>(dx);
   InT* Dp = static_cast<InT*>(D);

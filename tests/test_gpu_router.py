@@ -224,3 +224,37 @@ def test_full_chain_tiny_workload(smoe):
         e = rel_err(host(got), want)
         say(f"  {n} err {e:.2e}")
         assert e <= F32_TOL, n
+
+
+def test_router_bwd_many_tokens(smoe):
+    """9 M tokens: more 128-token chunks than the dx grid's y extent, so
+    blocks stride over chunks.  dx is per-token, checked against the oracle
+    on sampled tokens; dw against the property that each token's dlogits sum
+    to zero when its gates do (so every column of dw sums to ~0 over
+    experts), relative to the column's size."""
+    from workloads import bf16_bits, topk_softmax_routing
+    T, d, E, k = 9_000_000, 8, 4, 2
+    say(f"router bwd T={T} d={d} E={E} k={k} bf16")
+    rng = np.random.default_rng([345, 0])
+    xb = bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    wb = bf16_bits(rng.standard_normal((E, d), dtype=np.float32) * np.float32(d ** -0.5))
+    idx, gates = topk_softmax_routing(rng.standard_normal((T, E), dtype=np.float32), k)
+    dgates = rng.standard_normal((T, k), dtype=np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    xd = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    wd = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).cuda()
+    dw, dx = smoe.smoe_router_bwd(xd, wd, dev(idx), dev(gates), dev(dgates))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(7).choice(T, 4000, replace=False))
+    rows = np.concatenate([rows, np.arange(T - 300, T)])   # the last chunks too
+    x64 = (xb[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g64 = ((wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)).T   # G [d, E]
+    rb = oracle.router_bwd(x64, g64, idx[rows], gates[rows].astype(np.float64), dgates[rows].astype(np.float64))
+    e = rel_err_stored_bf16(host(dx[torch.from_numpy(rows).cuda()]), rb["dx"])
+    say(f"  dx (sampled) err {e:.2e}")
+    assert e <= F32_TOL
+    dwh = host(dw)
+    scale = np.abs(dwh).sum(axis=0)
+    colsum = np.abs(dwh.sum(axis=0))
+    say(f"  max |sum_e dw| / sum_e |dw| = {float((colsum / scale).max()):.2e}")
+    assert np.all(colsum <= 1e-3 * scale)
