@@ -203,14 +203,12 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(const uint16_t* _
     for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf(float(kHD));   // scale * log2(e)
   float m2 = -INFINITY, l = 0.f;
-  char* ktiles = smem;
-  char* vtiles = smem + kStepKeys * kRowB;
-  const char* ks = ktiles + kh * kKB * kRowB;
-  const char* vs = vtiles + kh * kKB * kRowB;
+  // two staging buffers of 64 keys (K tiles then V tiles), alternating by
+  // step, so one barrier per step both publishes a step and frees the other
+  constexpr int kBufBytes = 2 * kStepKeys * kRowB;
   const int krow = key_perm(lane & 31);
-
   // 64 keys of K and V per step, two 16-byte pieces of each per thread,
-  // loaded one step ahead into registers
+  // loaded ahead into registers
   uint4 kv[2], vv[2];
   auto step_load = [&](int sb) SMOE_INL {
 #pragma unroll
@@ -222,95 +220,109 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(const uint16_t* _
       vv[u] = ok ? *reinterpret_cast<const uint4*>(v + g * kHD + (i & 15) * 8) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  step_load(blo / kKB * kKB);
-  for (int sb0 = blo / kKB * kKB; sb0 <= bhi; sb0 += kStepKeys) {
-    __syncthreads();
-    // K in the row-read layout, V in the transposing layout
+  // K in the row-read layout, V in the transposing layout
+  auto step_store = [&](char* buf) SMOE_INL {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = threadIdx.x + u * kFwdThreads;
       const int row = i >> 4, c = i & 15, tr = row & 31;
-      *reinterpret_cast<uint4*>(ktiles + row * kRowB + ((c ^ swz_row(tr)) << 4)) = kv[u];
-      *reinterpret_cast<uint4*>(vtiles + row * kRowB + ((c ^ swz_tr(tr)) << 4)) = vv[u];
+      *reinterpret_cast<uint4*>(buf + row * kRowB + ((c ^ swz_row(tr)) << 4)) = kv[u];
+      *reinterpret_cast<uint4*>(buf + kStepKeys * kRowB + row * kRowB + ((c ^ swz_tr(tr)) << 4)) = vv[u];
     }
-    __syncthreads();
-    if (sb0 + kStepKeys <= bhi) step_load(sb0 + kStepKeys);
+  };
+  const int first = blo / kKB * kKB;
+  const int nsteps = (bhi - first) / kStepKeys + 1;
+  step_load(first);
+  step_store(smem);
+  if (nsteps > 1) step_load(first + kStepKeys);
+  __syncthreads();
+  for (int j = 0; j < nsteps; ++j) {
+    const int sb0 = first + j * kStepKeys;
+    const char* ks = smem + (j & 1) * kBufBytes + kh * kKB * kRowB;
+    const char* vs = smem + (j & 1) * kBufBytes + kStepKeys * kRowB + kh * kKB * kRowB;
     const int kb0 = sb0 + kKB * kh;
-    if (kb0 > whi || kb0 + kKB <= wlo) continue;   // nothing for this wave (uniform)
-    // scores for keys kb0 + pi(c), two accumulation chains
-    at_f32x16_t sa, sb;
+    if (!(kb0 > whi || kb0 + kKB <= wlo)) {   // this wave's tile has keys for its rows (uniform)
+      // scores for keys kb0 + pi(c), two accumulation chains
+      at_f32x16_t sa, sb;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sa[i] = sb[i] = 0.f;
+      for (int i = 0; i < 16; ++i) sa[i] = sb[i] = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; s += 2) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s, h), qf[s], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s + 1, h), qf[s + 1], sb, 0, 0, 0);
-    }
-    // V fragments now, so their LDS reads overlap the softmax below
-    at_bf16x8_t vfr[4][2];
+      for (int s = 0; s < 8; s += 2) {
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s, h), qf[s], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, krow, s + 1, h), qf[s + 1], sb, 0, 0, 0);
+      }
+      // V fragments now, so their LDS reads overlap the softmax below
+      at_bf16x8_t vfr[4][2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      vfr[nt][0] = tr_frag(vs, 32 * nt, 0, lane);
-      vfr[nt][1] = tr_frag(vs, 32 * nt, 1, lane);
-    }
-    float z[16];
-    float bm = -INFINITY;
-    // a tile inside every row's range of this wave needs no mask (uniform)
-    const bool inner = kb0 >= wlo_max && kb0 + kKB - 1 <= whi_min;
-    if (inner) {
+      for (int nt = 0; nt < 4; ++nt) {
+        vfr[nt][0] = tr_frag(vs, 32 * nt, 0, lane);
+        vfr[nt][1] = tr_frag(vs, 32 * nt, 1, lane);
+      }
+      float z[16];
+      float bm = -INFINITY;
+      // a tile inside every row's range of this wave needs no mask (uniform)
+      const bool inner = kb0 >= wlo_max && kb0 + kKB - 1 <= whi_min;
+      if (inner) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          z[i] = (sa[i] + sb[i]) * sl2;
+          bm = fmaxf(bm, z[i]);
+        }
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
+            const bool ok = key >= lo && key <= t;
+            const float zz = ok ? (sa[4 * q4 + i] + sb[4 * q4 + i]) * sl2 : -INFINITY;
+            z[4 * q4 + i] = zz;
+            bm = fmaxf(bm, zz);
+          }
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+      // The reference m2 moves only when a row's max exceeds it by more than
+      // 8 (base 2), so the probabilities stay below 2^8 and O and l are
+      // rescaled only on those steps (for the whole wave, when any row
+      // needs it).  A row with no key so far keeps m = -inf, l = 0, O = 0.
+      const bool grow = bm > m2 + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float mn = fmaxf(m2, bm);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
+        l *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nt][i] *= alpha;
+        m2 = mn;
+      }
+      const bool none = m2 == -INFINITY;
+      float p[16], ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        z[i] = (sa[i] + sb[i]) * sl2;
-        bm = fmaxf(bm, z[i]);
+        p[i] = none ? 0.f : __builtin_amdgcn_exp2f(z[i] - m2);
+        ps += p[i];
       }
-    } else {
+      ps += __shfl_xor(ps, 32, kWave);
+      l += ps;
+      at_bf16x8_t a0h, a0l, a1h, a1l;
+      acc_frags(p, 0, a0h, a0l);
+      acc_frags(p, 1, a1h, a1l);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb0 + key_perm(8 * q4 + 4 * h + i);
-          const bool ok = key >= lo && key <= t;
-          const float zz = ok ? (sa[4 * q4 + i] + sb[4 * q4 + i]) * sl2 : -INFINITY;
-          z[4 * q4 + i] = zz;
-          bm = fmaxf(bm, zz);
-        }
+      for (int nt = 0; nt < 4; ++nt) {
+        const at_bf16x8_t v0 = vfr[nt][0], v1 = vfr[nt][1];
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0h, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1h, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0l, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1l, acc[nt], 0, 0, 0);
+      }
+
     }
-    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-    // The reference m2 moves only when a row's max exceeds it by more than
-    // 8 (base 2), so the probabilities stay below 2^8 and O and l are
-    // rescaled only on those steps (for the whole wave, when any row
-    // needs it).  A row with no key so far keeps m = -inf, l = 0, O = 0.
-    const bool grow = bm > m2 + 8.f;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float mn = fmaxf(m2, bm);
-      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
-      l *= alpha;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[nt][i] *= alpha;
-      m2 = mn;
+    if (j + 1 < nsteps) {
+      step_store(smem + ((j + 1) & 1) * kBufBytes);   // read at step j - 1, freed by its barrier
+      if (j + 2 < nsteps) step_load(first + (j + 2) * kStepKeys);
     }
-    const bool none = m2 == -INFINITY;
-    float p[16], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = none ? 0.f : __builtin_amdgcn_exp2f(z[i] - m2);
-      ps += p[i];
-    }
-    ps += __shfl_xor(ps, 32, kWave);
-    l += ps;
-    at_bf16x8_t a0h, a0l, a1h, a1l;
-    acc_frags(p, 0, a0h, a0l);
-    acc_frags(p, 1, a1h, a1l);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const at_bf16x8_t v0 = vfr[nt][0], v1 = vfr[nt][1];
-      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0h, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1h, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, a0l, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, a1l, acc[nt], 0, 0, 0);
-    }
+    __syncthreads();
   }
   // the second key half hands its state to the first
   __syncthreads();
