@@ -172,14 +172,17 @@ def parse():
                     help="also run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl", "router", "attention", "sparsity"],
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl", "router", "attention", "sparsity",
+                                                            "combine"],
                     help="mixtral (the measured line); the others print supplementary lines: "
                          "granular = high-granularity Zipf SMoE-MLP, moa = Mixture-of-Attention "
                          "projections, pl = single ParallelLinear in its four layouts, router = the "
                          "top-k softmax router forward and backward at the three workloads' shapes, "
                          "attention = the Mixture-of-Attention core at the MoA workload's shape, "
                          "sparsity = SMoE-MLP at fixed E with k swept, each beside a dense MLP of the same "
-                         "active FLOPs, and the memory footprint of the Mixtral-shaped step")
+                         "active FLOPs, and the memory footprint of the Mixtral-shaped step; combine = "
+                         "the SMoE-MLP forward with the separate combine and with the combine fused into "
+                         "the W2 product, at the Mixtral and high-granularity shapes")
     return ap.parse_args()
 
 
@@ -370,6 +373,8 @@ def supplementary(args):
         return attention_line(args)
     if args.workload == "sparsity":
         return sparsity_line(args)
+    if args.workload == "combine":
+        return combine_line(args)
     if args.workload == "granular":
         w = make_config(4)
         T, k, E = w.T, w.k, w.E
@@ -520,6 +525,8 @@ def sparsity_line(args):
     a, bf = smoe.ACT_SWIGLU, smoe.BF16
     mem = {"saved": smoe.lib.smoe_mlp_saved_bytes(Tm, km, Em, dm, fm, a, bf),
            "fwd_workspace": smoe.lib.smoe_mlp_fwd_workspace_bytes(Tm, km, Em, dm, fm, a, bf),
+           "fwd_workspace_fused_combine": smoe.lib.smoe_mlp_fwd_fused_combine_workspace_bytes(Tm, km, Em, dm, fm,
+                                                                                              a, bf),
            "bwd_workspace": smoe.lib.smoe_mlp_bwd_workspace_bytes(Tm, km, Em, dm, fm, a, bf),
            "grouped_input_copy_avoided": Tm * km * dm * 2,
            "what": "Mixtral-shaped step; saved holds the routing arrays and h1, h3 (a is recomputed); the "
@@ -531,6 +538,54 @@ def sparsity_line(args):
             "config": {"workload": "SMoE-MLP fwd+bwd, T=16384, d_model=1024, d_ff=1024 per expert, E=16, GELU, "
                                    "k swept 1..16; dense twin E=1, k=1, d_ff=1024*k"},
             "points": pts, "best_ratio": best, "memory_bytes": mem}
+
+
+def combine_line(args):
+    """SMoE-MLP forward (bf16) with the separate combine (smoe_mlp_fwd) and
+    with the combine fused into the W2 product (smoe_mlp_fwd_fused_combine),
+    at the Mixtral shape (k = 2) and the high-granularity shape (k = 8):
+    device time per forward, and the W2 and combine launches of one call."""
+    import torch
+    import sparse_mixture_experts_top_amd as smoe
+    from workloads import make_config
+    steps, warmup = args.steps, args.warmup
+    res = {}
+    for cfg, label in ((3, "mixtral"), (4, "granular")):
+        w = make_config(cfg)
+        t = {n: _dev(w.tensors[n]) for n in ("x", "w1", "w2", "w3", "expert_idxs", "gates") if n in w.tensors}
+        ws = None
+        row = {"T": w.T, "k": w.k, "E": w.E}
+        for fused in (False, True):
+            def fwd():
+                smoe.smoe_mlp_fwd(t["x"], t["w1"], t["w2"], t["expert_idxs"], t["gates"], w.act, w3=t.get("w3"),
+                                  ws=ws, fused_combine=fused)
+            ms = _event_ms(fwd, steps, warmup)
+            evs = {r: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for r in ("down", "combine")}
+            for r in evs:
+                smoe.smoe_set_role_events(r, *evs[r])
+            fwd()
+            torch.cuda.synchronize()
+            for r in evs:
+                smoe.smoe_set_role_events(r, None, None)
+            row["fused" if fused else "separate"] = {
+                "fwd_ms": ms, "down_ms_last": evs["down"][0].elapsed_time(evs["down"][1]),
+                "combine_ms_last": evs["combine"][0].elapsed_time(evs["combine"][1])}
+        row["fused_over_separate"] = row["fused"]["fwd_ms"] / row["separate"]["fwd_ms"]
+        dims = (w.T, w.k, w.E, w.dims["d_model"], w.dims["d_ff"], smoe.ACT_SWIGLU if w.act == "swiglu"
+                else smoe.ACT_GELU, smoe.BF16)
+        row["separate"]["ws_bytes"] = smoe.lib.smoe_mlp_fwd_workspace_bytes(*dims)
+        row["fused"]["ws_bytes"] = smoe.lib.smoe_mlp_fwd_fused_combine_workspace_bytes(*dims)
+        res[label] = row
+        del t, w
+        torch.cuda.empty_cache()
+    return {"metric": "SMoE-MLP forward ms, separate vs fused combine (supplementary), 1 MI355X",
+            "value": res["mixtral"]["fused"]["fwd_ms"], "unit": "ms (fused, Mixtral shape)", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "SMoE-MLP forward: Mixtral shape (T=16384, d_model=4096, d_ff=14336, E=8, "
+                                   "k=2, SwiGLU) and high-granularity shape (T=16384, d_model=1024, d_ff=512, "
+                                   "E=64, k=8, Zipf, GELU)"},
+            "shapes": res}
 
 
 def attention_line(args):

@@ -188,6 +188,34 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2,
                  void* saved, size_t saved_bytes,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* smoe_mlp_fwd_fused_combine - smoe_mlp_fwd with the combine folded into the
+ * W2 product: each expert output row is scaled by its gate in the product's
+ * epilogue and added with fp32 atomics into an fp32 [T, d_model] token
+ * buffer (the front of the workspace), which one pass then rounds to `out`.
+ * This drops the [T*k, d_model] fp32 per-assignment rows' write and read.
+ * Same arguments, saved layout, limits and error codes as smoe_mlp_fwd;
+ * `saved` is interchangeable with it for smoe_mlp_bwd.  The workspace
+ * (smoe_mlp_fwd_fused_combine_workspace_bytes) holds T fp32 rows of
+ * d_model where smoe_mlp_fwd's holds T*k: the variant trades speed (one
+ * 4-byte atomic per element instead of 16-byte stores) for memory.  The
+ * order of the k fp32 additions per element is not fixed, so for k > 2
+ * results can differ between runs in the last fp32 bits before the final
+ * rounding (k <= 2 is exact: 0 + a + b = 0 + b + a).
+ * Article, para. 1 and 5 (the SMoE output as the gate-weighted sum of the
+ * chosen experts' outputs); project page, "How It Works" (scattered output).
+ * ------------------------------------------------------------------------ */
+size_t smoe_mlp_fwd_fused_combine_workspace_bytes(int64_t T, int32_t k,
+                                                  int32_t E, int64_t d_model,
+                                                  int64_t d_ff, int32_t act,
+                                                  int32_t dtype);
+int smoe_mlp_fwd_fused_combine(const void* x, const void* w1, const void* w3,
+                               const void* w2, int64_t T, int64_t d_model,
+                               int64_t d_ff, int32_t E, int32_t k,
+                               const int32_t* expert_idxs, const float* gates,
+                               int32_t act, int32_t dtype, void* out,
+                               void* saved, size_t saved_bytes,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * smoe_mlp_bwd - backward of smoe_mlp_fwd for upstream dout [T, d_model].
  *

@@ -57,6 +57,9 @@ _SIGS = {
     "smoe_mlp_fwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_mlp_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32, _i32,
                                     _vp, _vp, _sz, _vp, _sz, _vp]),
+    "smoe_mlp_fwd_fused_combine_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
+    "smoe_mlp_fwd_fused_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
+                                                  _i32, _i32, _vp, _vp, _sz, _vp, _sz, _vp]),
     "smoe_mlp_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_set_role_events": (ctypes.c_int, [_i32, _vp, _vp]),
     "smoe_probe_mfma_loop": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
@@ -247,8 +250,10 @@ def _mlp_dims(x, w1, w2, expert_idxs):
     return T, d_model, d_ff, E, k
 
 
-def smoe_mlp_fwd(x, w1, w2, expert_idxs, gates, act: str, w3=None, ws=None):
-    """SMoE-MLP forward; returns (out [T, d_model], saved buffer)."""
+def smoe_mlp_fwd(x, w1, w2, expert_idxs, gates, act: str, w3=None, ws=None, fused_combine=False):
+    """SMoE-MLP forward; returns (out [T, d_model], saved buffer).
+    fused_combine=True calls smoe_mlp_fwd_fused_combine (the gated k-sum
+    added with fp32 atomics inside the W2 product)."""
     _contig(x, w1, w2, w3, expert_idxs, gates)
     T, d_model, d_ff, E, k = _mlp_dims(x, w1, w2, expert_idxs)
     dev = x.device
@@ -256,12 +261,15 @@ def smoe_mlp_fwd(x, w1, w2, expert_idxs, gates, act: str, w3=None, ws=None):
     a = _ACTS[act]
     out = torch.empty((T, d_model), dtype=x.dtype, device=dev)
     saved = _ws(lib.smoe_mlp_saved_bytes(T, k, E, d_model, d_ff, a, dt), dev)
-    need = lib.smoe_mlp_fwd_workspace_bytes(T, k, E, d_model, d_ff, a, dt)
+    need = (lib.smoe_mlp_fwd_fused_combine_workspace_bytes if fused_combine
+            else lib.smoe_mlp_fwd_workspace_bytes)(T, k, E, d_model, d_ff, a, dt)
     if ws is None or ws.numel() < need:
         ws = _ws(need, dev)
-    _check(lib.smoe_mlp_fwd(_p(x), _p(w1), _p(w3), _p(w2), T, d_model, d_ff, E, k, _p(expert_idxs),
-                            _p(gates), a, dt, _p(out), _p(saved), saved.numel(), _p(ws), ws.numel(),
-                            _stream(dev)), "smoe_mlp_fwd")
+    fn, name = ((lib.smoe_mlp_fwd_fused_combine, "smoe_mlp_fwd_fused_combine") if fused_combine
+                else (lib.smoe_mlp_fwd, "smoe_mlp_fwd"))
+    _check(fn(_p(x), _p(w1), _p(w3), _p(w2), T, d_model, d_ff, E, k, _p(expert_idxs),
+              _p(gates), a, dt, _p(out), _p(saved), saved.numel(), _p(ws), ws.numel(),
+              _stream(dev)), name)
     return out, saved
 
 

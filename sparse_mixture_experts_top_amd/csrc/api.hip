@@ -232,12 +232,14 @@ struct MlpFwdWs {
   void* route = nullptr;
   void* a = nullptr;         // activation, grouped [M, d_ff]
   float* pairs = nullptr;    // expert outputs, scattered fp32 [M, d_model]
+                             // (fused combine: the fp32 token sums [T, d_model])
 };
-void layout_mlp_fwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t d_ff, int dtype, MlpFwdWs& w) {
+void layout_mlp_fwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t d_ff, int dtype, MlpFwdWs& w,
+                    bool fused = false) {
   const int64_t M = T * k;
   w.route = ar.take(route_ws_bytes(M, E));
   w.a = ar.take(size_t(M) * d_ff * esize(dtype));
-  w.pairs = static_cast<float*>(ar.take(size_t(M) * d_model * 4));
+  w.pairs = static_cast<float*>(ar.take(size_t(fused ? T : M) * d_model * 4));
 }
 
 struct MlpBwdWs {
@@ -756,10 +758,13 @@ size_t smoe_mlp_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_m
   return ar.used;
 }
 
-int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, int64_t T, int64_t d_model,
-                 int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs, const float* gates, int32_t act,
-                 int32_t dtype, void* out, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
-                 void* stream) {
+// fused: the down product adds its gated rows straight into an fp32 [T, d]
+// token buffer (fp32 atomics) in place of the per-assignment rows and the
+// separate combine; the buffer is the front of the per-assignment region.
+static int mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, int64_t T, int64_t d_model,
+                   int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs, const float* gates, int32_t act,
+                   int32_t dtype, void* out, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                   void* stream, bool fused) {
   SMOE_TRY(check_mlp(T, k, E, d_model, d_ff, act, dtype, w3));
   SMOE_TRY(need_ptr(w1, "w1"));
   SMOE_TRY(need_ptr(w2, "w2"));
@@ -777,7 +782,7 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
   if (saved_bytes < sl.total) return fail(SMOE_ERR_WORKSPACE, "saved_bytes=%zu < %zu", saved_bytes, sl.total);
   Arena ar(ws);
   MlpFwdWs wl;
-  layout_mlp_fwd(ar, T, k, E, d_model, d_ff, dtype, wl);
+  layout_mlp_fwd(ar, T, k, E, d_model, d_ff, dtype, wl, fused);
   if (ws_bytes < ar.used) return fail(SMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, ar.used);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* sv = static_cast<char*>(saved);
@@ -833,8 +838,16 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
   b.c0 = wl.pairs;
   b.c_scat = 1;
   b.ldc = d_model;
+  if (fused) {
+    b.gate = gates;
+    b.c_add_fan = k;
+  }
   GemmPlan pb;
   plan_gemm(b, pb, SEG_M, EPI_STORE, 0, bf16, 1);
+  if (fused) {
+    RoleTimer t(SMOE_ROLE_COMBINE, st);
+    SMOE_HIP(launch_zero(wl.pairs, size_t(T) * size_t(d_model) * sizeof(float), st), "mlp_fwd zero");
+  }
 
   // The m-tiles that exist whatever the routing (whole groups of 8 below
   // ceil(M / BM)) run both layers on the caller's stream; the remaining,
@@ -878,8 +891,36 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, 
     aux_lock.unlock();
   }
   RoleTimer t(SMOE_ROLE_COMBINE, st);
-  SMOE_HIP(launch_combine(wl.pairs, gates, T, k, d_model, out, bf16, st), "mlp_fwd combine");
+  if (fused)
+    SMOE_HIP(launch_combine(wl.pairs, nullptr, T, 1, d_model, out, bf16, st), "mlp_fwd convert");
+  else
+    SMOE_HIP(launch_combine(wl.pairs, gates, T, k, d_model, out, bf16, st), "mlp_fwd combine");
   return ok();
+}
+
+int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, int64_t T, int64_t d_model,
+                 int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs, const float* gates, int32_t act,
+                 int32_t dtype, void* out, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return mlp_fwd(x, w1, w3, w2, T, d_model, d_ff, E, k, expert_idxs, gates, act, dtype, out, saved, saved_bytes, ws,
+                 ws_bytes, stream, false);
+}
+
+size_t smoe_mlp_fwd_fused_combine_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff,
+                                                  int32_t act, int32_t dtype) {
+  (void)act;
+  Arena ar(nullptr);
+  MlpFwdWs w;
+  layout_mlp_fwd(ar, T, k, E, d_model, d_ff, dtype, w, true);
+  return ar.used;
+}
+
+int smoe_mlp_fwd_fused_combine(const void* x, const void* w1, const void* w3, const void* w2, int64_t T,
+                               int64_t d_model, int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs,
+                               const float* gates, int32_t act, int32_t dtype, void* out, void* saved,
+                               size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+  return mlp_fwd(x, w1, w3, w2, T, d_model, d_ff, E, k, expert_idxs, gates, act, dtype, out, saved, saved_bytes, ws,
+                 ws_bytes, stream, true);
 }
 
 size_t smoe_mlp_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act,

@@ -687,7 +687,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   };
   // staged output o -> global: row j of the fragment row goes to
   // base + rowoff(j) + colbase; rowoff / ok are held by lane j
-  auto flush = [&](int o, ST* base, int64_t rowoff, bool ok, int colbase) SMOE_INL {
+  // ADD: fp32 atomic adds of the four values instead of one store (the
+  // fused combine; several assignments add into one token's row)
+  auto flush = [&](int o, ST* base, int64_t rowoff, bool ok, int colbase, auto add) SMOE_INL {
     const uint32_t ro_lo = uint32_t(rowoff), ro_hi = uint32_t(uint64_t(rowoff) >> 32);
     static_for<32 / RPR>([&](auto i) SMOE_INL {
       const int j = int(i) * RPR + lane / CH, c = lane % CH;
@@ -696,9 +698,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
                                  uint32_t(__shfl(int(ro_lo), j, kWave)));
       const bool rok_j = __shfl(int(ok), j, kWave) != 0;
       const int colc = colbase + c * (16 / OB);
-      if (rok_j && colc < p.N) *reinterpret_cast<uint4*>(base + ro + colc) = d;
+      if (rok_j && colc < p.N) {
+        if constexpr (decltype(add)::value && std::is_same<ST, float>::value) {
+          float* dst = reinterpret_cast<float*>(base + ro + colc);
+          unsafeAtomicAdd(dst, __uint_as_float(d.x));
+          unsafeAtomicAdd(dst + 1, __uint_as_float(d.y));
+          unsafeAtomicAdd(dst + 2, __uint_as_float(d.z));
+          unsafeAtomicAdd(dst + 3, __uint_as_float(d.w));
+        } else {
+          *reinterpret_cast<uint4*>(base + ro + colc) = d;
+        }
+      }
     });
   };
+  constexpr std::false_type kStore{};
+  constexpr std::true_type kAdd{};
 
   if constexpr (MODE == SEG_K) {
     float* dst = (it.nitems == 1) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
@@ -712,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           put(0, fn, q, v);
         });
       });
-      flush(0, dst, int64_t(i) * p.N, i < p.Mo, T.n0 + wn * WN);
+      flush(0, dst, int64_t(i) * p.N, i < p.Mo, T.n0 + wn * WN, kStore);
     });
   } else {
     OutT* c0 = static_cast<OutT*>(p.c0);
@@ -874,21 +888,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       // staged rows -> global (grouped rows, or scattered for EPI_STORE)
       const int cb = T.n0 + (DUAL ? wn * (WN / 2) : wn * WN);
       if constexpr (EPI == EPI_STORE) {
-        if (c0) flush(0, c0, crow * p.ldc, rok[fm], cb);
+        if (c0) {
+          if (p.c_add_fan > 0)
+            flush(0, c0, (crow / p.c_add_fan) * p.ldc, rok[fm], cb, kAdd);
+          else
+            flush(0, c0, crow * p.ldc, rok[fm], cb, kStore);
+        }
       } else if constexpr (EPI == EPI_GELU_FWD) {
-        flush(0, c0, grow * p.ldc, rok[fm], cb);
-        flush(1, c1, grow * p.ldc, rok[fm], cb);
+        flush(0, c0, grow * p.ldc, rok[fm], cb, kStore);
+        flush(1, c1, grow * p.ldc, rok[fm], cb, kStore);
       } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-        flush(0, c0, grow * p.ldc, rok[fm], cb);
-        flush(1, c1, grow * p.ldc, rok[fm], cb);
-        flush(2, c2, grow * p.ldc, rok[fm], cb);
+        flush(0, c0, grow * p.ldc, rok[fm], cb, kStore);
+        flush(1, c1, grow * p.ldc, rok[fm], cb, kStore);
+        flush(2, c2, grow * p.ldc, rok[fm], cb, kStore);
       } else if constexpr (EPI == EPI_GELU_BWD) {
-        flush(0, c0, grow * p.ldc, rok[fm], cb);
-        flush(1, c2, grow * p.ldc, rok[fm], cb);
+        flush(0, c0, grow * p.ldc, rok[fm], cb, kStore);
+        flush(1, c2, grow * p.ldc, rok[fm], cb, kStore);
       } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        flush(0, c0, grow * p.ldc, rok[fm], cb);
-        flush(1, c1, grow * p.ldc, rok[fm], cb);
-        flush(2, c2, grow * p.ldc, rok[fm], cb);
+        flush(0, c0, grow * p.ldc, rok[fm], cb, kStore);
+        flush(1, c1, grow * p.ldc, rok[fm], cb, kStore);
+        flush(2, c2, grow * p.ldc, rok[fm], cb, kStore);
       }
     });
   }
@@ -1015,7 +1034,12 @@ __global__ __launch_bounds__(kFThreads) void gemm_f32_kernel(GemmArgs p) {
           if (c0) {
             if (p.gate)
               for (int j = 0; j < 4; ++j) v[j] *= g;
-            st4<float>(c0 + crow * p.ldc + n, v);
+            if (p.c_add_fan > 0) {
+              float* dst = c0 + (crow / p.c_add_fan) * p.ldc + n;
+              for (int j = 0; j < 4; ++j) unsafeAtomicAdd(dst + j, v[j]);
+            } else {
+              st4<float>(c0 + crow * p.ldc + n, v);
+            }
           }
         } else if constexpr (EPI == EPI_GELU_FWD) {
           float a[4];

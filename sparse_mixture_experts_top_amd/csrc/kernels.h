@@ -72,6 +72,8 @@ struct GemmArgs {
   void* c2;
   int64_t ldc;
   int c_scat;
+  int c_add_fan;       // SEG_M EPI_STORE, fp32 out: 0 stores row crow; f > 0 adds
+                       // (atomically) into row crow / f (the combine fused in)
   const float* gate;   // SEG_M epilogue gate, indexed by p = sidx[r]
   const void* aux0;    // SEG_M epilogue loads
   const void* aux1;

@@ -78,8 +78,9 @@ def test_parallel_linear_rejects_bad_arguments():
     assert call(gates=_fake(), wsb=16) == 4
 
 
-def test_mlp_rejects_bad_arguments():
-    f = lib.smoe_mlp_fwd
+@pytest.mark.parametrize("entry", ["smoe_mlp_fwd", "smoe_mlp_fwd_fused_combine"])
+def test_mlp_rejects_bad_arguments(entry):
+    f = getattr(lib, entry)
     base = [_fake(), _fake(), NULL, _fake(), 16, 64, 128, 4, 2, _fake(), _fake(), smoe.ACT_GELU,
             smoe.BF16, _fake(), _fake(), 1 << 30, _fake(), 1 << 30, NULL]
     a = list(base); a[11] = 5
@@ -90,6 +91,8 @@ def test_mlp_rejects_bad_arguments():
     assert f(*a) == 1                              # w3 given for GELU
     a = list(base); a[15] = 8
     assert f(*a) == 4                              # saved too small
+    a = list(base); a[17] = 8
+    assert f(*a) == 4                              # workspace too small
     g = lib.smoe_mlp_bwd
     assert g(_fake(), _fake(), _fake(), NULL, _fake(), 16, 64, 128, 4, 2, _fake(), _fake(),
              smoe.ACT_GELU, smoe.BF16, _fake(), 1 << 30, _fake(), _fake(), _fake(), _fake(), NULL,
@@ -180,3 +183,14 @@ def test_attention_rejects_bad_arguments():
 
     assert b(wsb=ws - 1) == 4
     assert b(dq=NULL) == 1
+
+
+def test_fused_combine_workspace_holds_token_rows_only():
+    """The fused-combine forward's workspace is smoe_mlp_fwd's less the
+    fp32 per-assignment rows beyond T: (T*k - T) * d_model * 4 bytes."""
+    for T, k, E, d, f in ((16384, 2, 8, 4096, 14336), (16384, 8, 64, 1024, 512), (7, 1, 4, 64, 64)):
+        for act in (smoe.ACT_GELU, smoe.ACT_SWIGLU):
+            for dt in (smoe.F32, smoe.BF16):
+                a = lib.smoe_mlp_fwd_workspace_bytes(T, k, E, d, f, act, dt)
+                b = lib.smoe_mlp_fwd_fused_combine_workspace_bytes(T, k, E, d, f, act, dt)
+                assert a - b == (T * k - T) * d * 4

@@ -120,3 +120,68 @@ def test_mlp_backward_with_second_stream(smoe):
         e = rel_err(got, rc[n])
         say(f"  {n}[cols] err {e:.2e}")
         assert e <= BF16_TOL, n
+
+
+@pytest.mark.parametrize("dtype,act,T,k,E,routing", [
+    ("f32", "gelu", 300, 2, 6, "softmax"),
+    ("bf16", "swiglu", 300, 2, 6, "softmax"),
+    ("bf16", "gelu", 1200, 3, 12, "zipf"),
+    ("bf16", "swiglu", 517, 8, 16, "softmax"),
+])
+def test_mlp_fused_combine(smoe, dtype, act, T, k, E, routing):
+    """smoe_mlp_fwd_fused_combine: out against the oracle to the same bar as
+    smoe_mlp_fwd and close to it; the saved buffer is bit-identical, so the
+    backward is unchanged; for k = 2 two runs agree bit for bit."""
+    say(f"mlp fused combine {dtype} {act} T={T} k={k} E={E} {routing}")
+    w = make_mlp(T, 136 if dtype == "f32" else 128, 200 if dtype == "f32" else 256, E, k, act, dtype,
+                 140 + k, routing=routing, w_std=0.06)
+    d = upload(w)
+    args = (d["x"], d["w1"], d["w2"], d["expert_idxs"], d["gates"], act)
+    o_ref, s_ref = smoe.smoe_mlp_fwd(*args, w3=d.get("w3"))
+    o1, s1 = smoe.smoe_mlp_fwd(*args, w3=d.get("w3"), fused_combine=True)
+    o2, _ = smoe.smoe_mlp_fwd(*args, w3=d.get("w3"), fused_combine=True)
+    torch.cuda.synchronize()
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    d_model, d_ff = w.dims["d_model"], w.dims["d_ff"]
+    v1 = smoe.saved_views(s1, T, k, E, d_model, d_ff, act, dt)
+    v_ref = smoe.saved_views(s_ref, T, k, E, d_model, d_ff, act, dt)
+    for n in v_ref:
+        assert torch.equal(v1[n], v_ref[n]), n
+    if k <= 2:
+        assert torch.equal(o1, o2)
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    f = lambda n: w.f32(n).astype(np.float64)
+    w3 = f("w3") if act == "swiglu" else None
+    idx, gates = w.tensors["expert_idxs"], w.tensors["gates"].astype(np.float64)
+    ref = oracle.mlp_fwd(f("x"), f("w1"), f("w2"), idx, gates, act, w3=w3,
+                         storage="f64" if dtype == "f32" else "bf16")
+    e = rel_err(host(o1), ref)
+    e_same = rel_err(host(o1), host(o_ref).astype(np.float64))
+    say(f"  out err {e:.2e}  vs unfused {e_same:.2e}")
+    assert e <= tol
+    assert e_same <= tol
+
+
+def test_mlp_fused_combine_with_second_stream(smoe):
+    """A shape whose forward runs its routing-dependent m-tiles on the second
+    stream (T=4096, d_model=2048, d_ff=512, E=8, k=2, SwiGLU, bf16): both
+    streams' W2 tiles add into the one token buffer; sampled tokens against
+    the oracle, all tokens against smoe_mlp_fwd."""
+    say("mlp fused combine with the second stream")
+    w = make_mlp(4096, 2048, 512, 8, 2, "swiglu", "bf16", 145, w_std=0.02)
+    d = upload(w)
+    args = (d["x"], d["w1"], d["w2"], d["expert_idxs"], d["gates"], "swiglu")
+    o_ref, _ = smoe.smoe_mlp_fwd(*args, w3=d["w3"])
+    o1, _ = smoe.smoe_mlp_fwd(*args, w3=d["w3"], fused_combine=True)
+    torch.cuda.synchronize()
+    e_same = rel_err(host(o1), host(o_ref).astype(np.float64))
+    say(f"  vs unfused {e_same:.2e}")
+    assert e_same <= BF16_TOL
+    f = lambda n: w.f32(n).astype(np.float64)
+    idx, gates = w.tensors["expert_idxs"], w.tensors["gates"].astype(np.float64)
+    toks = np.unique(np.concatenate([[0, w.T - 1], np.random.default_rng(1451).choice(w.T, 24, replace=False)]))
+    ref = oracle.mlp_fwd(f("x"), f("w1"), f("w2"), idx, gates, "swiglu", w3=f("w3"), storage="bf16",
+                         tokens=toks)
+    e = rel_err_stored_bf16(host(o1)[toks], ref[toks])
+    say(f"  out[tokens] err {e:.2e}")
+    assert e <= BF16_TOL
