@@ -145,3 +145,69 @@ def test_moa_layer_chain(smoe):
         e = rel_err_stored_bf16(host(got), want) if stored else rel_err(host(got), want)
         say(f"  {n} err {e:.2e}")
         assert e <= BF16_TOL, n
+
+
+def test_attention_scores_growing_along_the_sequence(smoe):
+    """Later keys scaled up by powers of two (exact in bf16) and q by 4, so
+    each row's maximum score climbs by far more than 8 (base 2) across the
+    64-key steps: every step moves the running maximum, and the output and
+    normaliser are rescaled many times.  Forward and backward against the
+    oracle on the same (scaled) inputs."""
+    B, S, E, k = 2, 300, 4, 2
+    say(f"moa attention growing scores B={B} S={S} E={E} k={k}")
+    w, sidx, f, d = setup(B, S, E, k, 440)
+    pos = np.arange(B * S) % S
+    scale = 2.0 ** np.floor(4 * pos / S)          # 1, 2, 4, 8 along each sequence
+    f["q"] = f["q"] * 4.0
+    f["k"] = f["k"] * scale[:, None]
+    d["q"], d["k"] = bf16_dev(f["q"]), bf16_dev(f["k"])
+    assert np.array_equal(host(d["q"]), f["q"]) and np.array_equal(host(d["k"]), f["k"])
+    ref = oracle.moa_attention_fwd(f["q"], f["k"], f["v"], sidx, k, S)
+    # the scores really span many rescales: the maximum of a row at the end
+    # of its sequence exceeds that of the first 64 keys by more than 8 / ln 2
+    z = (f["q"] @ f["k"].T) / np.sqrt(128.0)
+    tok = sidx // k
+    last = np.nonzero(tok % S == S - 1)[0]
+    assert last.size > 0
+    lo = (tok[last] // S) * S
+    early = np.array([z[r, l:l + 64].max() for r, l in zip(last, lo)])
+    full = np.array([z[r, l:t + 1].max() for r, l, t in zip(last, lo, tok[last])])
+    say(f"  max-score growth over the sequence: min {float((full - early).min()):.1f}")
+    assert np.all(full - early > 8 / np.log(2))
+    check_fwd(smoe, w, sidx, f, d)
+    check_bwd(smoe, w, sidx, f, d)
+    assert np.isfinite(ref["lse"]).all()
+
+
+def test_attention_one_token_sequences(smoe):
+    """seq_len = 1: every row sees only its own token's key, so o is that
+    token's v exactly and lse its single score.  In the backward the one
+    probability is 1, so dp - D = do.v - do.o = 0 up to the order of two
+    fp32 sums: dq and dk vanish to that rounding, and dv[t] is the sum of do
+    over t's k rows."""
+    B, S, E, k = 37, 1, 4, 3
+    say(f"moa attention seq_len 1, T={B} k={k}")
+    w, sidx, f, d = setup(B, S, E, k, 450)
+    o, lse = check_fwd(smoe, w, sidx, f, d)
+    tok = sidx // k
+    np.testing.assert_array_equal(host(o), f["v"][tok])
+    dq, dk, dv = smoe.smoe_moa_attention_bwd(d["q"], d["k"], d["v"], d["sidx"], k, S, o, lse, d["do"])
+    torch.cuda.synchronize()
+    want_dv = np.zeros_like(f["v"])
+    np.add.at(want_dv, tok, f["do"])
+    e = rel_err_stored_bf16(host(dv), want_dv)
+    rms_do = float(np.sqrt(np.mean(f["do"] ** 2)))
+    say(f"  dv err {e:.2e}  max|dq| {float(np.abs(host(dq)).max()):.1e}  max|dk| {float(np.abs(host(dk)).max()):.1e}")
+    assert e <= BF16_TOL
+    assert np.abs(host(dq)).max() <= 1e-4 * rms_do and np.abs(host(dk)).max() <= 1e-4 * rms_do
+
+
+def test_attention_no_tokens(smoe):
+    """T = 0: both calls succeed and return empty results."""
+    say("moa attention T=0")
+    e = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
+    sidx = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    o, lse = smoe.smoe_moa_attention_fwd(e(0, 128), e(0, 128), e(0, 128), sidx, 2, 16)
+    dq, dk, dv = smoe.smoe_moa_attention_bwd(e(0, 128), e(0, 128), e(0, 128), sidx, 2, 16, o, lse, e(0, 128))
+    torch.cuda.synchronize()
+    assert o.shape == (0, 128) and lse.shape == (0,) and dq.shape == (0, 128) and dk.shape == (0, 128)
