@@ -1,6 +1,7 @@
 """Pins for oracle.mlp_fwd / mlp_bwd / mlp_dw_cols: brute-force dense
 one-hot evaluation, torch fp64 autograd, central finite differences and the
-stated invariants (E=1,k=1 dense; token permutation; identical experts)."""
+stated invariants (E=1,k=1 dense; token permutation; identical experts; k = E
+with uniform gates as one wide dense MLP)."""
 import numpy as np
 import pytest
 import torch
@@ -155,3 +156,30 @@ def test_bf16_storage_rounds_at_the_stated_points(act):
                 a = rd(oracle.silu(h) * rd(x[t] @ w3[e]))
             ref[t] += gates[t, j] * (a @ w2[e])
     np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_all_experts_with_uniform_gates_is_one_wide_dense_mlp(act):
+    """k = E with every gate 1/E: the layer averages all experts, which is
+    one dense MLP whose hidden units are all experts' units side by side
+    (W1 columns concatenated, W2 rows stacked and scaled by 1/E), evaluated
+    here with torch's own GELU / SiLU in fp64.  Each token lists the experts
+    in its own shuffled order, which must not matter."""
+    rng = np.random.default_rng(61)
+    T, d, f, E = 7, 6, 5, 4
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((E, d, f)) * 0.5
+    w3 = rng.standard_normal((E, d, f)) * 0.5 if act == "swiglu" else None
+    w2 = rng.standard_normal((E, f, d)) * 0.5
+    idx = np.stack([rng.permutation(E) for _ in range(T)]).astype(np.int32)
+    gates = np.full((T, E), 1.0 / E)
+    out = oracle.mlp_fwd(x, w1, w2, idx, gates, act, w3=w3)
+    W1 = torch.tensor(np.concatenate(list(w1), axis=1))        # [d, E*f]
+    W2 = torch.tensor(np.concatenate(list(w2), axis=0)) / E    # [E*f, d]
+    h = torch.tensor(x) @ W1
+    if act == "gelu":
+        a = torch.nn.functional.gelu(h)
+    else:
+        a = torch.nn.functional.silu(h) * (torch.tensor(x) @ torch.tensor(np.concatenate(list(w3), axis=1)))
+    want = (a @ W2).numpy()
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-12)
