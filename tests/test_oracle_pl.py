@@ -41,11 +41,11 @@ def test_golden_tiny():
     np.testing.assert_array_equal(dg, b["dgates"])
 
 
-@pytest.mark.parametrize("xg,yg", [(False, False), (False, True), (True, False), (True, True)])
-@pytest.mark.parametrize("x_rows", ["T", "M"])
+# a grouped input always has T*k rows, so x_rows = "T" pairs only with a
+# scattered input
+@pytest.mark.parametrize("xg,yg,x_rows", [(False, False, "T"), (False, True, "T"), (False, False, "M"),
+                                          (False, True, "M"), (True, False, "M"), (True, True, "M")])
 def test_forward_vs_dense_one_hot(xg, yg, x_rows):
-    if xg and x_rows == "T":
-        pytest.skip("grouped input always has T*k rows")
     x_s, x_m, w, idx = _case(seed=1)
     T, k = idx.shape
     x = x_s if x_rows == "T" else x_m
