@@ -258,3 +258,23 @@ def test_router_bwd_many_tokens(smoe):
     colsum = np.abs(dwh.sum(axis=0))
     say(f"  max |sum_e dw| / sum_e |dw| = {float((colsum / scale).max()):.2e}")
     assert np.all(colsum <= 1e-3 * scale)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_large_logits(smoe, dtype):
+    """x scaled by 64 (exact in bf16 and fp32): logits of size ~64, so
+    exp of an unshifted logit would overflow fp32; the softmax over the
+    chosen k must shift by the top one.  Choices, gates, dw and dx against
+    the oracle, everything finite."""
+    T, d, E, k = 500, 256, 16, 4
+    say(f"router large logits T={T} d={d} E={E} k={k} {dtype}")
+    w = make_router(T, d, E, k, dtype, 360)
+    x = w.f32("x").astype(np.float64) * 64.0
+    g = w.f32("gate_w").astype(np.float64)
+    xd, gd = dev_tensor(w.tensors["x"]) * 64, wt_tensor(w.tensors["gate_w"])
+    assert np.array_equal(host(xd), x)
+    assert np.abs(x @ g).max() > 88.0          # exp(88.7) is the fp32 limit
+    r, ref = check_fwd(smoe, x, g, k, xd, gd)
+    assert torch.isfinite(r["gates"]).all()
+    dw, dx = check_bwd(smoe, x, g, ref, w.tensors["dgates"], xd, gd, dtype)
+    assert torch.isfinite(dw).all() and torch.isfinite(dx.float()).all()
