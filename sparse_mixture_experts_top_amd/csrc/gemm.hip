@@ -51,19 +51,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kThreads = 512;   // bf16 kernel
-#ifndef SMOE_BK
-#define SMOE_BK 32
-#endif
-#ifndef SMOE_NS
-#define SMOE_NS 4
-#endif
-#ifndef SMOE_SCHED
-#define SMOE_SCHED 0
-#endif
-constexpr int kBK = SMOE_BK;    // K of one pipeline stage (32 or 64)
-constexpr int kNS = SMOE_NS;    // LDS stages in flight
-static_assert(kBK == 32 || kBK == 64, "K step");
-static_assert(kNS >= 2, "stages");
+constexpr int kBK = 64;         // K of one pipeline stage: 128-byte rows of a K-contiguous operand
+constexpr int kNSL = kBK / 16;  // 16-wide k slices per stage
 constexpr uint32_t kOOB = 0xFFFFFFF0u;  // byte offset past every buffer: reads as 0
 
 enum Lay { LAY_K = 0, LAY_MN = 1 };
@@ -71,20 +60,19 @@ enum Lay { LAY_K = 0, LAY_MN = 1 };
 SMOE_DEV int fdiv(int x, uint32_t m, int s) { return int((uint64_t(uint32_t(x)) * m) >> s); }
 
 // K-layout tile: row j (one gathered token row, or one column of W read as
-// W^T) holds the stage's kBK values of k, KC 16-byte chunks.  Chunk c of row
-// j sits at chunk c ^ swz_k(j).  A 128-bit LDS read serves 16 lanes at a
-// time, i.e. 16 consecutive rows at one logical chunk; the 64 banks cover
-// 256 bytes = 2 rows of 128 bytes (kBK = 64) or 4 rows of 64 bytes (kBK =
-// 32), and the swizzle gives the rows that share banks distinct chunks.
+// W^T) holds the stage's 64 values of k, 128 bytes = 8 chunks of 16 bytes;
+// chunk c of row j sits at chunk c ^ swz_k(j).  A 128-bit LDS read serves
+// 16 lanes at a time, i.e. 16 consecutive rows at one logical chunk; the 64
+// banks cover 256 bytes = 2 rows, and the swizzle gives the 8 row pairs 8
+// distinct chunks.  A wave's copy instruction fills 8 whole rows: every
+// lane group of 8 reads one complete 128-byte line (whole lines move twice
+// as fast from L2 into LDS as half lines).
 struct KGeom {
   static constexpr int RB = 2 * kBK;    // bytes per row
   static constexpr int KC = kBK / 8;    // 16-byte chunks per row
   static constexpr int RPL = 64 / KC;   // rows per wave copy
 };
-SMOE_DEV int swz_k(int row) {
-  if constexpr (kBK == 64) return (row >> 1) & 7;
-  else return (row >> 2) & 3;
-}
+SMOE_DEV int swz_k(int row) { return (row >> 1) & 7; }
 // MN-layout: chunk c (8 mn) of k-row r is stored at chunk c ^ swz_mn(r).  A
 // 64-bit LDS read is served 32 lanes at a time; for a transposing fragment
 // read those 32 lanes take four aligned chunks from each of four consecutive
@@ -106,25 +94,17 @@ SMOE_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
   r.w = 0x00020000u;
   return r;
 }
-// The 64 lanes of the wave each copy 16 bytes (at byte offset voff of the
-// buffer) to wave_lds + 16 * lane, straight into LDS.  Written as inline asm
-// so that the compiler does not order later LDS reads of OTHER stages behind
-// these copies (it cannot tell the stages apart); the kernel waits for the
-// copies itself (wait_vmem) before the barrier that publishes a stage.  The
-// asm has no register outputs; its inputs are read when it issues.
-// The LDS address is the low 32 bits of the flat address of wave_lds (the
-// LDS aperture starts at a multiple of 4 GiB).
+// The 64 lanes of the wave each copy 16 bytes (at byte offset voff + soff
+// of the buffer) to wave_lds + 16 * lane, straight into LDS.  soff is the
+// wave-uniform part (a step's advance along k), so a copy inside the buffer
+// needs no vector arithmetic per step.  Written as inline asm so that the
+// compiler does not order later LDS reads of the OTHER stage behind these
+// copies (it cannot tell the stages apart); the kernel waits for the copies
+// itself (wait_vmem) before the barrier that publishes a stage.  The asm
+// has no register outputs; its inputs are read when it issues.  The LDS
+// address is the low 32 bits of the flat address of wave_lds (the LDS
+// aperture starts at a multiple of 4 GiB).
 SMOE_DEV uint32_t lds_addr(const char* p) { return uint32_t(reinterpret_cast<uintptr_t>(p)); }
-SMOE_DEV void dma16(rsrc_t r, char* wave_lds, uint32_t voff) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(wave_lds));
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(r), "s"(m0v)
-               : "memory", "m0");
-}
-// the same at byte offset voff + soff: soff is the wave-uniform part (the
-// step's advance along k), so a copy inside the buffer needs no vector
-// arithmetic per step.  Only used where voff + soff stays in range.
 SMOE_DEV void dma16s(rsrc_t r, char* wave_lds, uint32_t voff, uint32_t soff) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(wave_lds));
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
@@ -147,6 +127,8 @@ SMOE_DEV void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
+// wait until every LDS access of this wave is done: s_waitcnt lgkmcnt(0)
+SMOE_DEV void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Which tile this workgroup computes.  Returns false if none.
 struct TileInfo {
@@ -156,7 +138,6 @@ struct TileInfo {
   int n0;     // first output column (real)
   int nt;     // SEG_M n-tile index
 };
-
 template <int BM, int BN, int MODE, bool DUAL>
 SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
   // The grid is sized for an upper bound on the tiles; how many exist
@@ -280,22 +261,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2, STAGE = A_BYTES + B_BYTES;
   static_assert(BN >= 128 && BM >= 128, "tile");
   static_assert(!DUAL || (MODE == SEG_M && BLAY == LAY_MN && BN == 256), "dual B layout");
-  // one LDS object per stage, always named statically (the loop below is
-  // unrolled by kNS): the compiler can then tell a stage being read from the
-  // stages whose copies are still in flight
+  // two stage buffers, named statically (the loop below is unrolled by
+  // two): the compiler can then tell the stage being read from the one
+  // whose copies are in flight
   __shared__ __attribute__((aligned(16))) char smem0[STAGE];
   __shared__ __attribute__((aligned(16))) char smem1[STAGE];
-  __shared__ __attribute__((aligned(16))) char smem2[kNS > 2 ? STAGE : 16];
-  __shared__ __attribute__((aligned(16))) char smem3[kNS > 3 ? STAGE : 16];
-  __shared__ __attribute__((aligned(16))) char smem4[kNS > 4 ? STAGE : 16];
-  static_assert(kNS <= 5, "stages");
   auto stage = [&](auto s) SMOE_INL -> char* {
-    constexpr int S = decltype(s)::value % kNS;
-    if constexpr (S == 0) return smem0;
-    else if constexpr (S == 1) return smem1;
-    else if constexpr (S == 2) return smem2;
-    else if constexpr (S == 3) return smem3;
-    else return smem4;
+    if constexpr (decltype(s)::value % 2 == 0) return smem0;
+    else return smem1;
   };
 
   TileInfo T;
@@ -342,8 +315,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     }
     return make_rsrc(base, bytes);
   };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
   // row pitches in bytes (every operand is under 4 GiB)
   const uint32_t lda2 = uint32_t(p.lda * 2), ldb2 = uint32_t(p.ldb * 2);
   // SEG_K: all-ones when the operand's rows are gathered (a mask rather
@@ -356,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   // and columns outside the tile's valid range read other (in-range) data:
   // their products land only in outputs that are never stored.  Only k
   // beyond the end of the reduction must read zero, on both operands; the
-  // step that crosses it takes a per-lane path.
+  // step that crosses it masks the lanes past it.
   uint32_t a_off[NA], b_off[NB];
   int ka[NA], kb_[NB];
   // SEG_K: column byte offset of the lane (a_col / b_col) for gathered rows
@@ -413,24 +384,28 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   const rsrc_t rB1 = descB(std::integral_constant<int, 1>{});
 
   // SEG_K: the source rows of the gathered operand come from
-  // sorted_scattered_idxs.  The indices of the 32 grouped rows of step j are
-  // copied into an LDS ring (slot j % kRing, 64 dwords: every wave copies the
-  // same 64 indices, so each wave's count of copies per step is the same) in
-  // step j-5, ahead of the copies of stage j-2; the stage waits therefore
-  // also cover them, and the barrier of step j-3 publishes them before step
-  // j-3 issues stage j.  The indices are read back with LDS reads, which keep
-  // the LDS counter in order (no scalar loads in the loop).
-  constexpr int kRing = 8, kIdxAhead = kNS + 1;
-  constexpr int IDX = MODE == SEG_K ? 1 : 0;   // index copies per step
+  // sorted_scattered_idxs.  The indices of the 64 grouped rows of step j are
+  // copied into an LDS ring (slot j % kRing, one dword per lane) at the
+  // barrier of step j-4, so the wait before the barrier of step j-3
+  // covers them and that barrier publishes them; they are read into
+  // registers right after it and address the copies of stage j, issued at
+  // the barrier of step j-2.  Reading them back from LDS keeps the loop free
+  // of scalar loads and data-dependent branches.
+  // A gated weight gradient (EPI_PARTIAL_GATED) copies the rows' scales
+  // into a second ring the same way; the fragments of A are scaled in
+  // registers right before their multiplies, so no scaled copy of A exists.
+  constexpr int kRing = 8, kIdxAhead = 4;
+  constexpr bool GATED = MODE == SEG_K && EPI == EPI_PARTIAL_GATED;
   __shared__ __attribute__((aligned(16))) int ring[MODE == SEG_K ? kRing * 64 : 1];
+  __shared__ __attribute__((aligned(16))) float gring[GATED ? kRing * 64 : 1];
   auto idx_copy = [&](int j) SMOE_INL {
     if constexpr (MODE == SEG_K) {
       const uint32_t r = uint32_t(it.row0 + j * kBK + lane);
       dma4(make_rsrc(p.sidx, int64_t(p.M) * 4), reinterpret_cast<char*>(ring + (j % kRing) * 64), r * 4u);
+      if constexpr (GATED)
+        dma4(make_rsrc(p.kscale, int64_t(p.M) * 4), reinterpret_cast<char*>(gring + (j % kRing) * 64), r * 4u);
     }
   };
-  // the lane's raw indices for the copies of step j, read into registers
-  // right after the barrier that published them, ahead of the fragment reads
   constexpr int SA = MODE == SEG_K ? NA : 1, SB = MODE == SEG_K ? NB : 1;
   int gia[SA], gib[SB];
   auto idx_fetch = [&](int j) SMOE_INL {
@@ -438,92 +413,88 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       // read for both operands, gathered or not (no branch: the copies
       // select the index or the plain row)
       const int* slot = ring + (j % kRing) * 64;
-      static_for<NA>([&](auto t) SMOE_INL { gia[t] = slot[(int(t) * 8 + wave) * GA::RPI + lane / GA::CPR]; });
-      static_for<NB>([&](auto t) SMOE_INL { gib[t] = slot[(int(t) * 8 + wave) * GB::RPI + lane / GB::CPR]; });
+      static_for<NA>([&](auto t) SMOE_INL { gia[t] = slot[ka[t]]; });
+      static_for<NB>([&](auto t) SMOE_INL { gib[t] = slot[kb_[t]]; });
     }
   };
 
-  // ---------------- copy step kt into stage `stg` -------------------------
-  // SEG_M: a uniform branch on the K part picks the buffer descriptors.  A
-  // step inside the reduction advances every copy by one scalar offset; the
-  // step that crosses its end (a uniform branch, at most one per part)
-  // zero-fills the lanes past it.
-  auto issue_part = [&](auto part, int kl, char* stg) SMOE_INL {
-    constexpr int P = decltype(part)::value;
-    char* As = stg;
-    char* Bs = stg + A_BYTES;
-    const int Kp = P ? K1 : K0;
-    const rsrc_t& rA = P ? rA1 : rA0;
-    const rsrc_t& rB = P ? rB1 : rB0;
-    auto copies = [&](auto full) SMOE_INL {
-      constexpr bool F = decltype(full)::value;
-      // K-layout A: lane copies logical chunk (lane % KC) ^ swz_k(row)
-      static_for<NA>([&](auto t) SMOE_INL {
-        char* dst = As + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB;
-        if constexpr (F) dma16s(rA, dst, a_off[t], uint32_t(kl) * 2);
-        else dma16(rA, dst, kl + ka[t] < Kp ? a_off[t] + uint32_t(kl) * 2 : kOOB);
-      });
-      if constexpr (BLAY == LAY_K) {
-        static_for<NB>([&](auto t) SMOE_INL {
-          char* dst = Bs + (int(t) * 8 + wave) * KGeom::RPL * KGeom::RB;
-          if constexpr (F) dma16s(rB, dst, b_off[t], uint32_t(kl) * 2);
-          else dma16(rB, dst, kl + kb_[t] < Kp ? b_off[t] + uint32_t(kl) * 2 : kOOB);
-        });
-      } else {
-        // one K part: W[e] viewed [k][n] has K0 rows
-        static_for<NB>([&](auto t) SMOE_INL {
-          char* dst;
-          if constexpr (DUAL) {
-            using G = MnGeom<BN / 2>;
-            constexpr int tt = int(t) % (NB / 2);
-            dst = Bs + (int(t) / (NB / 2)) * (BN / 2) * kBK * 2 + (tt * 8 + wave) * G::RPI * G::RB;
-          } else {
-            dst = Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB;
-          }
-          // dual: loads t >= NB/2 read W3
-          const rsrc_t& r = (DUAL && int(t) >= NB / 2) ? rB1 : rB0;
-          if constexpr (F) dma16s(r, dst, b_off[t], uint32_t(kl) * ldb2);
-          else dma16(r, dst, kl + kb_[t] < K0 ? b_off[t] + uint32_t(kl) * ldb2 : kOOB);
-        });
-      }
-    };
-    const bool full = kl + kBK <= Kp && (BLAY == LAY_K || kl + kBK <= K0);
-    if (full) copies(std::true_type{});
-    else copies(std::false_type{});
-  };
-  auto issue = [&](int kt, char* stg) SMOE_INL {
+  // ---------------- copies of one stage ------------------------------------
+  // plan(kt) sets, for every copy of step kt, the lane's byte offset cv[c],
+  // the scalar offsets of the two operands and the descriptors; copy(c, stg)
+  // issues copy c into stage buffer stg.  A step inside the reduction adds
+  // the step's advance as the scalar offset; the step that crosses the end
+  // of a part (a uniform branch, at most one per part) masks the lanes
+  // past it instead.
+  uint32_t cv[LPS];
+  uint32_t csa = 0, csb = 0;
+  rsrc_t cra = rA0, crb = rB0;
+  auto plan = [&](int kt) SMOE_INL {
     if constexpr (MODE == SEG_M) {
-      if (kt >= KT0) issue_part(P1{}, (kt - KT0) * kBK, stg);
-      else issue_part(P0{}, kt * kBK, stg);
+      const bool p1 = kt >= KT0;
+      const int kl = (p1 ? kt - KT0 : kt) * kBK;
+      const int Kp = p1 ? K1 : K0;
+      cra = p1 ? rA1 : rA0;
+      crb = (BLAY == LAY_K && p1) ? rB1 : rB0;
+      const uint32_t sa = uint32_t(kl) * 2;
+      const uint32_t sb = BLAY == LAY_K ? uint32_t(kl) * 2 : uint32_t(kl) * ldb2;
+      if (kl + kBK <= Kp) {
+        static_for<NA>([&](auto t) SMOE_INL { cv[t] = a_off[t]; });
+        static_for<NB>([&](auto t) SMOE_INL { cv[NA + t] = b_off[t]; });
+        csa = sa;
+        csb = sb;
+      } else {
+        static_for<NA>([&](auto t) SMOE_INL { cv[t] = kl + ka[t] < Kp ? a_off[t] + sa : kOOB; });
+        static_for<NB>([&](auto t) SMOE_INL { cv[NA + t] = kl + kb_[t] < Kp ? b_off[t] + sb : kOOB; });
+        csa = csb = 0;
+      }
     } else {
-      // SEG_K: a plain operand advances by the step's first row (a scalar
-      // offset); a gathered one addresses each row from its index
-      char* As = stg;
-      char* Bs = stg + A_BYTES;
+      // a plain operand advances by the step's first row (a scalar offset);
+      // a gathered one addresses each row from its index
       const int r0 = it.row0 + kt * kBK;
       const uint32_t sa = (uint32_t(r0) * lda2) & uint32_t(~scat_a);
       const uint32_t sb = (uint32_t(r0) * ldb2) & uint32_t(~scat_b);
-      auto copies = [&](auto full) SMOE_INL {
-        constexpr bool F = decltype(full)::value;
-        static_for<NA>([&](auto t) SMOE_INL {
-          const uint32_t g = uint32_t(fdiv(gia[t], p.a_fan_m, p.a_fan_s)) * lda2 + a_col[t];
-          const uint32_t vo = (g & uint32_t(scat_a)) | (a_off[t] & uint32_t(~scat_a));
-          char* dst = As + (int(t) * 8 + wave) * GA::RPI * GA::RB;
-          if constexpr (F) dma16s(rA0, dst, vo, sa);
-          else dma16(rA0, dst, r0 + ka[t] < it.row1 ? vo + sa : kOOB);
-        });
-        static_for<NB>([&](auto t) SMOE_INL {
-          const uint32_t g = uint32_t(fdiv(gib[t], p.b_fan_m, p.b_fan_s)) * ldb2 + b_col[t];
-          const uint32_t vo = (g & uint32_t(scat_b)) | (b_off[t] & uint32_t(~scat_b));
-          char* dst = Bs + (int(t) * 8 + wave) * GB::RPI * GB::RB;
-          if constexpr (F) dma16s(rB0, dst, vo, sb);
-          else dma16(rB0, dst, r0 + kb_[t] < it.row1 ? vo + sb : kOOB);
-        });
-      };
-      if (r0 + kBK <= it.row1) copies(std::true_type{});
-      else copies(std::false_type{});
+      static_for<NA>([&](auto t) SMOE_INL {
+        const uint32_t g = uint32_t(fdiv(gia[t], p.a_fan_m, p.a_fan_s)) * lda2 + a_col[t];
+        cv[t] = (g & uint32_t(scat_a)) | (a_off[t] & uint32_t(~scat_a));
+      });
+      static_for<NB>([&](auto t) SMOE_INL {
+        const uint32_t g = uint32_t(fdiv(gib[t], p.b_fan_m, p.b_fan_s)) * ldb2 + b_col[t];
+        cv[NA + t] = (g & uint32_t(scat_b)) | (b_off[t] & uint32_t(~scat_b));
+      });
+      if (r0 + kBK <= it.row1) {
+        csa = sa;
+        csb = sb;
+      } else {
+        static_for<NA>([&](auto t) SMOE_INL { cv[t] = r0 + ka[t] < it.row1 ? cv[t] + sa : kOOB; });
+        static_for<NB>([&](auto t) SMOE_INL { cv[NA + t] = r0 + kb_[t] < it.row1 ? cv[NA + t] + sb : kOOB; });
+        csa = csb = 0;
+      }
+    }
+    // uniform by construction; say so, so that they stay scalar operands
+    csa = __builtin_amdgcn_readfirstlane(csa);
+    csb = __builtin_amdgcn_readfirstlane(csb);
+  };
+  // every copy instruction fills 1 KB of its operand's tile: 8 K-layout
+  // rows, or 64 / CPR MN-layout k-rows
+  auto copy = [&](auto c, char* stg) SMOE_INL {
+    constexpr int C = decltype(c)::value;
+    if constexpr (C < NA) {
+      dma16s(cra, stg + (C * 8 + wave) * 1024, cv[C], csa);
+    } else {
+      constexpr int t = C - NA;
+      char* Bs = stg + A_BYTES;
+      if constexpr (DUAL) {
+        // loads t >= NB/2 read W3 into the second sub-tile
+        constexpr int tt = t % (NB / 2);
+        dma16s(t >= NB / 2 ? rB1 : rB0, Bs + (t / (NB / 2)) * (BN / 2) * kBK * 2 + (tt * 8 + wave) * 1024, cv[C],
+               csb);
+      } else {
+        dma16s(crb, Bs + (t * 8 + wave) * 1024, cv[C], csb);
+      }
     }
   };
+  static_assert(KGeom::RPL * KGeom::RB == 1024 && GA::RPI * GA::RB == 1024 && GB::RPI * GB::RB == 1024,
+                "1 KB per copy");
 
   f32x16_t acc[FM][FN];
   static_for<FM>([&](auto i) SMOE_INL {
@@ -532,119 +503,159 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     });
   });
 
-  auto frags = [&](const char* stg, int s, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) SMOE_INL {
-    const char* As = stg;
+  // fragment of row block fm (A) / column block fn (B) of k slice s
+  auto frag_a = [&](const char* stg, auto fm, int s) SMOE_INL {
+    if constexpr (ALAY == LAY_K) return frag_k(stg, wm * WM + int(fm) * 32, s, lane);
+    else return frag_mn<BM>(stg, wm * WM + int(fm) * 32, s, lane);
+  };
+  auto frag_b = [&](const char* stg, auto fn, int s) SMOE_INL {
     const char* Bs = stg + A_BYTES;
-    static_for<FM>([&](auto fm) SMOE_INL {
-      if constexpr (ALAY == LAY_K) af[fm] = frag_k(As, wm * WM + fm * 32, s, lane);
-      else af[fm] = frag_mn<BM>(As, wm * WM + fm * 32, s, lane);
-    });
-    static_for<FN>([&](auto fn) SMOE_INL {
-      if constexpr (MODE == SEG_M && BLAY == LAY_K) {
-        bf[fn] = frag_k(Bs, wn * WN + fn * 32, s, lane);
-      } else if constexpr (DUAL) {
-        // fn 0: W1 sub-tile, fn 1: W3 sub-tile, same 32 columns
-        bf[fn] = frag_mn<BN / 2>(Bs + int(fn) * (BN / 2) * kBK * 2, wn * (WN / 2), s, lane);
-      } else {
-        bf[fn] = frag_mn<BN>(Bs, wn * WN + fn * 32, s, lane);
-      }
-    });
+    if constexpr (MODE == SEG_M && BLAY == LAY_K) {
+      return frag_k(Bs, wn * WN + int(fn) * 32, s, lane);
+    } else if constexpr (DUAL) {
+      // fn 0: W1 sub-tile, fn 1: W3 sub-tile, same 32 columns
+      return frag_mn<BN / 2>(Bs + int(fn) * (BN / 2) * kBK * 2, wn * (WN / 2), s, lane);
+    } else {
+      return frag_mn<BN>(Bs, wn * WN + int(fn) * 32, s, lane);
+    }
+  };
+  auto frags = [&](const char* stg, int s, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) SMOE_INL {
+    static_for<FM>([&](auto fm) SMOE_INL { af[fm] = frag_a(stg, fm, s); });
+    static_for<FN>([&](auto fn) SMOE_INL { bf[fn] = frag_b(stg, fn, s); });
+  };
+  // GATED: A fragments of slice s of step kt times their rows' scales.  A
+  // lane's fragment holds k-rows 16s + 8 (lane >> 5) + 0..7 of the step (one
+  // column each); each product is rounded to bf16 (nearest even), the value
+  // the contraction then takes.
+  auto scale_a = [&](bf16x8_t (&af)[FM], int kt, int s) SMOE_INL {
+    if constexpr (GATED) {
+      const float* gs = gring + (kt % kRing) * 64 + 16 * s + 8 * (lane >> 5);
+      const float4 g0 = *reinterpret_cast<const float4*>(gs);
+      const float4 g1 = *reinterpret_cast<const float4*>(gs + 4);
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      static_for<FM>([&](auto fm) SMOE_INL {
+        const uint4 w = __builtin_bit_cast(uint4, af[fm]);
+        const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+        uint32_t o[4];
+        static_for<4>([&](auto q) SMOE_INL {
+          const float lo = __uint_as_float(in[q] << 16) * gv[2 * int(q)];
+          const float hi = __uint_as_float(in[q] & 0xffff0000u) * gv[2 * int(q) + 1];
+          o[q] = pack_bf16x2(lo, hi);
+        });
+        af[fm] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+      });
+    }
   };
   // fragments of two 16-wide k slices: slot 0 / slot 1
   bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto mfma = [&](bf16x8_t (&A)[FM], bf16x8_t (&B)[FN], auto fm, auto fn) SMOE_INL {
+    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[fn], A[fm], acc[fm][fn], 0, 0, 0);
+  };
   auto mfmas = [&](bf16x8_t (&A)[FM], bf16x8_t (&B)[FN]) SMOE_INL {
-    static_for<FM>([&](auto fm) SMOE_INL {
-      static_for<FN>([&](auto fn) SMOE_INL {
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[fn], A[fm], acc[fm][fn], 0, 0, 0);
-      });
+    static_for<FM>([&](auto fm) SMOE_INL { static_for<FN>([&](auto fn) SMOE_INL { mfma(A, B, fm, fn); }); });
+  };
+  // LDS read instructions per slice: one per K-layout fragment, two per
+  // transposed (MN-layout) fragment
+  constexpr int kFragReads = FM * (ALAY == LAY_K ? 1 : 2) + FN * ((MODE == SEG_M && BLAY == LAY_K) ? 1 : 2);
+  // schedule of a slice: one multiply, then a share of the next slice's
+  // fragment reads, so the reads run under the multiplies
+  auto sched = [&]() SMOE_INL {
+    static_for<FM * FN>([&](auto i) SMOE_INL {
+      constexpr int r0 = int(i) * kFragReads / (FM * FN), r1 = (int(i) + 1) * kFragReads / (FM * FN);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);
     });
   };
 
   // ---------------- pipeline -----------------------------------------------
-  // kNS stages.  At the top of step kt each wave waits until its own copies
-  // of stages kt and kt+1 have landed (later stages may still be in flight);
-  // the barrier then publishes every wave's copies and frees the stage
-  // multiplied in step kt-1, which receives stage kt+kNS-1.  Because stage
-  // kt+1 is published one step early, each wave reads the first fragments
-  // of step kt+1 while the last multiplies of step kt run, and arrives at
-  // the next barrier with them in registers.  The barrier is a bare
-  // s_barrier: the fragment reads of step kt-1 were consumed by its
-  // multiplies, which is all the ordering the stages need.
-  static_assert(kNS >= 3, "the next stage is published one step early");
-  constexpr int NSL = kBK / 16;   // k slices per stage (even)
-  // LDS read instructions per slice: one per K-layout fragment, two per
-  // transposed (MN-layout) fragment
-  constexpr int kFragReads = FM * (ALAY == LAY_K ? 1 : 2) + FN * ((MODE == SEG_M && BLAY == LAY_K) ? 1 : 2);
+  // Two stage buffers of 64 k.  Step kt multiplies its four 16-wide slices,
+  // reading the fragments of slice j+1 while slice j multiplies.  Before the
+  // last slice (whose fragments are then in registers) each wave waits
+  // until its LDS reads are done and its copies of stage kt+1 have landed,
+  // and one barrier per step publishes stage kt+1 and frees stage kt's
+  // buffer.  The last slice's multiplies are then interleaved, one by one,
+  // with the copies of stage kt+2 into the freed buffer and with the reads
+  // of stage kt+1's first slice, so that the copy traffic, the barrier and
+  // the step change all run under multiplies.  A copy has one step to land.
   if constexpr (MODE == SEG_K) {
-    // indices of the steps issued before the loop's own index copies land
-    for (int j = 0; j < kIdxAhead; ++j) idx_copy(j);
+    for (int j = 0; j < kIdxAhead; ++j)
+      if (j < KT) idx_copy(j);
     wait_vmem<0>();
     asm volatile("s_barrier" ::: "memory");
+    idx_fetch(0);
   }
-  static_for<kNS - 1>([&](auto s) SMOE_INL {
-    if (int(s) < KT) {
-      if constexpr (MODE == SEG_K) idx_copy(int(s) + kIdxAhead);
-      idx_fetch(int(s));
-      issue(int(s), stage(s));
-    }
-  });
-  // first fragments of step 0 (read before the loop, so that every step's
-  // code sees the same outstanding LDS reads and the compiler's waits for
-  // them stay exact)
-  if (kNS - 2 < KT) wait_vmem<(kNS - 3) * (LPS + IDX)>();
-  else wait_vmem<0>();
+  plan(0);
+  static_for<LPS>([&](auto c) SMOE_INL { copy(c, smem0); });
+  if (1 < KT) {
+    idx_fetch(1);
+    plan(1);
+    static_for<LPS>([&](auto c) SMOE_INL { copy(c, smem1); });
+    wait_vmem<LPS>();
+  } else {
+    wait_vmem<0>();
+  }
   asm volatile("s_barrier" ::: "memory");
-  frags(stage(std::integral_constant<int, 0>{}), 0, fa0, fb0);
-  for (int k0 = 0; k0 < KT; k0 += kNS) {
-    static_for<kNS>([&](auto s) SMOE_INL {
+  if (2 < KT) idx_fetch(2);
+  frags(smem0, 0, fa0, fb0);
+  constexpr int CPM = (LPS + FM * FN - 1) / (FM * FN);   // copies per multiply of the last slice
+  for (int k0 = 0; k0 < KT; k0 += 2) {
+    static_for<2>([&](auto s) SMOE_INL {
       const int kt = k0 + int(s);
       if (kt < KT) {
-        if (kt + kNS - 2 < KT) wait_vmem<(kNS - 3) * (LPS + IDX)>();
-        else wait_vmem<0>();
+        char* cur = stage(s);
+        const char* nxt = stage(std::integral_constant<int, int(s) + 1>{});
+        static_assert(kNSL == 4, "four slices per stage");
+        scale_a(fa0, kt, 0);
+        frags(cur, 1, fa1, fb1);
+        mfmas(fa0, fb0);
+        sched();
+        scale_a(fa1, kt, 1);
+        frags(cur, 2, fa0, fb0);
+        mfmas(fa1, fb1);
+        sched();
+        scale_a(fa0, kt, 2);
+        frags(cur, 3, fa1, fb1);
+        mfmas(fa0, fb0);
+        sched();
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more = kt + 2 < KT;
+        if (more) plan(kt + 2);
+        wait_lds();
+        wait_vmem<0>();
         asm volatile("s_barrier" ::: "memory");
-        if (kt + kNS - 1 < KT) idx_fetch(kt + kNS - 1);
-        static_for<NSL>([&](auto j) SMOE_INL {
-          constexpr int J = decltype(j)::value;
-          auto& A = (J & 1) == 0 ? fa0 : fa1;
-          auto& B = (J & 1) == 0 ? fb0 : fb1;
-          auto& An = (J & 1) == 0 ? fa1 : fa0;
-          auto& Bn = (J & 1) == 0 ? fb1 : fb0;
-          // read the next slice (the next stage's first one after the last;
-          // unconditionally, so the outstanding LDS reads are the same on
-          // every path: after the last step the values are simply unused)
-          if constexpr (J + 1 < NSL) frags(stage(s), J + 1, An, Bn);
-          else frags(stage(std::integral_constant<int, int(s) + 1>{}), 0, An, Bn);
-          mfmas(A, B);
-#if SMOE_SCHED == 1
-          // schedule: one multiply, then a share of the fragment reads, so
-          // the reads of the next slice run under this slice's multiplies
-          static_for<FM * FN>([&](auto i) SMOE_INL {
-            constexpr int r0 = int(i) * kFragReads / (FM * FN), r1 = (int(i) + 1) * kFragReads / (FM * FN);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);
-          });
-#else
-          // schedule: every fragment read of the next slice first, then this
-          // slice's multiplies (a wave issues in order, so reads placed after
-          // a multiply would wait for the matrix unit)
-          __builtin_amdgcn_sched_group_barrier(0x100, kFragReads, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
-#endif
-          if constexpr (J == 0) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int nk = kt + kNS - 1;
-            if (nk < KT) {
-              // the index copy precedes the stage copies, so the stage waits
-              // cover it (see the ring above)
-              if constexpr (MODE == SEG_K) idx_copy(nk + kIdxAhead - (kNS - 1));
-              issue(nk, stage(std::integral_constant<int, int(s) + kNS - 1>{}));
+        if constexpr (MODE == SEG_K) {
+          if (kt + kIdxAhead < KT) idx_copy(kt + kIdxAhead);
+        }
+        scale_a(fa1, kt, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<FM * FN>([&](auto ii) SMOE_INL {
+          constexpr int I = decltype(ii)::value;
+          mfma(fa1, fb1, std::integral_constant<int, I / FN>{}, std::integral_constant<int, I % FN>{});
+          static_for<CPM>([&](auto cc) SMOE_INL {
+            constexpr int c = I * CPM + decltype(cc)::value;
+            if constexpr (c < LPS) {
+              if (more) copy(std::integral_constant<int, c>{}, cur);
             }
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          });
+          if constexpr (I < FM) fa0[I] = frag_a(nxt, std::integral_constant<int, I>{}, 0);
+          else if constexpr (I < FM + FN) fb0[I - FM] = frag_b(nxt, std::integral_constant<int, I - FM>{}, 0);
+          __builtin_amdgcn_sched_barrier(0);
         });
+        if constexpr (FM * FN < FM + FN) {
+          // more fragments than multiplies in the slice (small tiles)
+          static_for<FM + FN - FM * FN>([&](auto rr) SMOE_INL {
+            constexpr int I = FM * FN + decltype(rr)::value;
+            if constexpr (I < FM) fa0[I] = frag_a(nxt, std::integral_constant<int, I>{}, 0);
+            else fb0[I - FM] = frag_b(nxt, std::integral_constant<int, I - FM>{}, 0);
+          });
+        }
+        if constexpr (MODE == SEG_K) {
+          if (kt + 3 < KT) idx_fetch(kt + 3);
+        }
       }
     });
   }
+
 
   // ---------------- epilogue ----------------------------------------------
   // lane holds, for fragment (fm, fn): row (lane & 31) and columns
@@ -665,14 +676,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NOUT = (MODE == SEG_M && (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD)) ? 3
                        : (MODE == SEG_M && (EPI == EPI_GELU_FWD || EPI == EPI_GELU_BWD)) ? 2 : 1;
   static_assert((CH & (CH - 1)) == 0 && CH <= 64 && 32 % RPR == 0, "staging geometry");
-  static_assert(NOUT * 32 * RBE <= STAGE / 2, "staging slot");
+  static_assert(NOUT * 32 * RBE <= STAGE / 4, "staging slot");
   asm volatile("s_barrier" ::: "memory");
-  char* slot;
-  {
-    const int ob = (wave >> 1) & 3;
-    char* base = ob == 0 ? smem0 : ob == 1 ? smem1 : ob == 2 ? smem2 : smem3;
-    slot = base + (wave & 1) * (STAGE / 2);
-  }
+  // each wave stages into a quarter of one of the two stage buffers
+  char* const slot = (wave < 4 ? smem0 : smem1) + (wave & 3) * (STAGE / 4);
   // lane's 4 values of fragment (fn, q) of one fragment row -> output o
   auto put = [&](int o, auto fn, auto q, const float v[4]) SMOE_INL {
     const int row = lane & 31;
@@ -715,8 +722,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   constexpr std::true_type kAdd{};
 
   if constexpr (MODE == SEG_K) {
-    float* dst = (it.nitems == 1) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
-                                  : p.partial + int64_t(T.chunk) * p.Mo * p.N;
+    float* dst = (it.nitems == 1 && !p.dw_all_partial) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
+                                                       : p.partial + int64_t(T.chunk) * p.Mo * p.N;
     static_for<FM>([&](auto fm) SMOE_INL {
       const int i = T.m0 + wm * WM + fm * 32 + (lane & 31);
       static_for<FN>([&](auto fn) SMOE_INL {
@@ -946,7 +953,8 @@ __global__ __launch_bounds__(kFThreads) void gemm_f32_kernel(GemmArgs p) {
       const int r = it.row0 + k, i = T.m0 + m;
       if (r >= it.row1 || i >= p.Mo) return 0.f;
       const int src = p.a_scat ? p.sidx[r] / p.a_fan : r;
-      return a0[int64_t(src) * p.lda + i];
+      const float v = a0[int64_t(src) * p.lda + i];
+      return p.kscale ? p.kscale[r] * v : v;
     }
   };
   auto Bval = [&](int k, int n, int which) SMOE_INL -> float {  // n tile-local
@@ -1001,8 +1009,8 @@ __global__ __launch_bounds__(kFThreads) void gemm_f32_kernel(GemmArgs p) {
   }
 
   if constexpr (MODE == SEG_K) {
-    float* dst = (it.nitems == 1) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
-                                  : p.partial + int64_t(T.chunk) * p.Mo * p.N;
+    float* dst = (it.nitems == 1 && !p.dw_all_partial) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
+                                                       : p.partial + int64_t(T.chunk) * p.Mo * p.N;
     for (int i = 0; i < 4; ++i) {
       const int r = T.m0 + ty * 4 + i;
       const int j = T.n0 + tx * 4;
@@ -1186,7 +1194,7 @@ static void go_f32(const GemmArgs& a, const GemmPlan& pl, hipStream_t st) {
 // out_f32: 1 when c0 is fp32 (scattered pairs, weight gradients)
 static bool dispatch(const GemmArgs& a, const GemmPlan& pl, int out_f32, hipStream_t st) {
   if (!pl.bf16) {
-    if (pl.mode == SEG_K) { go_f32<SEG_K, EPI_PARTIAL, 0, false>(a, pl, st); return true; }
+    if (pl.mode == SEG_K) { go_f32<SEG_K, EPI_PARTIAL, 0, false>(a, pl, st); return true; }   // reads kscale itself
     switch (pl.epi) {
       case EPI_STORE:
         if (a.b_nk) go_f32<SEG_M, EPI_STORE, 1, false>(a, pl, st);
@@ -1199,7 +1207,10 @@ static bool dispatch(const GemmArgs& a, const GemmPlan& pl, int out_f32, hipStre
     }
     return false;
   }
-  if (pl.mode == SEG_K) return dispatch_tiles<SEG_K, EPI_PARTIAL, LAY_MN, false, float>(a, pl, st);
+  if (pl.mode == SEG_K) {
+    if (a.kscale) return dispatch_tiles<SEG_K, EPI_PARTIAL_GATED, LAY_MN, false, float>(a, pl, st);
+    return dispatch_tiles<SEG_K, EPI_PARTIAL, LAY_MN, false, float>(a, pl, st);
+  }
   switch (pl.epi) {
     case EPI_STORE:
       if (a.b_nk) {
