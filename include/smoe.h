@@ -24,14 +24,17 @@
  *
  * Conventions for every entry point.
  *  - Pointers to tensors are DEVICE pointers owned by the caller.  The
- *    library never allocates device memory, frees or synchronises; it only
- *    enqueues work on `stream` (a hipStream_t; NULL = the default stream)
- *    and returns (smoe_mlp_fwd and smoe_mlp_bwd also use one library-owned
- *    stream, forked from and joined back to `stream`; see smoe_mlp_bwd).
+ *    library never allocates device memory, frees or synchronises, and
+ *    creates no stream or event; it only enqueues work on `stream` (a
+ *    hipStream_t; NULL = the default stream) and returns.  The MLP entry
+ *    points can also use a second stream that the caller passes in (struct
+ *    smoe_aux below); every output is ordered on `stream` when they return.
  *  - Tensors are row-major.  Weights are [E, d_in, d_out]: y = x W[e].
  *    Index arrays are int32; gates and gradients of gates are fp32 [T, k].
  *  - `dtype` is SMOE_F32 or SMOE_BF16 and applies to x, weights, y, dx and
- *    saved activations.  Weight gradients are always fp32.
+ *    saved activations unless an entry point takes a separate dx_dtype.
+ *    Weight gradients are fp32 by default; the backward entry points take a
+ *    dw_dtype (SMOE_BF16: accumulated in fp32, rounded once).
  *  - Feature sizes (d_in, d_out, d_model, d_ff) must be multiples of 8 and
  *    rows must be 16-byte aligned; T*k must fit in int32.
  *  - bf16: T*k rows of any feature size, and one expert's weights, must
@@ -70,6 +73,22 @@ enum smoe_dtype { SMOE_F32 = 0, SMOE_BF16 = 1 };
 /* GELU: exact erf form, two matrices W1 -> act -> W2.
  * SWIGLU: silu(x W1[e]) * (x W3[e]) -> W2. */
 enum smoe_act { SMOE_ACT_GELU = 0, SMOE_ACT_SWIGLU = 1 };
+
+/* A second stream for the entry points that can run part of their work
+ * beside the rest (smoe_mlp_fwd, smoe_mlp_fwd_fused_combine, smoe_mlp_bwd).
+ * The caller creates and owns all three handles: `stream` (a hipStream_t of
+ * default priority) and two events (hipEvent_t; timing may be disabled).
+ * The library records fork_event on the caller's stream and makes `stream`
+ * wait for it, enqueues the side work, then records join_event on `stream`
+ * and makes the caller's stream wait for it before returning (also when it
+ * returns an error after the fork).  Calls that share one smoe_aux must be
+ * enqueued from one host thread at a time.  Passing NULL (or a struct with
+ * a NULL member) runs everything on the caller's stream. */
+typedef struct smoe_aux {
+  void* stream;
+  void* fork_event;
+  void* join_event;
+} smoe_aux;
 
 /* Static description of a status code. */
 const char* smoe_status_string(int status);
@@ -131,13 +150,22 @@ int smoe_parallel_linear_fwd(const void* x, int64_t x_rows, int64_t d_in,
  *   dy_r = gates ? gates[t][j] * dy[t] : dy[row of r]
  *   dx[input row of r] += dy_r W[e]^T   (k contributions summed, fp32,
  *                                        when a T-row x was read k times)
- *   dw[e]   = sum_r u_r^T dy_r          (fp32; experts with no rows get 0)
+ *   dw[e]   = sum_r u_r^T dy_r          (experts with no rows get 0)
  *   dgates[t][j] = <dy[t], u_r W[e]>    (only with gates)
  * Any of dx, dw, dgates may be NULL to skip it (dgates needs gates).
- * With gates, dw[e] = sum (g u_r)^T dy[t]; in bf16 runs g*u_r is rounded to
- * bf16 before it enters the dw contraction.
+ * dgates comes from the dx product as <dy[t] W[e]^T, u_r>, so no saved
+ * forward output is needed.
+ * dx_dtype: dx in SMOE_BF16 or SMOE_F32 (fp32 keeps the exact sum unrounded;
+ * fp32 runs need fp32).  dw_dtype: dw [E, d_in, d_out] in SMOE_F32 or
+ * SMOE_BF16 (summed in fp32, rounded once); accumulate_dw != 0 adds the
+ * gradient to what dw holds instead of overwriting it.
+ * With gates, dw[e] = sum (g u_r)^T dy[t]: the weight-gradient product
+ * scales each row it reads from x by the row's gate in registers (x is read
+ * in place; no scaled copy exists), and in bf16 runs g*u_r is rounded to
+ * bf16 before it enters the contraction.
  * Same page, first review, Summary (forward and backward through
- * ParallelLinear); article, para. 4 (per-expert gradients).
+ * ParallelLinear); article, para. 4 (per-expert gradients); catalogue
+ * record, abstract (no copied or padded input).
  * ------------------------------------------------------------------------ */
 size_t smoe_parallel_linear_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
                                                 int64_t x_rows, int64_t d_in,
@@ -150,7 +178,9 @@ int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in,
                              const int32_t* offsets,
                              int32_t x_grouped, int32_t y_grouped,
                              const float* gates, const void* dy,
-                             void* dx, float* dw, float* dgates, int32_t dtype,
+                             void* dx, int32_t dx_dtype,
+                             void* dw, int32_t dw_dtype, int32_t accumulate_dw,
+                             float* dgates, int32_t dtype,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -169,6 +199,10 @@ int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in,
  * In bf16 runs h (h1, h3) and a are stored in bf16; a is computed from the
  * stored h; expert outputs and the combine stay fp32 until the final
  * rounding of out.
+ * With `aux` (bf16 runs), both layers' routing-dependent m-tiles (those
+ * past the whole groups that exist whatever the routing) run on aux's
+ * stream beside the rest, so that layer 2's last, partly filled round
+ * overlaps layer 1's work.
  * Article, para. 1 and 5 (SMoE MLP); project page, "How It Works".
  * ------------------------------------------------------------------------ */
 size_t smoe_mlp_saved_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model,
@@ -186,7 +220,7 @@ int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2,
                  const int32_t* expert_idxs, const float* gates,
                  int32_t act, int32_t dtype, void* out,
                  void* saved, size_t saved_bytes,
-                 void* ws, size_t ws_bytes, void* stream);
+                 void* ws, size_t ws_bytes, const smoe_aux* aux, void* stream);
 
 /* smoe_mlp_fwd_fused_combine - smoe_mlp_fwd with the combine folded into the
  * W2 product: each expert output row is scaled by its gate in the product's
@@ -214,7 +248,8 @@ int smoe_mlp_fwd_fused_combine(const void* x, const void* w1, const void* w3,
                                const int32_t* expert_idxs, const float* gates,
                                int32_t act, int32_t dtype, void* out,
                                void* saved, size_t saved_bytes,
-                               void* ws, size_t ws_bytes, void* stream);
+                               void* ws, size_t ws_bytes, const smoe_aux* aux,
+                               void* stream);
 
 /* ------------------------------------------------------------------------
  * smoe_mlp_bwd - backward of smoe_mlp_fwd for upstream dout [T, d_model].
@@ -226,18 +261,17 @@ int smoe_mlp_fwd_fused_combine(const void* x, const void* w1, const void* w3,
  *   SWIGLU: dh1 = dA * h3 * silu'(h1);  dh3 = dA * silu(h1)
  *   dx[t] += dh W1[e]^T (+ dh3 W3[e]^T)            (fp32 k-sum)
  *   dw2[e] += (g a)^T dout[t];  dw1[e] += x[t]^T dh;  dw3[e] += x[t]^T dh3
- * Weight gradients are fp32 and fully written (experts with no tokens get
- * 0).  dw3 must be NULL unless SWIGLU.  dgates may be NULL.  `saved` is the
- * buffer filled by smoe_mlp_fwd with the same arguments.  In bf16 runs
+ * Weight gradients are fully written (experts with no tokens get 0), in
+ * dw_dtype: SMOE_F32, or SMOE_BF16 (summed in fp32, rounded once; bf16 runs
+ * only).  dw3 must be NULL unless SWIGLU.  dgates may be NULL.  `saved` is
+ * the buffer filled by smoe_mlp_fwd with the same arguments.  In bf16 runs
  * dh (dh1, dh3) and g*a are rounded to bf16 before they enter the
  * weight-gradient and dx contractions.
- * In bf16 runs part of the work runs on a second stream that the library
- * creates once per device (default priority, kept until the process ends):
- * here dw1, forked from `stream` with an event after the dx product's whole
- * rounds of tiles and joined back before dw2; in smoe_mlp_fwd both layers'
- * routing-dependent m-tiles, joined back before the combine.  Every output
- * is ordered on `stream` when the call returns, as for the other entry
- * points (and a capture of `stream` records both branches).
+ * With `aux` (bf16 runs), dw1 runs on aux's stream, forked after the dx
+ * product's whole rounds of tiles so that it fills the CUs that the last,
+ * partly filled round leaves idle, and joined back before dw2.  Every
+ * output is ordered on `stream` when the call returns (and a capture of
+ * `stream` records both branches).
  * ------------------------------------------------------------------------ */
 size_t smoe_mlp_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
                                     int64_t d_model, int64_t d_ff, int32_t act,
@@ -248,8 +282,9 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1,
                  const int32_t* expert_idxs, const float* gates,
                  int32_t act, int32_t dtype,
                  const void* saved, size_t saved_bytes,
-                 void* dx, float* dw1, float* dw3, float* dw2, float* dgates,
-                 void* ws, size_t ws_bytes, void* stream);
+                 void* dx, void* dw1, void* dw3, void* dw2, int32_t dw_dtype,
+                 float* dgates, void* ws, size_t ws_bytes,
+                 const smoe_aux* aux, void* stream);
 
 /* ------------------------------------------------------------------------
  * Measurement hook for benchmarks and profilers (not thread-safe).

@@ -23,7 +23,7 @@ __all__ = [
     "smoe_parallel_linear_bwd", "smoe_mlp_fwd", "smoe_mlp_bwd", "saved_views",
     "header_functions", "F32", "BF16", "ACT_GELU", "ACT_SWIGLU", "ROLES", "smoe_set_role_events",
     "smoe_probe_mfma_loop", "smoe_router_fwd", "smoe_router_bwd", "smoe_moa_attention_fwd",
-    "smoe_moa_attention_bwd",
+    "smoe_moa_attention_bwd", "SmoeAux", "default_aux",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +40,14 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+class SmoeAux(ctypes.Structure):
+    """struct smoe_aux: the caller's second stream and its fork / join events."""
+    _fields_ = [("stream", _vp), ("fork_event", _vp), ("join_event", _vp)]
+
+
+_AUXP = ctypes.POINTER(SmoeAux)
 _SIGS = {
     "smoe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "smoe_last_error": (ctypes.c_char_p, []),
@@ -51,15 +59,16 @@ _SIGS = {
                                                 _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp]),
     "smoe_parallel_linear_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32]),
     "smoe_parallel_linear_bwd": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i32, _i64, _i32, _vp, _vp,
-                                                _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+                                                _i32, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp,
+                                                _sz, _vp]),
     "smoe_mlp_saved_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_mlp_saved_offsets": (ctypes.c_int, [_i64, _i32, _i32, _i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "smoe_mlp_fwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_mlp_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32, _i32,
-                                    _vp, _vp, _sz, _vp, _sz, _vp]),
+                                    _vp, _vp, _sz, _vp, _sz, _AUXP, _vp]),
     "smoe_mlp_fwd_fused_combine_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_mlp_fwd_fused_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
-                                                  _i32, _i32, _vp, _vp, _sz, _vp, _sz, _vp]),
+                                                  _i32, _i32, _vp, _vp, _sz, _vp, _sz, _AUXP, _vp]),
     "smoe_mlp_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_set_role_events": (ctypes.c_int, [_i32, _vp, _vp]),
     "smoe_probe_mfma_loop": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
@@ -72,7 +81,7 @@ _SIGS = {
     "smoe_moa_attention_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _i32, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _sz, _vp]),
     "smoe_mlp_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32,
-                                    _i32, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+                                    _i32, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _AUXP, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -104,6 +113,35 @@ def _p(t: Optional[torch.Tensor]):
 
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_AUX = {}
+
+
+def default_aux(device) -> SmoeAux:
+    """A second stream (default priority) and two events for `device`,
+    created through torch once and kept for the process."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key not in _AUX:
+        with torch.cuda.device(key):
+            side = torch.cuda.Stream(device=key)
+            evs = [torch.cuda.Event(enable_timing=False), torch.cuda.Event(enable_timing=False)]
+            for ev in evs:        # torch creates the HIP event on first record
+                ev.record()
+            torch.cuda.current_stream(key).synchronize()
+        _AUX[key] = (side, evs, SmoeAux(side.cuda_stream, evs[0].cuda_event, evs[1].cuda_event))
+    return _AUX[key][2]
+
+
+def _aux_arg(aux, device):
+    """aux=True: the device's default second stream; False/None: none;
+    an SmoeAux: as given."""
+    if aux is True:
+        return ctypes.pointer(default_aux(device))
+    if isinstance(aux, SmoeAux):
+        return ctypes.pointer(aux)
+    return None
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -225,21 +263,29 @@ def smoe_parallel_linear_fwd(x, w, T, k, sorted_scattered_idxs, offsets, x_group
 
 def smoe_parallel_linear_bwd(x, w, T, k, sorted_scattered_idxs, offsets, x_grouped: bool,
                              y_grouped: bool, dy, gates=None, need_dx=True, need_dw=True,
-                             need_dgates=False):
-    """Backward of smoe_parallel_linear_fwd; returns (dx, dw fp32, dgates fp32)."""
-    _contig(x, w, dy, sorted_scattered_idxs, offsets, gates)
+                             need_dgates=False, dx_dtype=None, dw_dtype=torch.float32, dw=None,
+                             accumulate_dw=False):
+    """Backward of smoe_parallel_linear_fwd; returns (dx, dw, dgates fp32).
+    dx_dtype (default: x's dtype) and dw_dtype pick the output types; with
+    dw given and accumulate_dw the gradient is added to it."""
+    _contig(x, w, dy, sorted_scattered_idxs, offsets, gates, dw)
     E, d_in, d_out = w.shape
     dev = x.device
     dt = _dtype_code(x)
-    dx = torch.empty_like(x) if need_dx else None
-    dw = torch.empty((E, d_in, d_out), dtype=torch.float32, device=dev) if need_dw else None
+    dx_dt = x.dtype if dx_dtype is None else dx_dtype
+    dx = torch.empty(x.shape, dtype=dx_dt, device=dev) if need_dx else None
+    if dw is None and need_dw:
+        dw = torch.empty((E, d_in, d_out), dtype=dw_dtype, device=dev)
+        accumulate_dw = False
     dg = torch.empty((T, k), dtype=torch.float32, device=dev) if need_dgates else None
     ws = _ws(lib.smoe_parallel_linear_bwd_workspace_bytes(T, k, E, x.shape[0], d_in, d_out, int(x_grouped),
                                                           int(gates is not None), dt), dev)
     _check(lib.smoe_parallel_linear_bwd(_p(x), x.shape[0], d_in, _p(w), d_out, E, T, k,
                                         _p(sorted_scattered_idxs), _p(offsets), int(x_grouped),
-                                        int(y_grouped), _p(gates), _p(dy), _p(dx), _p(dw), _p(dg), dt,
-                                        _p(ws), ws.numel(), _stream(dev)), "smoe_parallel_linear_bwd")
+                                        int(y_grouped), _p(gates), _p(dy), _p(dx),
+                                        _dtype_code(dx) if dx is not None else dt, _p(dw),
+                                        _dtype_code(dw) if dw is not None else F32, int(accumulate_dw), _p(dg),
+                                        dt, _p(ws), ws.numel(), _stream(dev)), "smoe_parallel_linear_bwd")
     return dx, dw, dg
 
 
@@ -250,10 +296,12 @@ def _mlp_dims(x, w1, w2, expert_idxs):
     return T, d_model, d_ff, E, k
 
 
-def smoe_mlp_fwd(x, w1, w2, expert_idxs, gates, act: str, w3=None, ws=None, fused_combine=False):
+def smoe_mlp_fwd(x, w1, w2, expert_idxs, gates, act: str, w3=None, ws=None, fused_combine=False, aux=True):
     """SMoE-MLP forward; returns (out [T, d_model], saved buffer).
     fused_combine=True calls smoe_mlp_fwd_fused_combine (the gated k-sum
-    added with fp32 atomics inside the W2 product)."""
+    added with fp32 atomics inside the W2 product).  aux: the second stream
+    (True: the device's default one; False: run on the current stream only;
+    or an SmoeAux)."""
     _contig(x, w1, w2, w3, expert_idxs, gates)
     T, d_model, d_ff, E, k = _mlp_dims(x, w1, w2, expert_idxs)
     dev = x.device
@@ -269,29 +317,31 @@ def smoe_mlp_fwd(x, w1, w2, expert_idxs, gates, act: str, w3=None, ws=None, fuse
                 else (lib.smoe_mlp_fwd, "smoe_mlp_fwd"))
     _check(fn(_p(x), _p(w1), _p(w3), _p(w2), T, d_model, d_ff, E, k, _p(expert_idxs),
               _p(gates), a, dt, _p(out), _p(saved), saved.numel(), _p(ws), ws.numel(),
-              _stream(dev)), name)
+              _aux_arg(aux, dev), _stream(dev)), name)
     return out, saved
 
 
 def smoe_mlp_bwd(dout, x, w1, w2, expert_idxs, gates, act: str, saved, w3=None, ws=None,
-                 need_dgates=True):
-    """SMoE-MLP backward; returns dict dx, dw1, dw2, dw3 (fp32), dgates."""
+                 need_dgates=True, dw_dtype=torch.float32, aux=True):
+    """SMoE-MLP backward; returns dict dx, dw1, dw2, dw3 (dw_dtype), dgates.
+    aux as in smoe_mlp_fwd."""
     _contig(dout, x, w1, w2, w3, expert_idxs, gates, saved)
     T, d_model, d_ff, E, k = _mlp_dims(x, w1, w2, expert_idxs)
     dev = x.device
     dt = _dtype_code(x)
     a = _ACTS[act]
     dx = torch.empty_like(x)
-    dw1 = torch.empty(w1.shape, dtype=torch.float32, device=dev)
-    dw2 = torch.empty(w2.shape, dtype=torch.float32, device=dev)
-    dw3 = torch.empty(w1.shape, dtype=torch.float32, device=dev) if w3 is not None else None
+    dw1 = torch.empty(w1.shape, dtype=dw_dtype, device=dev)
+    dw2 = torch.empty(w2.shape, dtype=dw_dtype, device=dev)
+    dw3 = torch.empty(w1.shape, dtype=dw_dtype, device=dev) if w3 is not None else None
     dg = torch.empty((T, k), dtype=torch.float32, device=dev) if need_dgates else None
     need = lib.smoe_mlp_bwd_workspace_bytes(T, k, E, d_model, d_ff, a, dt)
     if ws is None or ws.numel() < need:
         ws = _ws(need, dev)
     _check(lib.smoe_mlp_bwd(_p(dout), _p(x), _p(w1), _p(w3), _p(w2), T, d_model, d_ff, E, k,
                             _p(expert_idxs), _p(gates), a, dt, _p(saved), saved.numel(), _p(dx), _p(dw1),
-                            _p(dw3), _p(dw2), _p(dg), _p(ws), ws.numel(), _stream(dev)), "smoe_mlp_bwd")
+                            _p(dw3), _p(dw2), _dtype_code(dw1), _p(dg), _p(ws), ws.numel(), _aux_arg(aux, dev),
+                            _stream(dev)), "smoe_mlp_bwd")
     return {"dx": dx, "dw1": dw1, "dw2": dw2, "dw3": dw3, "dgates": dg}
 
 

@@ -1,9 +1,9 @@
 // C ABI of the scattered mixture-of-experts hot path (declared in
 // include/smoe.h): host-side validation, workspace layout and the
 // launch sequence of each entry point.  Nothing here allocates,
-// synchronises or copies device memory; everything is enqueued on the
-// caller's stream.
-#include <mutex>
+// synchronises or copies device memory, and no HIP object (stream, event)
+// is created: work is enqueued on the caller's stream, and on the caller's
+// second stream where an entry point takes one (struct smoe_aux).
 #include <stdint.h>
 #include <string.h>
 
@@ -47,34 +47,34 @@ constexpr size_t kAlign = 256;
 // events attached by smoe_set_role_events
 hipEvent_t g_role_ev[SMOE_ROLE_COUNT][2] = {};
 
-// A second stream per device, forked from and joined back to the caller's
-// stream with events; created on first use (default priority) and kept
-// until the process ends.  The events are shared, so a call holds g_aux_mu
-// from its fork to its join: calls from several host threads then enqueue
-// their fork/join pairs one after another (their second-stream work runs in
-// that order).
-constexpr int kMaxDevices = 64;
-struct AuxStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-AuxStream g_aux[kMaxDevices];
-std::mutex g_aux_mu;
-// caller holds g_aux_mu
-hipError_t aux_stream(AuxStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  AuxStream& a = g_aux[dev];
-  if (!a.s) {
-    if ((e = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming)) != hipSuccess) return e;
+// The caller's second stream (struct smoe_aux), forked from the main
+// stream with one event and joined back with the other.  Once forked, the
+// join is recorded and waited for on every way out of the scope, errors
+// included, so that no work on the second stream is left unordered with
+// the caller's stream (and the buffers it reads) when the call returns.
+struct Fork {
+  const smoe_aux* aux;
+  hipStream_t main;
+  bool forked = false;
+  Fork(const smoe_aux* a, hipStream_t st) : aux(a && a->stream && a->fork_event && a->join_event ? a : nullptr), main(st) {}
+  bool usable() const { return aux != nullptr; }
+  hipStream_t side() const { return static_cast<hipStream_t>(aux->stream); }
+  hipError_t fork() {
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(aux->fork_event), main);
+    if (e != hipSuccess) return e;
+    e = hipStreamWaitEvent(side(), static_cast<hipEvent_t>(aux->fork_event), 0);
+    if (e == hipSuccess) forked = true;
+    return e;
   }
-  *out = &a;
-  return hipSuccess;
-}
+  hipError_t join() {
+    if (!forked) return hipSuccess;
+    forked = false;
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(aux->join_event), side());
+    hipError_t w = hipStreamWaitEvent(main, static_cast<hipEvent_t>(aux->join_event), 0);
+    return e != hipSuccess ? e : w;
+  }
+  ~Fork() { (void)join(); }
+};
 
 // Brackets the launches issued during its lifetime with the role's events.
 struct RoleTimer {
@@ -191,7 +191,7 @@ int dg_slots(int64_t M, int E, int64_t N, int bf16) {
 struct PlBwdWs {
   float* pairs = nullptr;    // dx contributions [M, d_in] when x was read k times
   float* dgpart = nullptr;   // [slots, M]
-  void* xg = nullptr;        // gate-scaled input rows, grouped [M, d_in]
+  float* gg = nullptr;       // the gates in grouped order [M] (the dw product's row scales)
   float* partial = nullptr;  // dw split-K partials
 };
 void layout_pl_bwd(Arena& ar, int64_t T, int k, int E, int64_t x_rows, int64_t d_in, int64_t d_out, bool x_grouped,
@@ -201,7 +201,7 @@ void layout_pl_bwd(Arena& ar, int64_t T, int k, int E, int64_t x_rows, int64_t d
   if (fan_k) w.pairs = static_cast<float*>(ar.take(size_t(M) * d_in * 4));
   if (with_gates) {
     w.dgpart = static_cast<float*>(ar.take(size_t(dg_slots(M, E, d_in, bf16)) * M * 4));
-    w.xg = ar.take(size_t(M) * d_in * (bf16 ? 2 : 4));
+    w.gg = static_cast<float*>(ar.take(size_t(M) * 4));
   }
   w.partial = static_cast<float*>(ar.take(dw_partial_bytes(M, E, d_in, d_out, bf16)));
 }
@@ -267,17 +267,24 @@ void layout_mlp_bwd(Arena& ar, int64_t T, int k, int E, int64_t d_model, int64_t
 }
 
 // Weight gradient dw[e] = sum over e's rows of A(r)^T B(r): GEMM + reduction.
-int run_dw(GemmArgs a, int bf16, float* dw, float* partial, hipStream_t st, int role, const char* where) {
+// An fp32 dw that is written (not accumulated) takes the single-chunk
+// experts straight from the product; a bf16 or accumulated dw takes every
+// chunk through the partials, and the reduction rounds or adds once.
+int run_dw(GemmArgs a, int bf16, void* dw, int dw_bf16, int accumulate, float* partial, hipStream_t st, int role,
+           const char* where) {
   a.c0 = dw;
   a.partial = partial;
+  a.dw_all_partial = (dw_bf16 || accumulate) ? 1 : 0;
   GemmPlan pl;
-  plan_gemm(a, pl, SEG_K, EPI_PARTIAL, 0, bf16, 1);
+  plan_gemm(a, pl, SEG_K, a.kscale ? EPI_PARTIAL_GATED : EPI_PARTIAL, 0, bf16, 1);
   {
     RoleTimer t(role, st);
     SMOE_HIP(launch_gemm(a, pl, st), where);
   }
   RoleTimer t(SMOE_ROLE_DW_REDUCE, st);
-  SMOE_HIP(launch_reduce_dw(partial, a.offsets, a.E, a.KS, int64_t(a.Mo) * a.N, dw, st), where);
+  SMOE_HIP(launch_reduce_dw(partial, a.offsets, a.E, a.KS, int64_t(a.Mo) * a.N, dw, a.dw_all_partial, accumulate,
+                            dw_bf16, st),
+           where);
   return SMOE_OK;
 }
 
@@ -320,7 +327,7 @@ const char* smoe_status_string(int status) {
 
 const char* smoe_last_error(void) { return g_last_error.c_str(); }
 
-int smoe_abi_version(void) { return 1; }
+int smoe_abi_version(void) { return 2; }
 
 static int check_router(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype) {
   if (dtype != SMOE_F32 && dtype != SMOE_BF16) return fail(SMOE_ERR_DTYPE, "dtype %d is not SMOE_F32/SMOE_BF16", dtype);
@@ -401,7 +408,7 @@ int smoe_router_bwd(const void* x, const void* w, int64_t T, int64_t d_model, in
   a.b0 = wl.D;
   a.ldb = ncol;
   a.b_rows = T;
-  SMOE_TRY(run_dw(a, bf16, wl.tmp, wl.partial, st, SMOE_ROLE_ROUTER_DW, "router_bwd dw"));
+  SMOE_TRY(run_dw(a, bf16, wl.tmp, 0, 0, wl.partial, st, SMOE_ROLE_ROUTER_DW, "router_bwd dw"));
   SMOE_HIP(launch_gate_dw_finish(wl.tmp, int(d_model), E, bf16, dw_out, st), "router_bwd dw");
   return ok();
 }
@@ -614,10 +621,15 @@ size_t smoe_parallel_linear_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E,
 int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in, const void* w, int64_t d_out, int32_t E,
                              int64_t T, int32_t k, const int32_t* sorted_scattered_idxs, const int32_t* offsets,
                              int32_t x_grouped, int32_t y_grouped, const float* gates, const void* dy, void* dx,
-                             float* dw, float* dgates, int32_t dtype, void* ws, size_t ws_bytes, void* stream) {
+                             int32_t dx_dtype, void* dw, int32_t dw_dtype, int32_t accumulate_dw, float* dgates,
+                             int32_t dtype, void* ws, size_t ws_bytes, void* stream) {
   SMOE_TRY(check_common(T, k, E, dtype));
   SMOE_TRY(check_dim(d_in, "d_in"));
   SMOE_TRY(check_dim(d_out, "d_out"));
+  if (dx_dtype != SMOE_F32 && dx_dtype != SMOE_BF16) return fail(SMOE_ERR_DTYPE, "dx_dtype %d", dx_dtype);
+  if (dw_dtype != SMOE_F32 && dw_dtype != SMOE_BF16) return fail(SMOE_ERR_DTYPE, "dw_dtype %d", dw_dtype);
+  if (dtype == SMOE_F32 && (dx_dtype != SMOE_F32 || dw_dtype != SMOE_F32))
+    return fail(SMOE_ERR_DTYPE, "fp32 runs give fp32 dx and dw");
   const int64_t M = T * k;
   if (x_grouped ? x_rows != M : (x_rows != T && x_rows != M))
     return fail(SMOE_ERR_SHAPE, "x_rows=%lld does not fit the layout", (long long)x_rows);
@@ -643,9 +655,11 @@ int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int fan = (!x_grouped && x_rows == T) ? k : 1;
   const bool fan_k = fan > 1;
+  const int dx_f32 = dx_dtype == SMOE_F32;
 
   if (M == 0) {
-    if (dw) SMOE_HIP(launch_zero(dw, size_t(E) * d_in * d_out * 4, st), "parallel_linear_bwd");
+    if (dw && !accumulate_dw)
+      SMOE_HIP(launch_zero(dw, size_t(E) * d_in * d_out * (dw_dtype == SMOE_BF16 ? 2 : 4), st), "parallel_linear_bwd");
     return ok();
   }
   // dx (and the gate gradient): dy rows against W^T
@@ -679,43 +693,41 @@ int smoe_parallel_linear_bwd(const void* x, int64_t x_rows, int64_t d_in, const 
     } else {
       a.c0 = dx;
       a.c_scat = !x_grouped;
-      plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, !bf16);
+      plan_gemm(a, pl, SEG_M, EPI_STORE, 0, bf16, dx_f32);
     }
     {
       RoleTimer t(SMOE_ROLE_PL_DX, st);
       SMOE_HIP(launch_gemm(a, pl, st), "parallel_linear_bwd dx gemm");
     }
-    if (fan_k && dx) SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_in, dx, bf16, st), "parallel_linear_bwd ksum");
+    if (fan_k && dx)
+      SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_in, dx, !dx_f32, st), "parallel_linear_bwd ksum");
     if (dgates)
       SMOE_HIP(launch_reduce_dg(wl.dgpart, pl.slots, int(M), offsets, E, sorted_scattered_idxs, dgates, st),
                "parallel_linear_bwd dgates");
   }
   if (dw) {
-    // with gates, dw[e] = sum (g u)^T dy[t]: the gate scales a grouped copy
-    // of the input rows, so the weight-gradient product reads plain operands
+    // dw[e] = sum (g u)^T dy[t]: with gates the product scales each row of
+    // its A operand (u, read in place) by the row's gate in registers
     GemmArgs a = blank_args(offsets, sorted_scattered_idxs, E, int(M));
     a.Mo = int(d_in);
     a.N = int(d_out);
     if (gates) {
-      SMOE_HIP(launch_scale_rows(x, x_grouped, fan, gates, sorted_scattered_idxs, offsets, E, int(M), d_in, wl.xg,
-                                 bf16, st),
-               "parallel_linear_bwd scale");
-      a.a0 = wl.xg;
-      a.a_rows = M;
-      a.a_scat = 0;
-    } else {
-      a.a0 = x;
-      a.a_rows = x_rows;
-      a.a_scat = !x_grouped;
-      a.a_fan = fan;
+      SMOE_HIP(launch_grouped_gates(gates, sorted_scattered_idxs, offsets, E, int(M), wl.gg, st),
+               "parallel_linear_bwd gates");
+      a.kscale = wl.gg;
     }
+    a.a0 = x;
+    a.a_rows = x_rows;
+    a.a_scat = !x_grouped;
+    a.a_fan = fan;
     a.lda = d_in;
     a.b0 = dy;
     a.ldb = d_out;
     a.b_rows = gates ? T : M;
     a.b_scat = gates ? 1 : !y_grouped;
     a.b_fan = gates ? k : 1;
-    SMOE_TRY(run_dw(a, bf16, dw, wl.partial, st, SMOE_ROLE_PL_DW, "parallel_linear_bwd dw"));
+    SMOE_TRY(run_dw(a, bf16, dw, dw_dtype == SMOE_BF16, accumulate_dw != 0, wl.partial, st, SMOE_ROLE_PL_DW,
+                    "parallel_linear_bwd dw"));
   }
   return ok();
 }
@@ -764,7 +776,7 @@ size_t smoe_mlp_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_m
 static int mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, int64_t T, int64_t d_model,
                    int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs, const float* gates, int32_t act,
                    int32_t dtype, void* out, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
-                   void* stream, bool fused) {
+                   const smoe_aux* aux, void* stream, bool fused) {
   SMOE_TRY(check_mlp(T, k, E, d_model, d_ff, act, dtype, w3));
   SMOE_TRY(need_ptr(w1, "w1"));
   SMOE_TRY(need_ptr(w2, "w2"));
@@ -849,30 +861,26 @@ static int mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2
     SMOE_HIP(launch_zero(wl.pairs, size_t(T) * size_t(d_model) * sizeof(float), st), "mlp_fwd zero");
   }
 
-  // The m-tiles that exist whatever the routing (whole groups of 8 below
-  // ceil(M / BM)) run both layers on the caller's stream; the remaining,
-  // routing-dependent m-tiles run both layers on a second stream beside
-  // them, so the last, partly filled round of layer 2 overlaps layer 1's
-  // work instead of leaving most CUs idle.  Each layer-2 tile reads only
-  // the rows its own m-tile's layer-1 tiles wrote, on the same stream.
+  // With the caller's second stream: the m-tiles that exist whatever the
+  // routing (whole groups of 8 below ceil(M / BM)) run both layers on the
+  // caller's stream; the remaining, routing-dependent m-tiles run both
+  // layers on the second stream beside them, so the last, partly filled
+  // round of layer 2 overlaps layer 1's work instead of leaving most CUs
+  // idle.  Each layer-2 tile reads only the rows its own m-tile's layer-1
+  // tiles wrote, on the same stream.
+  Fork fk(aux, st);
   const int64_t mt_head = (ceil_div64(M, pl.bm) / 8) * 8;
-  const bool split = bf16 && pl.bm == pb.bm && mt_head > 0 && mt_head * pb.n_tiles < pb.grid;
-  AuxStream* ax = nullptr;
-  std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
+  const bool split = fk.usable() && bf16 && pl.bm == pb.bm && mt_head > 0 && mt_head * pb.n_tiles < pb.grid;
   if (split) {
-    aux_lock.lock();
-    SMOE_HIP(aux_stream(&ax), "mlp_fwd stream");
-    SMOE_HIP(hipEventRecord(ax->fork, st), "mlp_fwd fork");
-    SMOE_HIP(hipStreamWaitEvent(ax->s, ax->fork, 0), "mlp_fwd fork");
+    SMOE_HIP(fk.fork(), "mlp_fwd fork");
     GemmArgs at = a, bt = b;
     GemmPlan plt = pl, pbt = pb;
     at.g_base = int(mt_head * pl.n_tiles);
     bt.g_base = int(mt_head * pb.n_tiles);
     plt.grid = (pl.grid - at.g_base + 7) / 8 * 8;
     pbt.grid = (pb.grid - bt.g_base + 7) / 8 * 8;
-    SMOE_HIP(launch_gemm(at, plt, ax->s), "mlp_fwd layer 1");
-    SMOE_HIP(launch_gemm(bt, pbt, ax->s), "mlp_fwd layer 2");
-    SMOE_HIP(hipEventRecord(ax->join, ax->s), "mlp_fwd join");
+    SMOE_HIP(launch_gemm(at, plt, fk.side()), "mlp_fwd layer 1");
+    SMOE_HIP(launch_gemm(bt, pbt, fk.side()), "mlp_fwd layer 2");
     a.g_count = int(mt_head * pl.n_tiles);
     b.g_count = int(mt_head * pb.n_tiles);
     pl.grid = a.g_count;
@@ -886,10 +894,7 @@ static int mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2
     RoleTimer t(SMOE_ROLE_DOWN, st);
     SMOE_HIP(launch_gemm(b, pb, st), "mlp_fwd layer 2");
   }
-  if (split) {
-    SMOE_HIP(hipStreamWaitEvent(st, ax->join, 0), "mlp_fwd join");
-    aux_lock.unlock();
-  }
+  SMOE_HIP(fk.join(), "mlp_fwd join");
   RoleTimer t(SMOE_ROLE_COMBINE, st);
   if (fused)
     SMOE_HIP(launch_combine(wl.pairs, nullptr, T, 1, d_model, out, bf16, st), "mlp_fwd convert");
@@ -901,9 +906,9 @@ static int mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2
 int smoe_mlp_fwd(const void* x, const void* w1, const void* w3, const void* w2, int64_t T, int64_t d_model,
                  int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs, const float* gates, int32_t act,
                  int32_t dtype, void* out, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 const smoe_aux* aux, void* stream) {
   return mlp_fwd(x, w1, w3, w2, T, d_model, d_ff, E, k, expert_idxs, gates, act, dtype, out, saved, saved_bytes, ws,
-                 ws_bytes, stream, false);
+                 ws_bytes, aux, stream, false);
 }
 
 size_t smoe_mlp_fwd_fused_combine_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff,
@@ -918,9 +923,9 @@ size_t smoe_mlp_fwd_fused_combine_workspace_bytes(int64_t T, int32_t k, int32_t 
 int smoe_mlp_fwd_fused_combine(const void* x, const void* w1, const void* w3, const void* w2, int64_t T,
                                int64_t d_model, int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs,
                                const float* gates, int32_t act, int32_t dtype, void* out, void* saved,
-                               size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+                               size_t saved_bytes, void* ws, size_t ws_bytes, const smoe_aux* aux, void* stream) {
   return mlp_fwd(x, w1, w3, w2, T, d_model, d_ff, E, k, expert_idxs, gates, act, dtype, out, saved, saved_bytes, ws,
-                 ws_bytes, stream, true);
+                 ws_bytes, aux, stream, true);
 }
 
 size_t smoe_mlp_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_model, int64_t d_ff, int32_t act,
@@ -933,9 +938,13 @@ size_t smoe_mlp_bwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_m
 
 int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3, const void* w2, int64_t T,
                  int64_t d_model, int64_t d_ff, int32_t E, int32_t k, const int32_t* expert_idxs, const float* gates,
-                 int32_t act, int32_t dtype, const void* saved, size_t saved_bytes, void* dx, float* dw1, float* dw3,
-                 float* dw2, float* dgates, void* ws, size_t ws_bytes, void* stream) {
+                 int32_t act, int32_t dtype, const void* saved, size_t saved_bytes, void* dx, void* dw1, void* dw3,
+                 void* dw2, int32_t dw_dtype, float* dgates, void* ws, size_t ws_bytes, const smoe_aux* aux,
+                 void* stream) {
   SMOE_TRY(check_mlp(T, k, E, d_model, d_ff, act, dtype, w3));
+  if (dw_dtype != SMOE_F32 && dw_dtype != SMOE_BF16) return fail(SMOE_ERR_DTYPE, "dw_dtype %d", dw_dtype);
+  if (dtype == SMOE_F32 && dw_dtype != SMOE_F32) return fail(SMOE_ERR_DTYPE, "fp32 runs give fp32 weight gradients");
+  const int dw_bf16 = dw_dtype == SMOE_BF16;
   if ((act == SMOE_ACT_SWIGLU) != (dw3 != nullptr)) return fail(SMOE_ERR_NULL, "dw3 must be given exactly for SWIGLU");
   SMOE_TRY(need_ptr(w1, "w1"));
   SMOE_TRY(need_ptr(w2, "w2"));
@@ -969,9 +978,10 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
   const bool swiglu = act == SMOE_ACT_SWIGLU;
 
   if (M == 0) {
-    SMOE_HIP(launch_zero(dw1, size_t(E) * d_model * d_ff * 4, st), "mlp_bwd");
-    SMOE_HIP(launch_zero(dw2, size_t(E) * d_model * d_ff * 4, st), "mlp_bwd");
-    if (dw3) SMOE_HIP(launch_zero(dw3, size_t(E) * d_model * d_ff * 4, st), "mlp_bwd");
+    const size_t wb = size_t(E) * d_model * d_ff * (dw_bf16 ? 2 : 4);
+    SMOE_HIP(launch_zero(dw1, wb, st), "mlp_bwd");
+    SMOE_HIP(launch_zero(dw2, wb, st), "mlp_bwd");
+    if (dw3) SMOE_HIP(launch_zero(dw3, wb, st), "mlp_bwd");
     return ok();
   }
 
@@ -1061,14 +1071,9 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
   d.ldc = d_model;
   GemmPlan pd;
   plan_gemm(d, pd, SEG_M, EPI_STORE, 0, bf16, 1);
+  Fork fk(aux, st);
   const int64_t head = whole_round_tiles(d, pd);
-  const bool overlap = head > 0 && head < pd.grid;
-  AuxStream* ax = nullptr;
-  std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
-  if (overlap) {
-    aux_lock.lock();
-    SMOE_HIP(aux_stream(&ax), "mlp_bwd stream");
-  }
+  const bool overlap = fk.usable() && head > 0 && head < pd.grid;
   {
     RoleTimer t(SMOE_ROLE_DX, st);
     if (overlap) {
@@ -1076,10 +1081,8 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
       p1.grid = head;
       d.g_count = int(head);
       SMOE_HIP(launch_gemm(d, p1, st), "mlp_bwd dx");
-      SMOE_HIP(hipEventRecord(ax->fork, st), "mlp_bwd fork");
-      SMOE_HIP(hipStreamWaitEvent(ax->s, ax->fork, 0), "mlp_bwd fork");
-      SMOE_TRY(run_dw(dw1a, bf16, dw1, wl.partial2, ax->s, SMOE_ROLE_DW1, "mlp_bwd dW1"));
-      SMOE_HIP(hipEventRecord(ax->join, ax->s), "mlp_bwd join");
+      SMOE_HIP(fk.fork(), "mlp_bwd fork");
+      SMOE_TRY(run_dw(dw1a, bf16, dw1, dw_bf16, 0, wl.partial2, fk.side(), SMOE_ROLE_DW1, "mlp_bwd dW1"));
       d.g_base = int(head);
       d.g_count = 0;
       p2.grid = (pd.grid - head + 7) / 8 * 8;
@@ -1092,14 +1095,11 @@ int smoe_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w3
     RoleTimer t(SMOE_ROLE_KSUM, st);
     SMOE_HIP(launch_combine(wl.pairs, nullptr, T, k, d_model, dx, bf16, st), "mlp_bwd ksum");
   }
-  if (overlap) {
-    SMOE_HIP(hipStreamWaitEvent(st, ax->join, 0), "mlp_bwd join");
-    aux_lock.unlock();
-  }
+  SMOE_HIP(fk.join(), "mlp_bwd join");
   // 3. the weight gradients
-  SMOE_TRY(run_dw(dw2a, bf16, dw2, wl.partial, st, SMOE_ROLE_DW2, "mlp_bwd dW2"));
-  if (!overlap) SMOE_TRY(run_dw(dw1a, bf16, dw1, wl.partial, st, SMOE_ROLE_DW1, "mlp_bwd dW1"));
-  if (swiglu) SMOE_TRY(run_dw(dw3a, bf16, dw3, wl.partial, st, SMOE_ROLE_DW3, "mlp_bwd dW3"));
+  SMOE_TRY(run_dw(dw2a, bf16, dw2, dw_bf16, 0, wl.partial, st, SMOE_ROLE_DW2, "mlp_bwd dW2"));
+  if (!overlap) SMOE_TRY(run_dw(dw1a, bf16, dw1, dw_bf16, 0, wl.partial, st, SMOE_ROLE_DW1, "mlp_bwd dW1"));
+  if (swiglu) SMOE_TRY(run_dw(dw3a, bf16, dw3, dw_bf16, 0, wl.partial, st, SMOE_ROLE_DW3, "mlp_bwd dW3"));
   return ok();
 }
 

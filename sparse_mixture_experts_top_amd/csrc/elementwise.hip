@@ -103,10 +103,13 @@ hipError_t launch_reduce_dg(const float* part, int slots, int M, const int* offs
 }
 
 // grid: (element blocks, E).  Experts whose rows formed one chunk were
-// written in place by the GEMM and are skipped.
+// written in place by the GEMM and are skipped, unless every chunk wrote a
+// partial (all_partial: a bf16 or accumulated result).
+template <class OutT>
 __global__ __launch_bounds__(kEwThreads) void reduce_dw_kernel(const float* __restrict__ partial,
                                                                const int* __restrict__ offsets, int KS,
-                                                               int64_t elems4, float* __restrict__ dw) {
+                                                               int64_t elems4, OutT* __restrict__ dw,
+                                                               int all_partial, int accumulate) {
   __shared__ int first_s, n_s;
   const int e = blockIdx.y;
   if (threadIdx.x == 0) {
@@ -117,11 +120,11 @@ __global__ __launch_bounds__(kEwThreads) void reduce_dw_kernel(const float* __re
   }
   __syncthreads();
   const int first = first_s, n = n_s;
-  if (n == 1) return;
-  float4* out = reinterpret_cast<float4*>(dw) + int64_t(e) * elems4;
+  if (n == 1 && !all_partial) return;
+  OutT* out = dw + int64_t(e) * elems4 * 4;
   const float4* pv = reinterpret_cast<const float4*>(partial) + int64_t(first) * elems4;
   for (int64_t i = blockIdx.x * int64_t(kEwThreads) + threadIdx.x; i < elems4; i += int64_t(gridDim.x) * kEwThreads) {
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
     // chunks in ascending order; four loads in flight before they are summed
     int c = 0;
     for (; c + 4 <= n; c += 4) {
@@ -130,58 +133,51 @@ __global__ __launch_bounds__(kEwThreads) void reduce_dw_kernel(const float* __re
       for (int q = 0; q < 4; ++q) v[q] = pv[int64_t(c + q) * elems4 + i];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        s.x += v[q].x; s.y += v[q].y; s.z += v[q].z; s.w += v[q].w;
+        s[0] += v[q].x; s[1] += v[q].y; s[2] += v[q].z; s[3] += v[q].w;
       }
     }
     for (; c < n; ++c) {
       const float4 v = pv[int64_t(c) * elems4 + i];
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      s[0] += v.x; s[1] += v.y; s[2] += v.z; s[3] += v.w;
     }
-    out[i] = s;
+    if (accumulate) {
+      float o[4];
+      ld4<OutT>(out + i * 4, o);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s[q] += o[q];
+    }
+    st4<OutT>(out + i * 4, s);
   }
 }
 
-hipError_t launch_reduce_dw(const float* partial, const int* offsets, int E, int KS, int64_t elems, float* dw,
-                            hipStream_t st) {
+hipError_t launch_reduce_dw(const float* partial, const int* offsets, int E, int KS, int64_t elems, void* dw,
+                            int all_partial, int accumulate, int out_bf16, hipStream_t st) {
   const int64_t e4 = elems / 4;
   if (e4 == 0 || E == 0) return hipSuccess;
   const unsigned gx = std::min<unsigned>(grid_for(e4, kEwThreads), 4096u);
-  hipLaunchKernelGGL(reduce_dw_kernel, dim3(gx, E), dim3(kEwThreads), 0, st, partial, offsets, KS, e4, dw);
+  if (out_bf16)
+    hipLaunchKernelGGL(reduce_dw_kernel<uint16_t>, dim3(gx, E), dim3(kEwThreads), 0, st, partial, offsets, KS, e4,
+                       static_cast<uint16_t*>(dw), all_partial, accumulate);
+  else
+    hipLaunchKernelGGL(reduce_dw_kernel<float>, dim3(gx, E), dim3(kEwThreads), 0, st, partial, offsets, KS, e4,
+                       static_cast<float*>(dw), all_partial, accumulate);
   return hipGetLastError();
 }
 
-// one grouped row per block-iteration, 4 columns per thread
-template <class T>
-__global__ __launch_bounds__(kEwThreads) void scale_rows_kernel(const T* __restrict__ x, int x_grouped, int fan,
-                                                                const float* __restrict__ gates,
-                                                                const int* __restrict__ sidx,
-                                                                const int* __restrict__ offsets, int E, int64_t d,
-                                                                T* __restrict__ out) {
+__global__ __launch_bounds__(kEwThreads) void grouped_gates_kernel(const float* __restrict__ gates,
+                                                                   const int* __restrict__ sidx,
+                                                                   const int* __restrict__ offsets, int E, int M,
+                                                                   float* __restrict__ gg) {
   const int rows = offsets[E];
-  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
-    const int s = sidx[r];
-    const int64_t xr = x_grouped ? r : s / fan;
-    const float g = gates[s];
-    for (int64_t c = int64_t(threadIdx.x) * 4; c < d; c += int64_t(kEwThreads) * 4) {
-      float v[4];
-      ld4<T>(x + xr * d + c, v);
-      for (int i = 0; i < 4; ++i) v[i] *= g;
-      st4<T>(out + int64_t(r) * d + c, v);
-    }
-  }
+  for (int r = blockIdx.x * kEwThreads + threadIdx.x; r < M; r += gridDim.x * kEwThreads)
+    gg[r] = r < rows ? gates[sidx[r]] : 0.f;
 }
 
-hipError_t launch_scale_rows(const void* x, int x_grouped, int fan, const float* gates, const int* sidx,
-                             const int* offsets, int E, int M, int64_t d, void* out, int bf16, hipStream_t st) {
+hipError_t launch_grouped_gates(const float* gates, const int* sidx, const int* offsets, int E, int M, float* gg,
+                                hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const unsigned g = unsigned(std::min(M, 1 << 16));
-  if (bf16)
-    hipLaunchKernelGGL(scale_rows_kernel<uint16_t>, dim3(g), dim3(kEwThreads), 0, st,
-                       static_cast<const uint16_t*>(x), x_grouped, fan, gates, sidx, offsets, E, d,
-                       static_cast<uint16_t*>(out));
-  else
-    hipLaunchKernelGGL(scale_rows_kernel<float>, dim3(g), dim3(kEwThreads), 0, st, static_cast<const float*>(x),
-                       x_grouped, fan, gates, sidx, offsets, E, d, static_cast<float*>(out));
+  hipLaunchKernelGGL(grouped_gates_kernel, dim3(grid_for(M, kEwThreads)), dim3(kEwThreads), 0, st, gates, sidx,
+                     offsets, E, M, gg);
   return hipGetLastError();
 }
 

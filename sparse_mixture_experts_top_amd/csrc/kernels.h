@@ -26,8 +26,9 @@ constexpr int kMaxExperts = 1024;
 //   KS rows):  C_e[i][j] += sum_{r in chunk} A(r,i) * B(r,j),  i < Mo, j < N
 //   A(r,i) = a0[arow(r) * lda + i],  B(r,j) = b0[brow(r) * ldb + j]
 //   brow(r) = b_scat ? sidx[r] / b_fan : r
-//   An expert with one chunk writes c0 + e*Mo*N directly; otherwise each
-//   chunk writes partial + chunk*Mo*N and reduce_dw() sums them.
+//   An expert with one chunk writes c0 + e*Mo*N directly (unless
+//   dw_all_partial); otherwise each chunk writes partial + chunk*Mo*N and
+//   reduce_dw() sums them.
 enum Mode { SEG_M = 0, SEG_K = 1 };
 
 // Epilogues (SEG_M).  v is the fp32 product; "stored" means rounded to the
@@ -40,7 +41,9 @@ enum Epi {
                    // c0 = stored(g v gelu'(h)); c2 = stored(g a)
   EPI_SWIGLU_BWD,  // v = dA/g; h1,h3 = aux0,aux1; a = stored(silu(h1) h3); dg += <a, v>;
                    // c0 = stored(g v h3 silu'(h1)); c1 = stored(g v silu(h1)); c2 = stored(g a)
-  EPI_PARTIAL      // SEG_K fp32 tile store
+  EPI_PARTIAL,     // SEG_K fp32 tile store
+  EPI_PARTIAL_GATED  // SEG_K fp32 tile store, A(r,i) scaled by kscale[r] first (bf16: the
+                     // scaled value rounded to bf16 before it enters the contraction)
 };
 
 struct GemmArgs {
@@ -81,6 +84,8 @@ struct GemmArgs {
   int aux_scat, aux_fan;
   float* dgpart;       // [slots][M]
   float* partial;      // SEG_K partial tiles [mt_ub][Mo*N]
+  int dw_all_partial;  // SEG_K: every chunk writes its partial (reduce_dw writes dw)
+  const float* kscale; // SEG_K EPI_PARTIAL_GATED: per grouped row scale of A
   // x / fan == (x * fan_m) >> fan_s for 0 <= x < 2^31 (set by plan_gemm)
   uint32_t a_fan_m, b_fan_m;
   int a_fan_s, b_fan_s;
@@ -158,13 +163,15 @@ hipError_t launch_combine(const float* pairs, const float* gates, int64_t T, int
 // dg[sidx[r]] = sum_s part[s*M + r] for r < offsets[E]
 hipError_t launch_reduce_dg(const float* part, int slots, int M, const int* offsets, int E, const int* sidx,
                             float* dg, hipStream_t st);
-// expert e with 0 chunks: dw[e] = 0; with >= 2 chunks: dw[e] = sum of its partials
-hipError_t launch_reduce_dw(const float* partial, const int* offsets, int E, int KS, int64_t elems, float* dw,
-                            hipStream_t st);
+// expert e with 0 chunks: dw[e] = 0; with >= 2 chunks (every expert if
+// all_partial): dw[e] = sum of its partials, in chunk order; accumulate adds
+// the sum to what dw holds; dw is fp32 or (out_bf16) bf16, rounded once
+hipError_t launch_reduce_dw(const float* partial, const int* offsets, int E, int KS, int64_t elems, void* dw,
+                            int all_partial, int accumulate, int out_bf16, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
-// out[r] = g[sidx[r]] * x[xrow(r)] for grouped rows r < offsets[E], rounded
-// to the storage type; xrow(r) = x_grouped ? r : sidx[r] / fan
-hipError_t launch_scale_rows(const void* x, int x_grouped, int fan, const float* gates, const int* sidx,
-                             const int* offsets, int E, int M, int64_t d, void* out, int bf16, hipStream_t st);
+// gg[r] = gates[sidx[r]] for grouped rows r < offsets[E], 0 for r < M past
+// them: the gates in grouped order (one float per assignment)
+hipError_t launch_grouped_gates(const float* gates, const int* sidx, const int* offsets, int E, int M, float* gg,
+                                hipStream_t st);
 
 }  // namespace smoe

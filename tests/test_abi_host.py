@@ -22,7 +22,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lib.smoe_abi_version() == 1
+    assert lib.smoe_abi_version() == 2
     for s in range(7):
         assert lib.smoe_status_string(s)
     assert lib.smoe_status_string(0) == b"ok"
@@ -78,11 +78,56 @@ def test_parallel_linear_rejects_bad_arguments():
     assert call(gates=_fake(), wsb=16) == 4
 
 
+def test_parallel_linear_bwd_rejects_bad_arguments():
+    """The backward's output types and accumulation flag are checked on the
+    host; fp32 runs take fp32 outputs only."""
+    f = lib.smoe_parallel_linear_bwd
+    args = dict(x=_fake(), x_rows=8, d_in=64, w=_fake(), d_out=64, E=4, T=8, k=2, sidx=_fake(), off=_fake(),
+                xg=0, yg=0, gates=NULL, dy=_fake(), dx=_fake(), dx_dtype=smoe.BF16, dw=_fake(),
+                dw_dtype=smoe.F32, acc=0, dg=NULL, dtype=smoe.BF16, ws=_fake(), wsb=1 << 20, st=NULL)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(dx_dtype=4) == 3
+    assert call(dw_dtype=-1) == 3
+    assert call(dtype=smoe.F32, dx_dtype=smoe.BF16, dw_dtype=smoe.F32) == 3
+    assert call(dtype=smoe.F32, dx_dtype=smoe.F32, dw_dtype=smoe.BF16) == 3
+    assert call(dg=_fake()) == 1                   # dgates needs gates
+    assert call(gates=_fake(), yg=1) == 2
+    assert call(wsb=0) == 4
+
+
+def test_gated_parallel_linear_bwd_keeps_no_scaled_copy_of_x():
+    """With gates, the workspace grows by the gate-gradient partials and
+    one float per assignment (the gates in grouped order, which scale the
+    weight-gradient product's rows in registers), never by a [T*k, d_in]
+    copy of the gate-scaled input."""
+    for T, k, E, d_in, d_out, xg in ((8192, 4, 16, 128, 2048, 1), (8192, 4, 16, 2048, 128, 0),
+                                     (16384, 2, 8, 4096, 4096, 0)):
+        for dt in (smoe.F32, smoe.BF16):
+            x_rows = T * k if xg else T
+            plain = lib.smoe_parallel_linear_bwd_workspace_bytes(T, k, E, x_rows, d_in, d_out, xg, 0, dt)
+            gated = lib.smoe_parallel_linear_bwd_workspace_bytes(T, k, E, x_rows, d_in, d_out, xg, 1, dt)
+            slots = 4 * ((d_in + 255) // 256) if dt == smoe.BF16 else (d_in + 63) // 64
+            extra = gated - plain
+            assert extra <= slots * T * k * 4 + T * k * 4 + 1024, (T, k, d_in, dt, extra)
+            assert extra < T * k * d_in * (2 if dt == smoe.BF16 else 4)
+
+
+def test_aux_struct_layout():
+    """struct smoe_aux is three pointers: stream, fork event, join event."""
+    assert ctypes.sizeof(smoe.SmoeAux) == 3 * ctypes.sizeof(ctypes.c_void_p)
+    assert [n for n, _ in smoe.SmoeAux._fields_] == ["stream", "fork_event", "join_event"]
+
+
 @pytest.mark.parametrize("entry", ["smoe_mlp_fwd", "smoe_mlp_fwd_fused_combine"])
 def test_mlp_rejects_bad_arguments(entry):
     f = getattr(lib, entry)
     base = [_fake(), _fake(), NULL, _fake(), 16, 64, 128, 4, 2, _fake(), _fake(), smoe.ACT_GELU,
-            smoe.BF16, _fake(), _fake(), 1 << 30, _fake(), 1 << 30, NULL]
+            smoe.BF16, _fake(), _fake(), 1 << 30, _fake(), 1 << 30, NULL, NULL]
     a = list(base); a[11] = 5
     assert f(*a) == 3                              # unknown activation
     a = list(base); a[11] = smoe.ACT_SWIGLU
@@ -94,9 +139,15 @@ def test_mlp_rejects_bad_arguments(entry):
     a = list(base); a[17] = 8
     assert f(*a) == 4                              # workspace too small
     g = lib.smoe_mlp_bwd
-    assert g(_fake(), _fake(), _fake(), NULL, _fake(), 16, 64, 128, 4, 2, _fake(), _fake(),
-             smoe.ACT_GELU, smoe.BF16, _fake(), 1 << 30, _fake(), _fake(), _fake(), _fake(), NULL,
-             _fake(), 1 << 30, NULL) == 1          # dw3 given for GELU
+
+    def bwd(dw3=NULL, dtype=smoe.BF16, dw_dtype=smoe.F32):
+        return g(_fake(), _fake(), _fake(), NULL, _fake(), 16, 64, 128, 4, 2, _fake(), _fake(),
+                 smoe.ACT_GELU, dtype, _fake(), 1 << 30, _fake(), _fake(), dw3, _fake(), dw_dtype, NULL,
+                 _fake(), 1 << 30, NULL, NULL)
+
+    assert bwd(dw3=_fake()) == 1                   # dw3 given for GELU
+    assert bwd(dw_dtype=5) == 3                    # unknown weight-gradient type
+    assert bwd(dtype=smoe.F32, dw_dtype=smoe.BF16) == 3   # fp32 runs give fp32 dw
 
 
 def test_bf16_operands_beyond_32bit_offsets_are_rejected():
@@ -116,7 +167,7 @@ def test_bf16_operands_beyond_32bit_offsets_are_rejected():
     g = lib.smoe_mlp_fwd
     # hidden rows [2 * 160000, 14336] bf16 = 9.2 GB
     assert g(_fake(), _fake(), NULL, _fake(), 160000, 64, 14336, 4, 2, _fake(), _fake(), smoe.ACT_GELU,
-             smoe.BF16, _fake(), _fake(), 1 << 40, _fake(), 1 << 40, NULL) == 2
+             smoe.BF16, _fake(), _fake(), 1 << 40, _fake(), 1 << 40, NULL, NULL) == 2
     assert b"hidden rows" in lib.smoe_last_error()
 
 
