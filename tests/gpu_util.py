@@ -50,12 +50,14 @@ def bf16_half_ulp(v) -> np.ndarray:
     return np.ldexp(1.0, e - 9)
 
 
-def rel_err_stored_bf16(got, ref) -> float:
-    """rel_err for a result the path stores in bf16: each element's error
-    beyond the final rounding to bf16 (half an ulp at its magnitude), over
-    RMS(oracle).  A bf16 tensor cannot hold an element of 8*RMS or more to
-    within 2e-2*RMS, so the bound applies to the computation before that one
-    storage rounding."""
+def rel_err_beyond_bf16_rounding(got, ref) -> float:
+    """For the outputs NAMED as exceptions to the plain bound only (each with
+    its reason and measured plain error in the design notes): each element's
+    error beyond the final rounding to bf16 (half an ulp at its magnitude),
+    over RMS(oracle).  A bf16 tensor cannot hold an element of 8 RMS or more
+    to within 2e-2 RMS, so for such a tensor the bound is applied to the
+    computation before its one storage rounding; the plain error is printed
+    beside it."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -64,6 +66,36 @@ def rel_err_stored_bf16(got, ref) -> float:
     excess = np.abs(got - ref) - bf16_half_ulp(np.maximum(np.abs(got), np.abs(ref)))
     worst = float(np.maximum(excess, 0.0).max(initial=0.0))
     return worst / rms if rms > 0.0 else worst
+
+
+def tokens_covering_tiles(sorted_scattered_idxs, offsets, k: int, block: int, extra: int, seed) -> np.ndarray:
+    """Tokens whose assignments put at least one grouped row in every block
+    of `block` rows of every expert's segment (the m-tiles of the grouped
+    products start at each expert's first row), plus each expert's first and
+    last row and `extra` more tokens at random: sorted, unique."""
+    s = np.asarray(sorted_scattered_idxs)
+    off = np.asarray(offsets)
+    rng = np.random.default_rng(seed)
+    rows = []
+    for e in range(off.size - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi <= lo:
+            continue
+        rows += [lo, hi - 1]
+        for b in range(lo, hi, block):
+            rows.append(int(rng.integers(b, min(b + block, hi))))
+    toks = s[np.asarray(rows, dtype=np.int64)] // k
+    T = s.size // k
+    more = rng.choice(T, min(extra, T), replace=False) if extra else np.zeros(0, dtype=np.int64)
+    return np.unique(np.concatenate([toks, more, [0, T - 1]]).astype(np.int64))
+
+
+def cols_covering(n: int, block: int, seed) -> np.ndarray:
+    """One column at random from every block of `block` columns of [0, n),
+    plus the first and the last: sorted, unique."""
+    rng = np.random.default_rng(seed)
+    c = [int(rng.integers(b, min(b + block, n))) for b in range(0, n, block)]
+    return np.unique(np.asarray(c + [0, n - 1], dtype=np.int64))
 
 
 def tol_for(w: Workload) -> float:

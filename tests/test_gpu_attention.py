@@ -1,9 +1,11 @@
 """smoe_moa_attention_fwd and _bwd on the GPU against the oracle: grouped
 query rows of several expert heads against shared K/V, causal within each
-sequence.  bf16 inputs; o, dq, dk, dv are stored in bf16 and held to 2e-2
-of their RMS beyond that final rounding; lse (fp32, from exact bf16
-products summed in fp32) to 1e-3 absolute.  The routing arrays are the
-oracle's.  The backward is given the oracle's forward (o rounded to bf16,
+sequence.  bf16 inputs; o, dq, dk, dv are bf16 and held to the plain bound
+max |gpu - oracle| <= 2e-2 RMS, except where a bf16 tensor cannot hold its
+own largest elements that closely (named in EXCEPT below, with the reason):
+those are held to 2e-2 RMS beyond their final rounding to bf16, and their
+plain error is printed.  lse (fp32, from exact bf16 products summed
+in fp32) to 1e-3 absolute.  The routing arrays are the oracle's.  The backward is given the oracle's forward (o rounded to bf16,
 as the forward stores it, and lse); D_r = do_r . o_r comes from that stored
 o on both sides."""
 import numpy as np
@@ -11,10 +13,34 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import BF16_TOL, dev_tensor, host, rel_err, rel_err_stored_bf16, say
+from tests.gpu_util import BF16_TOL, dev_tensor, host, rel_err, rel_err_beyond_bf16_rounding, say
 from workloads import make_moa_attention
 
 pytestmark = pytest.mark.gpu
+
+# Outputs whose largest elements lie far above their RMS: a row's output is
+# an average over its keys, so the first positions of each sequence (few
+# keys) carry values of a single v row (up to ~4.5) while long rows average
+# down; rounding such an element to bf16 alone errs by up to 2^-9 of it,
+# which can exceed 2e-2 of the tensor's RMS.
+# In the whole-layer chain the O projection's output and the Q projection's
+# input gradient inherit the same spread from o and dq (tokens at the start
+# of a sequence), so they are named there too.
+EXCEPT = ("o", "dq", "dk", "dv")
+EXCEPT_CHAIN = EXCEPT + ("out", "dx")
+
+
+def check_bf16(name, got, want, named=EXCEPT):
+    """Plain bound, or for the named exceptions the bound beyond the final
+    rounding to bf16; the plain error is printed either way."""
+    plain = rel_err(got, want)
+    if name in named:
+        e = rel_err_beyond_bf16_rounding(got, want)
+        say(f"  {name} max err / RMS {plain:.2e} (named exception; beyond its bf16 rounding {e:.2e})")
+        assert e <= BF16_TOL, name
+    else:
+        say(f"  {name} max err / RMS {plain:.2e}")
+        assert plain <= BF16_TOL, name
 
 
 def setup(B, S, E, k, cid, hd=128):
@@ -32,10 +58,9 @@ def check_fwd(smoe, w, sidx, f, d, rows=None):
     torch.cuda.synchronize()
     rows = np.arange(sidx.shape[0]) if rows is None else rows
     ref = oracle.moa_attention_fwd(f["q"][rows], f["k"], f["v"], sidx[rows], w.k, S)
-    e = rel_err_stored_bf16(host(o)[rows], ref["o"])
+    check_bf16("o", host(o)[rows], ref["o"])
     el = float(np.abs(host(lse)[rows] - ref["lse"]).max())
-    say(f"  o err {e:.2e}  lse max abs err {el:.2e}")
-    assert e <= BF16_TOL
+    say(f"  lse max abs err {el:.2e}")
     assert el <= 1e-3
     return o, lse
 
@@ -77,9 +102,7 @@ def check_bwd(smoe, w, sidx, f, d):
     dq, dk, dv = smoe.smoe_moa_attention_bwd(d["q"], d["k"], d["v"], d["sidx"], w.k, S, o, lse, d["do"])
     torch.cuda.synchronize()
     for n, got in (("dq", dq), ("dk", dk), ("dv", dv)):
-        e = rel_err_stored_bf16(host(got), rb[n])
-        say(f"  {n} err {e:.2e}")
-        assert e <= BF16_TOL, n
+        check_bf16(n, host(got), rb[n])
     return dq, dk, dv, o, lse
 
 
@@ -139,12 +162,9 @@ def test_moa_layer_chain(smoe):
     dx, dwq, _ = smoe.smoe_parallel_linear_bwd(dd["x"], dd["wq"], T, k, s, off, False, True, dq)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(s.cpu().numpy(), sidx)
-    for n, got, want, stored in (("out", out, ref_out, True), ("dx", dx, ref_dx, True), ("dk", dk, ab["dk"], True),
-                                 ("dv", dv, ab["dv"], True), ("dwq", dwq, ref_dwq, False),
-                                 ("dwo", dwo, ref_dwo, False), ("dgates", dg, ref_dg, False)):
-        e = rel_err_stored_bf16(host(got), want) if stored else rel_err(host(got), want)
-        say(f"  {n} err {e:.2e}")
-        assert e <= BF16_TOL, n
+    for n, got, want in (("out", out, ref_out), ("dx", dx, ref_dx), ("dk", dk, ab["dk"]), ("dv", dv, ab["dv"]),
+                         ("dwq", dwq, ref_dwq), ("dwo", dwo, ref_dwo), ("dgates", dg, ref_dg)):
+        check_bf16(n, host(got), want, EXCEPT_CHAIN)
 
 
 def test_attention_scores_growing_along_the_sequence(smoe):
@@ -195,10 +215,9 @@ def test_attention_one_token_sequences(smoe):
     torch.cuda.synchronize()
     want_dv = np.zeros_like(f["v"])
     np.add.at(want_dv, tok, f["do"])
-    e = rel_err_stored_bf16(host(dv), want_dv)
+    check_bf16("dv", host(dv), want_dv)
     rms_do = float(np.sqrt(np.mean(f["do"] ** 2)))
-    say(f"  dv err {e:.2e}  max|dq| {float(np.abs(host(dq)).max()):.1e}  max|dk| {float(np.abs(host(dk)).max()):.1e}")
-    assert e <= BF16_TOL
+    say(f"  max|dq| {float(np.abs(host(dq)).max()):.1e}  max|dk| {float(np.abs(host(dk)).max()):.1e}")
     assert np.abs(host(dq)).max() <= 1e-4 * rms_do and np.abs(host(dk)).max() <= 1e-4 * rms_do
 
 

@@ -95,3 +95,43 @@ def test_single_parallel_linear_workload(smoe, xg, yg):
     say(f"  y err {e:.2e}")
     assert e <= BF16_TOL
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("xg,x_rows,use_gates", [(False, "T", False), (True, "M", True), (False, "T", True)])
+def test_backward_output_types_and_accumulation(smoe, xg, x_rows, use_gates):
+    """dx_dtype = fp32 keeps the exact sum unrounded (the bf16 dx is exactly
+    its rounding); dw_dtype = bf16 is the fp32 dw rounded once; with
+    accumulate_dw the gradient is added to the given dw (fp32 and bf16)."""
+    w = make_pl(900, 136, 200, 6, 3, "bf16", 121, x_std=1.0, w_std=0.1, with_gates=use_gates)
+    say(f"pl backward output types xg={xg} x_rows={x_rows} gates={use_gates}")
+    x_np, rt = _setup(smoe, w, xg, x_rows)
+    T, k = w.T, w.k
+    xd, wd = dev_tensor(x_np), dev_tensor(w.tensors["w"])
+    gd = dev_tensor(w.tensors["gates"]) if use_gates else None
+    dyd = dev_tensor(w.tensors["dy_comb"] if use_gates else w.tensors["dy"])
+    s, off = rt["sorted_scattered_idxs"], rt["offsets"]
+    dx16, dw32, _ = smoe.smoe_parallel_linear_bwd(xd, wd, T, k, s, off, xg, False, dyd, gd)
+    dx32, dw16, _ = smoe.smoe_parallel_linear_bwd(xd, wd, T, k, s, off, xg, False, dyd, gd,
+                                                  dx_dtype=torch.float32, dw_dtype=torch.bfloat16)
+    init32 = torch.randn(dw32.shape, device="cuda", dtype=torch.float32)
+    init16 = init32.to(torch.bfloat16)
+    acc32, acc16 = init32.clone(), init16.clone()
+    smoe.smoe_parallel_linear_bwd(xd, wd, T, k, s, off, xg, False, dyd, gd, need_dx=False, dw=acc32,
+                                  accumulate_dw=True)
+    smoe.smoe_parallel_linear_bwd(xd, wd, T, k, s, off, xg, False, dyd, gd, need_dx=False, dw=acc16,
+                                  accumulate_dw=True)
+    torch.cuda.synchronize()
+    assert dx32.dtype == torch.float32 and dw16.dtype == torch.bfloat16
+    assert torch.equal(dx16, dx32.to(torch.bfloat16))
+    assert torch.equal(dw16, dw32.to(torch.bfloat16))
+    assert torch.equal(acc32, dw32 + init32)
+    assert torch.equal(acc16, (dw32 + init16.float()).to(torch.bfloat16))
+    # and the fp32 dx against the oracle
+    f = lambda n: w.f32(n).astype(np.float64)
+    xs = f("x_grouped") if (xg or x_rows == "M") else f("x")
+    gates = w.tensors["gates"].astype(np.float64) if use_gates else None
+    rdx, _, _ = oracle.parallel_linear_bwd(xs, f("w"), w.tensors["expert_idxs"], xg, False,
+                                           f("dy_comb") if use_gates else f("dy"), gates=gates, storage="bf16")
+    e = rel_err(host(dx32), rdx)
+    say(f"  dx (fp32) max err / RMS {e:.2e}")
+    assert e <= BF16_TOL

@@ -14,13 +14,16 @@ choice must be a valid top-k (distinct ids whose oracle logits lie within
 the bound of the sorted ones).  The gates are checked against the softmax of
 the oracle's logits at the GPU's ids.  The backward takes the oracle's
 forward choice as input on both sides; dw is fp32 (tolerance 1e-4 of its
-RMS), dx is stored in the input dtype (bf16: beyond its final rounding)."""
+RMS), dx is in the input dtype: fp32 is held to 1e-4 of its RMS; bf16 dx is
+a named exception to the plain 2e-2 bound (tokens with large dlogits put
+elements far above the RMS, whose own bf16 rounding exceeds 2e-2 RMS): it is
+held to 1e-4 RMS beyond its final rounding, and its plain error printed."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from tests.gpu_util import F32_TOL, dev_tensor, host, rel_err, rel_err_stored_bf16, say
+from tests.gpu_util import F32_TOL, dev_tensor, host, rel_err, rel_err_beyond_bf16_rounding, say
 from workloads import bf16_bits_to_f32, make_config, make_router
 
 pytestmark = pytest.mark.gpu
@@ -87,8 +90,12 @@ def check_bwd(smoe, x, g, ref_fwd, dgates, xd, gd, dtype, dx_in=None, dx_in_d=No
     assert e <= F32_TOL
     want_dx = rb["dx"] + (dx_in if dx_in is not None else 0.0)
     got_dx = host(dx)
-    e = rel_err(got_dx, want_dx) if dtype == "f32" else rel_err_stored_bf16(got_dx, want_dx)
-    say(f"  dx err {e:.2e}")
+    e = rel_err(got_dx, want_dx)
+    if dtype == "f32":
+        say(f"  dx max err / RMS {e:.2e}")
+    else:
+        plain, e = e, rel_err_beyond_bf16_rounding(got_dx, want_dx)
+        say(f"  dx max err / RMS {plain:.2e} (named exception; beyond its bf16 rounding {e:.2e})")
     assert e <= F32_TOL
     return dg, dx
 
@@ -250,8 +257,10 @@ def test_router_bwd_many_tokens(smoe):
     x64 = (xb[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     g64 = ((wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)).T   # G [d, E]
     rb = oracle.router_bwd(x64, g64, idx[rows], gates[rows].astype(np.float64), dgates[rows].astype(np.float64))
-    e = rel_err_stored_bf16(host(dx[torch.from_numpy(rows).cuda()]), rb["dx"])
-    say(f"  dx (sampled) err {e:.2e}")
+    got_dx = host(dx[torch.from_numpy(rows).cuda()])
+    e = rel_err_beyond_bf16_rounding(got_dx, rb["dx"])
+    say(f"  dx (sampled) max err / RMS {rel_err(got_dx, rb['dx']):.2e} (named exception; beyond its bf16 rounding "
+        f"{e:.2e})")
     assert e <= F32_TOL
     dwh = host(dw)
     scale = np.abs(dwh).sum(axis=0)

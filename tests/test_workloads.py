@@ -47,19 +47,45 @@ def test_pl_workload_shapes():
     assert w.tensors["dy"].shape == (128, 16)
 
 
-def test_bf16_half_ulp_bounds_rounding():
-    """The stored-bf16 error metric removes exactly the largest rounding
-    error: half an ulp at each magnitude (checked against bf16 rounding)."""
+def test_tile_covering_samples():
+    """The full-size parity samples: every block of rows of every expert's
+    grouped segment holds a sampled token's row, and every column block a
+    sampled column."""
     import oracle
-    from tests.gpu_util import bf16_half_ulp, rel_err_stored_bf16
+    from tests.gpu_util import cols_covering, tokens_covering_tiles
+    rng = np.random.default_rng(3)
+    T, k, E = 3000, 2, 7
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    r = oracle.route(idx, E)
+    toks = tokens_covering_tiles(r["sorted_scattered_idxs"], r["offsets"], k, 128, 5, 1)
+    chosen = np.zeros(T, dtype=bool)
+    chosen[toks] = True
+    rows_hit = chosen[r["sorted_scattered_idxs"] // k]
+    for e in range(E):
+        lo, hi = r["offsets"][e], r["offsets"][e + 1]
+        for b in range(lo, hi, 128):
+            assert rows_hit[b:min(b + 128, hi)].any(), (e, b)
+        assert rows_hit[lo] and rows_hit[hi - 1]
+    c = cols_covering(1000, 256, 2)
+    assert c[0] == 0 and c[-1] == 999
+    for b in range(0, 1000, 256):
+        assert ((c >= b) & (c < b + 256)).any()
+
+
+def test_bf16_half_ulp_bounds_rounding():
+    """The metric used for the named exceptions to the plain bound removes
+    exactly the largest rounding error, half an ulp at each magnitude
+    (checked against the oracle's bf16 rounding), and nothing more."""
+    import oracle
+    from tests.gpu_util import bf16_half_ulp, rel_err_beyond_bf16_rounding
     v = np.random.default_rng(5).standard_normal(20000) * np.exp(np.random.default_rng(6).uniform(-8, 8, 20000))
     r = oracle.bf16_round(v)
     assert np.all(np.abs(r - v) <= bf16_half_ulp(v) * (1 + 1e-12))
-    # at 10 * RMS a bf16 value can be off by more than 2e-2 * RMS ...
+    # at 10 RMS a bf16 value can be off by more than 2e-2 RMS ...
     x = np.concatenate([np.ones(999) * 0.1, [10.03]])
     assert np.abs(oracle.bf16_round(x) - x).max() / np.sqrt(np.mean(x ** 2)) > 2e-2
-    # ... which the stored metric does not count, while any further error counts
-    assert rel_err_stored_bf16(oracle.bf16_round(x), x) == 0.0
+    # ... which this metric does not count, while any further error counts
+    assert rel_err_beyond_bf16_rounding(oracle.bf16_round(x), x) == 0.0
     y = oracle.bf16_round(x).copy()
     y[0] += 0.05
-    assert rel_err_stored_bf16(y, x) > 0.0
+    assert rel_err_beyond_bf16_rounding(y, x) > 0.0
