@@ -119,6 +119,23 @@ int smoe_route(const int32_t* expert_idxs, int64_t T, int32_t k, int32_t E,
                void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * smoe_route_noalloc - smoe_route for callers that cannot allocate device
+ * memory (code under stream capture into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation): the same kernels, outputs and errors,
+ * with the chunk histograms in a static device array of the library
+ * (4 MiB per device, held until the process ends) instead of a workspace.
+ * Sizes with ceil(T*k / 4096) * E > 2^20 are rejected (SMOE_ERR_SHAPE,
+ * nothing enqueued); nothing is allocated or freed.  Every call on one
+ * device shares that array (each call writes what it reads, so nothing
+ * carries over between calls): calls that overlap on one device (on
+ * different streams, or from several host threads) race and must be
+ * ordered by the caller.
+ * ------------------------------------------------------------------------ */
+int smoe_route_noalloc(const int32_t* expert_idxs, int64_t T, int32_t k, int32_t E,
+                       int32_t* sorted_expert_idxs, int32_t* sorted_scattered_idxs,
+                       int32_t* counts, int32_t* offsets, void* stream);
+
+/* ------------------------------------------------------------------------
  * smoe_parallel_linear_fwd - scatter2scatter forward (all four layouts).
  *
  * For every grouped row r (expert e, assignment p = sorted_scattered_idxs[r]):

@@ -54,6 +54,7 @@ _SIGS = {
     "smoe_abi_version": (ctypes.c_int, []),
     "smoe_route_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "smoe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "smoe_route_noalloc": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "smoe_parallel_linear_fwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64, _i32, _i32]),
     "smoe_parallel_linear_fwd": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i32, _i64, _i32, _vp, _vp,
                                                 _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp]),

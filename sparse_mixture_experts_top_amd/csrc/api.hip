@@ -536,6 +536,26 @@ int smoe_route(const int32_t* expert_idxs, int64_t T, int32_t k, int32_t E, int3
   return ok();
 }
 
+int smoe_route_noalloc(const int32_t* expert_idxs, int64_t T, int32_t k, int32_t E, int32_t* sorted_expert_idxs,
+                       int32_t* sorted_scattered_idxs, int32_t* counts, int32_t* offsets, void* stream) {
+  SMOE_TRY(check_common(T, k, E, SMOE_F32));
+  const int64_t M = T * k;
+  if (M > 0 && (!expert_idxs || !sorted_expert_idxs || !sorted_scattered_idxs))
+    return fail(SMOE_ERR_NULL, "routing arrays must not be NULL");
+  if (!counts || !offsets) return fail(SMOE_ERR_NULL, "counts/offsets must not be NULL");
+  const size_t need = route_ws_bytes(M, E) / sizeof(int);
+  if (need > route_static_scratch_ints())
+    return fail(SMOE_ERR_SHAPE, "T*k=%lld with E=%d needs %zu ints of scratch, beyond the static %zu "
+                "(ceil(T*k/4096)*E must not exceed it)", (long long)M, E, need, route_static_scratch_ints());
+  int* scr = nullptr;
+  size_t cap = 0;
+  SMOE_HIP(route_static_scratch(&scr, &cap), "smoe_route_noalloc scratch");
+  SMOE_HIP(launch_route(expert_idxs, int(M), E, sorted_expert_idxs, sorted_scattered_idxs, counts, offsets, scr,
+                        static_cast<hipStream_t>(stream)),
+           "smoe_route_noalloc");
+  return ok();
+}
+
 // ------------------------------------------------------ parallel linear --
 size_t smoe_parallel_linear_fwd_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t d_in, int64_t d_out,
                                                 int32_t with_gates, int32_t dtype) {

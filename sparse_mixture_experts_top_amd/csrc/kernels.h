@@ -153,6 +153,10 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& plan, hipStream_t st);
 
 // routing
 size_t route_ws_bytes(int64_t M, int E);
+// device address (this device) and size in ints of the routing kernels'
+// static scratch, for the allocation-free entry point
+hipError_t route_static_scratch(int** ptr, size_t* ints);
+size_t route_static_scratch_ints();
 hipError_t launch_route(const int* eidx, int M, int E, int* s_exp, int* s_sct, int* counts, int* offsets,
                         void* ws, hipStream_t st);
 

@@ -13,6 +13,8 @@
 //  3. route_scatter : each chunk ranks its elements among equal experts with
 //                     wave64 ballots (match by bit planes of the expert id),
 //                     in ascending p, and writes them at their final rows.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -128,6 +130,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(const int* __rest
     __syncthreads();
   }
 }
+
+// Scratch of the allocation-free routing entry point (smoe_route_noalloc):
+// the chunk histograms live in this device-resident array instead of a
+// caller workspace.  Each device the library runs on holds its own copy
+// until the process ends.  Host code never passes the array's name to a
+// kernel (in host code it is a stand-in, not a device address): it asks
+// for the device address once per device and uses that.
+constexpr size_t kRouteScratchInts = size_t(1) << 20;   // 4 MiB
+static __device__ __align__(256) int scratch[kRouteScratchInts];
+
+hipError_t route_static_scratch(int** ptr, size_t* ints) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<int*>(p);
+  }
+  *ptr = addr[dev];
+  *ints = kRouteScratchInts;
+  return hipSuccess;
+}
+
+size_t route_static_scratch_ints() { return kRouteScratchInts; }
 
 size_t route_ws_bytes(int64_t M, int E) {
   const int64_t nb = (M + kChunk - 1) / kChunk;
