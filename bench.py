@@ -114,6 +114,101 @@ def pmc_summary(dir_fetch, dir_write, copy_bytes):
     return "\n".join(lines)
 
 
+def _read_durations(d):
+    """{dispatch id: duration ns} from the kernel trace of a rocprofv3 run."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    assert files, f"no kernel_trace.csv under {d}"
+    out = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                out[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return out
+
+
+def _short_kernel(name):
+    """Kernel name without its argument list (template arguments kept)."""
+    n = name.split("(")[0].replace("void ", "").replace("smoe::", "")
+    return n if len(n) < 140 else n[:137] + "..."
+
+
+def kernel_traffic_summary(dir_fetch, dir_write, copy_bytes):
+    """Text summary of two rocprofv3 runs of one command (--kernel-trace
+    --pmc FETCH_SIZE, then WRITE_SIZE) with --copy-mib: per kernel, its
+    launches, mean duration and mean HBM bytes fetched and written per
+    launch, each counter scaled by its reading for the copy kernel of known
+    size in the same run."""
+    per = {}
+    scales = {}
+    for ctr, d in (("FETCH_SIZE", dir_fetch), ("WRITE_SIZE", dir_write)):
+        disp = _read_dispatches(d)
+        copy = [v for _, n, v in disp if COPY_KERNEL_HINT in n and "smoe" not in n]
+        assert copy, ctr
+        scales[ctr] = copy_bytes / (float(np.median(copy)) * 1024.0)
+        for _, n, v in disp:
+            if "smoe" not in n:
+                continue
+            per.setdefault(_short_kernel(n), {}).setdefault(ctr, []).append(v * 1024.0 * scales[ctr])
+    dur = _read_durations(dir_fetch)
+    names = {}
+    for k, n, _ in _read_dispatches(dir_fetch):
+        if "smoe" in n:
+            names.setdefault(_short_kernel(n), []).append(dur[k])
+    lines = [f"counter scale: FETCH_SIZE {scales['FETCH_SIZE']:.4f}, WRITE_SIZE {scales['WRITE_SIZE']:.4f} "
+             f"bytes per counted byte (copy kernel of {copy_bytes} bytes)",
+             "kernel | launches | mean ms (under the profiler) | MB fetched | MB written | GB/s"]
+    for n, ds in sorted(names.items(), key=lambda kv: -sum(kv[1])):
+        f = float(np.mean(per[n]["FETCH_SIZE"])) if "FETCH_SIZE" in per[n] else 0.0
+        w = float(np.mean(per[n].get("WRITE_SIZE", [0.0])))
+        ms = float(np.mean(ds)) / 1e6
+        lines.append(f"{n} | {len(ds)} | {ms:.4f} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / (ms * 1e-3) / 1e9:.0f}")
+    lines.append(f"kernel_sources_sha256_16: {kernel_sources_hash()}")
+    return "\n".join(lines)
+
+
+def mfma_busy_summary(d):
+    """Text summary of one rocprofv3 run with --kernel-trace and
+    --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES: per
+    grouped-product role, the clock (GRBM_GUI_ACTIVE is summed over the 8
+    XCDs: cycles per XCD / duration) and the matrix cores' busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES counts busy cycles summed over the 1024 SIMDs,
+    32 per 32x32x16 multiply: busy / (1024 x cycles per XCD)); the
+    register-only MFMA loop of the same run is the reference."""
+    rows = {}
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    assert files, f"no counter_collection.csv under {d}"
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                key = int(r["Dispatch_Id"])
+                e = rows.setdefault(key, {"name": r["Kernel_Name"]})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dur = _read_durations(d)
+    disp = [(k, rows[k]) for k in sorted(rows)]
+    gemm = [(k, e) for k, e in disp if GEMM_KERNEL_HINT in e["name"]]
+    loop = [(k, e) for k, e in disp if "mfma_loop_kernel" in e["name"]]
+    assert gemm and len(gemm) % len(GEMM_ORDER) == 0, len(gemm)
+
+    def stats(items):
+        cyc = np.mean([e["GRBM_GUI_ACTIVE"] / 8.0 for _, e in items])
+        busy = np.mean([e["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * e["GRBM_GUI_ACTIVE"] / 8.0) for _, e in items])
+        ns = np.mean([dur[k] for k, _ in items])
+        return ns / 1e6, cyc / ns, busy
+
+    lines = [f"{len(gemm) // len(GEMM_ORDER)} steps; per launch: ms (under the profiler), clock GHz, "
+             f"matrix cores busy (fraction of cycles), busy x clock / 2.4 GHz (fraction of the bf16 peak rate)"]
+    for i, role in enumerate(GEMM_ORDER):
+        items = gemm[i::len(GEMM_ORDER)]
+        ms, ghz, busy = stats(items)
+        lines.append(f"  launch {i} {role:>4}: {ms:8.3f} ms  {ghz:5.2f} GHz  busy {busy:5.3f}  "
+                     f"rate {busy * ghz / 2.4:5.3f}")
+    if loop:
+        ms, ghz, busy = stats(loop)
+        lines.append(f"  mfma loop probe: {ms:8.3f} ms  {ghz:5.2f} GHz  busy {busy:5.3f}  rate {busy * ghz / 2.4:5.3f}")
+    lines.append(f"kernel_sources_sha256_16: {kernel_sources_hash()}")
+    return "\n".join(lines)
+
+
 def read_traffic(role):
     """HBM bytes per launch of a role's kernel from the committed counter
     summary, or None if absent or taken on other kernel sources."""
@@ -172,6 +267,12 @@ def parse():
                     help="also run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--kernel-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the per-kernel traffic summary of two rocprofv3 --kernel-trace --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of any workload run with --copy-mib, and exit")
+    ap.add_argument("--busy-summary", metavar="DIR",
+                    help="print the clock / matrix-core busy summary of one rocprofv3 run with "
+                         "--kernel-trace --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES and exit")
     ap.add_argument("--workload", default="mixtral", choices=["mixtral", "granular", "moa", "pl", "router", "attention", "sparsity",
                                                             "combine"],
                     help="mixtral (the measured line); the others print supplementary lines: "
@@ -200,7 +301,15 @@ def cpu_baseline(w, n_tokens):
     oracle.mlp_bwd(x, w1, w2, idx, gates, w.act, dout, w3=w3, storage="bf16", tokens=toks)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    affinity = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(min(threads, affinity)), "kind": "oracle",
+            "cpu_model": model, "affinity_cores": affinity, "blas_threads": int(threads),
             "sample": f"{n_tokens} seeded tokens of the same workload, fwd+bwd per token and "
                       f"choice in fp64 ({dt:.1f} s); per-token cost is constant so tokens/s "
                       f"extrapolates to the full batch"}
@@ -210,6 +319,12 @@ def main():
     args = parse()
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary, copy_bytes=(args.copy_mib or 1024) << 20))
+        return
+    if args.kernel_traffic:
+        print(kernel_traffic_summary(*args.kernel_traffic, copy_bytes=(args.copy_mib or 1024) << 20))
+        return
+    if args.busy_summary:
+        print(mfma_busy_summary(args.busy_summary))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build runs the hot path "
