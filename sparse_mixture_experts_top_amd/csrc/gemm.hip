@@ -258,18 +258,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int ALAY = MODE == SEG_M ? LAY_K : LAY_MN;
   constexpr int FM = BM / 64, FN = BN / 128;   // fragments per wave
   constexpr int WM = BM / 2, WN = BN / 4;      // wave tile
-  constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2;
   static_assert(BN >= 128 && BM >= 128, "tile");
   static_assert(!DUAL || (MODE == SEG_M && BLAY == LAY_MN && BN == 256), "dual B layout");
-  // two stage buffers, named statically (the loop below is unrolled by
-  // two): the compiler can then tell the stage being read from the one
-  // whose copies are in flight
-  __shared__ __attribute__((aligned(16))) char smem0[STAGE];
-  __shared__ __attribute__((aligned(16))) char smem1[STAGE];
-  auto stage = [&](auto s) SMOE_INL -> char* {
-    if constexpr (decltype(s)::value % 2 == 0) return smem0;
-    else return smem1;
-  };
+  // Stage buffers of 64 k.  Rows mode keeps three A buffers and two B
+  // buffers (160 KB at 256 x 256): the A copies of a stage then have two
+  // steps to land and are spread over the first three slices of a step,
+  // and only the B copies share the last slice.  Weights mode keeps two of
+  // each (its index rings take the rest of the LDS).
+  constexpr bool A3 = MODE == SEG_M;
+  constexpr int NBA = A3 ? 3 : 2;
+  constexpr int LDS_BYTES = NBA * A_BYTES + 2 * B_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  auto abuf = [&](auto s) SMOE_INL -> char* { return lds + (decltype(s)::value % NBA) * A_BYTES; };
+  auto bbuf = [&](auto s) SMOE_INL -> char* { return lds + NBA * A_BYTES + (decltype(s)::value % 2) * B_BYTES; };
+  constexpr int UNROLL = A3 ? 6 : 2;
 
   TileInfo T;
   if (!tile_of_block<BM, BN, MODE, DUAL>(p, T)) return;
@@ -419,78 +423,93 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   };
 
   // ---------------- copies of one stage ------------------------------------
-  // plan(kt) sets, for every copy of step kt, the lane's byte offset cv[c],
-  // the scalar offsets of the two operands and the descriptors; copy(c, stg)
-  // issues copy c into stage buffer stg.  A step inside the reduction adds
-  // the step's advance as the scalar offset; the step that crosses the end
-  // of a part (a uniform branch, at most one per part) masks the lanes
-  // past it instead.
-  uint32_t cv[LPS];
+  // planA(kt) / planB(kt) set, for every copy of an operand at step kt, the
+  // lane's byte offset (cva / cvb), the operand's scalar offset and its
+  // descriptor; copyA(c, buf) / copyB(c, buf) issue copy c into a stage
+  // buffer.  A step inside the reduction adds the step's advance as the
+  // scalar offset; the step that crosses the end of a part (a uniform
+  // branch, at most one per part) masks the lanes past it instead.
+  uint32_t cva[NA], cvb[NB];
   uint32_t csa = 0, csb = 0;
   rsrc_t cra = rA0, crb = rB0;
-  auto plan = [&](int kt) SMOE_INL {
+  auto planA = [&](int kt) SMOE_INL {
     if constexpr (MODE == SEG_M) {
       const bool p1 = kt >= KT0;
       const int kl = (p1 ? kt - KT0 : kt) * kBK;
       const int Kp = p1 ? K1 : K0;
       cra = p1 ? rA1 : rA0;
-      crb = (BLAY == LAY_K && p1) ? rB1 : rB0;
       const uint32_t sa = uint32_t(kl) * 2;
-      const uint32_t sb = BLAY == LAY_K ? uint32_t(kl) * 2 : uint32_t(kl) * ldb2;
       if (kl + kBK <= Kp) {
-        static_for<NA>([&](auto t) SMOE_INL { cv[t] = a_off[t]; });
-        static_for<NB>([&](auto t) SMOE_INL { cv[NA + t] = b_off[t]; });
+        static_for<NA>([&](auto t) SMOE_INL { cva[t] = a_off[t]; });
         csa = sa;
-        csb = sb;
       } else {
-        static_for<NA>([&](auto t) SMOE_INL { cv[t] = kl + ka[t] < Kp ? a_off[t] + sa : kOOB; });
-        static_for<NB>([&](auto t) SMOE_INL { cv[NA + t] = kl + kb_[t] < Kp ? b_off[t] + sb : kOOB; });
-        csa = csb = 0;
+        static_for<NA>([&](auto t) SMOE_INL { cva[t] = kl + ka[t] < Kp ? a_off[t] + sa : kOOB; });
+        csa = 0;
       }
     } else {
       // a plain operand advances by the step's first row (a scalar offset);
       // a gathered one addresses each row from its index
       const int r0 = it.row0 + kt * kBK;
       const uint32_t sa = (uint32_t(r0) * lda2) & uint32_t(~scat_a);
-      const uint32_t sb = (uint32_t(r0) * ldb2) & uint32_t(~scat_b);
       static_for<NA>([&](auto t) SMOE_INL {
         const uint32_t g = uint32_t(fdiv(gia[t], p.a_fan_m, p.a_fan_s)) * lda2 + a_col[t];
-        cv[t] = (g & uint32_t(scat_a)) | (a_off[t] & uint32_t(~scat_a));
-      });
-      static_for<NB>([&](auto t) SMOE_INL {
-        const uint32_t g = uint32_t(fdiv(gib[t], p.b_fan_m, p.b_fan_s)) * ldb2 + b_col[t];
-        cv[NA + t] = (g & uint32_t(scat_b)) | (b_off[t] & uint32_t(~scat_b));
+        cva[t] = (g & uint32_t(scat_a)) | (a_off[t] & uint32_t(~scat_a));
       });
       if (r0 + kBK <= it.row1) {
         csa = sa;
-        csb = sb;
       } else {
-        static_for<NA>([&](auto t) SMOE_INL { cv[t] = r0 + ka[t] < it.row1 ? cv[t] + sa : kOOB; });
-        static_for<NB>([&](auto t) SMOE_INL { cv[NA + t] = r0 + kb_[t] < it.row1 ? cv[NA + t] + sb : kOOB; });
-        csa = csb = 0;
+        static_for<NA>([&](auto t) SMOE_INL { cva[t] = r0 + ka[t] < it.row1 ? cva[t] + sa : kOOB; });
+        csa = 0;
       }
     }
-    // uniform by construction; say so, so that they stay scalar operands
+    // uniform by construction; say so, so that it stays a scalar operand
     csa = __builtin_amdgcn_readfirstlane(csa);
+  };
+  auto planB = [&](int kt) SMOE_INL {
+    if constexpr (MODE == SEG_M) {
+      const bool p1 = kt >= KT0;
+      const int kl = (p1 ? kt - KT0 : kt) * kBK;
+      const int Kp = p1 ? K1 : K0;
+      crb = (BLAY == LAY_K && p1) ? rB1 : rB0;
+      const uint32_t sb = BLAY == LAY_K ? uint32_t(kl) * 2 : uint32_t(kl) * ldb2;
+      if (kl + kBK <= Kp) {
+        static_for<NB>([&](auto t) SMOE_INL { cvb[t] = b_off[t]; });
+        csb = sb;
+      } else {
+        static_for<NB>([&](auto t) SMOE_INL { cvb[t] = kl + kb_[t] < Kp ? b_off[t] + sb : kOOB; });
+        csb = 0;
+      }
+    } else {
+      const int r0 = it.row0 + kt * kBK;
+      const uint32_t sb = (uint32_t(r0) * ldb2) & uint32_t(~scat_b);
+      static_for<NB>([&](auto t) SMOE_INL {
+        const uint32_t g = uint32_t(fdiv(gib[t], p.b_fan_m, p.b_fan_s)) * ldb2 + b_col[t];
+        cvb[t] = (g & uint32_t(scat_b)) | (b_off[t] & uint32_t(~scat_b));
+      });
+      if (r0 + kBK <= it.row1) {
+        csb = sb;
+      } else {
+        static_for<NB>([&](auto t) SMOE_INL { cvb[t] = r0 + kb_[t] < it.row1 ? cvb[t] + sb : kOOB; });
+        csb = 0;
+      }
+    }
     csb = __builtin_amdgcn_readfirstlane(csb);
   };
   // every copy instruction fills 1 KB of its operand's tile: 8 K-layout
   // rows, or 64 / CPR MN-layout k-rows
-  auto copy = [&](auto c, char* stg) SMOE_INL {
+  auto copyA = [&](auto c, char* buf) SMOE_INL {
     constexpr int C = decltype(c)::value;
-    if constexpr (C < NA) {
-      dma16s(cra, stg + (C * 8 + wave) * 1024, cv[C], csa);
+    dma16s(cra, buf + (C * 8 + wave) * 1024, cva[C], csa);
+  };
+  auto copyB = [&](auto c, char* buf) SMOE_INL {
+    constexpr int t = decltype(c)::value;
+    if constexpr (DUAL) {
+      // loads t >= NB/2 read W3 into the second sub-tile
+      constexpr int tt = t % (NB / 2);
+      dma16s(t >= NB / 2 ? rB1 : rB0, buf + (t / (NB / 2)) * (BN / 2) * kBK * 2 + (tt * 8 + wave) * 1024, cvb[t],
+             csb);
     } else {
-      constexpr int t = C - NA;
-      char* Bs = stg + A_BYTES;
-      if constexpr (DUAL) {
-        // loads t >= NB/2 read W3 into the second sub-tile
-        constexpr int tt = t % (NB / 2);
-        dma16s(t >= NB / 2 ? rB1 : rB0, Bs + (t / (NB / 2)) * (BN / 2) * kBK * 2 + (tt * 8 + wave) * 1024, cv[C],
-               csb);
-      } else {
-        dma16s(crb, Bs + (t * 8 + wave) * 1024, cv[C], csb);
-      }
+      dma16s(crb, buf + (t * 8 + wave) * 1024, cvb[t], csb);
     }
   };
   static_assert(KGeom::RPL * KGeom::RB == 1024 && GA::RPI * GA::RB == 1024 && GB::RPI * GB::RB == 1024,
@@ -503,13 +522,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     });
   });
 
-  // fragment of row block fm (A) / column block fn (B) of k slice s
-  auto frag_a = [&](const char* stg, auto fm, int s) SMOE_INL {
-    if constexpr (ALAY == LAY_K) return frag_k(stg, wm * WM + int(fm) * 32, s, lane);
-    else return frag_mn<BM>(stg, wm * WM + int(fm) * 32, s, lane);
+  // fragment of row block fm (A) / column block fn (B) of k slice s, from
+  // an A or B stage buffer
+  auto frag_a = [&](const char* As, auto fm, int s) SMOE_INL {
+    if constexpr (ALAY == LAY_K) return frag_k(As, wm * WM + int(fm) * 32, s, lane);
+    else return frag_mn<BM>(As, wm * WM + int(fm) * 32, s, lane);
   };
-  auto frag_b = [&](const char* stg, auto fn, int s) SMOE_INL {
-    const char* Bs = stg + A_BYTES;
+  auto frag_b = [&](const char* Bs, auto fn, int s) SMOE_INL {
     if constexpr (MODE == SEG_M && BLAY == LAY_K) {
       return frag_k(Bs, wn * WN + int(fn) * 32, s, lane);
     } else if constexpr (DUAL) {
@@ -518,10 +537,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     } else {
       return frag_mn<BN>(Bs, wn * WN + int(fn) * 32, s, lane);
     }
-  };
-  auto frags = [&](const char* stg, int s, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) SMOE_INL {
-    static_for<FM>([&](auto fm) SMOE_INL { af[fm] = frag_a(stg, fm, s); });
-    static_for<FN>([&](auto fn) SMOE_INL { bf[fn] = frag_b(stg, fn, s); });
   };
   // GATED: A fragments of slice s of step kt times their rows' scales.  A
   // lane's fragment holds k-rows 16s + 8 (lane >> 5) + 0..7 of the step (one
@@ -551,32 +566,58 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   auto mfma = [&](bf16x8_t (&A)[FM], bf16x8_t (&B)[FN], auto fm, auto fn) SMOE_INL {
     acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[fn], A[fm], acc[fm][fn], 0, 0, 0);
   };
-  auto mfmas = [&](bf16x8_t (&A)[FM], bf16x8_t (&B)[FN]) SMOE_INL {
-    static_for<FM>([&](auto fm) SMOE_INL { static_for<FN>([&](auto fn) SMOE_INL { mfma(A, B, fm, fn); }); });
+  // One 16-wide k slice in a fixed order: each multiply, then the copies
+  // placed after it (cp(I)), then one fragment read of the next slice (slice
+  // ns of buffers na / nb), so that the reads and copies run under the
+  // multiplies and no copy burst holds them up.
+  constexpr int NM = FM * FN;
+  auto slice = [&](bf16x8_t (&A)[FM], bf16x8_t (&B)[FN], bf16x8_t (&An)[FM], bf16x8_t (&Bn)[FN], const char* na,
+                   const char* nb, int ns, auto cp) SMOE_INL {
+    static_for<NM>([&](auto ii) SMOE_INL {
+      constexpr int I = decltype(ii)::value;
+      mfma(A, B, std::integral_constant<int, I / FN>{}, std::integral_constant<int, I % FN>{});
+      cp(std::integral_constant<int, I>{});
+      if constexpr (I < FM) An[I] = frag_a(na, std::integral_constant<int, I>{}, ns);
+      else if constexpr (I < FM + FN) Bn[I - FM] = frag_b(nb, std::integral_constant<int, I - FM>{}, ns);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (NM < FM + FN) {
+      // more fragments than multiplies in the slice (small tiles)
+      static_for<FM + FN - NM>([&](auto rr) SMOE_INL {
+        constexpr int I = NM + decltype(rr)::value;
+        if constexpr (I < FM) An[I] = frag_a(na, std::integral_constant<int, I>{}, ns);
+        else Bn[I - FM] = frag_b(nb, std::integral_constant<int, I - FM>{}, ns);
+      });
+    }
   };
-  // LDS read instructions per slice: one per K-layout fragment, two per
-  // transposed (MN-layout) fragment
+
+  // Weights mode, slices 0-2 (no copies): the next slice's reads first in
+  // program order, then the multiplies, and the scheduler interleaves them,
+  // one multiply and a share of the reads at a time.
   constexpr int kFragReads = FM * (ALAY == LAY_K ? 1 : 2) + FN * ((MODE == SEG_M && BLAY == LAY_K) ? 1 : 2);
-  // schedule of a slice: one multiply, then a share of the next slice's
-  // fragment reads, so the reads run under the multiplies
-  auto sched = [&]() SMOE_INL {
-    static_for<FM * FN>([&](auto i) SMOE_INL {
-      constexpr int r0 = int(i) * kFragReads / (FM * FN), r1 = (int(i) + 1) * kFragReads / (FM * FN);
+  auto slice_sched = [&](bf16x8_t (&A)[FM], bf16x8_t (&B)[FN], bf16x8_t (&An)[FM], bf16x8_t (&Bn)[FN],
+                         const char* na, const char* nb, int ns) SMOE_INL {
+    static_for<FM>([&](auto fm) SMOE_INL { An[fm] = frag_a(na, fm, ns); });
+    static_for<FN>([&](auto fn) SMOE_INL { Bn[fn] = frag_b(nb, fn, ns); });
+    static_for<FM>([&](auto fm) SMOE_INL { static_for<FN>([&](auto fn) SMOE_INL { mfma(A, B, fm, fn); }); });
+    static_for<NM>([&](auto i) SMOE_INL {
+      constexpr int r0 = int(i) * kFragReads / NM, r1 = (int(i) + 1) * kFragReads / NM;
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);
     });
   };
 
   // ---------------- pipeline -----------------------------------------------
-  // Two stage buffers of 64 k.  Step kt multiplies its four 16-wide slices,
-  // reading the fragments of slice j+1 while slice j multiplies.  Before the
-  // last slice (whose fragments are then in registers) each wave waits
-  // until its LDS reads are done and its copies of stage kt+1 have landed,
-  // and one barrier per step publishes stage kt+1 and frees stage kt's
-  // buffer.  The last slice's multiplies are then interleaved, one by one,
-  // with the copies of stage kt+2 into the freed buffer and with the reads
-  // of stage kt+1's first slice, so that the copy traffic, the barrier and
-  // the step change all run under multiplies.  A copy has one step to land.
+  // Step kt multiplies the four 16-wide slices of stage kt, reading the
+  // fragments of slice j+1 while slice j multiplies.  Before the last slice
+  // (whose fragments are then in registers) each wave waits until its LDS
+  // reads are done and its copies of stage kt+1 have landed; one barrier per
+  // step then publishes stage kt+1 and frees the buffers of stage kt.  The
+  // last slice reads stage kt+1's first slice.  Rows mode: the A copies of
+  // stage kt+2 go into the third A buffer during slices 0-2 (two steps to
+  // land), the B copies of stage kt+2 into the freed B buffer during the
+  // last slice (one step to land).  Weights mode: both operands' copies of
+  // stage kt+2 go into the freed buffers during the last slice.
   if constexpr (MODE == SEG_K) {
     for (int j = 0; j < kIdxAhead; ++j)
       if (j < KT) idx_copy(j);
@@ -584,78 +625,105 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     asm volatile("s_barrier" ::: "memory");
     idx_fetch(0);
   }
-  plan(0);
-  static_for<LPS>([&](auto c) SMOE_INL { copy(c, smem0); });
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  planA(0);
+  static_for<NA>([&](auto c) SMOE_INL { copyA(c, abuf(I0{})); });
+  planB(0);
+  static_for<NB>([&](auto c) SMOE_INL { copyB(c, bbuf(I0{})); });
   if (1 < KT) {
     idx_fetch(1);
-    plan(1);
-    static_for<LPS>([&](auto c) SMOE_INL { copy(c, smem1); });
+    planA(1);
+    static_for<NA>([&](auto c) SMOE_INL { copyA(c, abuf(I1{})); });
+    planB(1);
+    static_for<NB>([&](auto c) SMOE_INL { copyB(c, bbuf(I1{})); });
     wait_vmem<LPS>();
   } else {
     wait_vmem<0>();
   }
   asm volatile("s_barrier" ::: "memory");
   if (2 < KT) idx_fetch(2);
-  frags(smem0, 0, fa0, fb0);
-  constexpr int CPM = (LPS + FM * FN - 1) / (FM * FN);   // copies per multiply of the last slice
-  for (int k0 = 0; k0 < KT; k0 += 2) {
-    static_for<2>([&](auto s) SMOE_INL {
+  static_for<FM>([&](auto fm) SMOE_INL { fa0[fm] = frag_a(abuf(I0{}), fm, 0); });
+  static_for<FN>([&](auto fn) SMOE_INL { fb0[fn] = frag_b(bbuf(I0{}), fn, 0); });
+  static_assert(kNSL == 4, "four slices per stage");
+  for (int k0 = 0; k0 < KT; k0 += UNROLL) {
+    static_for<UNROLL>([&](auto s) SMOE_INL {
       const int kt = k0 + int(s);
       if (kt < KT) {
-        char* cur = stage(s);
-        const char* nxt = stage(std::integral_constant<int, int(s) + 1>{});
-        static_assert(kNSL == 4, "four slices per stage");
-        scale_a(fa0, kt, 0);
-        frags(cur, 1, fa1, fb1);
-        mfmas(fa0, fb0);
-        sched();
-        scale_a(fa1, kt, 1);
-        frags(cur, 2, fa0, fb0);
-        mfmas(fa1, fb1);
-        sched();
-        scale_a(fa0, kt, 2);
-        frags(cur, 3, fa1, fb1);
-        mfmas(fa0, fb0);
-        sched();
-        __builtin_amdgcn_sched_barrier(0);
+        using S1 = std::integral_constant<int, int(s) + 1>;
+        using S2 = std::integral_constant<int, int(s) + 2>;
+        const char* ca = abuf(s);
+        const char* cb = bbuf(s);
+        const char* na = abuf(S1{});
+        const char* nb = bbuf(S1{});
         const bool more = kt + 2 < KT;
-        if (more) plan(kt + 2);
+        // rows mode: A copies of stage kt+2, spread over slices 0-2
+        if constexpr (A3) {
+          if (more) planA(kt + 2);
+        }
+        auto acp = [&](auto sl) SMOE_INL {
+          return [&](auto ii) SMOE_INL {
+            if constexpr (A3) {
+              constexpr int I = decltype(ii)::value;
+              static_for<NA>([&](auto cc) SMOE_INL {
+                constexpr int c = decltype(cc)::value, pos = c * 3 * NM / NA;
+                if constexpr (pos / NM == decltype(sl)::value && pos % NM == I) {
+                  if (more) copyA(cc, abuf(S2{}));
+                }
+              });
+            }
+          };
+        };
+        if constexpr (A3) {
+          slice(fa0, fb0, fa1, fb1, ca, cb, 1, acp(std::integral_constant<int, 0>{}));
+          slice(fa1, fb1, fa0, fb0, ca, cb, 2, acp(std::integral_constant<int, 1>{}));
+          slice(fa0, fb0, fa1, fb1, ca, cb, 3, acp(std::integral_constant<int, 2>{}));
+        } else {
+          scale_a(fa0, kt, 0);
+          slice_sched(fa0, fb0, fa1, fb1, ca, cb, 1);
+          scale_a(fa1, kt, 1);
+          slice_sched(fa1, fb1, fa0, fb0, ca, cb, 2);
+          scale_a(fa0, kt, 2);
+          slice_sched(fa0, fb0, fa1, fb1, ca, cb, 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+          if constexpr (!A3) planA(kt + 2);
+          planB(kt + 2);
+        }
         wait_lds();
-        wait_vmem<0>();
+        // stage kt+1 must have landed; rows mode: this step's A copies of
+        // stage kt+2 (the last issued) may still be in flight
+        if (A3 && more) wait_vmem<A3 ? NA : 0>();
+        else wait_vmem<0>();
         asm volatile("s_barrier" ::: "memory");
         if constexpr (MODE == SEG_K) {
           if (kt + kIdxAhead < KT) idx_copy(kt + kIdxAhead);
         }
         scale_a(fa1, kt, 3);
         __builtin_amdgcn_sched_barrier(0);
-        static_for<FM * FN>([&](auto ii) SMOE_INL {
+        // last slice: the copies of stage kt+2 into this step's freed buffers
+        constexpr int LC = A3 ? NB : NA + NB;
+        auto lcp = [&](auto ii) SMOE_INL {
           constexpr int I = decltype(ii)::value;
-          mfma(fa1, fb1, std::integral_constant<int, I / FN>{}, std::integral_constant<int, I % FN>{});
-          static_for<CPM>([&](auto cc) SMOE_INL {
-            constexpr int c = I * CPM + decltype(cc)::value;
-            if constexpr (c < LPS) {
-              if (more) copy(std::integral_constant<int, c>{}, cur);
+          static_for<LC>([&](auto cc) SMOE_INL {
+            constexpr int c = decltype(cc)::value;
+            if constexpr (c * NM / LC == I) {
+              if (more) {
+                if constexpr (A3) copyB(cc, bbuf(s));
+                else if constexpr (c < NA) copyA(cc, abuf(s));
+                else copyB(std::integral_constant<int, c - NA>{}, bbuf(s));
+              }
             }
           });
-          if constexpr (I < FM) fa0[I] = frag_a(nxt, std::integral_constant<int, I>{}, 0);
-          else if constexpr (I < FM + FN) fb0[I - FM] = frag_b(nxt, std::integral_constant<int, I - FM>{}, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        if constexpr (FM * FN < FM + FN) {
-          // more fragments than multiplies in the slice (small tiles)
-          static_for<FM + FN - FM * FN>([&](auto rr) SMOE_INL {
-            constexpr int I = FM * FN + decltype(rr)::value;
-            if constexpr (I < FM) fa0[I] = frag_a(nxt, std::integral_constant<int, I>{}, 0);
-            else fb0[I - FM] = frag_b(nxt, std::integral_constant<int, I - FM>{}, 0);
-          });
-        }
+        };
+        slice(fa1, fb1, fa0, fb0, na, nb, 0, lcp);
         if constexpr (MODE == SEG_K) {
           if (kt + 3 < KT) idx_fetch(kt + 3);
         }
       }
     });
   }
-
 
   // ---------------- epilogue ----------------------------------------------
   // lane holds, for fragment (fm, fn): row (lane & 31) and columns
@@ -676,10 +744,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NOUT = (MODE == SEG_M && (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD)) ? 3
                        : (MODE == SEG_M && (EPI == EPI_GELU_FWD || EPI == EPI_GELU_BWD)) ? 2 : 1;
   static_assert((CH & (CH - 1)) == 0 && CH <= 64 && 32 % RPR == 0, "staging geometry");
-  static_assert(NOUT * 32 * RBE <= STAGE / 4, "staging slot");
+  static_assert(NOUT * 32 * RBE <= LDS_BYTES / 8 && (LDS_BYTES / 8) % 16 == 0, "staging slot");
   asm volatile("s_barrier" ::: "memory");
-  // each wave stages into a quarter of one of the two stage buffers
-  char* const slot = (wave < 4 ? smem0 : smem1) + (wave & 3) * (STAGE / 4);
+  // each wave stages into an eighth of the stage buffers
+  char* const slot = lds + wave * (LDS_BYTES / 8);
   // lane's 4 values of fragment (fn, q) of one fragment row -> output o
   auto put = [&](int o, auto fn, auto q, const float v[4]) SMOE_INL {
     const int row = lane & 31;
