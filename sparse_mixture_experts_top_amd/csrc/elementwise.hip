@@ -83,22 +83,49 @@ hipError_t launch_combine(const float* pairs, const float* gates, int64_t T, int
   return hipGetLastError();
 }
 
+// dg[sidx[r]] = sum over slots of part[slot][r].  A block takes 64 grouped
+// rows; its four waves sum disjoint quarters of the slots (one row per lane,
+// four loads in flight), and the quarter sums are added in wave order, so
+// the result does not depend on timing.
 __global__ __launch_bounds__(kEwThreads) void reduce_dg_kernel(const float* __restrict__ part, int slots, int M,
                                                                const int* __restrict__ offsets, int E,
                                                                const int* __restrict__ sidx, float* __restrict__ dg) {
+  __shared__ float qs[kEwThreads / kWave][kWave];
   const int rows = offsets[E];
-  for (int r = blockIdx.x * kEwThreads + threadIdx.x; r < rows; r += gridDim.x * kEwThreads) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  constexpr int NW = kEwThreads / kWave;
+  const int q0 = w * slots / NW, q1 = (w + 1) * slots / NW;
+  for (int base = blockIdx.x * kWave; base < rows; base += gridDim.x * kWave) {
+    const int r = base + lane;
     float s = 0.f;
-    for (int q = 0; q < slots; ++q) s += part[int64_t(q) * M + r];
-    dg[sidx[r]] = s;
+    if (r < rows) {
+      int q = q0;
+      for (; q + 4 <= q1; q += 4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = part[int64_t(q + u) * M + r];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s += v[u];
+      }
+      for (; q < q1; ++q) s += part[int64_t(q) * M + r];
+    }
+    qs[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && r < rows) {
+      float t = qs[0][lane];
+#pragma unroll
+      for (int u = 1; u < NW; ++u) t += qs[u][lane];
+      dg[sidx[r]] = t;
+    }
+    __syncthreads();
   }
 }
 
 hipError_t launch_reduce_dg(const float* part, int slots, int M, const int* offsets, int E, const int* sidx,
                             float* dg, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_dg_kernel, dim3(grid_for(M, kEwThreads)), dim3(kEwThreads), 0, st, part, slots, M,
-                     offsets, E, sidx, dg);
+  hipLaunchKernelGGL(reduce_dg_kernel, dim3(grid_for(M, kWave)), dim3(kEwThreads), 0, st, part, slots, M, offsets,
+                     E, sidx, dg);
   return hipGetLastError();
 }
 
