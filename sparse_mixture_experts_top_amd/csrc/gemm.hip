@@ -30,11 +30,13 @@
 //  - The MFMA is issued with the B fragment first, so each lane ends up
 //    holding one output row and runs of 4 consecutive columns: epilogue
 //    stores are 8 bytes (bf16) or 16 bytes (fp32) wide.
-//  - Workgroups are renumbered so that each XCD (blockIdx % 8 on MI355X)
-//    receives an equal, contiguous run of the tiles that exist (counted on
-//    the device from the expert row counts), ordered in groups of 8 m-tiles
-//    sweeping n, so concurrent tiles on one XCD share A rows and weight
-//    panels in that XCD's L2 and no XCD idles on the grid's empty tail.
+//  - Workgroups are renumbered over the tiles that exist (counted on the
+//    device from the expert row counts), ordered in groups of 8 m-tiles
+//    sweeping n.  Each XCD (blockIdx % 8 on MI355X) takes runs of 32
+//    consecutive tiles, the 8 XCDs neighbouring runs at the same time: the
+//    concurrent tiles on one XCD share A rows and weight panels in its L2,
+//    the XCDs share them in the last-level cache, and no XCD idles on the
+//    grid's empty tail.
 //
 // fp32 kernel: the same contract with plain FMA on 64x64 tiles, used for
 // fp32 runs (a small, launch-bound regime).
@@ -141,13 +143,17 @@ struct TileInfo {
 template <int BM, int BN, int MODE, bool DUAL>
 SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
   // The grid is sized for an upper bound on the tiles; how many exist
-  // depends on the per-expert row counts and is counted here.  Blocks are
-  // dealt to the XCDs round-robin (block b runs on XCD b % 8): each XCD
-  // takes a contiguous run of this launch's real tiles, the runs as even as
-  // the count divides, and the blocks past a run have no tile.  (Runs over
-  // the upper-bound range would leave the last XCDs with the empty tail:
-  // with 8 experts and 2 split-K chunks' room, 2 of 10 chunks are empty.)
-  constexpr int kXcd = 8;
+  // depends on the per-expert row counts and is counted here.  Block b runs
+  // on XCD b % 8, and an XCD's blocks start in order, 32 at a time (one per
+  // CU).  The real tiles are dealt in rounds of 8 x 32: XCD x takes the
+  // x-th run of 32 consecutive tiles of each round, so the 8 XCDs work on
+  // neighbouring tiles at the same time (the same A panels with different
+  // n-tiles, or the same weight panels) and the copies they share come
+  // from the last-level cache instead of HBM.  The tiles past the last
+  // whole round are dealt in 8 even runs.  The blocks past an XCD's share
+  // have no tile.  (Dealing over the upper-bound range would leave the
+  // last XCDs with the empty tail.)
+  constexpr int kXcd = 8, kRun = 32;
   constexpr int GM = 8;
   constexpr int NCOLS = DUAL ? BN / 2 : BN;
   int n_real, units = 0;
@@ -162,11 +168,19 @@ SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
   const int lo = MODE == SEG_M ? p.g_base : 0;
   const int hi = (MODE == SEG_M && p.g_count > 0) ? min(n_real, lo + p.g_count) : n_real;
   if (hi <= lo) return false;
-  const int per = (hi - lo + kXcd - 1) / kXcd;
-  const int j = int(blockIdx.x) / kXcd;
-  if (j >= per) return false;
-  const int g = lo + (int(blockIdx.x) % kXcd) * per + j;
-  if (g >= hi) return false;
+  const int n = hi - lo, x = int(blockIdx.x) % kXcd, j = int(blockIdx.x) / kXcd;
+  const int full = n / (kXcd * kRun);
+  int g;
+  if (j < full * kRun) {
+    g = lo + (j / kRun) * (kXcd * kRun) + x * kRun + j % kRun;
+  } else {
+    const int rem = n - full * kXcd * kRun;
+    const int per = (rem + kXcd - 1) / kXcd;
+    const int jj = j - full * kRun;
+    if (jj >= per) return false;
+    g = lo + full * kXcd * kRun + x * per + jj;
+    if (g >= hi) return false;
+  }
   if constexpr (MODE == SEG_M) {
     // groups of GM m-tiles sweeping the n-tiles: concurrent tiles on an XCD
     // share GM A panels and a few weight panels
