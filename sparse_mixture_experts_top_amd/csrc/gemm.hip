@@ -774,20 +774,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       *reinterpret_cast<float4*>(rb + ((c ^ (row & (CH - 1))) << 4)) = make_float4(v[0], v[1], v[2], v[3]);
     }
   };
-  // staged output o -> global: row j of the fragment row goes to
-  // base + rowoff(j) + colbase; rowoff / ok are held by lane j
+  // staged output o -> global: row j (0..31) of the fragment row goes to
+  // base + rowoff(j) + colbase, or nowhere when rowoff(j) < 0.
   // ADD: fp32 atomic adds of the four values instead of one store (the
   // fused combine; several assignments add into one token's row)
-  auto flush = [&](int o, ST* base, int64_t rowoff, bool ok, int colbase, auto add) SMOE_INL {
-    const uint32_t ro_lo = uint32_t(rowoff), ro_hi = uint32_t(uint64_t(rowoff) >> 32);
+  auto flush = [&](int o, ST* base, auto rowoff, int colbase, auto add) SMOE_INL {
     static_for<32 / RPR>([&](auto i) SMOE_INL {
       const int j = int(i) * RPR + lane / CH, c = lane % CH;
       const uint4 d = *reinterpret_cast<const uint4*>(slot + o * 32 * RBE + j * RBE + ((c ^ (j & (CH - 1))) << 4));
-      const int64_t ro = int64_t((uint64_t(uint32_t(__shfl(int(ro_hi), j, kWave))) << 32) |
-                                 uint32_t(__shfl(int(ro_lo), j, kWave)));
-      const bool rok_j = __shfl(int(ok), j, kWave) != 0;
+      const int64_t ro = rowoff(j);
       const int colc = colbase + c * (16 / OB);
-      if (rok_j && colc < p.N) {
+      if (ro >= 0 && colc < p.N) {
         if constexpr (decltype(add)::value && std::is_same<ST, float>::value) {
           float* dst = reinterpret_cast<float*>(base + ro + colc);
           unsafeAtomicAdd(dst, __uint_as_float(d.x));
@@ -800,6 +797,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       }
     });
   };
+  // row offsets for flush: rows first + j of a dense range (stored below
+  // end), computed by every lane; or rows held by the lanes of the fragment
+  // row (lane j: row j, or -1), fetched with one shuffle
+  auto dense_rows = [](int64_t first, int64_t end, int64_t ld) SMOE_INL {
+    return [=](int j) SMOE_INL -> int64_t { return first + j < end ? (first + j) * ld : int64_t(-1); };
+  };
+  auto held_rows = [](int held, int64_t ld) SMOE_INL {
+    return [=](int j) SMOE_INL -> int64_t {
+      const int r = __shfl(held, j, kWave);
+      return r >= 0 ? int64_t(r) * ld : int64_t(-1);
+    };
+  };
   constexpr std::false_type kStore{};
   constexpr std::true_type kAdd{};
 
@@ -807,7 +816,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     float* dst = (it.nitems == 1 && !p.dw_all_partial) ? static_cast<float*>(p.c0) + int64_t(it.e) * p.Mo * p.N
                                                        : p.partial + int64_t(T.chunk) * p.Mo * p.N;
     static_for<FM>([&](auto fm) SMOE_INL {
-      const int i = T.m0 + wm * WM + fm * 32 + (lane & 31);
       static_for<FN>([&](auto fn) SMOE_INL {
         static_for<4>([&](auto q) SMOE_INL {
           const float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1],
@@ -815,7 +823,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           put(0, fn, q, v);
         });
       });
-      flush(0, dst, int64_t(i) * p.N, i < p.Mo, T.n0 + wn * WN, kStore);
+      flush(0, dst, dense_rows(T.m0 + wm * WM + fm * 32, p.Mo, p.N), T.n0 + wn * WN, kStore);
     });
   } else {
     OutT* c0 = static_cast<OutT*>(p.c0);
@@ -851,7 +859,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
     // used.  Double-buffered over fm so the reads of row fm+1 are in flight
     // while row fm is computed and stored.  Masked lanes read a clamped,
     // valid address.
-    const int hh = lane >> 5;
+    const int hh = lane >> 5;   // the half of the chunk pair a lane reads
     uint4 rx0[2][FNR][2], rx1[2][AUX1 ? FNR : 1][2];
     auto load_aux = [&](auto fm, auto buf) SMOE_INL {
       if constexpr (AUX0) {
@@ -869,15 +877,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         }
       }
     };
-    // the lane's 4 values of chunk q of fragment fn from the 16-byte reads
+    // the lane's 4 values of chunk q of fragment fn from the 16-byte reads:
+    // lane l < 32 keeps the low halves of its reads and takes the low halves
+    // of lane l + 32's; lane l >= 32 keeps its high halves and takes lane
+    // l - 32's.  gfx950's v_permlane32_swap exchanges the upper 32 lanes of
+    // one register with the lower 32 lanes of another, which is exactly
+    // that (a VALU operation, no LDS round trip).
     auto aux_vals = [&](uint4 (&rx)[2], uint2 (&ax)[4]) SMOE_INL {
       static_for<2>([&](auto j) SMOE_INL {
-        const uint2 lo = make_uint2(rx[j].x, rx[j].y), hi = make_uint2(rx[j].z, rx[j].w);
-        const uint2 own = hh ? hi : lo, send = hh ? lo : hi;
-        const uint2 recv = make_uint2(uint32_t(__shfl_xor(int(send.x), 32, kWave)),
-                                      uint32_t(__shfl_xor(int(send.y), 32, kWave)));
-        ax[int(j)] = hh ? recv : own;
-        ax[2 + int(j)] = hh ? own : recv;
+        const auto sx = __builtin_amdgcn_permlane32_swap(rx[j].x, rx[j].z, false, false);
+        const auto sy = __builtin_amdgcn_permlane32_swap(rx[j].y, rx[j].w, false, false);
+        ax[int(j)] = make_uint2(sx[0], sy[0]);
+        ax[2 + int(j)] = make_uint2(sx[1], sy[1]);
       });
     };
     auto unpack = [&](uint2 w, float v[4]) SMOE_INL { unpack4_bf16(w, v); };
@@ -886,8 +897,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
       constexpr int BUF = int(fm) & 1;
       if constexpr (int(fm) + 1 < FM)
         load_aux(std::integral_constant<int, int(fm) + 1>{}, std::integral_constant<int, BUF ^ 1>{});
-      const int64_t grow = gr[fm];
-      const int64_t crow = p.c_scat ? sp[fm] : grow;
+      const int rowbase = it.row0 + wm * WM + fm * 32;   // grouped row of lane 0 of the fragment row
       float dgacc = 0.f;
       static_for<FNR>([&](auto fn) SMOE_INL {
         uint2 ax0[4], ax1[4];
@@ -895,16 +905,20 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           if (aux0_on) aux_vals(rx0[BUF][fn], ax0);
         }
         if constexpr (AUX1) aux_vals(rx1[BUF][fn], ax1);
+        // every lane computes all of its chunks (rows and columns outside
+        // the tile's valid range compute on in-range data that is never
+        // stored); only the gate-gradient sums leave out columns past N
         static_for<4>([&](auto q) SMOE_INL {
-          const int n = col(fn, q);
-          if (rok[fm] && n < p.N) {
+          const bool cok = col(fn, q) < p.N;
+          {
             float v[4] = {acc[fm][fn][4 * int(q)], acc[fm][fn][4 * int(q) + 1], acc[fm][fn][4 * int(q) + 2],
                           acc[fm][fn][4 * int(q) + 3]};
             if constexpr (EPI == EPI_STORE) {
               if (p.dgpart) {
                 float xv[4];
                 unpack(ax0[q], xv);
-                dgacc += xv[0] * v[0] + xv[1] * v[1] + xv[2] * v[2] + xv[3] * v[3];
+                const float dot = xv[0] * v[0] + xv[1] * v[1] + xv[2] * v[2] + xv[3] * v[3];
+                dgacc += cok ? dot : 0.f;
               }
               if (p.gate) {
                 static_for<4>([&](auto i) SMOE_INL { v[i] *= g[fm]; });
@@ -938,11 +952,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
               unpack(ax0[q], h);
               static_for<4>([&](auto i) SMOE_INL { a[i] = gelu_f(h[i]); });
               unpack4_bf16(pack4_bf16(a), a);   // a as stored in the forward
+              float dot = 0.f;
               static_for<4>([&](auto i) SMOE_INL {
-                dgacc += a[i] * v[i];
+                dot += a[i] * v[i];
                 dh[i] = g[fm] * v[i] * gelu_grad_f(h[i]);
                 ag[i] = g[fm] * a[i];
               });
+              dgacc += cok ? dot : 0.f;
               put(0, fn, q, dh);
               put(1, fn, q, ag);
             } else if constexpr (EPI == EPI_SWIGLU_BWD) {
@@ -956,13 +972,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
                 a[i] = si[i] * h3[i];
               });
               unpack4_bf16(pack4_bf16(a), a);   // a as stored in the forward
+              float dot = 0.f;
               static_for<4>([&](auto i) SMOE_INL {
-                dgacc += a[i] * v[i];
+                dot += a[i] * v[i];
                 const float dA = g[fm] * v[i];
                 d1[i] = dA * h3[i] * (sg[i] * (1.0f + h1[i] * (1.0f - sg[i])));
                 d3[i] = dA * si[i];
                 ag[i] = g[fm] * a[i];
               });
+              dgacc += cok ? dot : 0.f;
               put(0, fn, q, d1);
               put(1, fn, q, d3);
               put(2, fn, q, ag);
@@ -971,32 +989,40 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         });
       });
       if (p.dgpart) {
-        dgacc += __shfl_xor(dgacc, 32, kWave);
+        // lane l < 32 adds lane l + 32's partial sum of the same row
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dgacc), __float_as_uint(dgacc), false, false);
+        dgacc += __uint_as_float(sw[1]);
         if (lane < 32 && rok[fm]) p.dgpart[int64_t(T.nt * 4 + wn) * p.M + gr[fm]] = dgacc;
       }
       // staged rows -> global (grouped rows, or scattered for EPI_STORE)
       const int cb = T.n0 + (DUAL ? wn * (WN / 2) : wn * WN);
+      const auto grouped = dense_rows(rowbase, it.row1, p.ldc);
       if constexpr (EPI == EPI_STORE) {
         if (c0) {
-          if (p.c_add_fan > 0)
-            flush(0, c0, (crow / p.c_add_fan) * p.ldc, rok[fm], cb, kAdd);
-          else
-            flush(0, c0, crow * p.ldc, rok[fm], cb, kStore);
+          if (p.c_scat || p.c_add_fan > 0) {
+            int hr = p.c_scat ? sp[fm] : gr[fm];
+            if (p.c_add_fan > 0) hr /= p.c_add_fan;
+            const auto rows = held_rows(rok[fm] ? hr : -1, p.ldc);
+            if (p.c_add_fan > 0) flush(0, c0, rows, cb, kAdd);
+            else flush(0, c0, rows, cb, kStore);
+          } else {
+            flush(0, c0, grouped, cb, kStore);
+          }
         }
       } else if constexpr (EPI == EPI_GELU_FWD) {
-        flush(0, c0, grow * p.ldc, rok[fm], cb, kStore);
-        flush(1, c1, grow * p.ldc, rok[fm], cb, kStore);
+        flush(0, c0, grouped, cb, kStore);
+        flush(1, c1, grouped, cb, kStore);
       } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-        flush(0, c0, grow * p.ldc, rok[fm], cb, kStore);
-        flush(1, c1, grow * p.ldc, rok[fm], cb, kStore);
-        flush(2, c2, grow * p.ldc, rok[fm], cb, kStore);
+        flush(0, c0, grouped, cb, kStore);
+        flush(1, c1, grouped, cb, kStore);
+        flush(2, c2, grouped, cb, kStore);
       } else if constexpr (EPI == EPI_GELU_BWD) {
-        flush(0, c0, grow * p.ldc, rok[fm], cb, kStore);
-        flush(1, c2, grow * p.ldc, rok[fm], cb, kStore);
+        flush(0, c0, grouped, cb, kStore);
+        flush(1, c2, grouped, cb, kStore);
       } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        flush(0, c0, grow * p.ldc, rok[fm], cb, kStore);
-        flush(1, c1, grow * p.ldc, rok[fm], cb, kStore);
-        flush(2, c2, grow * p.ldc, rok[fm], cb, kStore);
+        flush(0, c0, grouped, cb, kStore);
+        flush(1, c1, grouped, cb, kStore);
+        flush(2, c2, grouped, cb, kStore);
       }
     });
   }
