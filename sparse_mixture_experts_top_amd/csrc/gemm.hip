@@ -281,6 +281,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
   // and only the B copies share the last slice.  Weights mode keeps two of
   // each (its index rings take the rest of the LDS).
   constexpr bool A3 = MODE == SEG_M;
+  constexpr bool KSPLIT = MODE == SEG_K;   // weights mode: B copies one step later
   constexpr int NBA = A3 ? 3 : 2;
   constexpr int LDS_BYTES = NBA * A_BYTES + 2 * B_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -693,6 +694,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
           slice(fa1, fb1, fa0, fb0, ca, cb, 2, acp(std::integral_constant<int, 1>{}));
           slice(fa0, fb0, fa1, fb1, ca, cb, 3, acp(std::integral_constant<int, 2>{}));
         } else {
+          // weights mode: the B copies of stage kt+1 (planned in step kt-1,
+          // into the B buffer that step freed) go first, apart from the A
+          // copies issued in step kt-1's last slice
+          if (KSPLIT && kt >= 1 && kt + 1 < KT) {
+            static_for<NB>([&](auto cc) SMOE_INL { copyB(cc, bbuf(S1{})); });
+          }
           scale_a(fa0, kt, 0);
           slice_sched(fa0, fb0, fa1, fb1, ca, cb, 1);
           scale_a(fa1, kt, 1);
@@ -717,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs p) {
         scale_a(fa1, kt, 3);
         __builtin_amdgcn_sched_barrier(0);
         // last slice: the copies of stage kt+2 into this step's freed buffers
-        constexpr int LC = A3 ? NB : NA + NB;
+        constexpr int LC = A3 ? NB : (KSPLIT ? NA : NA + NB);
         auto lcp = [&](auto ii) SMOE_INL {
           constexpr int I = decltype(ii)::value;
           static_for<LC>([&](auto cc) SMOE_INL {
