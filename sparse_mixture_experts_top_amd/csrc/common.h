@@ -152,6 +152,31 @@ struct Item {
   int nitems;  // items of this expert
 };
 
+// Item `item` from the lanes' per-expert values (expert c + lane: rows
+// [lo, hi), n items, excl items before it in the chunk of 64 experts that
+// starts at item index base); false if no lane holds it.
+SMOE_DEV bool item_of_lanes(int c, int E, int unit, int item, int base, int lo, int hi, int n, int excl, Item& it) {
+  const int e = c + lane_id();
+  const bool hit = (e < E) && item >= base + excl && item < base + excl + n;
+  const unsigned long long m = __ballot(hit);
+  if (!m) return false;
+  const int src = __ffsll((long long)m) - 1;
+  const int ex = __shfl(excl, src, kWave);
+  const int lo_s = __shfl(lo, src, kWave);
+  const int hi_s = __shfl(hi, src, kWave);
+  const int n_s = __shfl(n, src, kWave);
+  const int local = item - base - ex;
+  // the same on every lane: make that visible to the compiler, so that
+  // values derived from the item (buffer descriptors, loop bounds) live in
+  // scalar registers
+  it.e = __builtin_amdgcn_readfirstlane(c + src);
+  it.row0 = __builtin_amdgcn_readfirstlane(lo_s + local * unit);
+  it.row1 = __builtin_amdgcn_readfirstlane(min(hi_s, lo_s + local * unit + unit));
+  it.first = __builtin_amdgcn_readfirstlane(local == 0);
+  it.nitems = __builtin_amdgcn_readfirstlane(n_s);
+  return true;
+}
+
 SMOE_DEV bool find_item(const int* __restrict__ offsets, int E, int unit, int item, Item& it) {
   const int l = lane_id();
   int base = 0;
@@ -162,29 +187,32 @@ SMOE_DEV bool find_item(const int* __restrict__ offsets, int E, int unit, int it
     const int cnt = hi > lo ? hi - lo : 0;
     const int n = (cnt + unit - 1) / unit;
     const int incl = wave_incl_scan(n);
-    const int excl = incl - n;
-    const bool hit = (e < E) && item >= base + excl && item < base + incl;
-    const unsigned long long m = __ballot(hit);
-    if (m) {
-      const int src = __ffsll((long long)m) - 1;
-      const int ex = __shfl(excl, src, kWave);
-      const int lo_s = __shfl(lo, src, kWave);
-      const int hi_s = __shfl(hi, src, kWave);
-      const int n_s = __shfl(n, src, kWave);
-      const int local = item - base - ex;
-      // the same on every lane: make that visible to the compiler, so that
-      // values derived from the item (buffer descriptors, loop bounds) live
-      // in scalar registers
-      it.e = __builtin_amdgcn_readfirstlane(c + src);
-      it.row0 = __builtin_amdgcn_readfirstlane(lo_s + local * unit);
-      it.row1 = __builtin_amdgcn_readfirstlane(min(hi_s, lo_s + local * unit + unit));
-      it.first = __builtin_amdgcn_readfirstlane(local == 0);
-      it.nitems = __builtin_amdgcn_readfirstlane(n_s);
-      return true;
-    }
+    if (item_of_lanes(c, E, unit, item, base, lo, hi, n, incl - n, it)) return true;
     base += __shfl(incl, kWave - 1, kWave);
   }
   return false;
+}
+
+// Up to 64 experts in one pass (one per lane): the offsets are read and
+// scanned once for both the item count and the item lookup.
+struct ItemScan {
+  int lo, hi, n, excl;
+  int total;   // items of all experts (wave-uniform)
+};
+SMOE_DEV ItemScan scan_items(const int* __restrict__ offsets, int E, int unit) {
+  const int e = lane_id();
+  ItemScan s;
+  s.lo = s.hi = 0;
+  if (e < E) { s.lo = offsets[e]; s.hi = offsets[e + 1]; }
+  const int cnt = s.hi > s.lo ? s.hi - s.lo : 0;
+  s.n = (cnt + unit - 1) / unit;
+  const int incl = wave_incl_scan(s.n);
+  s.excl = incl - s.n;
+  s.total = __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
+  return s;
+}
+SMOE_DEV bool pick_item(const ItemScan& s, int E, int unit, int item, Item& it) {
+  return item_of_lanes(0, E, unit, item, 0, s.lo, s.hi, s.n, s.excl, it);
 }
 
 // Items of all experts together: the sum over e of ceil(count_e / unit)

@@ -159,12 +159,22 @@ SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
   int n_real, units = 0;
   const int ntn = (p.N + NCOLS - 1) / NCOLS;
   const int ti = (p.Mo + BM - 1) / BM, tj = (p.N + BN - 1) / BN, tpc = ti * tj;
+  const int unit = MODE == SEG_M ? BM : p.KS;
+  // up to 64 experts: one read and scan of the offsets for the count and the
+  // lookup; more: a pass for each
+  const bool one_pass = p.E <= kWave;
+  ItemScan sc;
+  if (one_pass) sc = scan_items(p.offsets, p.E, unit);
+  const int items = one_pass ? sc.total : total_items(p.offsets, p.E, unit);
   if constexpr (MODE == SEG_M) {
-    units = total_items(p.offsets, p.E, BM);   // real m-tiles
+    units = items;   // real m-tiles
     n_real = units * ntn;
   } else {
-    n_real = total_items(p.offsets, p.E, p.KS) * tpc;
+    n_real = items * tpc;
   }
+  auto locate = [&](int item, Item& it) SMOE_INL {
+    return one_pass ? pick_item(sc, p.E, unit, item, it) : find_item(p.offsets, p.E, unit, item, it);
+  };
   const int lo = MODE == SEG_M ? p.g_base : 0;
   const int hi = (MODE == SEG_M && p.g_count > 0) ? min(n_real, lo + p.g_count) : n_real;
   if (hi <= lo) return false;
@@ -192,7 +202,7 @@ SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
     t.n0 = t.nt * NCOLS;
     t.m0 = 0;
     t.chunk = 0;
-    return find_item(p.offsets, p.E, BM, mt, t.it);
+    return locate(mt, t.it);
   } else {
     t.chunk = g / tpc;
     const int rem = g - t.chunk * tpc;
@@ -205,7 +215,7 @@ SMOE_DEV bool tile_of_block(const GemmArgs& p, TileInfo& t) {
     t.m0 = (group * GM + local % gs) * BM;
     t.n0 = (local / gs) * BN;
     t.nt = 0;
-    return find_item(p.offsets, p.E, p.KS, t.chunk, t.it);
+    return locate(t.chunk, t.it);
   }
 }
 
