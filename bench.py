@@ -49,7 +49,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 GEMM_ROLES = ["up", "down", "dA", "dW2", "dX", "dW1", "dW3"]
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
+KERNEL_SOURCES = ["gemm.hip", "gemm_kernel.h", "gemm_store_k.hip", "gemm_store_mn.hip", "gemm_act_fwd.hip",
+                  "gemm_act_bwd.hip", "gemm_dw.hip", "common.h", "kernels.h"]
 # one step launches the grouped-product kernel once per role, in this order
 # (route, then up, down, combine, dA, dgates, dW2, dX, k-sum, dW1, dW3)
 # grouped-product launches of one step in enqueue order: the forward

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "gemm.hip", "elementwise.hip", "gate.hip", "attn.hip", "probe.hip", "api.hip"]
+SOURCES = ["route.hip", "gemm.hip", "gemm_store_k.hip", "gemm_store_mn.hip", "gemm_act_fwd.hip", "gemm_act_bwd.hip", "gemm_dw.hip", "elementwise.hip", "gate.hip", "attn.hip", "probe.hip", "api.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

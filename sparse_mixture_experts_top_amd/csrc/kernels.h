@@ -108,6 +108,7 @@ struct GemmPlan {
   int dual;      // SwiGLU dual B (W1 and W3 share the A tile)
   int bf16;      // 1: MFMA bf16 kernel; 0: fp32 kernel
   int bm, bn;    // tile (bf16 kernel: 128 or 256 each)
+  int nw;        // bf16 kernel: waves per workgroup (8, or 4 for 256 x 256 rows-mode tiles)
   int slots;     // dg partial slots written per row
   int n_tiles;   // tiles along N (SEG_M) or tiles per chunk (SEG_K)
   int out_f32;   // SEG_M EPI_STORE: c0 is fp32 (else the storage type)
