@@ -449,15 +449,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
   };
   constexpr int SA = MODE == SEG_K ? NA : 1, SB = MODE == SEG_K ? NB : 1;
   int gia[SA], gib[SB];
-  auto idx_fetch = [&](int j) SMOE_INL {
+  // reads for both operands, gathered or not (no branch: the general plans
+  // select the index or the plain row); the steady plans read only the
+  // gathered operand's
+  auto idx_fetch_of = [&](int j, auto want_a, auto want_b) SMOE_INL {
     if constexpr (MODE == SEG_K) {
-      // read for both operands, gathered or not (no branch: the copies
-      // select the index or the plain row)
       const int* slot = ring + (j % kRing) * 64;
-      static_for<NA>([&](auto t) SMOE_INL { gia[t] = slot[ka[t]]; });
-      static_for<NB>([&](auto t) SMOE_INL { gib[t] = slot[kb_[t]]; });
+      if constexpr (decltype(want_a)::value) static_for<NA>([&](auto t) SMOE_INL { gia[t] = slot[ka[t]]; });
+      if constexpr (decltype(want_b)::value) static_for<NB>([&](auto t) SMOE_INL { gib[t] = slot[kb_[t]]; });
     }
   };
+  auto idx_fetch = [&](int j) SMOE_INL { idx_fetch_of(j, std::true_type{}, std::true_type{}); };
 
   // ---------------- copies of one stage ------------------------------------
   // planA(kt) / planB(kt) set, for every copy of an operand at step kt, the
@@ -547,11 +549,34 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
     crb = (BLAY == LAY_K && p1) ? rB1 : rB0;
     csb = __builtin_amdgcn_readfirstlane(BLAY == LAY_K ? kl * 2 : kl * ldb2);
   };
+  // Weights mode, a stage of 64 rows that all lie inside the chunk: the
+  // gathered operand's copies take their rows' offsets from the indices,
+  // the plain operand's keep their lanes' offsets and advance by a scalar
+  // offset (no masks, no selects between the two forms).
+  auto planA_k = [&](int kt, auto gathered) SMOE_INL {
+    if constexpr (decltype(gathered)::value) {
+      static_for<NA>([&](auto t) SMOE_INL { cva[t] = uint32_t(fdiv(gia[t], p.a_fan_m, p.a_fan_s)) * lda2 + a_col[t]; });
+      csa = 0;
+    } else {
+      csa = __builtin_amdgcn_readfirstlane(uint32_t(it.row0 + kt * kBK) * lda2);
+    }
+  };
+  auto planB_k = [&](int kt, auto gathered) SMOE_INL {
+    if constexpr (decltype(gathered)::value) {
+      static_for<NB>([&](auto t) SMOE_INL { cvb[t] = uint32_t(fdiv(gib[t], p.b_fan_m, p.b_fan_s)) * ldb2 + b_col[t]; });
+      csb = 0;
+    } else {
+      // the copies that use it run at the next step's start, which may be
+      // a general step: keep the general form's lane offsets
+      static_for<NB>([&](auto t) SMOE_INL { cvb[t] = b_off[t]; });
+      csb = __builtin_amdgcn_readfirstlane(uint32_t(it.row0 + kt * kBK) * ldb2);
+    }
+  };
   // every copy instruction fills 1 KB of its operand's tile: 8 K-layout
-  // rows, or 64 / CPR MN-layout k-rows.  STEADY: the lane offsets at k = 0.
-  auto copyA = [&](auto c, char* buf, auto steady) SMOE_INL {
+  // rows, or 64 / CPR MN-layout k-rows.  BASE: the lane offsets at k = 0.
+  auto copyA = [&](auto c, char* buf, auto base) SMOE_INL {
     constexpr int C = decltype(c)::value;
-    dma16s(cra, buf + (C * NW + wave) * 1024, decltype(steady)::value ? a_off[C] : cva[C], csa);
+    dma16s(cra, buf + (C * NW + wave) * 1024, decltype(base)::value ? a_off[C] : cva[C], csa);
   };
   auto copyB = [&](auto c, char* buf, auto steady) SMOE_INL {
     constexpr int t = decltype(c)::value;
@@ -681,7 +706,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   constexpr std::false_type kMasked{};
-  constexpr std::true_type kSteady{};
+  // step forms: general; steady rows mode; steady weights mode with the B
+  // operand gathered (form 2, A gathered, is not instantiated)
+  constexpr std::integral_constant<int, 0> kGeneral{};
+  constexpr std::integral_constant<int, 1> kSteady{};
+  constexpr std::integral_constant<int, 3> kSteadyGB{};
   planA(0);
   static_for<NA>([&](auto c) SMOE_INL { copyA(c, abuf(I0{}), kMasked); });
   planB(0);
@@ -704,8 +733,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
   // One step kt (s = kt mod UNROLL picks the buffers).  STEADY (rows mode,
   // K parts whole multiples of the step, and stage kt+2 inside the
   // reduction): no masking and no per-copy conditions.
-  auto step = [&](auto s, const int kt, auto steady_c, const bool more_rt) SMOE_INL {
-        constexpr bool STEADY = decltype(steady_c)::value;
+  auto step = [&](auto s, const int kt, auto form, const bool more_rt) SMOE_INL {
+        constexpr int SC = decltype(form)::value;
+        constexpr bool STEADY = SC != 0;
+        // copies of A from the lanes' base offsets: steady rows mode, and
+        // steady weights mode with a plain A
+        constexpr std::integral_constant<bool, SC == 1 || SC == 3> a_base{};
+        constexpr std::integral_constant<bool, SC == 1> b_base{};
         using S1 = std::integral_constant<int, int(s) + 1>;
         using S2 = std::integral_constant<int, int(s) + 2>;
         const char* ca = abuf(s);
@@ -725,7 +759,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
               static_for<NA>([&](auto cc) SMOE_INL {
                 constexpr int c = decltype(cc)::value, pos = c * 3 * NM / NA;
                 if constexpr (pos / NM == decltype(sl)::value && pos % NM == I) {
-                  if (more) copyA(cc, abuf(S2{}), steady_c);
+                  if (more) copyA(cc, abuf(S2{}), a_base);
                 }
               });
             }
@@ -750,8 +784,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
           slice_sched(fa0, fb0, fa1, fb1, ca, cb, 3);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY) {
+        if constexpr (SC == 1) {
           planB_steady(kt + 2);
+        } else if constexpr (SC == 3) {
+          planA_k(kt + 2, std::false_type{});
+          planB_k(kt + 2, std::true_type{});
         } else if (more) {
           if constexpr (!A3) planA(kt + 2);
           planB(kt + 2);
@@ -775,8 +812,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
             constexpr int c = decltype(cc)::value;
             if constexpr (c * NM / LC == I) {
               if (more) {
-                if constexpr (A3) copyB(cc, bbuf(s), steady_c);
-                else if constexpr (c < NA) copyA(cc, abuf(s), kMasked);
+                if constexpr (A3) copyB(cc, bbuf(s), b_base);
+                else if constexpr (c < NA) copyA(cc, abuf(s), a_base);
                 else copyB(std::integral_constant<int, c - NA>{}, bbuf(s), kMasked);
               }
             }
@@ -784,7 +821,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
         };
         slice(fa1, fb1, fa0, fb0, na, nb, 0, lcp);
         if constexpr (MODE == SEG_K) {
-          if (kt + 3 < KT) idx_fetch(kt + 3);
+          if (kt + 3 < KT) idx_fetch_of(kt + 3, std::integral_constant<bool, SC != 3>{}, std::integral_constant<bool, SC != 2>{});
         }
   };
   int k0 = 0;
@@ -793,11 +830,23 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
       for (; k0 + UNROLL + 2 <= KT; k0 += UNROLL)
         static_for<UNROLL>([&](auto s) SMOE_INL { step(s, k0 + int(s), kSteady, true); });
     }
+  } else if constexpr (!GATED) {
+    // steady while stage kt+2 holds 64 rows of the chunk, for a plain A and
+    // a gathered B (the W2 weight gradient over the upstream gradient).  A
+    // gathered A (the weight gradients over x) takes the general form: its
+    // steady form measured 7 % slower (the extra registers it holds push an
+    // LDS address into scratch, and the reload before the loop costs a
+    // wait for every copy in flight on each pass)
+    const int KTF = K0 / kBK;
+    if (!p.a_scat && p.b_scat) {
+      for (; k0 + UNROLL + 2 <= KTF; k0 += UNROLL)
+        static_for<UNROLL>([&](auto s) SMOE_INL { step(s, k0 + int(s), kSteadyGB, true); });
+    }
   }
   for (; k0 < KT; k0 += UNROLL) {
     static_for<UNROLL>([&](auto s) SMOE_INL {
       const int kt = k0 + int(s);
-      if (kt < KT) step(s, kt, kMasked, kt + 2 < KT);
+      if (kt < KT) step(s, kt, kGeneral, kt + 2 < KT);
     });
   }
 
@@ -922,7 +971,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
     // while row fm is computed and stored.  Masked lanes read a clamped,
     // valid address.
     const int hh = lane >> 5;   // the half of the chunk pair a lane reads
-    uint4 rx0[2][FNR][2], rx1[2][AUX1 ? FNR : 1][2];
+    // 4 waves: twice the columns per lane, so one buffer (the accumulators
+    // already fill the AGPRs)
+    constexpr int NBUF = NW == 4 ? 1 : 2;
+    uint4 rx0[NBUF][FNR][2], rx1[NBUF][AUX1 ? FNR : 1][2];
     auto load_aux = [&](auto fm, auto buf) SMOE_INL {
       if constexpr (AUX0) {
         if (aux0_on) {
@@ -954,10 +1006,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
       });
     };
     auto unpack = [&](uint2 w, float v[4]) SMOE_INL { unpack4_bf16(w, v); };
-    load_aux(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    if constexpr (NBUF == 2) load_aux(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     static_for<FM>([&](auto fm) SMOE_INL {
-      constexpr int BUF = int(fm) & 1;
-      if constexpr (int(fm) + 1 < FM)
+      constexpr int BUF = int(fm) % NBUF;
+      if constexpr (NBUF == 1) load_aux(fm, std::integral_constant<int, 0>{});
+      else if constexpr (int(fm) + 1 < FM)
         load_aux(std::integral_constant<int, int(fm) + 1>{}, std::integral_constant<int, BUF ^ 1>{});
       const int rowbase = it.row0 + wm * WM + fm * 32;   // grouped row of lane 0 of the fragment row
       float dgacc = 0.f;
@@ -1097,7 +1150,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int MODE, int EPI, int BLAY, bool DUAL, class OutT>
 inline void go_bf16(const GemmArgs& a, const GemmPlan& pl, hipStream_t st) {
-  if constexpr (BM == 256 && BN == 256 && MODE == SEG_M) {
+  if constexpr (BM == 256 && BN == 256) {
     if (pl.nw == 4) {
       hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 4, MODE, EPI, BLAY, DUAL, OutT>), dim3(unsigned(pl.grid)),
                          dim3(256), 0, st, a);
