@@ -233,11 +233,13 @@ bool plan_gemm(GemmArgs& a, GemmPlan& pl, int mode, int epi, int dual, int bf16,
       const int ncols = dual ? pl.bn / 2 : pl.bn;
       pl.n_tiles = int(ceil_div(a.N, ncols));
       // 256 x 256 tiles of the dual (W1 | W3) forward and of the W^T product
-      // run as 4 waves, one per SIMD, each 128 x 128: a third fewer LDS
-      // fragment bytes per multiply than 8 waves of 128 x 64, which the
-      // power-limited clock turns into speed; epilogues that read operands
-      // (the activation backward) and the W2 forward measured faster with 8
-      if (pl.bm == 256 && pl.bn == 256 && (dual || (epi == EPI_STORE && a.b_nk))) pl.nw = 4;
+      // over long reductions run as 4 waves, one per SIMD, each 128 x 128: a
+      // third fewer LDS fragment bytes per multiply than 8 waves of 128 x 64,
+      // which the power-limited clock turns into speed.  Measured slower
+      // with 4: epilogues that read operands (the activation backward), the
+      // W2 forward, and short reductions (8 steps of 64: the tile's fill and
+      // epilogue, with no second wave per SIMD, cost 0.16 ms against 0.12)
+      if (pl.bm == 256 && pl.bn == 256 && a.K >= 4096 && (dual || (epi == EPI_STORE && a.b_nk))) pl.nw = 4;
       pl.slots = (pl.nw / 2) * pl.n_tiles;
       pl.grid = pad8(int64_t(a.mt_ub) * pl.n_tiles);
     } else {
