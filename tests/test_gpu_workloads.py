@@ -8,6 +8,9 @@ outputs:
 * high-granularity SMoE-MLP (T=16384, d_model=1024, d_ff=512, E=64, k=8,
   Zipf routing with empty experts, GELU): the same samples; empty experts
   get exactly zero weight gradients.
+* a mid-size SwiGLU SMoE-MLP (T=4096, d_model=4096, d_ff=2048, E=8, k=2)
+  that runs the 4-wave kernels under a steep Zipf routing (an empty
+  expert, experts smaller than one tile, one hot expert).
 * Mixture-of-Attention projections (T=8192, d_model=2048, 16 head experts
   of 128, k=4): Q = scattered-in / grouped-out, O = grouped-in /
   scattered-out with the gate-weighted combine, forward and backward.
@@ -28,16 +31,16 @@ import torch
 
 import oracle
 from tests.gpu_util import BF16_TOL, cols_covering, host, rel_err, say, tokens_covering_tiles, upload
-from workloads import make_config
+from workloads import make_config, make_mlp
 
 pytestmark = pytest.mark.gpu
 
 
 def _check_mlp_workload(smoe, cid, block, extra, seed, col_block=256):
-    w = make_config(cid)
+    w = make_config(cid) if isinstance(cid, int) else cid
     T, k, E = w.T, w.k, w.E
     d, f, act = w.dims["d_model"], w.dims["d_ff"], w.act
-    say(f"workload {cid}: T={T} d={d} d_ff={f} E={E} k={k} {act}")
+    say(f"workload {w.name}: T={T} d={d} d_ff={f} E={E} k={k} {act}")
     dd = upload(w, ["x", "w1", "w2", "w3", "expert_idxs", "gates", "dout"])
     out, saved = smoe.smoe_mlp_fwd(dd["x"], dd["w1"], dd["w2"], dd["expert_idxs"], dd["gates"], act,
                                    w3=dd.get("w3"))
@@ -85,6 +88,18 @@ def _check_mlp_workload(smoe, cid, block, extra, seed, col_block=256):
 
 def test_mixtral_shaped_mlp(smoe):
     _check_mlp_workload(smoe, 3, block=256, extra=8, seed=301)
+
+
+def test_four_wave_products_with_ragged_experts(smoe):
+    """The 4-wave 256 x 256 tiles (the dual W1 | W3 forward and the dX
+    product, both over reductions of 4096: d_model 4096, 2 d_ff = 4096, with
+    more than 512 tiles) under a steep Zipf routing: an empty expert, three
+    experts with fewer rows than one tile (54, 101, 177 rows), and one expert
+    holding half the assignments.  Every m-tile and every n-tile of the
+    weight gradients holds a checked value."""
+    w = make_mlp(4096, 4096, 2048, 8, 2, "swiglu", "bf16", 31, routing="zipf", w_std=0.02, zipf_s=3.0, n_dead=1)
+    counts = _check_mlp_workload(smoe, w, block=256, extra=8, seed=311)
+    assert (counts == 0).sum() == 1 and ((counts > 0) & (counts < 256)).sum() == 3 and counts.max() > 4000
 
 
 def test_high_granularity_zipf_mlp(smoe):
