@@ -1150,7 +1150,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int MODE, int EPI, int BLAY, bool DUAL, class OutT>
 inline void go_bf16(const GemmArgs& a, const GemmPlan& pl, hipStream_t st) {
-  if constexpr (BM == 256 && BN == 256) {
+  if constexpr (BM == 256 && BN == 256 && MODE == SEG_M) {
     if (pl.nw == 4) {
       hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 4, MODE, EPI, BLAY, DUAL, OutT>), dim3(unsigned(pl.grid)),
                          dim3(256), 0, st, a);
