@@ -230,16 +230,4 @@ SMOE_DEV int total_items(const int* __restrict__ offsets, int E, int unit) {
   return __builtin_amdgcn_readfirstlane(__shfl(wave_incl_scan(s), kWave - 1, kWave));
 }
 
-// Number of items of expert e and the index of its first item (one lane).
-SMOE_DEV void expert_items(const int* __restrict__ offsets, int e, int unit, int& first_item, int& n) {
-  int base = 0;
-  for (int i = 0; i < e; ++i) {
-    const int c = offsets[i + 1] - offsets[i];
-    base += (c + unit - 1) / unit;
-  }
-  const int c = offsets[e + 1] - offsets[e];
-  first_item = base;
-  n = (c + unit - 1) / unit;
-}
-
 }  // namespace smoe

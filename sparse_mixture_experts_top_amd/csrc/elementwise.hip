@@ -139,11 +139,23 @@ __global__ __launch_bounds__(kEwThreads) void reduce_dw_kernel(const float* __re
                                                                int all_partial, int accumulate) {
   __shared__ int first_s, n_s;
   const int e = blockIdx.y;
-  if (threadIdx.x == 0) {
-    int first, n;
-    expert_items(offsets, e, KS, first, n);
-    first_s = first;
-    n_s = n;
+  if (threadIdx.x < kWave) {
+    // chunks of the experts before e: one wave sums them 64 experts at a
+    // time (a serial walk by one thread made every block wait E loads)
+    const int lane = threadIdx.x;
+    int before = 0;
+    for (int i0 = 0; i0 < e; i0 += kWave) {
+      const int i = i0 + lane;
+      int items = 0;
+      if (i < e) items = (offsets[i + 1] - offsets[i] + KS - 1) / KS;
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) items += __shfl_xor(items, o, kWave);
+      before += items;
+    }
+    if (lane == 0) {
+      first_s = before;
+      n_s = (offsets[e + 1] - offsets[e] + KS - 1) / KS;
+    }
   }
   __syncthreads();
   const int first = first_s, n = n_s;
