@@ -69,6 +69,38 @@ def test_forward_backward_small(smoe, dtype, xg, yg, x_rows, use_gates):
     assert np.all(host(dw)[5:] == 0.0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_experts_split_weight_gradient(smoe, dtype):
+    """More than 64 experts (100, five of them empty) with about 490 rows
+    each: the grouped products' tile lookup takes its path for more than 64
+    experts, and the weight gradient splits every expert into row chunks
+    whose partials are summed by the reduction, which counts the chunks
+    before an expert 64 experts at a time."""
+    w = make_pl(24576, 128, 128, 100, 2, dtype, 121, x_std=1.0, w_std=0.1)
+    idx = w.tensors["expert_idxs"]
+    idx[idx >= 95] = (idx[idx >= 95] * 13) % 95
+    idx[:, 1] = np.where(idx[:, 0] == idx[:, 1], (idx[:, 0] + 1) % 95, idx[:, 1])
+    say(f"pl many experts {dtype}: E=100, counts {np.bincount(idx.ravel(), minlength=100)[[0, 63, 64, 99]]}")
+    x_np, rt = _setup(smoe, w, False, "T")
+    T, k = w.T, w.k
+    xd = dev_tensor(x_np)
+    wd = dev_tensor(w.tensors["w"])
+    y = smoe.smoe_parallel_linear_fwd(xd, wd, T, k, rt["sorted_scattered_idxs"], rt["offsets"], False, True, None)
+    dx, dw, _ = smoe.smoe_parallel_linear_bwd(xd, wd, T, k, rt["sorted_scattered_idxs"], rt["offsets"], False, True,
+                                              dev_tensor(w.tensors["dy"]), None, need_dgates=False)
+    torch.cuda.synchronize()
+    f = lambda n: w.f32(n).astype(np.float64)
+    ref = oracle.parallel_linear_fwd(f("x"), f("w"), idx, False, True)
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    storage = "bf16" if dtype == "bf16" else "f64"
+    rdx, rdw, _ = oracle.parallel_linear_bwd(f("x"), f("w"), idx, False, True, f("dy"), storage=storage)
+    for name, got, want in (("y", y, ref), ("dx", dx, rdx), ("dw", dw, rdw)):
+        e = rel_err(host(got), want)
+        say(f"  {name} err {e:.2e}")
+        assert e <= tol, name
+    assert np.all(host(dw)[95:] == 0.0)
+
+
 def _sample_tokens(T, n, seed):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n, replace=False)]))
